@@ -1,0 +1,481 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each test checks the oracle against something it does not compute itself: hand-worked
+examples from the pages' definitions (tests/golden/), exact cases, closed forms, library
+routines (numpy order statistics and quantiles, torch's scaled-dot-product attention), an
+exact-rational emulation of IEEE fp32 fused multiply-add, error bounds of fp32 summation,
+and invariants of the method.  None of these tests touches a GPU.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_causal_mean_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f32(x):
+    if isinstance(x, str):
+        return np.array([int(x, 16)], np.uint32).view(np.float32)[0]
+    return np.float32(x)
+
+
+def _small(**kw):
+    base = dict(name="t", batch=1, seqlen=512, n_q_heads=2, n_kv_heads=1, head_dim=32,
+                block=64, dtype=wl.F32, score_mode=wl.KMEAN, output_aware=0, k_max=2, k_min=2,
+                budget_kind=wl.BUDGET_CONST, n_sink=0, rho=2.0, q=0.25, seed=7)
+    base.update(kw)
+    return wl.Workload(**base)
+
+
+def _randn(shape, seed, dtype=torch.float32):
+    g = np.random.default_rng(seed)
+    return torch.from_numpy(g.standard_normal(shape).astype(np.float32)).to(dtype)
+
+
+# ------------------------------------------------------------------ exact fp32 emulation
+
+def _round_f32(x: Fraction) -> np.float32:
+    """Correctly rounded (nearest, ties to even) conversion of an exact rational to fp32."""
+    if x == 0:
+        return np.float32(0.0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    ulp = Fraction(2) ** (e - 23)
+    m = a / ulp
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return np.float32(sign * float(fl * ulp))
+
+
+def _fma_exact(a, b, c) -> np.float32:
+    return _round_f32(Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c)))
+
+
+def test_round_f32_helper_matches_numpy_on_sums():
+    # The emulation helper itself: exact sums of two floats rounded once equal numpy fp32 add.
+    g = np.random.default_rng(3)
+    for _ in range(200):
+        a, b = g.standard_normal(2).astype(np.float32) * np.float32(10.0) ** g.integers(-3, 3, 2)
+        a, b = np.float32(a), np.float32(b)
+        assert _round_f32(Fraction(float(a)) + Fraction(float(b))) == a + b
+
+
+@pytest.mark.parametrize("mode", [wl.KMEAN, wl.KMINMAX])
+def test_row_score_is_fp32_fma_chain(mode):
+    """Row scores equal an exact-rational emulation of the fused multiply-add chain."""
+    w = _small(head_dim=16, block=16, seqlen=64, score_mode=mode)
+    cfg = oracle.make_cfg(w)
+    Q = _randn((1, 64, 2, 16), 11)
+    K = _randn((1, 64, 1, 16), 12)
+    s = oracle.pool(cfg, K)
+    q = Q.numpy()
+    for (pos, h, j) in [(0, 0, 0), (17, 1, 1), (40, 0, 2), (63, 1, 3), (33, 0, 0)]:
+        want = np.float32(0.0)
+        for c in range(16):
+            qc = q[0, pos, h, c]
+            if mode == wl.KMEAN:
+                x = s["kA"][0, j, 0, c]
+            else:
+                x = s["kB"][0, j, 0, c] if qc >= 0 else s["kA"][0, j, 0, c]
+            want = _fma_exact(qc, x, want)
+        got = oracle.row_score(cfg, Q, s, 0, pos, h, j)
+        assert got.view(np.uint32) == want.view(np.uint32), (pos, h, j, got, want)
+
+
+def test_row_score_chain_differs_from_unfused():
+    # The pin above can tell fused from unfused arithmetic: on these inputs a multiply-then-add
+    # chain rounds differently somewhere.
+    g = np.random.default_rng(5)
+    q = g.standard_normal(128).astype(np.float32)
+    x = g.standard_normal(128).astype(np.float32)
+    fused, unfused = np.float32(0), np.float32(0)
+    for c in range(128):
+        fused = _fma_exact(q[c], x[c], fused)
+        unfused = np.float32(unfused + np.float32(q[c] * x[c]))
+    assert fused != unfused
+
+
+# ------------------------------------------------------------------------ summaries
+
+def test_pool_constant_keys_exact():
+    w = _small(head_dim=8, block=64, seqlen=256)
+    cfg = oracle.make_cfg(w)
+    vals = np.array([[0.5, -3.0, 7.25, 0.0, 1.0, -0.125, 2.0, 96.0]], np.float32)
+    K = np.empty((1, 256, 1, 8), np.float32)
+    for j in range(4):
+        K[0, j * 64:(j + 1) * 64, 0, :] = vals * (j + 1)
+    s = oracle.pool(cfg, torch.from_numpy(K))
+    for j in range(4):
+        np.testing.assert_array_equal(s["kA"][0, j, 0], vals[0] * (j + 1))
+    cfgb = oracle.make_cfg(w.resized(score_mode=wl.KMINMAX))
+    sb = oracle.pool(cfgb, torch.from_numpy(K))
+    np.testing.assert_array_equal(sb["kA"], sb["kB"])
+    np.testing.assert_array_equal(sb["kA"][0, 2, 0], vals[0] * 3)
+
+
+def test_pool_mean_within_fp32_sum_bound():
+    w = _small(head_dim=32, block=64, seqlen=512, dtype=wl.BF16)
+    cfg = oracle.make_cfg(w)
+    K = _randn((1, 512, 1, 32), 21, torch.bfloat16)
+    s = oracle.pool(cfg, K)
+    k64 = K.double().numpy().reshape(1, 8, 64, 1, 32)
+    exact = k64.mean(axis=2)
+    bound = 64 * 2.0 ** -24 * np.abs(k64).mean(axis=2) * 1.01
+    err = np.abs(s["kA"].astype(np.float64) - exact)
+    assert np.all(err <= bound + 1e-30)
+
+
+def test_pool_minmax_equal_library_min_max():
+    w = _small(head_dim=32, block=64, seqlen=512, dtype=wl.BF16, score_mode=wl.KMINMAX)
+    cfg = oracle.make_cfg(w)
+    K = _randn((1, 512, 1, 32), 22, torch.bfloat16)
+    s = oracle.pool(cfg, K)
+    k = K.float().numpy().reshape(1, 8, 64, 1, 32)
+    np.testing.assert_array_equal(s["kA"], k.min(axis=2) + np.float32(0))
+    np.testing.assert_array_equal(s["kB"], k.max(axis=2) + np.float32(0))
+
+
+def test_vnorm_exact_powers_of_two_and_library_norm():
+    w = _small(head_dim=16, block=64, seqlen=256, output_aware=1)
+    cfg = oracle.make_cfg(w)
+    V = np.zeros((1, 256, 1, 16), np.float32)
+    for j in range(4):
+        V[0, j * 64:(j + 1) * 64, 0, 3] = 2.0 ** (j - 1)
+    K = np.zeros_like(V)
+    s = oracle.pool(cfg, torch.from_numpy(K), torch.from_numpy(V))
+    np.testing.assert_array_equal(s["vn"][0, :, 0], np.float32([0.5, 1, 2, 4]))
+    Vr = _randn((1, 256, 1, 16), 23)
+    s2 = oracle.pool(cfg, torch.from_numpy(K), Vr)
+    ref = np.linalg.norm(Vr.double().numpy().reshape(4, 64, 16), axis=2).mean(axis=1)
+    np.testing.assert_allclose(s2["vn"][0, :, 0], ref, rtol=2e-6)
+
+
+# ---------------------------------------------------------------------- block scores
+
+def test_quest_bound_is_upper_bound():
+    """The K-min/K-max score bounds q.k for every key of the block (Quest backbone)."""
+    w = _small(head_dim=32, block=64, seqlen=512, dtype=wl.BF16, score_mode=wl.KMINMAX,
+               n_q_heads=1)
+    cfg = oracle.make_cfg(w)
+    Q = _randn((1, 512, 1, 32), 31, torch.bfloat16)
+    K = _randn((1, 512, 1, 32), 32, torch.bfloat16)
+    s = oracle.pool(cfg, K)
+    q, k = Q.double().numpy()[0, :, 0], K.double().numpy()[0, :, 0]
+    for pos in [0, 100, 300, 511]:
+        for j in range(8):
+            sc = float(oracle.row_score(cfg, Q, s, 0, pos, 0, j))
+            true_max = (k[j * 64:(j + 1) * 64] @ q[pos]).max()
+            slack = 40 * 2.0 ** -24 * np.abs(q[pos]) @ np.maximum(np.abs(s["kA"][0, j, 0]),
+                                                                   np.abs(s["kB"][0, j, 0]))
+            assert true_max <= sc + slack
+            # and it is attained when the block holds a single distinct key
+    Kc = np.repeat(K.float().numpy()[:, ::64], 64, axis=1)
+    s1 = oracle.pool(cfg, torch.from_numpy(Kc).to(torch.bfloat16))
+    for pos in [5, 400]:
+        for j in range(8):
+            sc = float(oracle.row_score(cfg, Q, s1, 0, pos, 0, j))
+            exact = float(Kc[0, j * 64, 0].astype(np.float64) @ q[pos])
+            assert abs(sc - exact) <= 40 * 2.0 ** -24 * np.abs(q[pos]) @ np.abs(Kc[0, j * 64, 0])
+
+
+def test_mean_pool_score_is_mean_of_dot_products():
+    w = _small(head_dim=32, block=64, seqlen=512, dtype=wl.BF16, n_q_heads=1)
+    cfg = oracle.make_cfg(w)
+    Q = _randn((1, 512, 1, 32), 41, torch.bfloat16)
+    K = _randn((1, 512, 1, 32), 42, torch.bfloat16)
+    s = oracle.pool(cfg, K)
+    q, k = Q.double().numpy()[0, :, 0], K.double().numpy()[0, :, 0]
+    for pos in [3, 260, 511]:
+        for j in range(8):
+            sc = float(oracle.row_score(cfg, Q, s, 0, pos, 0, j))
+            exact = (k[j * 64:(j + 1) * 64] @ q[pos]).mean()
+            bound = 100 * 2.0 ** -24 * (np.abs(q[pos]) @ np.abs(k[j * 64:(j + 1) * 64]).mean(0))
+            assert abs(sc - exact) <= bound + 1e-12
+
+
+def test_tile_score_is_max_over_rows_of_emulated_chain():
+    w = _small(head_dim=8, block=16, seqlen=64, n_q_heads=1)
+    cfg = oracle.make_cfg(w)
+    Q = _randn((1, 64, 1, 8), 51)
+    K = _randn((1, 64, 1, 8), 52)
+    s = oracle.pool(cfg, K)
+    q = Q.numpy()[0, :, 0]
+    t = 3
+    S = oracle.tile_scores(cfg, Q, s, 0, 0, t)
+    assert np.isnan(S[t])
+    for j in range(t):
+        rows = []
+        for i in range(t * 16, t * 16 + 16):
+            acc = np.float32(0)
+            for c in range(8):
+                acc = _fma_exact(q[i, c], s["kA"][0, j, 0, c], acc)
+            rows.append(acc)
+        assert S[j] == max(rows) + np.float32(0)
+
+
+# ---------------------------------------------------------------- constructed selection
+
+def _constructed(output_aware=0, vscale=1.0):
+    g = json.load(open(os.path.join(GOLDEN, "constructed_selection.json")))
+    w = _small(seqlen=512, n_q_heads=2, n_kv_heads=1, head_dim=64, block=64, k_max=g["k"],
+               k_min=g["k"], rho=g["rho"], q=g["q"], output_aware=output_aware)
+    Q = np.zeros((1, 512, 2, 64), np.float32)
+    Q[0, :, 0, 0] = 1.0
+    Q[0, :, 1, 1] = 1.0
+    K = np.zeros((1, 512, 1, 64), np.float32)
+    for j in range(8):
+        K[0, j * 64:(j + 1) * 64, 0, 0] = g["c"][j]
+        K[0, j * 64:(j + 1) * 64, 0, 1] = g["d"][j]
+    V = np.zeros_like(K)
+    V[0, :, 0, 5] = vscale
+    return g, w, torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V)
+
+
+@pytest.mark.parametrize("oam", [0, 1])
+def test_constructed_selection_golden(oam):
+    g, w, Q, K, V = _constructed(output_aware=oam, vscale=4.0)
+    cfg = oracle.make_cfg(w)
+    assert cfg.width == 5
+    s = oracle.pool(cfg, K, V)
+    out = oracle.select(cfg, Q, s)
+    want_sigma = np.array([[_f32(x) for x in row] for row in g["sigma"]], np.float32)
+    np.testing.assert_array_equal(out["sigma"][0].view(np.uint32), want_sigma.view(np.uint32))
+    want_sbar = np.array([_f32(x) for x in g["sigma_bar"]], np.float32)
+    np.testing.assert_array_equal(out["sigma_bar"][0].view(np.uint32), want_sbar.view(np.uint32))
+    assert out["tau"][0] == np.float32(g["tau"])
+    np.testing.assert_array_equal(out["gate"][0], g["gate"])
+    np.testing.assert_array_equal(out["kv_idx"][0], g["kv_idx"])
+    np.testing.assert_array_equal(out["kv_cnt"][0], g["kv_cnt"])
+    # The one-tile entry point agrees with the whole selection.
+    for t in range(8):
+        one = oracle.select_tile(cfg, Q, s, 0, t)
+        np.testing.assert_array_equal(one["sigma"], out["sigma"][0, :, t])
+        assert one["sigma_bar"] == out["sigma_bar"][0, t]
+        tr = int(out["gate"][0, t])
+        np.testing.assert_array_equal(one["lists"][tr], out["kv_idx"][0, :, t])
+        np.testing.assert_array_equal(one["cnts"][tr], out["kv_cnt"][0, :, t])
+
+
+def test_budget_schedule_golden():
+    g = json.load(open(os.path.join(GOLDEN, "budget_schedule.json")))
+    w = wl.WORKLOADS["stem_32k"]
+    assert w.n_blocks == g["n"]
+    cfg = oracle.make_cfg(w)
+    assert [oracle.budget(cfg, t) for t in g["t"]] == g["k"]
+    # constant budget
+    assert oracle.budget(oracle.make_cfg(wl.WORKLOADS["llama8b_32k"]), 300) == 32
+
+
+def test_index_widths():
+    assert [wl.WORKLOADS[n].index_width() for n in wl.WORKLOAD_ORDER] == [9, 65, 129, 97, 131]
+
+
+# --------------------------------------------------------------- random-input invariants
+
+def _random_case(seed, **kw):
+    w = _small(**kw)
+    cfg = oracle.make_cfg(w)
+    dt = torch.bfloat16 if w.dtype == wl.BF16 else torch.float32
+    Q = _randn((w.batch, w.seqlen, w.n_q_heads, w.head_dim), seed, dt)
+    K = _randn((w.batch, w.seqlen, w.n_kv_heads, w.head_dim), seed + 1, dt)
+    V = _randn((w.batch, w.seqlen, w.n_kv_heads, w.head_dim), seed + 2, dt)
+    s = oracle.pool(cfg, K, V)
+    return w, cfg, Q, K, V, s
+
+
+CASES = [
+    dict(seed=100, batch=2, seqlen=1024, n_q_heads=4, n_kv_heads=2, head_dim=16, block=32,
+         k_max=3, k_min=3, q=0.3),
+    dict(seed=200, batch=1, seqlen=1024, n_q_heads=2, n_kv_heads=1, head_dim=16, block=32,
+         k_max=6, k_min=2, budget_kind=wl.BUDGET_LINEAR_DECAY, n_sink=2, output_aware=1,
+         q=0.1, dtype=wl.BF16),
+    dict(seed=300, batch=1, seqlen=768, n_q_heads=4, n_kv_heads=4, head_dim=16, block=32,
+         k_max=4, k_min=4, score_mode=wl.KMINMAX, q=0.5, dtype=wl.BF16),
+    dict(seed=400, batch=1, seqlen=512, n_q_heads=2, n_kv_heads=1, head_dim=16, block=32,
+         k_max=2, k_min=2, rho=3.5, q=1.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_selection_invariants(case):
+    case = dict(case)
+    seed = case.pop("seed")
+    w, cfg, Q, K, V, s = _random_case(seed, **case)
+    out = oracle.select(cfg, Q, s)
+    n, W = w.n_blocks, cfg.width
+    for b in range(w.batch):
+        elig = np.zeros(n, bool)
+        for t in range(n):
+            forced = {t} | set(range(min(w.n_sink, t)))
+            nfree = t + 1 - len(forced)
+            kt = oracle.budget(cfg, t)
+            elig[t] = nfree > kt
+            for h in range(w.n_q_heads):
+                lst = out["kv_idx"][b, h, t]
+                cnt = out["kv_cnt"][b, h, t]
+                got = lst[:cnt]
+                assert np.all(lst[cnt:] == -1)
+                assert np.all(np.diff(got) > 0) and got[0] >= 0 and got[-1] == t  # diagonal
+                assert forced <= set(got.tolist())
+                tr = out["gate"][b, t]
+                keep = min(int(math.floor(w.rho * kt)) if tr else kt, nfree)
+                assert cnt == len(forced) + keep <= W
+                sg = out["sigma"][b, h, t]
+                assert 0.0 <= sg <= 1.0
+                if not elig[t]:
+                    assert sg == 1.0
+        # quantile gate vs numpy's inverted-CDF quantile over the eligible tiles
+        sb = out["sigma_bar"][b]
+        M = int(elig.sum())
+        if w.q > 0 and M > 0:
+            tau = np.quantile(sb[elig], w.q, method="inverted_cdf")
+            assert out["tau"][b] == np.float32(tau)
+            np.testing.assert_array_equal(out["gate"][b], (elig & (sb <= tau)).astype(np.uint8))
+            assert out["gate"][b].sum() >= math.ceil(w.q * M)
+        # sigma_bar is the fp32 head mean
+        acc = np.zeros(n, np.float32)
+        for h in range(w.n_q_heads):
+            acc = acc + out["sigma"][b, h]
+        np.testing.assert_array_equal(sb, acc / np.float32(w.n_q_heads))
+
+
+def test_selection_top_k_is_brute_force_ranking():
+    """Kept free blocks are exactly the top of a full stable sort of the tile scores."""
+    w, cfg, Q, K, V, s = _random_case(500, seqlen=512, head_dim=16, block=32, k_max=3, k_min=3,
+                                      n_q_heads=2, n_kv_heads=1, q=0.4)
+    out = oracle.select(cfg, Q, s)
+    for h in range(2):
+        for t in range(w.n_blocks):
+            S = oracle.tile_scores(cfg, Q, s, 0, h, t)
+            free = [j for j in range(t + 1) if j != t]
+            order = sorted(free, key=lambda j: (-S[j], j))
+            keep = len(out["kv_idx"][0, h, t][:out["kv_cnt"][0, h, t]]) - 1
+            assert sorted(order[:keep] + [t]) == out["kv_idx"][0, h, t][:keep + 1].tolist()
+            if len(free) > 3:
+                a, b, c = S[order[0]], S[order[2]], S[order[3]]
+                want = np.float32(0) if a == c else np.float32(b - c) / np.float32(a - c)
+                assert out["sigma"][0, h, t] == want
+
+
+def test_gate_special_cases():
+    base = dict(seqlen=768, head_dim=16, block=32, k_max=3, k_min=3, n_q_heads=2, n_kv_heads=1)
+    w, cfg, Q, K, V, s = _random_case(600, q=0.0, **base)
+    none = oracle.select(cfg, Q, s)
+    assert none["gate"].sum() == 0 and none["tau"][0] == -np.inf
+    off = oracle.select(oracle.make_cfg(w, gate_mode=wl.GATE_OFF, q=0.7), Q, s)
+    np.testing.assert_array_equal(off["kv_idx"], none["kv_idx"])
+    allq = oracle.select(oracle.make_cfg(w, q=1.0), Q, s)
+    elig = np.array([t > 3 for t in range(w.n_blocks)])
+    np.testing.assert_array_equal(allq["gate"][0], elig.astype(np.uint8))
+    r1 = oracle.select(oracle.make_cfg(w, q=1.0, rho=1.0), Q, s)
+    np.testing.assert_array_equal(r1["kv_cnt"], none["kv_cnt"])
+    np.testing.assert_array_equal(r1["kv_idx"], none["kv_idx"][..., :r1["kv_idx"].shape[-1]])
+    assert np.all(none["kv_idx"][..., r1["kv_idx"].shape[-1]:] == -1)
+    fixed = oracle.select(oracle.make_cfg(w, gate_mode=wl.GATE_FIXED, tau_fixed=0.5), Q, s)
+    np.testing.assert_array_equal(fixed["gate"][0],
+                                  (elig & (fixed["sigma_bar"][0] <= 0.5)).astype(np.uint8))
+
+
+def test_output_aware_exact_scaling_leaves_selection_unchanged():
+    w, cfg, Q, K, V, s = _random_case(700, seqlen=768, head_dim=16, block=32, k_max=3, k_min=3,
+                                      n_q_heads=2, n_kv_heads=1)
+    plain = oracle.select(cfg, Q, s)
+    V2 = torch.zeros_like(V)
+    V2[..., 0] = 8.0
+    cfg2 = oracle.make_cfg(w, output_aware=1)
+    s2 = oracle.pool(cfg2, K, V2)
+    np.testing.assert_array_equal(s2["vn"], 8.0)
+    oam = oracle.select(cfg2, Q, s2)
+    for key in ("kv_idx", "kv_cnt", "sigma", "gate"):
+        np.testing.assert_array_equal(oam[key], plain[key])
+
+
+# --------------------------------------------------------------------------- attention
+
+def _dense_sdpa(Q, K, V, scale):
+    B, N, Hq, d = Q.shape
+    G = Hq // K.shape[2]
+    q = Q.double().permute(0, 2, 1, 3)
+    k = K.double().repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    v = V.double().repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=scale)
+    logits = (q @ k.transpose(-1, -2)) * scale
+    mask = torch.ones(N, N, dtype=torch.bool).tril()
+    lse = torch.logsumexp(logits.masked_fill(~mask, -math.inf), dim=-1)
+    return o.permute(0, 2, 1, 3).numpy(), lse.permute(0, 2, 1).numpy()
+
+
+def test_attention_dense_limit_equals_library_sdpa():
+    """k covering every block reduces the sparse pass to dense causal attention."""
+    w, cfg, Q, K, V, s = _random_case(800, batch=2, seqlen=512, n_q_heads=4, n_kv_heads=2,
+                                      head_dim=32, block=32, k_max=16, k_min=16)
+    out = oracle.select(cfg, Q, s)
+    n = w.n_blocks
+    assert np.all(out["kv_cnt"][..., :] == np.arange(1, n + 1))
+    scale = 1.0 / math.sqrt(32)
+    O, lse = oracle.forward(cfg, Q, K, V, out["kv_idx"], out["kv_cnt"], scale)
+    Od, lsed = _dense_sdpa(Q, K, V, np.float32(scale).item())
+    np.testing.assert_allclose(O, Od, atol=1e-12, rtol=1e-10)
+    np.testing.assert_allclose(lse, lsed, atol=1e-12, rtol=1e-10)
+
+
+def test_attention_equals_masked_dense_softmax():
+    w, cfg, Q, K, V, s = _random_case(900, seqlen=512, n_q_heads=2, n_kv_heads=1, head_dim=16,
+                                      block=32, k_max=3, k_min=3)
+    out = oracle.select(cfg, Q, s)
+    scale = 0.25
+    O, lse = oracle.forward(cfg, Q, K, V, out["kv_idx"], out["kv_cnt"], scale)
+    q, k, v = Q.double().numpy()[0], K.double().numpy()[0, :, 0], V.double().numpy()[0, :, 0]
+    N = w.seqlen
+    for h in range(2):
+        mask = np.zeros((N, N), bool)
+        for t in range(w.n_blocks):
+            for j in out["kv_idx"][0, h, t][:out["kv_cnt"][0, h, t]]:
+                mask[t * 32:(t + 1) * 32, j * 32:(j + 1) * 32] = True
+        mask &= np.tri(N, dtype=bool)
+        z = np.where(mask, (q[:, h] @ k.T) * scale, -np.inf)
+        p = np.exp(z - z.max(1, keepdims=True))
+        ref = (p / p.sum(1, keepdims=True)) @ v
+        np.testing.assert_allclose(O[0, :, h], ref, atol=1e-12, rtol=1e-10)
+
+
+def test_attention_invariants():
+    w, cfg, Q, K, V, s = _random_case(1000, seqlen=512, n_q_heads=2, n_kv_heads=1, head_dim=16,
+                                      block=32, k_max=3, k_min=3)
+    out = oracle.select(cfg, Q, s)
+    O, _ = oracle.forward(cfg, Q, K, V, out["kv_idx"], out["kv_cnt"], 0.25)
+    # row 0 attends only to itself
+    np.testing.assert_allclose(O[0, 0, :, :], V.double().numpy()[0, 0, [0, 0], :], atol=1e-15)
+    # constant value rows give that constant everywhere
+    Vc = torch.ones_like(V) * 3.5
+    Oc, _ = oracle.forward(cfg, Q, K, Vc, out["kv_idx"], out["kv_cnt"], 0.25)
+    np.testing.assert_allclose(Oc, 3.5, atol=1e-13)
+    # block order does not matter (online softmax is permutation invariant)
+    rev = out["kv_idx"].copy()
+    for idx in np.ndindex(rev.shape[:3]):
+        c = out["kv_cnt"][idx]
+        rev[idx][:c] = rev[idx][:c][::-1]
+    Or, _ = oracle.forward(cfg, Q, K, V, rev, out["kv_cnt"], 0.25)
+    np.testing.assert_allclose(Or, O, atol=1e-13)
+    # a sampled-row call equals the full call
+    rows = np.array([[0, 1, 5], [0, 0, 511], [0, 1, 300]], np.int64)
+    Os, _ = oracle.forward(cfg, Q, K, V, out["kv_idx"], out["kv_cnt"], 0.25, rows=rows)
+    for r, (b, h, p) in enumerate(rows):
+        np.testing.assert_array_equal(Os[r], O[b, p, h])
