@@ -1,0 +1,224 @@
+"""Throughput of one block-sparse prefill attention layer on one MI355X.
+
+A step is one pass of the whole hot path over one batch: sparse_attn_score (block
+summaries), sparse_attn_select (scores, top-k, cut margin, gate, lists) and
+sparse_attn_forward (online-softmax attention over the selected blocks), on inputs already
+resident in HBM.  The workload is the 128K-token prefill (1 x 131072 tokens, 32 q / 8 kv
+heads, d = 128, bf16, block = tile = 128, k = 64, rho = 2, q = 0.1) unless --workload names
+another.  Prints ONE JSON line on stdout; progress goes to stderr.
+
+  value         tokens/s = B * N * steps / timed seconds
+  roofline      the attention kernel (the dominant one) against bf16 matrix-core peak, on
+                effective FLOPs (4 * tile * block * d per listed block), timed with HIP
+                events on the stream it runs on
+  score_roofline  the block-summary kernel against HBM peak (algorithmic bytes: keys read
+                once, summaries written once), timed after evicting the caches
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload (see "sample")
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from block_sparse_causal_mean_amd import api  # noqa: E402
+from block_sparse_causal_mean_amd import workloads as wl  # noqa: E402
+
+METRIC = "sparse prefill attn tokens/s at 128k (1 GPU); % bf16 MFMA peak; HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def traffic_from_profiles(name: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if recorded for this kernel
+    source (profiles/<name>.json carries the source digest it was measured on)."""
+    path = os.path.join(ROOT, "profiles", name + ".json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "block_sparse_causal_mean_amd", "csrc", rec.get("source", ""))
+    if not os.path.exists(src):
+        return None
+    import hashlib
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if digest != rec.get("source_sha256"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def effective_flops(w: wl.Workload, kv_cnt: torch.Tensor) -> float:
+    return 4.0 * w.tile * w.block * w.head_dim * float(kv_cnt.sum().item())
+
+
+def time_score_cold(pf: api.Prefill, K, V, reps: int = 10) -> float:
+    """Mean duration (ms) of the summary kernel(s) with the caches evicted before each run."""
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream()
+    total = 0.0
+    for _ in range(reps):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        pf.score(K, V)
+        e1.record(s)
+        e1.synchronize()
+        total += e0.elapsed_time(e1)
+    del flush
+    return total / reps
+
+
+def cpu_baseline(w: wl.Workload, inp, n_tiles: int = 6) -> dict:
+    """The oracle on a bounded sample: block summaries of the whole sequence, then the
+    selection and the attention of every row of `n_tiles` query tiles spread over the
+    sequence (all heads), with the untripped budget."""
+    import oracle
+    cfg = oracle.make_cfg(w)
+    threads = oracle.threads()
+    t0 = time.perf_counter()
+    summ = oracle.pool(cfg, inp["K"], inp["V"])
+    t_pool = time.perf_counter() - t0
+    n = w.n_blocks
+    tiles = sorted(set(int(x) for x in np.linspace(n // 4, n - 1, n_tiles)))
+    t_sel = t_fwd = 0.0
+    for t in tiles:
+        b = 0
+        t1 = time.perf_counter()
+        one = oracle.select_tile(cfg, inp["Q"], summ, b, t)
+        t_sel += time.perf_counter() - t1
+        rows = np.array([(b, h, p) for h in range(w.n_q_heads)
+                         for p in range(t * w.tile, (t + 1) * w.tile)], np.int64)
+        idx = np.zeros((w.batch, w.n_q_heads, n, cfg.width), np.int32)
+        cnt = np.zeros((w.batch, w.n_q_heads, n), np.int32)
+        idx[b, :, t] = one["lists"][0]
+        cnt[b, :, t] = one["cnts"][0]
+        t1 = time.perf_counter()
+        oracle.forward(cfg, inp["Q"], inp["K"], inp["V"], idx, cnt, 1.0 / math.sqrt(w.head_dim),
+                       rows=rows)
+        t_fwd += time.perf_counter() - t1
+        log(f"  cpu oracle tile {t}: select {t_sel:.1f}s forward {t_fwd:.1f}s")
+    tok = len(tiles) * w.tile
+    per_token = t_pool / (w.batch * w.seqlen) + (t_sel + t_fwd) / tok
+    return {
+        "value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": (f"block summaries of all {w.batch * w.seqlen} tokens ({t_pool:.2f}s), then "
+                   f"selection + attention of every row of {len(tiles)} query tiles "
+                   f"{tiles} x {w.n_q_heads} heads ({tok} tokens, {t_sel:.2f}s + {t_fwd:.2f}s); "
+                   f"tokens/s = 1 / (pool s per token + tile s per token)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=wl.HEADLINE, choices=wl.WORKLOAD_ORDER)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design note, not a measured configuration.",
+              file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    w = wl.WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}: generating inputs")
+    t0 = time.perf_counter()
+    inp = wl.make_inputs(w)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s; copying to the GPU")
+    torch.cuda.set_device(0)
+    dev = {k: v.cuda() for k, v in inp.items()}
+    Q, K, V = dev["Q"], dev["K"], dev["V"]
+    pf = api.Prefill(w, keep_stats=True)
+    s = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        pf.run(Q, K, V)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup steps done")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(s)
+        pf.score(K, V)
+        ev[i][1].record(s)
+        pf.select(Q)
+        ev[i][2].record(s)
+        pf.forward(Q, K, V)
+        ev[i][3].record(s)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    stage = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(3)]
+                      for i in range(args.steps)])
+    ms_score, ms_select, ms_fwd = stage.mean(axis=0)
+    log(f"[bench] {args.steps} steps in {elapsed:.3f}s: score {ms_score:.3f} ms, select "
+        f"{ms_select:.3f} ms, forward {ms_fwd:.3f} ms")
+
+    tokens = w.batch * w.seqlen
+    value = tokens * args.steps / elapsed
+    flops = effective_flops(w, pf.kv_cnt)
+    achieved = flops / (ms_fwd * 1e-3) / 1e12
+    dense = 4.0 * w.head_dim * w.seqlen * (w.seqlen + 1) / 2 * w.batch * w.n_q_heads
+    traffic = traffic_from_profiles("attn_fwd_" + w.name)
+
+    ms_cold = time_score_cold(pf, K, V)
+    kv_bytes = w.batch * w.seqlen * w.n_kv_heads * w.head_dim * 2
+    score_bytes = kv_bytes * (2 if w.output_aware else 1) + pf.summ.numel() * 4
+    score_gbs = score_bytes / (ms_cold * 1e-3) / 1e9
+
+    gate = pf.gate.float().mean().item()
+    density = float(pf.kv_cnt.sum().item()) / (w.batch * w.n_q_heads * w.n_blocks *
+                                               (w.n_blocks + 1) / 2)
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen,
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "block": w.block, "tile": w.tile,
+                   "score_mode": "kminmax" if w.score_mode == wl.KMINMAX else "kmean",
+                   "output_aware": bool(w.output_aware), "k_max": w.k_max, "k_min": w.k_min,
+                   "budget": "linear_decay" if w.budget_kind else "const", "n_sink": w.n_sink,
+                   "rho": w.rho, "q": w.q, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "kernel": "attn_bf16 (sparse_attn_forward)",
+                     "flops_per_launch": flops, "ms_per_launch": ms_fwd},
+        "score_roofline": {"bound": "hbm", "achieved": score_gbs, "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": score_gbs / PEAK_HBM_GBS,
+                           "bytes_per_launch": score_bytes, "ms_per_launch_cold": ms_cold,
+                           "kernel": "pool_keys (sparse_attn_score)"},
+        "stages_ms": {"score": ms_score, "select": ms_select, "forward": ms_fwd},
+        "selection": {"density_of_causal": density, "trip_fraction": gate,
+                      "dense_causal_flops": dense, "effective_flops": flops},
+    }
+    if not args.no_cpu_baseline and rank == 0:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    else:
+        out["cpu_baseline"] = None
+    if rank == 0:
+        print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,233 @@
+"""Python binding of libsparse_attn.so (the C ABI in include/sparse_attn.h).
+
+Argument marshalling only: torch tensors supply device memory and the current HIP stream;
+every step of the method runs in the library's HIP kernels.  The library must have been
+built (``python -m block_sparse_causal_mean_amd.build`` or ``__graft_entry__.build()``);
+there is no fallback, so a missing or unloadable library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+from . import workloads as wl
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
+
+SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_HIP = 0, -1, -2, -3
+SA_F32, SA_BF16 = 0, 1
+SA_KMEAN, SA_KMINMAX = 0, 1
+SA_K_CONST, SA_K_LINEAR_DECAY = 0, 1
+SA_GATE_QUANTILE, SA_GATE_FIXED, SA_GATE_OFF = 0, 1, 2
+
+# Every function the header declares, checked by the tests against the built library.
+EXPORTS = ("sparse_attn_summary_bytes", "sparse_attn_select_workspace_bytes",
+           "sparse_attn_index_width", "sparse_attn_score", "sparse_attn_select",
+           "sparse_attn_forward", "sparse_attn_last_error")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in (
+        "batch", "seqlen", "n_q_heads", "n_kv_heads", "head_dim", "block", "tile", "dtype",
+        "score_mode", "output_aware")]
+
+
+class Budget(ctypes.Structure):
+    _fields_ = [("k_max", ctypes.c_int32), ("k_min", ctypes.c_int32), ("kind", ctypes.c_int32),
+                ("n_sink", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
+                ("tau_fixed", ctypes.c_float), ("rho", ctypes.c_double), ("q", ctypes.c_double)]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"status {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads the HIP library (raises if it is missing: there is no other code path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build the HIP extension first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, PP, PB = ctypes.c_void_p, ctypes.POINTER(Problem), ctypes.POINTER(Budget)
+    lib.sparse_attn_summary_bytes.argtypes = [PP]
+    lib.sparse_attn_summary_bytes.restype = ctypes.c_size_t
+    lib.sparse_attn_select_workspace_bytes.argtypes = [PP, PB]
+    lib.sparse_attn_select_workspace_bytes.restype = ctypes.c_size_t
+    lib.sparse_attn_index_width.argtypes = [PP, PB]
+    lib.sparse_attn_index_width.restype = ctypes.c_int32
+    lib.sparse_attn_score.argtypes = [PP, P, P, P, P]
+    lib.sparse_attn_select.argtypes = [PP, PB, P, P, P, ctypes.c_size_t, P, P, P, P, P, P, P]
+    lib.sparse_attn_forward.argtypes = [PP, P, P, P, P, P, ctypes.c_int32, ctypes.c_float, P,
+                                        ctypes.c_int32, P, P]
+    lib.sparse_attn_last_error.argtypes = []
+    lib.sparse_attn_last_error.restype = ctypes.c_char_p
+    for f in ("sparse_attn_score", "sparse_attn_select", "sparse_attn_forward"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().sparse_attn_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != SA_OK:
+        raise SparseAttnError(rc, last_error())
+
+
+def problem(w: wl.Workload) -> Problem:
+    return Problem(batch=w.batch, seqlen=w.seqlen, n_q_heads=w.n_q_heads,
+                   n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, block=w.block, tile=w.tile,
+                   dtype=w.dtype, score_mode=w.score_mode, output_aware=w.output_aware)
+
+
+def budget(w: wl.Workload) -> Budget:
+    return Budget(k_max=w.k_max, k_min=w.k_min, kind=w.budget_kind, n_sink=w.n_sink,
+                  gate_mode=w.gate_mode, tau_fixed=w.tau_fixed, rho=w.rho, q=w.q)
+
+
+def summary_bytes(p: Problem) -> int:
+    n = load().sparse_attn_summary_bytes(ctypes.byref(p))
+    if n == 0:
+        _check(SA_ERR_INVALID)
+    return n
+
+
+def select_workspace_bytes(p: Problem, b: Budget) -> int:
+    n = load().sparse_attn_select_workspace_bytes(ctypes.byref(p), ctypes.byref(b))
+    if n == 0:
+        _check(SA_ERR_INVALID)
+    return n
+
+
+def index_width(p: Problem, b: Budget) -> int:
+    w = load().sparse_attn_index_width(ctypes.byref(p), ctypes.byref(b))
+    _check(min(w, 0))
+    return w
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, nbytes: Optional[int] = None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _elt(p: Problem) -> int:
+    return 4 if p.dtype == SA_F32 else 2
+
+
+def score(p: Problem, K: torch.Tensor, V: Optional[torch.Tensor], summaries: torch.Tensor,
+          stream=None):
+    kv = p.batch * p.seqlen * p.n_kv_heads * p.head_dim * _elt(p)
+    _check(load().sparse_attn_score(ctypes.byref(p), _ptr(K, "K", kv), _ptr(V, "V", kv),
+                                    _ptr(summaries, "summaries", summary_bytes(p)),
+                                    _stream(stream)))
+
+
+def select(p: Problem, b: Budget, Q: torch.Tensor, summaries: torch.Tensor, ws: torch.Tensor,
+           kv_idx: torch.Tensor, kv_cnt: torch.Tensor, sigma=None, sigma_bar=None, gate=None,
+           tau=None, stream=None):
+    n = p.seqlen // p.block
+    bhn = p.batch * p.n_q_heads * n
+    W = index_width(p, b)
+    _check(load().sparse_attn_select(
+        ctypes.byref(p), ctypes.byref(b),
+        _ptr(Q, "Q", p.batch * p.seqlen * p.n_q_heads * p.head_dim * _elt(p)),
+        _ptr(summaries, "summaries", summary_bytes(p)), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _ptr(kv_idx, "kv_idx", bhn * W * 4),
+        _ptr(kv_cnt, "kv_cnt", bhn * 4), _ptr(sigma, "sigma", bhn * 4),
+        _ptr(sigma_bar, "sigma_bar", p.batch * n * 4), _ptr(gate, "gate", p.batch * n),
+        _ptr(tau, "tau", p.batch * 4), _stream(stream)))
+
+
+def forward(p: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+            kv_idx: torch.Tensor, kv_cnt: torch.Tensor, W: int, softmax_scale: float,
+            O: torch.Tensor, out_dtype: int, lse: Optional[torch.Tensor] = None, stream=None):
+    n = p.seqlen // p.block
+    q_bytes = p.batch * p.seqlen * p.n_q_heads * p.head_dim
+    kv = p.batch * p.seqlen * p.n_kv_heads * p.head_dim * _elt(p)
+    _check(load().sparse_attn_forward(
+        ctypes.byref(p), _ptr(Q, "Q", q_bytes * _elt(p)), _ptr(K, "K", kv), _ptr(V, "V", kv),
+        _ptr(kv_idx, "kv_idx", p.batch * p.n_q_heads * n * W * 4),
+        _ptr(kv_cnt, "kv_cnt", p.batch * p.n_q_heads * n * 4), W, softmax_scale,
+        _ptr(O, "O", q_bytes * (4 if out_dtype == SA_F32 else 2)), out_dtype,
+        _ptr(lse, "lse", p.batch * p.n_q_heads * p.seqlen * 4), _stream(stream)))
+
+
+class Prefill:
+    """Device buffers for one workload shape and the three calls of a prefill layer.
+
+    Allocation (torch) happens once here; ``run`` only enqueues the three library calls.
+    """
+
+    def __init__(self, w: wl.Workload, device="cuda", out_dtype: Optional[int] = None,
+                 keep_stats: bool = True, with_lse: bool = False):
+        self.w = w
+        self.p = problem(w)
+        self.b = budget(w)
+        self.W = index_width(self.p, self.b)
+        n = w.n_blocks
+        dev = torch.device(device)
+        self.out_dtype = w.dtype if out_dtype is None else out_dtype
+        self.summ = torch.empty(summary_bytes(self.p) // 4, dtype=torch.float32, device=dev)
+        self.ws = torch.empty(select_workspace_bytes(self.p, self.b), dtype=torch.uint8,
+                              device=dev)
+        self.kv_idx = torch.empty((w.batch, w.n_q_heads, n, self.W), dtype=torch.int32,
+                                  device=dev)
+        self.kv_cnt = torch.empty((w.batch, w.n_q_heads, n), dtype=torch.int32, device=dev)
+        if keep_stats:
+            self.sigma = torch.empty((w.batch, w.n_q_heads, n), dtype=torch.float32, device=dev)
+            self.sigma_bar = torch.empty((w.batch, n), dtype=torch.float32, device=dev)
+            self.gate = torch.empty((w.batch, n), dtype=torch.uint8, device=dev)
+            self.tau = torch.empty((w.batch,), dtype=torch.float32, device=dev)
+        else:
+            self.sigma = self.sigma_bar = self.gate = self.tau = None
+        odt = torch.float32 if self.out_dtype == SA_F32 else torch.bfloat16
+        self.O = torch.empty((w.batch, w.seqlen, w.n_q_heads, w.head_dim), dtype=odt,
+                             device=dev)
+        self.lse = (torch.empty((w.batch, w.n_q_heads, w.seqlen), dtype=torch.float32,
+                                device=dev) if with_lse else None)
+        self.scale = 1.0 / math.sqrt(w.head_dim)
+
+    def score(self, K, V, stream=None):
+        score(self.p, K, V if self.w.output_aware else None, self.summ, stream)
+
+    def select(self, Q, stream=None):
+        select(self.p, self.b, Q, self.summ, self.ws, self.kv_idx, self.kv_cnt, self.sigma,
+               self.sigma_bar, self.gate, self.tau, stream)
+
+    def forward(self, Q, K, V, stream=None):
+        forward(self.p, Q, K, V, self.kv_idx, self.kv_cnt, self.W, self.scale, self.O,
+                self.out_dtype, self.lse, stream)
+
+    def run(self, Q, K, V, stream=None):
+        self.score(K, V, stream)
+        self.select(Q, stream)
+        self.forward(Q, K, V, stream)
+        return self.O

@@ -1,0 +1,202 @@
+// C ABI of the block-sparse causal prefill library: argument validation, buffer sizes and
+// kernel dispatch.  Every check runs on the host before any HIP call, so an invalid call
+// enqueues nothing and touches no device.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr int kMaxTiles = 16384;  // LDS sizing of the ranking and gate kernels
+
+int check_problem(const sa_problem* p, sa::Dims* D) {
+  if (!p) return fail(SA_ERR_INVALID, "problem is NULL");
+  if (p->batch < 1 || p->seqlen < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1)
+    return fail(SA_ERR_INVALID, "batch, seqlen and head counts must be >= 1");
+  if (p->n_q_heads % p->n_kv_heads)
+    return fail(SA_ERR_INVALID, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                p->n_q_heads, p->n_kv_heads);
+  if (p->dtype != SA_BF16 && p->dtype != SA_F32)
+    return fail(SA_ERR_INVALID, "dtype must be SA_BF16 or SA_F32");
+  if (p->score_mode != SA_KMEAN && p->score_mode != SA_KMINMAX)
+    return fail(SA_ERR_INVALID, "score_mode must be SA_KMEAN or SA_KMINMAX");
+  if (p->output_aware != 0 && p->output_aware != 1)
+    return fail(SA_ERR_INVALID, "output_aware must be 0 or 1");
+  if (p->block < 1 || p->tile < 1) return fail(SA_ERR_INVALID, "block and tile must be >= 1");
+  if (p->seqlen % p->block)
+    return fail(SA_ERR_INVALID, "seqlen (%d) must be a multiple of block (%d)", p->seqlen,
+                p->block);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(SA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", p->head_dim);
+  if (p->block != 64 && p->block != 128)
+    return fail(SA_ERR_UNSUPPORTED, "block %d unsupported (64 or 128)", p->block);
+  if (p->tile != p->block)
+    return fail(SA_ERR_UNSUPPORTED, "tile (%d) must equal block (%d)", p->tile, p->block);
+  const long long n = p->seqlen / p->block;
+  if (n > kMaxTiles)
+    return fail(SA_ERR_UNSUPPORTED, "seqlen / block = %lld tiles exceeds %d", n, kMaxTiles);
+  if ((long long)p->batch * p->n_q_heads * n > 0x7fffffffLL)
+    return fail(SA_ERR_UNSUPPORTED, "batch * n_q_heads * tiles exceeds the launch grid");
+  if (D) {
+    D->B = p->batch;
+    D->N = p->seqlen;
+    D->Hq = p->n_q_heads;
+    D->Hkv = p->n_kv_heads;
+    D->G = p->n_q_heads / p->n_kv_heads;
+    D->d = p->head_dim;
+    D->blk = p->block;
+    D->n = (int)n;
+    D->dtype = p->dtype;
+    D->score_mode = p->score_mode;
+    D->oam = p->output_aware;
+  }
+  return SA_OK;
+}
+
+int check_budget(const sa_budget* b, const sa::Dims& D, sa::BudgetDev* bd) {
+  if (!b) return fail(SA_ERR_INVALID, "budget is NULL");
+  if (b->k_min < 1 || b->k_max < b->k_min)
+    return fail(SA_ERR_INVALID, "need 1 <= k_min (%d) <= k_max (%d)", b->k_min, b->k_max);
+  if (b->kind != SA_K_CONST && b->kind != SA_K_LINEAR_DECAY)
+    return fail(SA_ERR_INVALID, "kind must be SA_K_CONST or SA_K_LINEAR_DECAY");
+  if (b->n_sink < 0) return fail(SA_ERR_INVALID, "n_sink must be >= 0");
+  if (b->gate_mode != SA_GATE_QUANTILE && b->gate_mode != SA_GATE_FIXED &&
+      b->gate_mode != SA_GATE_OFF)
+    return fail(SA_ERR_INVALID, "gate_mode must be QUANTILE, FIXED or OFF");
+  if (!(b->rho >= 1.0) || !isfinite(b->rho) || b->rho * b->k_max > 1e9)
+    return fail(SA_ERR_INVALID, "rho must be finite and >= 1");
+  if (b->gate_mode == SA_GATE_QUANTILE && !(b->q >= 0.0 && b->q <= 1.0))
+    return fail(SA_ERR_INVALID, "q must lie in [0, 1]");
+  if (b->gate_mode == SA_GATE_FIXED && isnan(b->tau_fixed))
+    return fail(SA_ERR_INVALID, "tau_fixed is NaN");
+  if (bd) {
+    bd->k_max = b->k_max;
+    bd->k_min = b->k_min;
+    bd->kind = b->kind;
+    bd->n_sink = b->n_sink;
+    bd->gate_mode = b->gate_mode;
+    bd->tau_fixed = b->tau_fixed;
+    bd->rho = b->rho;
+    bd->q = b->q;
+    const long long ex = (long long)floor(b->rho * (double)b->k_max);
+    long long r = ex > b->k_max ? ex : b->k_max;
+    if (r > D.n) r = D.n;
+    bd->R = (int)(r > 0 ? r : 1);
+    long long w = 1 + (long long)b->n_sink + ex;
+    if (w > D.n) w = D.n;
+    bd->W = (int)w;
+  }
+  return SA_OK;
+}
+
+size_t summary_bytes(const sa::Dims& D) {
+  const size_t plane = (size_t)D.B * D.n * D.Hkv * D.d * sizeof(float);
+  size_t total = plane * (D.score_mode == SA_KMINMAX ? 2 : 1);
+  if (D.oam) total += (size_t)D.B * D.n * D.Hkv * sizeof(float);
+  return total;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SA_OK;
+  return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sparse_attn_summary_bytes(const sa_problem* p) {
+  sa::Dims D;
+  if (check_problem(p, &D) != SA_OK) return 0;
+  return summary_bytes(D);
+}
+
+size_t sparse_attn_select_workspace_bytes(const sa_problem* p, const sa_budget* b) {
+  sa::Dims D;
+  sa::BudgetDev bd;
+  if (check_problem(p, &D) != SA_OK || check_budget(b, D, &bd) != SA_OK) return 0;
+  return sa::select_ws_layout(D, bd).total;
+}
+
+int32_t sparse_attn_index_width(const sa_problem* p, const sa_budget* b) {
+  sa::Dims D;
+  sa::BudgetDev bd;
+  int rc = check_problem(p, &D);
+  if (rc != SA_OK) return rc;
+  if ((rc = check_budget(b, D, &bd)) != SA_OK) return rc;
+  return bd.W;
+}
+
+int sparse_attn_score(const sa_problem* p, const void* K, const void* V, void* summaries,
+                      void* stream) {
+  sa::Dims D;
+  int rc = check_problem(p, &D);
+  if (rc != SA_OK) return rc;
+  if (!K || !summaries) return fail(SA_ERR_INVALID, "K and summaries must be non-NULL");
+  if (D.oam && !V) return fail(SA_ERR_INVALID, "V is required when output_aware is set");
+  g_err.clear();
+  return hip_status(sa::launch_pool(D, K, V, static_cast<float*>(summaries),
+                                    static_cast<hipStream_t>(stream)),
+                    "sparse_attn_score launch");
+}
+
+int sparse_attn_select(const sa_problem* p, const sa_budget* b, const void* Q,
+                       const void* summaries, void* ws, size_t ws_bytes, int32_t* kv_idx,
+                       int32_t* kv_cnt, float* sigma, float* sigma_bar, uint8_t* gate,
+                       float* tau, void* stream) {
+  sa::Dims D;
+  sa::BudgetDev bd;
+  int rc = check_problem(p, &D);
+  if (rc != SA_OK) return rc;
+  if ((rc = check_budget(b, D, &bd)) != SA_OK) return rc;
+  if (!Q || !summaries || !ws || !kv_idx || !kv_cnt)
+    return fail(SA_ERR_INVALID, "Q, summaries, ws, kv_idx and kv_cnt must be non-NULL");
+  const size_t need = sa::select_ws_layout(D, bd).total;
+  if (ws_bytes < need)
+    return fail(SA_ERR_INVALID, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  g_err.clear();
+  return hip_status(sa::launch_select(D, bd, Q, static_cast<const float*>(summaries),
+                                      static_cast<char*>(ws), kv_idx, kv_cnt, sigma, sigma_bar,
+                                      gate, tau, static_cast<hipStream_t>(stream)),
+                    "sparse_attn_select launch");
+}
+
+int sparse_attn_forward(const sa_problem* p, const void* Q, const void* K, const void* V,
+                        const int32_t* kv_idx, const int32_t* kv_cnt, int32_t W,
+                        float softmax_scale, void* O, int32_t out_dtype, float* lse,
+                        void* stream) {
+  sa::Dims D;
+  int rc = check_problem(p, &D);
+  if (rc != SA_OK) return rc;
+  if (!Q || !K || !V || !kv_idx || !kv_cnt || !O)
+    return fail(SA_ERR_INVALID, "Q, K, V, kv_idx, kv_cnt and O must be non-NULL");
+  if (W < 1) return fail(SA_ERR_INVALID, "W must be >= 1");
+  if (out_dtype != SA_F32 && out_dtype != SA_BF16)
+    return fail(SA_ERR_INVALID, "out_dtype must be SA_F32 or SA_BF16");
+  if (!isfinite(softmax_scale)) return fail(SA_ERR_INVALID, "softmax_scale is not finite");
+  g_err.clear();
+  return hip_status(sa::launch_forward(D, Q, K, V, kv_idx, kv_cnt, W, softmax_scale, O,
+                                       out_dtype, lse, static_cast<hipStream_t>(stream)),
+                    "sparse_attn_forward launch");
+}
+
+const char* sparse_attn_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,414 @@
+// Sparse attention over the selected KV blocks: a FlashAttention-style online-softmax pass.
+//
+// Stem page, implementation note: the method runs block-sparse attention kernels over the
+// chosen blocks after block-level scoring; gated-selection page, Metodologia step 5: every
+// tile's list has the same padded shape (sentinel -1).  ART page, section 2.4: the online
+// softmax is invariant to the order of the KV blocks, and the causal mask is applied before
+// accumulation.
+//
+// bf16 kernel (attn_bf16): one workgroup per (batch, q head, query tile), BLK/32 waves, each
+// wave owns 32 query rows.  Per listed block the kernel computes S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 coordinates from LDS, B = the wave's Q
+// fragment kept in registers for the whole tile), so each lane's accumulator holds logits of
+// ONE query row for 16 keys.  That makes the row max and row sum lane-local (plus one swap
+// with the lane 32 apart), and the probabilities P^T are already laid out as the B operand
+// of the second product O^T += V^T P^T: the contraction index (keys) is permuted
+// consistently in the V^T operand instead of moving P through LDS.  K is staged in LDS
+// row-major and V transposed (both padded against bank conflicts); the next listed block is
+// prefetched into registers while the current one is computed.  fp32 accumulation
+// throughout.  The second product runs in fp16 (v_mfma_f32_32x32x16_f16): P in [0, 1] keeps
+// 11 significant bits instead of bf16's 8, and V converts from bf16 to fp16 exactly while it
+// is transposed into LDS (bf16 V must stay below 65504 in magnitude).
+//
+// fp32 kernel (attn_f32): one thread per query row, fp32 VALU arithmetic with the same
+// online softmax; it serves fp32 inputs, where no bf16 rounding is acceptable.
+//
+// Launch order is latest tile first (late tiles carry the most blocks), with the q heads of
+// one kv head launched next to each other so their K/V blocks are shared through L2.
+
+#include "common.h"
+
+namespace sa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Maps a workgroup id to (b, h, t): tiles latest first; within a tile, heads in order.
+__device__ __forceinline__ void decode_wg(const Dims& dm, int& b, int& h, int& t) {
+  const int BH = dm.B * dm.Hq;
+  const int id = (int)blockIdx.x;
+  t = dm.n - 1 - id / BH;
+  const int bh = id - (id / BH) * BH;
+  b = bh / dm.Hq;
+  h = bh - b * dm.Hq;
+}
+
+// Index of the next usable list entry at or after e, or -1: the list ends at cnt or at the
+// first negative entry; entries after the tile (j > t) are skipped.
+__device__ __forceinline__ int next_entry(const int32_t* __restrict__ list, int cnt, int e,
+                                          int t) {
+  for (; e < cnt; ++e) {
+    const int j = list[e];
+    if (j < 0) return -1;
+    if (j <= t) return e;
+  }
+  return -1;
+}
+
+union U4 {
+  uint4 v;
+  uint32_t w[4];
+};
+
+template <int D, int BLK>
+struct Tiles {
+  static constexpr int NT = BLK * 2;              // BLK/32 waves of 64
+  static constexpr int KS = D + 8;                // LDS row stride of K (elements)
+  static constexpr int VS = BLK + 4;              // LDS row stride of V^T (elements)
+  static constexpr int KCH = BLK * D / 8;         // 16-byte chunks of a K block
+  static constexpr int KPT = KCH / NT;            // per thread
+  static constexpr int VMT = (BLK / 4) * (D / 8); // 4-key x 8-coordinate micro tiles of V
+  static constexpr int VPT = VMT / NT;            // per thread
+  static constexpr size_t LDS = sizeof(uint16_t) * ((size_t)BLK * KS + (size_t)D * VS);
+  static_assert(KCH % NT == 0 && VMT % NT == 0, "tile split");
+};
+
+template <int D, int BLK>
+__device__ __forceinline__ void load_block(const uint16_t* __restrict__ K,
+                                           const uint16_t* __restrict__ V, size_t row0,
+                                           int rstride, U4 (&kr)[Tiles<D, BLK>::KPT],
+                                           U4 (&vr)[Tiles<D, BLK>::VPT][4]) {
+  using TL = Tiles<D, BLK>;
+#pragma unroll
+  for (int i = 0; i < TL::KPT; ++i) {
+    const int c = threadIdx.x + i * TL::NT;
+    const int r = c / (D / 8), col = c - r * (D / 8);
+    kr[i].v = *reinterpret_cast<const uint4*>(K + (row0 + r) * rstride + col * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < TL::VPT; ++i) {
+    const int m = threadIdx.x + i * TL::NT;
+    const int kg = m / (D / 8), col = m - kg * (D / 8);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      vr[i][k].v = *reinterpret_cast<const uint4*>(V + (row0 + 4 * kg + k) * rstride + col * 8);
+  }
+}
+
+template <int D, int BLK>
+__device__ __forceinline__ void store_block(uint16_t* Ks, uint16_t* Vt,
+                                            const U4 (&kr)[Tiles<D, BLK>::KPT],
+                                            const U4 (&vr)[Tiles<D, BLK>::VPT][4]) {
+  using TL = Tiles<D, BLK>;
+#pragma unroll
+  for (int i = 0; i < TL::KPT; ++i) {
+    const int c = threadIdx.x + i * TL::NT;
+    const int r = c / (D / 8), col = c - r * (D / 8);
+    *reinterpret_cast<uint4*>(Ks + r * TL::KS + col * 8) = kr[i].v;
+  }
+#pragma unroll
+  for (int i = 0; i < TL::VPT; ++i) {
+    const int m = threadIdx.x + i * TL::NT;
+    const int kg = m / (D / 8), col = m - kg * (D / 8);
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      // Coordinate col*8+dd of keys 4kg..4kg+3, bf16 -> fp32 (exact) -> fp16 (exact for
+      // |v| in [2^-14, 65504]; smaller magnitudes keep an absolute error below 2^-25).
+      const int wd = dd >> 1;
+      float x[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[k] = (dd & 1) ? bf16_hi(vr[i][k].w[wd]) : bf16_lo(vr[i][k].w[wd]);
+      const f16x2 p01 = __builtin_convertvector((f32x2){x[0], x[1]}, f16x2);
+      const f16x2 p23 = __builtin_convertvector((f32x2){x[2], x[3]}, f16x2);
+      uint2 pk;
+      pk.x = *reinterpret_cast<const uint32_t*>(&p01);
+      pk.y = *reinterpret_cast<const uint32_t*>(&p23);
+      *reinterpret_cast<uint2*>(Vt + (col * 8 + dd) * TL::VS + 4 * kg) = pk;
+    }
+  }
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK * 2) void attn_bf16(Dims dm, const uint16_t* __restrict__ Q,
+                                                     const uint16_t* __restrict__ K,
+                                                     const uint16_t* __restrict__ V,
+                                                     const int32_t* __restrict__ kv_idx,
+                                                     const int32_t* __restrict__ kv_cnt,
+                                                     int W, float scale_log2,
+                                                     void* __restrict__ O, int out_f32,
+                                                     float* __restrict__ lse) {
+  using TL = Tiles<D, BLK>;
+  constexpr int KT = BLK / 32;  // 32-key tiles per block
+  constexpr int DT = D / 32;    // 32-coordinate tiles of the output
+  constexpr int DC = D / 16;    // 16-coordinate chunks of the QK^T contraction
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  uint16_t* Ks = smem;
+  uint16_t* Vt = smem + BLK * TL::KS;
+
+  int b, h, t;
+  decode_wg(dm, b, h, t);
+  const int g = h / dm.G;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const size_t bht = ((size_t)b * dm.Hq + h) * dm.n + t;
+  const int32_t* list = kv_idx + bht * W;
+  const int cnt = min(kv_cnt[bht], W);
+  const int qrow = t * BLK + wv * 32 + l32;  // this lane's query position
+  const int rstride = dm.Hkv * D;
+
+  // Q fragment (B operand of S^T = K Q^T): lane holds coordinates 16c + 8*hi .. +7 of its row.
+  bf16x8 qf[DC];
+  {
+    const uint16_t* qp = Q + (((size_t)b * dm.N + qrow) * dm.Hq + h) * D + 8 * hi;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
+  }
+
+  f32x16 acc_o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) acc_o[i] = (f32x16){};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  U4 kr[TL::KPT];
+  U4 vr[TL::VPT][4];
+  const size_t kvbase = (size_t)b * dm.N;
+  const uint16_t* Kg = K + (size_t)g * D;
+  const uint16_t* Vg = V + (size_t)g * D;
+
+  int e = next_entry(list, cnt, 0, t);
+  if (e >= 0) {
+    load_block<D, BLK>(Kg, Vg, kvbase + (size_t)list[e] * BLK, rstride, kr, vr);
+    store_block<D, BLK>(Ks, Vt, kr, vr);
+  }
+  __syncthreads();
+
+  while (e >= 0) {
+    const int j = list[e];
+    const int e2 = next_entry(list, cnt, e + 1, t);
+    if (e2 >= 0) load_block<D, BLK>(Kg, Vg, kvbase + (size_t)list[e2] * BLK, rstride, kr, vr);
+
+    // S^T = K Q^T for the block: KT tiles of 32 keys x 32 queries.
+    f32x16 s[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      s[kt] = (f32x16){};
+      const uint16_t* kp = Ks + (kt * 32 + l32) * TL::KS + 8 * hi;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + 16 * c);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kt], 0, 0, 0);
+      }
+    }
+
+    // Online softmax in the log2 domain.  Lane value (kt, i, r) is key kt*32 + 8i + 4*hi + r.
+    const bool masked = j >= t;
+    const int qloc = wv * 32 + l32;
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float x = s[kt][v] * scale_log2;
+        if (masked) {
+          const int kloc = kt * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+          if (j > t || kloc > qloc) x = -INFINITY;
+        }
+        s[kt][v] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float m_new = fmaxf(m_run, mloc);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+
+    float psum = 0.0f;
+    f16x8 pf[KT][2];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(s[kt][v] - m_use);
+        psum += p;
+        pf[kt][v >> 3][v & 7] = (_Float16)p;
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
+
+    // O^T += V^T P^T.  B operand slot 8*hi + 4i' + r of pf[kt][half] is key
+    // kt*32 + 16*half + 8i' + 4*hi + r; the A operand reads V^T at the same keys.
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint16_t* vp = Vt + (dt * 32 + l32) * TL::VS + 4 * hi;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int k0 = kt * 32 + 16 * half;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vp + k0);
+          const uint2 up = *reinterpret_cast<const uint2*>(vp + k0 + 8);
+          const uint4 raw = make_uint4(lo.x, lo.y, up.x, up.y);
+          const f16x8 a = *reinterpret_cast<const f16x8*>(&raw);
+          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[kt][half], acc_o[dt], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+    if (e2 >= 0) store_block<D, BLK>(Ks, Vt, kr, vr);
+    __syncthreads();
+    e = e2;
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const size_t orow = (((size_t)b * dm.N + qrow) * dm.Hq + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = dt * 32 + 8 * i + 4 * hi;
+      const float o0 = acc_o[dt][4 * i] * inv, o1 = acc_o[dt][4 * i + 1] * inv;
+      const float o2 = acc_o[dt][4 * i + 2] * inv, o3 = acc_o[dt][4 * i + 3] * inv;
+      if (out_f32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(O) + orow + d0) =
+            make_float4(o0, o1, o2, o3);
+      } else {
+        uint2 pk;
+        pk.x = f32_to_bf16_bits(o0) | (f32_to_bf16_bits(o1) << 16);
+        pk.y = f32_to_bf16_bits(o2) | (f32_to_bf16_bits(o3) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(O) + orow + d0) = pk;
+      }
+    }
+  if (lse && hi == 0)
+    lse[((size_t)b * dm.Hq + h) * dm.N + qrow] =
+        l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------- fp32 (VALU) path
+
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK) void attn_f32(Dims dm, const float* __restrict__ Q,
+                                                const float* __restrict__ K,
+                                                const float* __restrict__ V,
+                                                const int32_t* __restrict__ kv_idx,
+                                                const int32_t* __restrict__ kv_cnt, int W,
+                                                float scale, void* __restrict__ O, int out_f32,
+                                                float* __restrict__ lse) {
+  extern __shared__ float fsm[];
+  float* Kb = fsm;            // [BLK][D]
+  float* Vb = fsm + BLK * D;  // [BLK][D]
+  int b, h, t;
+  decode_wg(dm, b, h, t);
+  const int g = h / dm.G;
+  const size_t bht = ((size_t)b * dm.Hq + h) * dm.n + t;
+  const int32_t* list = kv_idx + bht * W;
+  const int cnt = min(kv_cnt[bht], W);
+  const int qrow = t * BLK + threadIdx.x;
+  const int rstride = dm.Hkv * D;
+
+  float q[D], o[D];
+  const float* qp = Q + (((size_t)b * dm.N + qrow) * dm.Hq + h) * D;
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    q[c] = qp[c];
+    o[c] = 0.0f;
+  }
+  float m = -INFINITY, l = 0.0f;
+  for (int e = next_entry(list, cnt, 0, t); e >= 0; e = next_entry(list, cnt, e + 1, t)) {
+    const int j = list[e];
+    const size_t row0 = (size_t)b * dm.N + (size_t)j * BLK;
+    for (int x = threadIdx.x; x < BLK * D; x += BLK) {
+      const int r = x / D, c = x - r * D;
+      Kb[x] = K[(row0 + r) * rstride + (size_t)g * D + c];
+      Vb[x] = V[(row0 + r) * rstride + (size_t)g * D + c];
+    }
+    __syncthreads();
+    for (int r = 0; r < BLK; ++r) {
+      if ((size_t)j * BLK + r > (size_t)qrow) break;
+      float sdot = 0.0f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) sdot = __builtin_fmaf(q[c], Kb[r * D + c], sdot);
+      const float z = sdot * scale;
+      const float mn = fmaxf(m, z);
+      const float a = __expf(m - mn), p = __expf(z - mn);
+      l = l * a + p;
+#pragma unroll
+      for (int c = 0; c < D; ++c) o[c] = __builtin_fmaf(p, Vb[r * D + c], o[c] * a);
+      m = mn;
+    }
+    __syncthreads();
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const size_t orow = (((size_t)b * dm.N + qrow) * dm.Hq + h) * D;
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    if (out_f32)
+      static_cast<float*>(O)[orow + c] = o[c] * inv;
+    else
+      static_cast<uint16_t*>(O)[orow + c] = (uint16_t)f32_to_bf16_bits(o[c] * inv);
+  }
+  if (lse)
+    lse[((size_t)b * dm.Hq + h) * dm.N + qrow] = l > 0.0f ? m + __logf(l) : -INFINITY;
+}
+
+template <int D, int BLK>
+hipError_t launch_bf16(const Dims& dm, const void* Q, const void* K, const void* V,
+                       const int32_t* kv_idx, const int32_t* kv_cnt, int W, float scale,
+                       void* O, int out_dtype, float* lse, hipStream_t s) {
+  using TL = Tiles<D, BLK>;
+  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
+  hipError_t e = allow_lds(attn_bf16<D, BLK>, TL::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bf16<D, BLK>), dim3(grid), dim3(TL::NT), TL::LDS, s, dm,
+                     static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                     static_cast<const uint16_t*>(V), kv_idx, kv_cnt, W, scale * kLog2e, O,
+                     out_dtype == SA_F32 ? 1 : 0, lse);
+  return hipGetLastError();
+}
+
+template <int D, int BLK>
+hipError_t launch_f32(const Dims& dm, const void* Q, const void* K, const void* V,
+                      const int32_t* kv_idx, const int32_t* kv_cnt, int W, float scale,
+                      void* O, int out_dtype, float* lse, hipStream_t s) {
+  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
+  const size_t lds = sizeof(float) * 2 * BLK * D;
+  hipError_t e = allow_lds(attn_f32<D, BLK>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_f32<D, BLK>), dim3(grid), dim3(BLK), lds, s, dm,
+                     static_cast<const float*>(Q), static_cast<const float*>(K),
+                     static_cast<const float*>(V), kv_idx, kv_cnt, W, scale, O,
+                     out_dtype == SA_F32 ? 1 : 0, lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_forward(const Dims& dm, const void* Q, const void* K, const void* V,
+                          const int32_t* kv_idx, const int32_t* kv_cnt, int W, float scale,
+                          void* O, int out_dtype, float* lse, hipStream_t s) {
+  if (dm.dtype == SA_BF16) {
+    if (dm.d == 64)
+      return dm.blk == 64
+                 ? launch_bf16<64, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
+                 : launch_bf16<64, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s);
+    return dm.blk == 64
+               ? launch_bf16<128, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
+               : launch_bf16<128, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s);
+  }
+  if (dm.d == 64)
+    return dm.blk == 64
+               ? launch_f32<64, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
+               : launch_f32<64, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s);
+  return dm.blk == 64
+             ? launch_f32<128, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
+             : launch_f32<128, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s);
+}
+
+}  // namespace sa

@@ -1,0 +1,399 @@
+// Block selection for block-sparse causal prefill: tile scores, top-k, cut margin, quantile
+// gate, expansion and sentinel-padded lists.
+//
+// "Uncertainty-Gated Selection for Block-Sparse Attention" page, Metodologia:
+//   step 2  per query tile, a block's score is the maximum over the tile's query rows; a
+//           top-k over blocks gives the initial kv_idx;
+//   step 3  the normalised cut margin sigma = (s_(k-1) - s_(k)) / (s_(0) - s_(k)) over the
+//           sorted scores, per tile and head;
+//   step 4  sigma averaged over heads and compared with a per-layer empirical quantile q;
+//   step 5  tiles that trip keep the top floor(rho * k) blocks, the others k, and the lists
+//           are padded with sentinels so every tile has the same shape.
+// Stem page, Metodologia A: the budget k_t may decay linearly with the tile's position, and
+// early blocks act as anchors (here: n_sink blocks always kept).
+//
+// Three stream-ordered launches, no host synchronisation:
+//   score_rank  one workgroup per (b, h, t), tiles launched latest-first (they carry the most
+//               blocks).  One wave per 64 query rows; lane = query row, with the row held in
+//               registers as fp32.  Each block summary is read by the whole wave at one
+//               uniform address (scalar loads), so every fused multiply-add takes one operand
+//               from a scalar register and the row scores run as independent per-lane
+//               chains in coordinate order.  The wave's maximum over rows goes to LDS as an
+//               order-preserving 64-bit key (score, then lower index first), merged across
+//               the tile's waves with an LDS atomic max, then sorted by a bitonic network.
+//   gate        one workgroup per batch element: head mean, eligible count, the quantile's
+//               order statistic (bitonic sort of the eligible sigma_bar), gate bits.
+//   emit        one wave per (b, h, t): forced blocks and the kept ranked blocks marked in
+//               an LDS bitmap, then written out in ascending order with a wave prefix sum.
+//
+// The arithmetic that decides selections is IEEE fp32 with a fixed order (compiled without
+// contraction): row score = fused multiply-add chain over coordinates in order, starting at
+// +0; tile score = maximum over rows, with -0 mapped to +0, times the value norm when the
+// score is output-aware; sigma = two subtractions and a correctly rounded division;
+// sigma_bar = sum over heads in order divided by the head count; the quantile rank
+// ceil(q * M) in fp64.
+
+#include "common.h"
+
+namespace sa {
+namespace {
+
+__device__ __forceinline__ int budget_at(const BudgetDev& bd, int t, int n) {
+  if (bd.kind == SA_K_CONST) return bd.k_max;
+  const long long k = (long long)bd.k_max * (n - t) / n;
+  return k > bd.k_min ? (int)k : bd.k_min;
+}
+__device__ __forceinline__ int n_free(const BudgetDev& bd, int t) {
+  return t - (t < bd.n_sink ? t : bd.n_sink);
+}
+__device__ __forceinline__ int expanded(const BudgetDev& bd, int k) {
+  return (int)floor(bd.rho * (double)k);
+}
+__device__ __forceinline__ int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Bitonic sort of P (a power of two) 64-bit keys in LDS, descending, by NT threads.
+template <int NT>
+__device__ void bitonic_desc(unsigned long long* keys, int P) {
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = threadIdx.x; i < (P >> 1); i += NT) {
+        const int lo = ((i & ~(jj - 1)) << 1) | (i & (jj - 1));
+        const int hi = lo + jj;
+        const unsigned long long a = keys[lo], b = keys[hi];
+        const bool desc = (lo & k) == 0;
+        if (desc ? (a < b) : (a > b)) {
+          keys[lo] = b;
+          keys[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <typename T, int D>
+struct QRow;
+template <int D>
+struct QRow<uint16_t, D> {
+  __device__ __forceinline__ static void load(const uint16_t* p, float* q) {
+#pragma unroll
+    for (int c = 0; c < D; c += 8) {
+      uint4 v = *reinterpret_cast<const uint4*>(p + c);
+      q[c + 0] = bf16_lo(v.x); q[c + 1] = bf16_hi(v.x);
+      q[c + 2] = bf16_lo(v.y); q[c + 3] = bf16_hi(v.y);
+      q[c + 4] = bf16_lo(v.z); q[c + 5] = bf16_hi(v.z);
+      q[c + 6] = bf16_lo(v.w); q[c + 7] = bf16_hi(v.w);
+    }
+  }
+};
+template <int D>
+struct QRow<float, D> {
+  __device__ __forceinline__ static void load(const float* p, float* q) {
+#pragma unroll
+    for (int c = 0; c < D; c += 4) {
+      float4 v = *reinterpret_cast<const float4*>(p + c);
+      q[c] = v.x; q[c + 1] = v.y; q[c + 2] = v.z; q[c + 3] = v.w;
+    }
+  }
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// ----------------------------------------------------------------------- score_rank
+
+template <typename T, int MODE, int OAM, int D, int TILE>
+__global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
+                                                   const T* __restrict__ Q,
+                                                   const float* __restrict__ summ,
+                                                   int* __restrict__ ranked,
+                                                   float* __restrict__ sigma) {
+  extern __shared__ unsigned long long keys[];
+  constexpr int NT = TILE;  // one lane per query row
+  const int n = dm.n;
+  const int BH = dm.B * dm.Hq;
+  const int t = n - 1 - (int)(blockIdx.x / BH);
+  const int bh = (int)(blockIdx.x % BH);
+  const int b = bh / dm.Hq, h = bh - b * dm.Hq;
+  const int g = h / dm.G;
+  const size_t bht = (size_t)bh * n + t;
+
+  const int kt = budget_at(bd, t, n);
+  const int nf = n_free(bd, t);
+  if (nf <= kt) {  // not eligible: every free block is kept, nothing to rank
+    if (threadIdx.x == 0) sigma[bht] = 1.0f;
+    return;
+  }
+  const int j0 = t < bd.n_sink ? t : bd.n_sink;  // first free block
+  const int P = next_pow2(nf);
+  for (int f = threadIdx.x; f < P; f += NT)
+    keys[f] = f < nf ? (unsigned long long)(0xffffffffu - (unsigned)(j0 + f)) : 0ull;
+  __syncthreads();
+
+  const int row = t * TILE + threadIdx.x;
+  float q[D];
+  QRow<T, D>::load(Q + (((size_t)b * dm.N + row) * dm.Hq + h) * D, q);
+
+  const size_t plane = (size_t)dm.B * n * dm.Hkv * D;
+  const float* kbase = summ + (((size_t)b * n) * dm.Hkv + g) * D;
+  const size_t kstride = (size_t)dm.Hkv * D;
+  const float* vn = summ + plane * (MODE == SA_KMINMAX ? 2 : 1) + ((size_t)b * n) * dm.Hkv + g;
+  const bool lead = (threadIdx.x & 63) == 0;
+
+  for (int j = j0; j < t; ++j) {
+    const float* kb = kbase + (size_t)j * kstride;
+    float s = 0.0f;
+    if (MODE == SA_KMEAN) {
+#pragma unroll
+      for (int c = 0; c < D; ++c) s = __builtin_fmaf(q[c], kb[c], s);
+    } else {
+      const float* kx = kb + plane;
+#pragma unroll
+      for (int c = 0; c < D; ++c) s = __builtin_fmaf(q[c], q[c] >= 0.0f ? kx[c] : kb[c], s);
+    }
+    float m = canon(wave_max(s));
+    if (OAM) m = canon(m * vn[(size_t)j * dm.Hkv]);
+    if (lead) {
+      const unsigned long long key =
+          ((unsigned long long)order_key(m) << 32) | (0xffffffffu - (unsigned)j);
+      atomicMax(&keys[j - j0], key);
+    }
+  }
+  __syncthreads();
+  bitonic_desc<NT>(keys, P);
+
+  const int R = min(max(expanded(bd, kt), kt), nf);
+  int* out = ranked + bht * bd.R;
+  for (int r = threadIdx.x; r < R; r += NT) out[r] = (int)(0xffffffffu - (unsigned)keys[r]);
+  if (threadIdx.x == 0) {
+    const float s0 = order_key_inv((unsigned)(keys[0] >> 32));
+    const float sk1 = order_key_inv((unsigned)(keys[kt - 1] >> 32));
+    const float sk = order_key_inv((unsigned)(keys[kt] >> 32));
+    const float num = sk1 - sk;
+    const float den = s0 - sk;
+    sigma[bht] = den == 0.0f ? 0.0f : __fdiv_rn(num, den);
+  }
+}
+
+// ----------------------------------------------------------------------------- gate
+
+constexpr int kGateThreads = 1024;
+
+__global__ __launch_bounds__(kGateThreads) void gate_kernel(Dims dm, BudgetDev bd,
+                                                            const float* __restrict__ sigma,
+                                                            float* __restrict__ sigma_bar,
+                                                            uint8_t* __restrict__ gate,
+                                                            float* __restrict__ tau) {
+  extern __shared__ float gsh[];  // sbar[n], then sort buffer [P]
+  __shared__ int M;
+  const int n = dm.n, b = blockIdx.x;
+  float* sbar = gsh;
+  float* buf = gsh + n;
+  if (threadIdx.x == 0) M = 0;
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += kGateThreads) {
+    float acc = 0.0f;
+    for (int h = 0; h < dm.Hq; ++h) acc = acc + sigma[((size_t)b * dm.Hq + h) * n + t];
+    const float sb = __fdiv_rn(acc, (float)dm.Hq);
+    sbar[t] = sb;
+    sigma_bar[(size_t)b * n + t] = sb;
+    if (n_free(bd, t) > budget_at(bd, t, n)) buf[atomicAdd(&M, 1)] = sb;
+  }
+  __syncthreads();
+  const int m = M;
+  float tb = -INFINITY;
+  if (bd.gate_mode == SA_GATE_QUANTILE) {
+    const int P = next_pow2(m > 0 ? m : 1);
+    for (int i = m + threadIdx.x; i < P; i += kGateThreads) buf[i] = INFINITY;
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int i = threadIdx.x; i < (P >> 1); i += kGateThreads) {
+          const int lo = ((i & ~(jj - 1)) << 1) | (i & (jj - 1));
+          const int hi = lo + jj;
+          const float a = buf[lo], c = buf[hi];
+          const bool asc = (lo & k) == 0;
+          if (asc ? (a > c) : (a < c)) {
+            buf[lo] = c;
+            buf[hi] = a;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    double rq = ceil(bd.q * (double)m);
+    const int r = rq < 0.0 ? 0 : (rq > (double)m ? m : (int)rq);
+    if (r > 0) tb = buf[r - 1];
+  } else if (bd.gate_mode == SA_GATE_FIXED) {
+    tb = bd.tau_fixed;
+  }
+  for (int t = threadIdx.x; t < n; t += kGateThreads) {
+    const bool elig = n_free(bd, t) > budget_at(bd, t, n);
+    gate[(size_t)b * n + t] =
+        (uint8_t)(bd.gate_mode != SA_GATE_OFF && elig && sbar[t] <= tb);
+  }
+  if (threadIdx.x == 0) tau[b] = tb;
+}
+
+// ----------------------------------------------------------------------------- emit
+
+constexpr int kEmitWaves = 4;
+
+__global__ __launch_bounds__(64 * kEmitWaves) void emit_kernel(Dims dm, BudgetDev bd,
+                                                               const int* __restrict__ ranked,
+                                                               const uint8_t* __restrict__ gate,
+                                                               int32_t* __restrict__ kv_idx,
+                                                               int32_t* __restrict__ kv_cnt) {
+  extern __shared__ unsigned int bits[];  // [kEmitWaves][nwords]
+  const int n = dm.n;
+  const int nwords = (n + 31) >> 5;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t item = (size_t)blockIdx.x * kEmitWaves + w;
+  const size_t total = (size_t)dm.B * dm.Hq * n;
+  const bool live = item < total;
+  const int t = live ? (int)(item % n) : 0;
+  const int b = live ? (int)(item / ((size_t)dm.Hq * n)) : 0;
+  unsigned int* bm = bits + w * nwords;
+
+  const int kt = budget_at(bd, t, n);
+  const int nf = n_free(bd, t);
+  const bool elig = live && nf > kt;
+  int keep = 0;
+  if (elig) {
+    const bool tripped = gate[(size_t)b * n + t] != 0;
+    keep = min(tripped ? expanded(bd, kt) : kt, nf);
+    for (int i = lane; i <= (t >> 5); i += 64) bm[i] = 0u;
+  }
+  __syncthreads();
+  if (elig) {
+    const int* rk = ranked + item * bd.R;
+    for (int e = lane; e < keep; e += 64) {
+      const int j = rk[e];
+      atomicOr(&bm[j >> 5], 1u << (j & 31));
+    }
+    if (lane == 0) atomicOr(&bm[t >> 5], 1u << (t & 31));
+    for (int j = lane; j < bd.n_sink; j += 64) atomicOr(&bm[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  if (!live) return;
+  int32_t* out = kv_idx + item * bd.W;
+  int cnt;
+  if (!elig) {  // every block 0..t is kept
+    cnt = t + 1;
+    for (int e = lane; e < cnt; e += 64) out[e] = e;
+  } else {
+    const int nw = (t >> 5) + 1;
+    int base = 0;
+    for (int w0 = 0; w0 < nw; w0 += 64) {
+      const unsigned int word = (w0 + lane < nw) ? bm[w0 + lane] : 0u;
+      const int pc = __popc(word);
+      int incl = pc;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      int pos = base + incl - pc;
+      unsigned int rest = word;
+      while (rest) {
+        const int bit = __ffs(rest) - 1;
+        rest &= rest - 1;
+        out[pos++] = ((w0 + lane) << 5) + bit;
+      }
+      base += __shfl(incl, 63);
+    }
+    cnt = base;
+  }
+  for (int e = cnt + lane; e < bd.W; e += 64) out[e] = -1;
+  if (lane == 0) kv_cnt[item] = cnt;
+}
+
+template <typename T, int MODE, int OAM, int D, int TILE>
+hipError_t launch_score(const Dims& dm, const BudgetDev& bd, const void* Q, const float* summ,
+                        int* ranked, float* sigma, hipStream_t s) {
+  int P = 1;
+  while (P < dm.n) P <<= 1;
+  const size_t lds = sizeof(unsigned long long) * P;
+  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
+  hipError_t e = allow_lds(score_rank<T, MODE, OAM, D, TILE>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((score_rank<T, MODE, OAM, D, TILE>), dim3(grid), dim3(TILE), lds, s, dm,
+                     bd, static_cast<const T*>(Q), summ, ranked, sigma);
+  return hipGetLastError();
+}
+
+template <typename T, int MODE, int OAM>
+hipError_t score_by_shape(const Dims& dm, const BudgetDev& bd, const void* Q, const float* summ,
+                          int* ranked, float* sigma, hipStream_t s) {
+  if (dm.d == 64)
+    return dm.blk == 64 ? launch_score<T, MODE, OAM, 64, 64>(dm, bd, Q, summ, ranked, sigma, s)
+                        : launch_score<T, MODE, OAM, 64, 128>(dm, bd, Q, summ, ranked, sigma, s);
+  return dm.blk == 64 ? launch_score<T, MODE, OAM, 128, 64>(dm, bd, Q, summ, ranked, sigma, s)
+                      : launch_score<T, MODE, OAM, 128, 128>(dm, bd, Q, summ, ranked, sigma, s);
+}
+
+template <typename T>
+hipError_t score_dispatch(const Dims& dm, const BudgetDev& bd, const void* Q, const float* summ,
+                          int* ranked, float* sigma, hipStream_t s) {
+  if (dm.score_mode == SA_KMEAN)
+    return dm.oam ? score_by_shape<T, SA_KMEAN, 1>(dm, bd, Q, summ, ranked, sigma, s)
+                  : score_by_shape<T, SA_KMEAN, 0>(dm, bd, Q, summ, ranked, sigma, s);
+  return dm.oam ? score_by_shape<T, SA_KMINMAX, 1>(dm, bd, Q, summ, ranked, sigma, s)
+                : score_by_shape<T, SA_KMINMAX, 0>(dm, bd, Q, summ, ranked, sigma, s);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+SelectWs select_ws_layout(const Dims& dm, const BudgetDev& bd) {
+  SelectWs w;
+  const size_t bhn = (size_t)dm.B * dm.Hq * dm.n;
+  w.ranked = 0;
+  w.sigma = align256(w.ranked + sizeof(int) * bhn * bd.R);
+  w.sigma_bar = align256(w.sigma + sizeof(float) * bhn);
+  w.gate = align256(w.sigma_bar + sizeof(float) * (size_t)dm.B * dm.n);
+  w.tau = align256(w.gate + (size_t)dm.B * dm.n);
+  w.total = align256(w.tau + sizeof(float) * dm.B);
+  return w;
+}
+
+hipError_t launch_select(const Dims& dm, const BudgetDev& bd, const void* Q, const float* summ,
+                         char* ws, int32_t* kv_idx, int32_t* kv_cnt, float* sigma,
+                         float* sigma_bar, uint8_t* gate, float* tau, hipStream_t s) {
+  const SelectWs L = select_ws_layout(dm, bd);
+  int* ranked = reinterpret_cast<int*>(ws + L.ranked);
+  if (!sigma) sigma = reinterpret_cast<float*>(ws + L.sigma);
+  if (!sigma_bar) sigma_bar = reinterpret_cast<float*>(ws + L.sigma_bar);
+  if (!gate) gate = reinterpret_cast<uint8_t*>(ws + L.gate);
+  if (!tau) tau = reinterpret_cast<float*>(ws + L.tau);
+
+  hipError_t e = dm.dtype == SA_BF16
+                     ? score_dispatch<uint16_t>(dm, bd, Q, summ, ranked, sigma, s)
+                     : score_dispatch<float>(dm, bd, Q, summ, ranked, sigma, s);
+  if (e != hipSuccess) return e;
+
+  int P = 1;
+  while (P < dm.n) P <<= 1;
+  const size_t glds = sizeof(float) * ((size_t)dm.n + P);
+  if ((e = allow_lds(gate_kernel, glds)) != hipSuccess) return e;
+  hipLaunchKernelGGL(gate_kernel, dim3((unsigned)dm.B), dim3(kGateThreads), glds, s, dm, bd,
+                     sigma, sigma_bar, gate, tau);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  const size_t total = (size_t)dm.B * dm.Hq * dm.n;
+  const unsigned grid = (unsigned)((total + kEmitWaves - 1) / kEmitWaves);
+  const size_t elds = sizeof(unsigned int) * kEmitWaves * (size_t)((dm.n + 31) / 32);
+  hipLaunchKernelGGL(emit_kernel, dim3(grid), dim3(64 * kEmitWaves), elds, s, dm, bd, ranked,
+                     gate, kv_idx, kv_cnt);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,166 @@
+/*
+ * sparse_attn.h -- C ABI of the block-sparse causal prefill attention library (gfx950).
+ *
+ * The method, in the order the calls run it:
+ *
+ *   sparse_attn_score    Block summaries of the keys: mean-pooled keys or per-coordinate
+ *                        K-min/K-max bounds, plus the mean value-row L2 norm when the
+ *                        output-aware score is on.  ("Uncertainty-Gated Selection for
+ *                        Block-Sparse Attention" page, Metodologia step 1; Stem page,
+ *                        Metodologia B and the three-stage implementation note.)
+ *   sparse_attn_select   Per query tile and head: tile score = max over the tile's rows,
+ *                        top-k under a constant or position-decaying budget, the normalised
+ *                        cut margin sigma = (s_(k-1) - s_(k)) / (s_(0) - s_(k)), its mean
+ *                        over heads, a per-call quantile gate, top-floor(rho*k) expansion of
+ *                        tripped tiles, and sentinel-padded block lists.  (Gated-selection
+ *                        page, Metodologia steps 2-5; Stem page, Metodologia A.)
+ *   sparse_attn_forward  FlashAttention-style online-softmax attention over the listed KV
+ *                        blocks only, causal.  (Stem page, implementation note; ART page,
+ *                        section 2.4 on order invariance of the online softmax.)
+ *
+ * Conventions shared by every call:
+ *   - Q is [B, N, Hq, d], K and V are [B, N, Hkv, d], O is [B, N, Hq, d]: contiguous, row
+ *     major (BSHD).  Query head h reads kv head h / (Hq / Hkv).
+ *   - Every pointer argument is device memory allocated and owned by the caller; the
+ *     library never allocates, frees or keeps a pointer after a call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work and
+ *     return; results are ready when the stream is.  A fault inside a kernel surfaces at the
+ *     caller's next synchronisation of that stream.
+ *   - Return value: SA_OK, or a negative status.  Arguments are validated on the host
+ *     before any HIP call, so an invalid call enqueues nothing.  sparse_attn_last_error()
+ *     gives the calling thread's last message.
+ *   - Supported in this version: head_dim in {64, 128}; block == tile in {64, 128};
+ *     seqlen % block == 0; Hq % Hkv == 0; bf16 or fp32 inputs.
+ */
+#ifndef SPARSE_ATTN_H_
+#define SPARSE_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SA_OK = 0,
+  SA_ERR_INVALID = -1,     /* bad argument: null pointer, out-of-range value, small buffer */
+  SA_ERR_UNSUPPORTED = -2, /* valid but not supported by this build (shape, dtype) */
+  SA_ERR_HIP = -3          /* a HIP call failed (launch, device query) */
+};
+
+enum { SA_F32 = 0, SA_BF16 = 1 };                            /* element types */
+enum { SA_KMEAN = 0, SA_KMINMAX = 1 };                       /* block score backbones */
+enum { SA_K_CONST = 0, SA_K_LINEAR_DECAY = 1 };              /* budget schedules */
+enum { SA_GATE_QUANTILE = 0, SA_GATE_FIXED = 1, SA_GATE_OFF = 2 }; /* gate threshold source */
+
+/* Shapes and scoring mode. */
+typedef struct sa_problem {
+  int32_t batch;        /* B >= 1 */
+  int32_t seqlen;       /* N, a multiple of block */
+  int32_t n_q_heads;    /* Hq, a multiple of n_kv_heads */
+  int32_t n_kv_heads;   /* Hkv >= 1 */
+  int32_t head_dim;     /* d: 64 or 128 */
+  int32_t block;        /* key block size: 64 or 128 */
+  int32_t tile;         /* query tile size: must equal block */
+  int32_t dtype;        /* SA_BF16 or SA_F32, for Q, K and V */
+  int32_t score_mode;   /* SA_KMEAN: mean-pooled keys; SA_KMINMAX: per-coordinate bound */
+  int32_t output_aware; /* 1: tile score times the block's mean value-row L2 norm */
+} sa_problem;
+
+/* Budget, forced blocks and gate.  n = seqlen / block tiles (= blocks) per sequence. */
+typedef struct sa_budget {
+  int32_t k_max;     /* free blocks kept per tile (constant budget), or the decay's start */
+  int32_t k_min;     /* floor of the decaying budget; 1 <= k_min <= k_max */
+  int32_t kind;      /* SA_K_CONST: k_t = k_max; SA_K_LINEAR_DECAY:
+                        k_t = max(k_min, floor(k_max * (n - t) / n)) */
+  int32_t n_sink;    /* blocks 0 .. n_sink-1 are always kept (on top of k); >= 0 */
+  int32_t gate_mode; /* SA_GATE_QUANTILE: tau_b = ceil(q*M_b)-th smallest sigma_bar over
+                        batch element b's M_b eligible tiles; SA_GATE_FIXED: tau = tau_fixed;
+                        SA_GATE_OFF: no tile trips */
+  float tau_fixed;   /* threshold for SA_GATE_FIXED */
+  double rho;        /* expansion factor >= 1: a tripped tile keeps floor(rho * k_t) */
+  double q;          /* quantile in [0, 1] for SA_GATE_QUANTILE */
+} sa_budget;
+
+/*
+ * Bytes of the block-summary buffer `sparse_attn_score` fills, for this problem.
+ * Layout (all fp32, n = seqlen / block):
+ *   SA_KMEAN:   kmean [B, n, Hkv, d]
+ *   SA_KMINMAX: kmin  [B, n, Hkv, d] followed by kmax [B, n, Hkv, d]
+ *   then, if output_aware: vnorm [B, n, Hkv]
+ * Returns 0 for an invalid problem (see sparse_attn_last_error).
+ */
+size_t sparse_attn_summary_bytes(const sa_problem* p);
+
+/* Bytes of device workspace `sparse_attn_select` needs.  0 for invalid arguments. */
+size_t sparse_attn_select_workspace_bytes(const sa_problem* p, const sa_budget* b);
+
+/*
+ * W, the entries per padded list: min(n, 1 + n_sink + floor(rho * k_max)).
+ * Returns a negative status for invalid arguments.
+ */
+int32_t sparse_attn_index_width(const sa_problem* p, const sa_budget* b);
+
+/*
+ * Block summaries (gated-selection page, Metodologia step 1; Stem page, output-aware metric).
+ *   K          [B, N, Hkv, d] in p->dtype.
+ *   V          [B, N, Hkv, d]; read only when p->output_aware, may be NULL otherwise.
+ *   summaries  sparse_attn_summary_bytes(p) bytes, written.
+ * Per block j and kv head g: kmean = (sum of the block's key rows in row order, fp32) / block;
+ * kmin/kmax = per-coordinate min/max (exact); vnorm = (sum over rows in order of the fp32
+ * L2 norm of the value row) / block.
+ */
+int sparse_attn_score(const sa_problem* p, const void* K, const void* V, void* summaries,
+                      void* stream);
+
+/*
+ * Selection (gated-selection page, Metodologia steps 2-5; Stem page, Metodologia A).
+ *   Q          [B, N, Hq, d] in p->dtype.
+ *   summaries  from sparse_attn_score on the same problem.
+ *   ws         sparse_attn_select_workspace_bytes(p, b) bytes of scratch, contents ignored.
+ *   kv_idx     int32 [B, Hq, n, W], W = sparse_attn_index_width(p, b): tile t's kept blocks
+ *              in ascending order (so the diagonal block t is last), then -1 sentinels.
+ *   kv_cnt     int32 [B, Hq, n]: number of non-sentinel entries.
+ *   sigma      optional (NULL to skip) fp32 [B, Hq, n]: cut margin per tile and head; 1.0
+ *              for a tile with at most k_t free candidates (not eligible).
+ *   sigma_bar  optional fp32 [B, n]: mean of sigma over the Hq heads.
+ *   gate       optional uint8 [B, n]: 1 where the tile tripped and kept floor(rho * k_t).
+ *   tau        optional fp32 [B]: the threshold used (-inf when nothing can trip).
+ * Free blocks of tile t are the causal blocks 0..t minus the forced ones (the diagonal t and
+ * the n_sink first blocks); they rank by tile score, ties to the lower index.  Scores are
+ * fp32 with a fixed reduction order, so the lists are reproducible bit for bit.
+ */
+int sparse_attn_select(const sa_problem* p, const sa_budget* b, const void* Q,
+                       const void* summaries, void* ws, size_t ws_bytes, int32_t* kv_idx,
+                       int32_t* kv_cnt, float* sigma, float* sigma_bar, uint8_t* gate,
+                       float* tau, void* stream);
+
+/*
+ * Sparse attention (Stem page, three-stage implementation; gated-selection page, step 5).
+ *   Q, K, V        BSHD in p->dtype.
+ *   kv_idx, kv_cnt as written by sparse_attn_select (any order of blocks is accepted; the
+ *                  list of query tile t ends at kv_cnt or at the first negative entry;
+ *                  entries must be distinct blocks <= t, others are skipped).
+ *   W              row stride of kv_idx (its last dimension), >= 1.
+ *   softmax_scale  logit scale, normally 1/sqrt(d).
+ *   O              [B, N, Hq, d] in out_dtype (SA_BF16 or SA_F32), written.
+ *   lse            optional fp32 [B, Hq, N]: natural-log log-sum-exp of the scaled logits.
+ * Row i of tile t attends to every key of its listed blocks at a position <= i.
+ * Precision: fp32 accumulation.  With bf16 inputs, Q K^T runs on bf16 matrix cores and P V on
+ * fp16 ones (P rounded to fp16, V converted exactly from bf16), so bf16 V values must lie
+ * below 65504 in magnitude.  fp32 inputs are computed in fp32 throughout.
+ */
+int sparse_attn_forward(const sa_problem* p, const void* Q, const void* K, const void* V,
+                        const int32_t* kv_idx, const int32_t* kv_cnt, int32_t W,
+                        float softmax_scale, void* O, int32_t out_dtype, float* lse,
+                        void* stream);
+
+/* The calling thread's last error message ("" if none).  Valid until its next call. */
+const char* sparse_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H_ */

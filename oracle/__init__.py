@@ -211,5 +211,10 @@ def forward(cfg: OracleCfg, Q, K, V, kv_idx, kv_cnt, softmax_scale: float, rows=
     return O, lse
 
 
+def threads() -> int:
+    """Host threads the oracle's parallel loops use."""
+    return int(_load().oracle_threads())
+
+
 def budget(cfg: OracleCfg, t: int) -> int:
     return int(_load().oracle_budget(ctypes.byref(cfg), t))

@@ -503,3 +503,7 @@ int oracle_cpu_ok(void) {
   __builtin_cpu_init();
   return __builtin_cpu_supports("fma") ? 1 : 0;
 }
+
+/* Threads the oracle's parallel loops use (OpenMP's current maximum). */
+#include <omp.h>
+int oracle_threads(void) { return omp_get_max_threads(); }

@@ -1,0 +1,157 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares, its structs have
+the layout the binding assumes, and invalid arguments are rejected before any HIP call."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_causal_mean_amd import api
+from block_sparse_causal_mean_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.LIB_PATH):
+        from block_sparse_causal_mean_amd import build
+        build.build()
+    return api.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_binding_exports():
+    assert _declared() == sorted(api.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared():
+        assert name in syms, name
+        assert hasattr(lib, name)
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "sparse_attn.h"\n'
+        "int main(void){\n"
+        'printf("%zu %zu %zu %zu %zu\\n", sizeof(sa_problem), sizeof(sa_budget),'
+        " offsetof(sa_budget, tau_fixed), offsetof(sa_budget, rho), offsetof(sa_budget, q));\n"
+        "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [ctypes.sizeof(api.Problem), ctypes.sizeof(api.Budget),
+            api.Budget.tau_fixed.offset, api.Budget.rho.offset, api.Budget.q.offset]
+    assert got == want
+
+
+def _ok_problem():
+    return api.problem(wl.WORKLOADS["llama8b_32k"])
+
+
+def _ok_budget():
+    return api.budget(wl.WORKLOADS["llama8b_32k"])
+
+
+def test_sizes(lib):
+    p, b = _ok_problem(), _ok_budget()
+    assert api.index_width(p, b) == 65
+    assert api.summary_bytes(p) == 1 * 512 * 8 * 128 * 4
+    assert api.select_workspace_bytes(p, b) >= 32 * 512 * 64 * 4
+    p5, b5 = api.problem(wl.WORKLOADS["stem_32k"]), api.budget(wl.WORKLOADS["stem_32k"])
+    assert api.summary_bytes(p5) == 4 * 512 * 8 * 128 * 4 + 4 * 512 * 8 * 4
+    assert api.index_width(p5, b5) == 131
+    p4 = api.problem(wl.WORKLOADS["quest_64k"])
+    assert api.summary_bytes(p4) == 2 * 1024 * 8 * 128 * 4
+
+
+BAD_PROBLEMS = [
+    (dict(head_dim=96), api.SA_ERR_UNSUPPORTED),
+    (dict(block=32, tile=32), api.SA_ERR_UNSUPPORTED),
+    (dict(tile=128), api.SA_ERR_UNSUPPORTED),
+    (dict(seqlen=1000), api.SA_ERR_INVALID),
+    (dict(n_q_heads=30), api.SA_ERR_INVALID),
+    (dict(batch=0), api.SA_ERR_INVALID),
+    (dict(dtype=7), api.SA_ERR_INVALID),
+    (dict(score_mode=2), api.SA_ERR_INVALID),
+    (dict(output_aware=3), api.SA_ERR_INVALID),
+    (dict(seqlen=64 * 16385), api.SA_ERR_UNSUPPORTED),
+]
+
+BAD_BUDGETS = [
+    dict(k_min=0), dict(k_max=3, k_min=5), dict(kind=5), dict(n_sink=-1), dict(gate_mode=9),
+    dict(rho=0.5), dict(rho=float("inf")), dict(q=1.5), dict(q=-0.1), dict(q=float("nan")),
+]
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("over,code", BAD_PROBLEMS)
+def test_invalid_problem_rejected_before_hip(lib, over, code):
+    p = _ok_problem()
+    for k, v in over.items():
+        setattr(p, k, v)
+    b = _ok_budget()
+    assert lib.sparse_attn_summary_bytes(ctypes.byref(p)) == 0
+    assert lib.sparse_attn_score(ctypes.byref(p), FAKE, FAKE, FAKE, None) == code
+    assert api.last_error()
+    assert lib.sparse_attn_select(ctypes.byref(p), ctypes.byref(b), FAKE, FAKE, FAKE, 1 << 40,
+                                  FAKE, FAKE, None, None, None, None, None) == code
+    assert lib.sparse_attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 65, 0.1, FAKE,
+                                   api.SA_BF16, None, None) == code
+
+
+@pytest.mark.parametrize("over", BAD_BUDGETS)
+def test_invalid_budget_rejected_before_hip(lib, over):
+    p, b = _ok_problem(), _ok_budget()
+    for k, v in over.items():
+        setattr(b, k, v)
+    assert lib.sparse_attn_index_width(ctypes.byref(p), ctypes.byref(b)) == api.SA_ERR_INVALID
+    assert lib.sparse_attn_select(ctypes.byref(p), ctypes.byref(b), FAKE, FAKE, FAKE, 1 << 40,
+                                  FAKE, FAKE, None, None, None, None, None) == api.SA_ERR_INVALID
+
+
+def test_null_pointers_and_small_buffers_rejected(lib):
+    p, b = _ok_problem(), _ok_budget()
+    r = lib.sparse_attn_score(ctypes.byref(p), None, FAKE, FAKE, None)
+    assert r == api.SA_ERR_INVALID and "non-NULL" in api.last_error()
+    p5 = api.problem(wl.WORKLOADS["stem_32k"])
+    assert lib.sparse_attn_score(ctypes.byref(p5), FAKE, None, FAKE, None) == api.SA_ERR_INVALID
+    need = api.select_workspace_bytes(p, b)
+    r = lib.sparse_attn_select(ctypes.byref(p), ctypes.byref(b), FAKE, FAKE, FAKE, need - 1,
+                               FAKE, FAKE, None, None, None, None, None)
+    assert r == api.SA_ERR_INVALID and "workspace" in api.last_error()
+    r = lib.sparse_attn_select(ctypes.byref(p), ctypes.byref(b), FAKE, FAKE, FAKE, need, None,
+                               FAKE, None, None, None, None, None)
+    assert r == api.SA_ERR_INVALID
+    assert lib.sparse_attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0.1, FAKE,
+                                   api.SA_BF16, None, None) == api.SA_ERR_INVALID
+    assert lib.sparse_attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 65, 0.1, FAKE,
+                                   5, None, None) == api.SA_ERR_INVALID
+    assert lib.sparse_attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 65,
+                                   float("inf"), FAKE, api.SA_BF16, None,
+                                   None) == api.SA_ERR_INVALID
+    assert lib.sparse_attn_score(None, FAKE, FAKE, FAKE, None) == api.SA_ERR_INVALID
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    w = wl.WORKLOADS["tiny_ref"]
+    x = torch.zeros(4)
+    with pytest.raises(ValueError):
+        api.score(api.problem(w), x, None, x)

@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same inputs.
+
+Selections (summaries, kv_idx, kv_cnt, sigma, sigma_bar, gate, tau) must match bit for bit;
+attention outputs within max-abs 1e-4 (fp32 inputs) or 2e-2 (bf16 inputs, fp32 accumulation),
+plus half a bf16 ulp of |O| when the output itself is stored in bf16.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_causal_mean_amd import api
+from block_sparse_causal_mean_amd import workloads as wl
+
+from parity import (assert_selection_equal, assert_summaries_equal, check_structure, out_tol,
+                    run_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+WL = wl.WORKLOADS
+
+# Small cases: the five recipes at sizes the oracle finishes in seconds (budgets scaled so
+# that many tiles are eligible and some trip), plus shapes with ragged counts and d = 64.
+SMALL = {
+    "tiny_ref": WL["tiny_ref"],
+    "llama8b_n32": WL["llama8b_32k"].resized(seqlen=2048, k_max=8, k_min=8),
+    "prefill_n32_planted": WL["prefill_128k"].resized(seqlen=4096, k_max=6, k_min=6),
+    "quest_n32": WL["quest_64k"].resized(seqlen=2048, k_max=6, k_min=6),
+    "stem_b2_n32": WL["stem_32k"].resized(batch=2, seqlen=2048, k_max=16, k_min=4),
+    "ragged_b3_n13_d64": WL["llama8b_32k"].resized(batch=3, seqlen=832, n_q_heads=6,
+                                                    n_kv_heads=2, head_dim=64, k_max=3,
+                                                    k_min=3, q=0.3),
+    "d64_blk128_quest_oam": WL["quest_64k"].resized(seqlen=2560, n_q_heads=4, n_kv_heads=2,
+                                                     head_dim=64, block=128, k_max=3, k_min=3,
+                                                     output_aware=1, n_sink=1),
+    "f32_d128_blk128": WL["tiny_ref"].resized(seqlen=2048, block=128, n_q_heads=4,
+                                               n_kv_heads=2, head_dim=128, k_max=3, k_min=3,
+                                               output_aware=1, score_mode=wl.KMINMAX),
+}
+
+MAX_ORACLE_ROWS = 6000
+
+
+def sample_rows(w, rng, max_rows=MAX_ORACLE_ROWS):
+    """All rows when cheap, else every row of tiles 0, 1 and n-1 of head 0 plus random rows."""
+    total = w.batch * w.seqlen * w.n_q_heads
+    if total <= max_rows:
+        return None
+    T = w.block
+    fixed = []
+    for t in (0, 1, w.n_blocks - 1):
+        for i in range(t * T, (t + 1) * T):
+            fixed.append((0, 0, i))
+    k = max_rows - len(fixed)
+    rnd = np.stack([rng.integers(0, w.batch, k), rng.integers(0, w.n_q_heads, k),
+                    rng.integers(0, w.seqlen, k)], axis=1)
+    return np.concatenate([np.array(fixed, np.int64), rnd.astype(np.int64)])
+
+
+def compare_outputs(w, g, inp, out_dtype, rows, with_lse=False):
+    cfg = oracle.make_cfg(w)
+    O_ref, lse_ref = oracle.forward(cfg, inp["Q"], inp["K"], inp["V"], g["kv_idx"],
+                                    g["kv_cnt"], g["scale"], rows=rows)
+    if rows is None:
+        O = g["O"]
+        lse = g.get("lse")
+    else:
+        O = g["O"][rows[:, 0], rows[:, 2], rows[:, 1]]
+        lse = g["lse"][rows[:, 0], rows[:, 1], rows[:, 2]] if with_lse else None
+        lse_ref = lse_ref
+    tol = out_tol(w, out_dtype, O_ref)
+    err = np.abs(O.astype(np.float64) - O_ref)
+    say(f"  max|O - O_ref| = {err.max():.3e}")
+    assert np.all(err <= tol), f"max err {err.max()} at {np.unravel_index(err.argmax(), err.shape)}"
+    if with_lse:
+        lse_ref_arr = lse_ref if rows is not None else lse_ref.transpose(0, 2, 1)
+        np.testing.assert_allclose(lse, lse_ref_arr, atol=1e-3 if w.dtype == wl.BF16 else 1e-5)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_pipeline_parity_small(name):
+    w = SMALL[name]
+    inp = wl.make_inputs(w)
+    cfg = oracle.make_cfg(w)
+    say(f"[{name}] oracle pool/select")
+    o_sum = oracle.pool(cfg, inp["K"], inp["V"])
+    o_sel = oracle.select(cfg, inp["Q"], o_sum)
+    out_dtype = api.SA_F32
+    say(f"[{name}] GPU pipeline (score, select, forward) fp32 out")
+    g = run_gpu(w, inp, out_dtype=out_dtype, with_lse=True)
+    assert_summaries_equal(w, g, o_sum)
+    assert_selection_equal(g, o_sel)
+    check_structure(w, g["kv_idx"], g["kv_cnt"], g["gate"], g["sigma"], g["sigma_bar"],
+                    g["tau"])
+    rows = sample_rows(w, np.random.default_rng(5))
+    compare_outputs(w, g, inp, out_dtype, rows, with_lse=True)
+    if w.dtype == wl.BF16:
+        say(f"[{name}] GPU pipeline bf16 out")
+        g2 = run_gpu(w, inp, out_dtype=api.SA_BF16)
+        np.testing.assert_array_equal(g2["kv_idx"], g["kv_idx"])
+        compare_outputs(w, g2, inp, api.SA_BF16, rows)
+
+
+def test_trips_happen_in_small_cases():
+    # The small cases exercise the gate: some tiles trip and expand.
+    w = SMALL["llama8b_n32"]
+    g = run_gpu(w, wl.make_inputs(w))
+    assert g["gate"].sum() >= 1
+    assert (g["kv_cnt"] > 1 + w.k_max).any()
+
+
+EDGE = {
+    "single_tile": WL["llama8b_32k"].resized(seqlen=64, k_max=2, k_min=2),
+    "dense_limit": WL["llama8b_32k"].resized(seqlen=1024, n_q_heads=4, n_kv_heads=2, k_max=64,
+                                             k_min=64),
+    "q0_no_trips": WL["llama8b_32k"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=1, k_max=4,
+                                             k_min=4, q=0.0),
+    "q1_all_trip": WL["llama8b_32k"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=1, k_max=4,
+                                             k_min=4, q=1.0),
+    "rho1": WL["llama8b_32k"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=1, k_max=4,
+                                      k_min=4, rho=1.0, q=0.5),
+    "rho_frac": WL["llama8b_32k"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=1, k_max=3,
+                                          k_min=3, rho=2.5, q=0.5),
+    "gate_off": WL["llama8b_32k"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=1, k_max=4,
+                                          k_min=4, gate_mode=wl.GATE_OFF),
+    "gate_fixed": WL["llama8b_32k"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=1, k_max=4,
+                                            k_min=4, gate_mode=wl.GATE_FIXED, tau_fixed=0.3),
+    "sinks_exceed": WL["stem_32k"].resized(batch=1, seqlen=640, n_q_heads=4, n_kv_heads=2,
+                                           n_sink=12, k_max=4, k_min=2),
+    "k1": WL["quest_64k"].resized(seqlen=1280, n_q_heads=8, n_kv_heads=8, k_max=1, k_min=1),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_cases(name):
+    w = EDGE[name]
+    inp = wl.make_inputs(w)
+    cfg = oracle.make_cfg(w)
+    say(f"[{name}] oracle + GPU")
+    o_sum = oracle.pool(cfg, inp["K"], inp["V"])
+    o_sel = oracle.select(cfg, inp["Q"], o_sum)
+    g = run_gpu(w, inp, out_dtype=api.SA_F32)
+    assert_summaries_equal(w, g, o_sum)
+    assert_selection_equal(g, o_sel)
+    check_structure(w, g["kv_idx"], g["kv_cnt"], g["gate"], g["sigma"], g["sigma_bar"],
+                    g["tau"])
+    compare_outputs(w, g, inp, api.SA_F32, sample_rows(w, np.random.default_rng(1)))
+    if name == "dense_limit":
+        assert np.all(g["kv_cnt"] == np.arange(1, w.n_blocks + 1))
+    if name == "q0_no_trips" or name == "gate_off":
+        assert g["gate"].sum() == 0
+    if name == "q1_all_trip":  # tau is the largest eligible sigma_bar: every eligible tile trips
+        assert g["gate"].sum() == w.n_blocks - w.k_max - 1
+
+
+def test_forward_any_block_order_and_skipped_entries():
+    """Order invariance of the online softmax (ART page, section 2.4); entries after the tile,
+    and a sentinel that cuts the list short, are honoured.  Every variant must meet the parity
+    bar against the oracle on the original lists."""
+    w = WL["stem_32k"].resized(batch=1, seqlen=1024, n_q_heads=4, n_kv_heads=2, k_max=4,
+                               k_min=2)
+    inp = wl.make_inputs(w)
+    d = {k: v.cuda() for k, v in inp.items()}
+    pf = api.Prefill(w, out_dtype=api.SA_F32)
+    pf.run(d["Q"], d["K"], d["V"])
+    torch.cuda.synchronize()
+    idx = pf.kv_idx.clone()
+    cnt = pf.kv_cnt.clone()
+    cfg = oracle.make_cfg(w)
+    O_ref, _ = oracle.forward(cfg, inp["Q"], inp["K"], inp["V"], idx.cpu().numpy(),
+                              cnt.cpu().numpy(), pf.scale)
+    base = pf.O.clone()
+
+    def check(O, label):
+        err = np.abs(O.cpu().numpy().astype(np.float64) - O_ref).max()
+        say(f"  {label}: max|O - O_ref| = {err:.3e}")
+        assert err <= 2e-2
+        assert (O - base).abs().max().item() <= 2e-3
+
+    check(base, "ascending")
+    rev = idx.clone()
+    for b, h, t in np.ndindex(*idx.shape[:3]):
+        c = int(cnt[b, h, t])
+        rev[b, h, t, :c] = idx[b, h, t, :c].flip(0)
+    pf.kv_idx.copy_(rev)
+    pf.forward(d["Q"], d["K"], d["V"])
+    torch.cuda.synchronize()
+    check(pf.O, "reversed")
+    # a wider list with a block after the tile first, then the list, then a sentinel before
+    # kv_cnt is reached
+    n, W = w.n_blocks, pf.W
+    W2 = W + 3
+    wide = torch.full((1, 4, n, W2), -1, dtype=torch.int32, device="cuda")
+    cnt2 = torch.zeros_like(cnt)
+    for h in range(4):
+        for t in range(n):
+            c = int(cnt[0, h, t])
+            row = idx[0, h, t, :c].tolist()
+            if t + 1 < n:
+                row = [t + 1] + row  # after the tile: skipped
+            wide[0, h, t, :len(row)] = torch.tensor(row, dtype=torch.int32)
+            cnt2[0, h, t] = len(row) + 2  # count runs past the sentinel
+    O2 = torch.empty_like(pf.O)
+    api.forward(pf.p, d["Q"], d["K"], d["V"], wide, cnt2, W2, pf.scale, O2, api.SA_F32)
+    torch.cuda.synchronize()
+    check(O2, "skipped entries")
+
+
+def test_runs_are_deterministic():
+    w = SMALL["stem_b2_n32"]
+    inp = wl.make_inputs(w)
+    a = run_gpu(w, inp)
+    b = run_gpu(w, inp)
+    for k in ("kA", "vn", "kv_idx", "kv_cnt", "sigma", "sigma_bar", "gate", "tau", "O"):
+        np.testing.assert_array_equal(a[k], b[k])
