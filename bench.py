@@ -82,10 +82,11 @@ def time_score_cold(pf: api.Prefill, K, V, reps: int = 10) -> float:
     return total / reps
 
 
-def cpu_baseline(w: wl.Workload, inp, n_tiles: int = 6) -> dict:
+def cpu_baseline(w: wl.Workload, inp, budget_s: float = 15.0, max_tiles: int = 48) -> dict:
     """The oracle on a bounded sample: block summaries of the whole sequence, then the
-    selection and the attention of every row of `n_tiles` query tiles spread over the
-    sequence (all heads), with the untripped budget."""
+    selection and the attention of every row of query tiles spread evenly over the second
+    half-plus of the sequence (all heads, untripped budget), until about `budget_s` seconds
+    of CPU work are spent."""
     import oracle
     cfg = oracle.make_cfg(w)
     threads = oracle.threads()
@@ -93,9 +94,15 @@ def cpu_baseline(w: wl.Workload, inp, n_tiles: int = 6) -> dict:
     summ = oracle.pool(cfg, inp["K"], inp["V"])
     t_pool = time.perf_counter() - t0
     n = w.n_blocks
-    tiles = sorted(set(int(x) for x in np.linspace(n // 4, n - 1, n_tiles)))
+    order = [int(x) for x in np.linspace(n // 4, n - 1, max_tiles)]
+    rng = np.random.default_rng(0)
+    order = list(rng.permutation(sorted(set(order))))
+    tiles = []
     t_sel = t_fwd = 0.0
-    for t in tiles:
+    for t in order:
+        if t_sel + t_fwd + t_pool >= budget_s:
+            break
+        tiles.append(int(t))
         b = 0
         t1 = time.perf_counter()
         one = oracle.select_tile(cfg, inp["Q"], summ, b, t)
@@ -110,8 +117,9 @@ def cpu_baseline(w: wl.Workload, inp, n_tiles: int = 6) -> dict:
         oracle.forward(cfg, inp["Q"], inp["K"], inp["V"], idx, cnt, 1.0 / math.sqrt(w.head_dim),
                        rows=rows)
         t_fwd += time.perf_counter() - t1
-        log(f"  cpu oracle tile {t}: select {t_sel:.1f}s forward {t_fwd:.1f}s")
+        log(f"  cpu oracle tile {t}: select {t_sel:.1f}s forward {t_fwd:.1f}s (cumulative)")
     tok = len(tiles) * w.tile
+    tiles = sorted(tiles)
     per_token = t_pool / (w.batch * w.seqlen) + (t_sel + t_fwd) / tok
     return {
         "value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle",

@@ -40,14 +40,22 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Maps a workgroup id to (b, h, t): tiles latest first; within a tile, heads in order.
+// Maps a workgroup id to (b, h, t).  Logical order: (batch, kv head) outermost, then tiles
+// latest first (late tiles carry the most blocks), then the q heads of the kv head.
+// Workgroups are dealt to the 8 XCDs round-robin by id, so when the count divides evenly the
+// id is remapped to give each XCD a contiguous range of that order: one XCD then works on one
+// kv head's tiles at a time and its L2 holds the blocks those tiles share.
 __device__ __forceinline__ void decode_wg(const Dims& dm, int& b, int& h, int& t) {
-  const int BH = dm.B * dm.Hq;
-  const int id = (int)blockIdx.x;
-  t = dm.n - 1 - id / BH;
-  const int bh = id - (id / BH) * BH;
-  b = bh / dm.Hq;
-  h = bh - b * dm.Hq;
+  const int U = dm.B * dm.Hq * dm.n;
+  int id = (int)blockIdx.x;
+  if ((U & 7) == 0) id = (id & 7) * (U >> 3) + (id >> 3);
+  const int per_pair = dm.n * dm.G;  // tiles x q heads of one (batch, kv head)
+  const int pair = id / per_pair;
+  const int rest = id - pair * per_pair;
+  t = dm.n - 1 - rest / dm.G;
+  const int r = rest - (rest / dm.G) * dm.G;
+  b = pair / dm.Hkv;
+  h = (pair - b * dm.Hkv) * dm.G + r;
 }
 
 // Index of the next usable list entry at or after e, or -1: the list ends at cnt or at the
@@ -67,17 +75,26 @@ union U4 {
   uint32_t w[4];
 };
 
+// Work split of the bf16 kernel: BLK/32 query groups of 32 rows times 2 key halves, one wave
+// each.  The two waves of a query group keep separate online-softmax states over their key
+// halves and merge them once at the end, so two waves per SIMD interleave their matrix-core
+// and vector work.
 template <int D, int BLK>
 struct Tiles {
-  static constexpr int NT = BLK * 2;              // BLK/32 waves of 64
-  static constexpr int KS = D + 8;                // LDS row stride of K (elements)
-  static constexpr int VS = BLK + 4;              // LDS row stride of V^T (elements)
-  static constexpr int KCH = BLK * D / 8;         // 16-byte chunks of a K block
-  static constexpr int KPT = KCH / NT;            // per thread
-  static constexpr int VMT = (BLK / 4) * (D / 8); // 4-key x 8-coordinate micro tiles of V
-  static constexpr int VPT = VMT / NT;            // per thread
-  static constexpr size_t LDS = sizeof(uint16_t) * ((size_t)BLK * KS + (size_t)D * VS);
-  static_assert(KCH % NT == 0 && VMT % NT == 0, "tile split");
+  static constexpr int QG = BLK / 32;              // query groups
+  static constexpr int NW = QG * 2;                // waves
+  static constexpr int NT = 64 * NW;               // threads (= 4 * BLK)
+  static constexpr int HK = BLK / 2;               // keys per wave per block
+  static constexpr int KT = HK / 32;               // 32-key tiles per wave per block
+  static constexpr int KS = D + 8;                 // LDS row stride of K (elements)
+  static constexpr int VS = BLK + 4;               // LDS row stride of V^T (elements)
+  static constexpr int KCH = BLK * D / 8;          // 16-byte chunks of a K block
+  static constexpr int KPT = (KCH + NT - 1) / NT;  // per thread
+  static constexpr int VMT = (BLK / 4) * (D / 8);  // 4-key x 8-coordinate micro tiles of V
+  static constexpr int VPT = (VMT + NT - 1) / NT;  // per thread
+  static constexpr size_t KV_LDS = sizeof(uint16_t) * ((size_t)BLK * KS + (size_t)D * VS);
+  static constexpr size_t MERGE_LDS = sizeof(float) * (size_t)QG * 64 * (D / 32 * 16 + 2);
+  static constexpr size_t LDS = KV_LDS > MERGE_LDS ? KV_LDS : MERGE_LDS;
 };
 
 template <int D, int BLK>
@@ -89,16 +106,21 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ K,
 #pragma unroll
   for (int i = 0; i < TL::KPT; ++i) {
     const int c = threadIdx.x + i * TL::NT;
-    const int r = c / (D / 8), col = c - r * (D / 8);
-    kr[i].v = *reinterpret_cast<const uint4*>(K + (row0 + r) * rstride + col * 8);
+    if (TL::KCH % TL::NT == 0 || c < TL::KCH) {
+      const int r = c / (D / 8), col = c - r * (D / 8);
+      kr[i].v = *reinterpret_cast<const uint4*>(K + (row0 + r) * rstride + col * 8);
+    }
   }
 #pragma unroll
   for (int i = 0; i < TL::VPT; ++i) {
     const int m = threadIdx.x + i * TL::NT;
-    const int kg = m / (D / 8), col = m - kg * (D / 8);
+    if (TL::VMT % TL::NT == 0 || m < TL::VMT) {
+      const int kg = m / (D / 8), col = m - kg * (D / 8);
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      vr[i][k].v = *reinterpret_cast<const uint4*>(V + (row0 + 4 * kg + k) * rstride + col * 8);
+      for (int k = 0; k < 4; ++k)
+        vr[i][k].v =
+            *reinterpret_cast<const uint4*>(V + (row0 + 4 * kg + k) * rstride + col * 8);
+    }
   }
 }
 
@@ -110,44 +132,51 @@ __device__ __forceinline__ void store_block(uint16_t* Ks, uint16_t* Vt,
 #pragma unroll
   for (int i = 0; i < TL::KPT; ++i) {
     const int c = threadIdx.x + i * TL::NT;
-    const int r = c / (D / 8), col = c - r * (D / 8);
-    *reinterpret_cast<uint4*>(Ks + r * TL::KS + col * 8) = kr[i].v;
+    if (TL::KCH % TL::NT == 0 || c < TL::KCH) {
+      const int r = c / (D / 8), col = c - r * (D / 8);
+      *reinterpret_cast<uint4*>(Ks + r * TL::KS + col * 8) = kr[i].v;
+    }
   }
 #pragma unroll
   for (int i = 0; i < TL::VPT; ++i) {
     const int m = threadIdx.x + i * TL::NT;
-    const int kg = m / (D / 8), col = m - kg * (D / 8);
+    if (TL::VMT % TL::NT == 0 || m < TL::VMT) {
+      const int kg = m / (D / 8), col = m - kg * (D / 8);
 #pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      // Coordinate col*8+dd of keys 4kg..4kg+3, bf16 -> fp32 (exact) -> fp16 (exact for
-      // |v| in [2^-14, 65504]; smaller magnitudes keep an absolute error below 2^-25).
-      const int wd = dd >> 1;
-      float x[4];
+      for (int dd = 0; dd < 8; ++dd) {
+        // Coordinate col*8+dd of keys 4kg..4kg+3, bf16 -> fp32 (exact) -> fp16 (exact for
+        // |v| in [2^-14, 65504]; smaller magnitudes keep an absolute error below 2^-25).
+        const int wd = dd >> 1;
+        float x[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) x[k] = (dd & 1) ? bf16_hi(vr[i][k].w[wd]) : bf16_lo(vr[i][k].w[wd]);
-      const f16x2 p01 = __builtin_convertvector((f32x2){x[0], x[1]}, f16x2);
-      const f16x2 p23 = __builtin_convertvector((f32x2){x[2], x[3]}, f16x2);
-      uint2 pk;
-      pk.x = *reinterpret_cast<const uint32_t*>(&p01);
-      pk.y = *reinterpret_cast<const uint32_t*>(&p23);
-      *reinterpret_cast<uint2*>(Vt + (col * 8 + dd) * TL::VS + 4 * kg) = pk;
+        for (int k = 0; k < 4; ++k)
+          x[k] = (dd & 1) ? bf16_hi(vr[i][k].w[wd]) : bf16_lo(vr[i][k].w[wd]);
+        const f16x2 p01 = __builtin_convertvector((f32x2){x[0], x[1]}, f16x2);
+        const f16x2 p23 = __builtin_convertvector((f32x2){x[2], x[3]}, f16x2);
+        uint2 pk;
+        pk.x = *reinterpret_cast<const uint32_t*>(&p01);
+        pk.y = *reinterpret_cast<const uint32_t*>(&p23);
+        *reinterpret_cast<uint2*>(Vt + (col * 8 + dd) * TL::VS + 4 * kg) = pk;
+      }
     }
   }
 }
 
+// A row's running maximum is only raised when a new logit exceeds it by more than this many
+// powers of two; until then probabilities may reach 2^kLazy, which fp16 P and the fp32
+// accumulators hold exactly enough, and the rescale of O is skipped.
+constexpr float kLazy = 8.0f;
+
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) void attn_bf16(Dims dm, const uint16_t* __restrict__ Q,
-                                                     const uint16_t* __restrict__ K,
-                                                     const uint16_t* __restrict__ V,
-                                                     const int32_t* __restrict__ kv_idx,
-                                                     const int32_t* __restrict__ kv_cnt,
-                                                     int W, float scale_log2,
-                                                     void* __restrict__ O, int out_f32,
-                                                     float* __restrict__ lse) {
+__global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BLK>::NT
+    Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const int32_t* __restrict__ kv_idx,
+    const int32_t* __restrict__ kv_cnt, int W, float scale_log2, void* __restrict__ O,
+    int out_f32, float* __restrict__ lse) {
   using TL = Tiles<D, BLK>;
-  constexpr int KT = BLK / 32;  // 32-key tiles per block
-  constexpr int DT = D / 32;    // 32-coordinate tiles of the output
-  constexpr int DC = D / 16;    // 16-coordinate chunks of the QK^T contraction
+  constexpr int KT = TL::KT;
+  constexpr int DT = D / 32;  // 32-coordinate tiles of the output
+  constexpr int DC = D / 16;  // 16-coordinate chunks of the QK^T contraction
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* Ks = smem;
   uint16_t* Vt = smem + BLK * TL::KS;
@@ -156,11 +185,13 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16(Dims dm, const uint16_t* __
   decode_wg(dm, b, h, t);
   const int g = h / dm.G;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int qg = wv % TL::QG, kh = wv / TL::QG;  // query group, key half
   const int l32 = lane & 31, hi = lane >> 5;
   const size_t bht = ((size_t)b * dm.Hq + h) * dm.n + t;
   const int32_t* list = kv_idx + bht * W;
   const int cnt = min(kv_cnt[bht], W);
-  const int qrow = t * BLK + wv * 32 + l32;  // this lane's query position
+  const int qloc = qg * 32 + l32;  // this lane's query row within the tile
+  const int qrow = t * BLK + qloc;
   const int rstride = dm.Hkv * D;
 
   // Q fragment (B operand of S^T = K Q^T): lane holds coordinates 16c + 8*hi .. +7 of its row.
@@ -174,7 +205,8 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16(Dims dm, const uint16_t* __
   f32x16 acc_o[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) acc_o[i] = (f32x16){};
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY;  // running max of raw logits (before scaling) for this lane's row
+  float l_run = 0.0f;       // this lane's share of the row's softmax denominator
 
   U4 kr[TL::KPT];
   U4 vr[TL::VPT][4];
@@ -194,12 +226,12 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16(Dims dm, const uint16_t* __
     const int e2 = next_entry(list, cnt, e + 1, t);
     if (e2 >= 0) load_block<D, BLK>(Kg, Vg, kvbase + (size_t)list[e2] * BLK, rstride, kr, vr);
 
-    // S^T = K Q^T for the block: KT tiles of 32 keys x 32 queries.
+    // S^T = K Q^T over this wave's key half: KT tiles of 32 keys x 32 queries.
     f32x16 s[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       s[kt] = (f32x16){};
-      const uint16_t* kp = Ks + (kt * 32 + l32) * TL::KS + 8 * hi;
+      const uint16_t* kp = Ks + (kh * TL::HK + kt * 32 + l32) * TL::KS + 8 * hi;
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + 16 * c);
@@ -207,27 +239,36 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16(Dims dm, const uint16_t* __
       }
     }
 
-    // Online softmax in the log2 domain.  Lane value (kt, i, r) is key kt*32 + 8i + 4*hi + r.
-    const bool masked = j >= t;
-    const int qloc = wv * 32 + l32;
+    // Online softmax.  Lane value (kt, i, r) is key kh*HK + kt*32 + 8i + 4*hi + r of the
+    // block; the causal mask only touches the diagonal block.
+    if (j >= t) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kloc = kh * TL::HK + kt * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+          if (j > t || kloc > qloc) s[kt][v] = -INFINITY;
+        }
+    }
     float mloc = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = s[kt][v] * scale_log2;
-        if (masked) {
-          const int kloc = kt * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-          if (j > t || kloc > qloc) x = -INFINITY;
-        }
-        s[kt][v] = x;
-        mloc = fmaxf(mloc, x);
-      }
+      for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[kt][v]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    // Raise the running max only when a logit exceeds it by more than 2^kLazy in
+    // probability; the first finite block always sets it.
+    const bool raise = mloc > m_run && (m_run == -INFINITY || (mloc - m_run) * scale_log2 > kLazy);
+    if (__any(raise)) {
+      const float m_new = raise ? mloc : m_run;
+      const float alpha = m_run == -INFINITY ? 0.0f
+                                             : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
+    }
+    const float mc = m_run == -INFINITY ? 0.0f : -m_run * scale_log2;
 
     float psum = 0.0f;
     f16x8 pf[KT][2];
@@ -235,19 +276,17 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16(Dims dm, const uint16_t* __
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(s[kt][v] - m_use);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], scale_log2, mc));
         psum += p;
         pf[kt][v >> 3][v & 7] = (_Float16)p;
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
+    l_run += psum;
 
     // O^T += V^T P^T.  B operand slot 8*hi + 4i' + r of pf[kt][half] is key
-    // kt*32 + 16*half + 8i' + 4*hi + r; the A operand reads V^T at the same keys.
+    // kh*HK + kt*32 + 16*half + 8i' + 4*hi + r; the A operand reads V^T at the same keys.
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* vp = Vt + (dt * 32 + l32) * TL::VS + 4 * hi;
+      const uint16_t* vp = Vt + (dt * 32 + l32) * TL::VS + kh * TL::HK + 4 * hi;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -266,7 +305,26 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16(Dims dm, const uint16_t* __
     e = e2;
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // Merge the two key halves of each query group through LDS (the K/V buffer is free now).
+  float* mrg = reinterpret_cast<float*>(smem);
+  float* mO = mrg + (size_t)qg * 64 * (DT * 16 + 2);  // [DT*16 values][64 lanes], then m, l
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mO[(dt * 16 + v) * 64 + lane] = acc_o[dt][v];
+    mO[DT * 16 * 64 + lane] = m_run;
+    mO[(DT * 16 + 1) * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const float m1 = mO[DT * 16 * 64 + lane];
+  const float l1 = mO[(DT * 16 + 1) * 64 + lane];
+  const float m = fmaxf(m_run, m1);
+  const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_run - m) * scale_log2);
+  const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
+  const float l_lane = l_run * a0 + l1 * a1;
+  const float l_tot = l_lane + __shfl_xor(l_lane, 32);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const size_t orow = (((size_t)b * dm.N + qrow) * dm.Hq + h) * D;
 #pragma unroll
@@ -274,21 +332,25 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16(Dims dm, const uint16_t* __
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d0 = dt * 32 + 8 * i + 4 * hi;
-      const float o0 = acc_o[dt][4 * i] * inv, o1 = acc_o[dt][4 * i + 1] * inv;
-      const float o2 = acc_o[dt][4 * i + 2] * inv, o3 = acc_o[dt][4 * i + 3] * inv;
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = 4 * i + r;
+        o[r] = (acc_o[dt][v] * a0 + mO[(dt * 16 + v) * 64 + lane] * a1) * inv;
+      }
       if (out_f32) {
         *reinterpret_cast<float4*>(static_cast<float*>(O) + orow + d0) =
-            make_float4(o0, o1, o2, o3);
+            make_float4(o[0], o[1], o[2], o[3]);
       } else {
         uint2 pk;
-        pk.x = f32_to_bf16_bits(o0) | (f32_to_bf16_bits(o1) << 16);
-        pk.y = f32_to_bf16_bits(o2) | (f32_to_bf16_bits(o3) << 16);
+        pk.x = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+        pk.y = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(O) + orow + d0) = pk;
       }
     }
   if (lse && hi == 0)
     lse[((size_t)b * dm.Hq + h) * dm.N + qrow] =
-        l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        l_tot > 0.0f ? (m * scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------- fp32 (VALU) path
