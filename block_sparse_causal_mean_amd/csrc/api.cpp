@@ -106,12 +106,7 @@ int check_budget(const sa_budget* b, const sa::Dims& D, sa::BudgetDev* bd) {
   return SA_OK;
 }
 
-size_t summary_bytes(const sa::Dims& D) {
-  const size_t plane = (size_t)D.B * D.n * D.Hkv * D.d * sizeof(float);
-  size_t total = plane * (D.score_mode == SA_KMINMAX ? 2 : 1);
-  if (D.oam) total += (size_t)D.B * D.n * D.Hkv * sizeof(float);
-  return total;
-}
+size_t summary_bytes(const sa::Dims& D) { return sa::summary_layout(D).bytes; }
 
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return SA_OK;

@@ -40,24 +40,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Maps a workgroup id to (b, h, t).  Logical order: (batch, kv head) outermost, then tiles
-// latest first (late tiles carry the most blocks), then the q heads of the kv head.
-// Workgroups are dealt to the 8 XCDs round-robin by id, so when the count divides evenly the
-// id is remapped to give each XCD a contiguous range of that order: one XCD then works on one
-// kv head's tiles at a time and its L2 holds the blocks those tiles share.
-__device__ __forceinline__ void decode_wg(const Dims& dm, int& b, int& h, int& t) {
-  const int U = dm.B * dm.Hq * dm.n;
-  int id = (int)blockIdx.x;
-  if ((U & 7) == 0) id = (id & 7) * (U >> 3) + (id >> 3);
-  const int per_pair = dm.n * dm.G;  // tiles x q heads of one (batch, kv head)
-  const int pair = id / per_pair;
-  const int rest = id - pair * per_pair;
-  t = dm.n - 1 - rest / dm.G;
-  const int r = rest - (rest / dm.G) * dm.G;
-  b = pair / dm.Hkv;
-  h = (pair - b * dm.Hkv) * dm.G + r;
-}
-
 // Index of the next usable list entry at or after e, or -1: the list ends at cnt or at the
 // first negative entry; entries after the tile (j > t) are skipped.
 __device__ __forceinline__ int next_entry(const int32_t* __restrict__ list, int cnt, int e,
@@ -182,7 +164,7 @@ __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BL
   uint16_t* Vt = smem + BLK * TL::KS;
 
   int b, h, t;
-  decode_wg(dm, b, h, t);
+  decode_tile(dm, b, h, t);
   const int g = h / dm.G;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int qg = wv % TL::QG, kh = wv / TL::QG;  // query group, key half
@@ -367,7 +349,7 @@ __global__ __launch_bounds__(BLK) void attn_f32(Dims dm, const float* __restrict
   float* Kb = fsm;            // [BLK][D]
   float* Vb = fsm + BLK * D;  // [BLK][D]
   int b, h, t;
-  decode_wg(dm, b, h, t);
+  decode_tile(dm, b, h, t);
   const int g = h / dm.G;
   const size_t bht = ((size_t)b * dm.Hq + h) * dm.n + t;
   const int32_t* list = kv_idx + bht * W;

@@ -52,6 +52,49 @@ struct BudgetDev {
   int W;  // entries per padded list
 };
 
+// Layout of the block-summary buffer.  The public part (documented in the header) comes
+// first: the fp32 planes [B, n, Hkv, d] (kmean, or kmin then kmax) and, when output-aware,
+// vnorm [B, n, Hkv].  The library-private part follows: knorm [B, n, Hkv] (fp32 L2 norm of
+// each block's scoring vector) and, 256-byte aligned, a bf16 hi and lo split of every fp32
+// plane (hi = bf16(x), lo = bf16(x - hi)) used by the matrix-core score prefilter.
+struct SummaryLayout {
+  size_t plane;    // elements of one [B, n, Hkv, d] plane
+  int nplanes;     // 1 (kmean) or 2 (kmin, kmax)
+  size_t vn;       // float offset of vnorm (valid when output-aware)
+  size_t kn;       // float offset of knorm
+  size_t bf_byte;  // byte offset of the bf16 planes: hi(0), lo(0), hi(1), lo(1)
+  size_t bytes;    // total
+};
+inline SummaryLayout summary_layout(const Dims& D) {
+  SummaryLayout L;
+  L.plane = (size_t)D.B * D.n * D.Hkv * D.d;
+  L.nplanes = D.score_mode == SA_KMINMAX ? 2 : 1;
+  const size_t blocks = (size_t)D.B * D.n * D.Hkv;
+  L.vn = L.plane * L.nplanes;
+  L.kn = L.vn + (D.oam ? blocks : 0);
+  L.bf_byte = ((L.kn + blocks) * sizeof(float) + 255) & ~(size_t)255;
+  L.bytes = L.bf_byte + (size_t)L.nplanes * 2 * L.plane * sizeof(uint16_t);
+  return L;
+}
+
+// Maps a workgroup id to (b, h, t).  Logical order: (batch, kv head) outermost, then tiles
+// latest first (late tiles carry the most blocks), then the q heads of the kv head.
+// Workgroups are dealt to the 8 XCDs round-robin by id, so when the count divides evenly the
+// id is remapped to give each XCD a contiguous range of that order: one XCD then works on one
+// kv head's tiles at a time and its L2 holds the blocks (and block summaries) they share.
+__device__ __forceinline__ void decode_tile(const Dims& dm, int& b, int& h, int& t) {
+  const int U = dm.B * dm.Hq * dm.n;
+  int id = (int)blockIdx.x;
+  if ((U & 7) == 0) id = (id & 7) * (U >> 3) + (id >> 3);
+  const int per_pair = dm.n * dm.G;  // tiles x q heads of one (batch, kv head)
+  const int pair = id / per_pair;
+  const int rest = id - pair * per_pair;
+  t = dm.n - 1 - rest / dm.G;
+  const int r = rest - (rest / dm.G) * dm.G;
+  b = pair / dm.Hkv;
+  h = (pair - b * dm.Hkv) * dm.G + r;
+}
+
 // Workspace layout of sparse_attn_select (byte offsets, 256-byte aligned).
 struct SelectWs {
   size_t ranked, sigma, sigma_bar, gate, tau, total;

@@ -13,7 +13,9 @@
 //   [Hkv, d] is contiguous, so each thread owns 16 bytes of the span and walks the block's
 //   rows in order: every load instruction of a wave reads 1 KiB contiguous, and the fp32
 //   accumulation per coordinate runs in row order (the fixed reduction order the selection
-//   relies on for reproducible results).
+//   relies on for reproducible results).  It also writes, for the selection's matrix-core
+//   prefilter, each summary's bf16 hi/lo split and the block's L2 norm (an upper bound
+//   ingredient only: it never decides a selection by itself).
 // value_norms: one workgroup per (batch, block).  Each (row, kv head) pair's squared norm is
 //   a fused multiply-add chain over the d coordinates in order, by one thread; the square
 //   roots go to LDS and one thread per kv head sums them in row order.
@@ -45,15 +47,25 @@ struct Vec16<float> {
   }
 };
 
-template <typename T, int MODE, int BLK>
+// Splits x into bf16 hi = RN(x) and lo = RN(x - hi) (x - hi is exact in fp32), packed as
+// bf16 bits into the low halves of the returned pair.
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16_bits(x);
+  lo = f32_to_bf16_bits(x - __uint_as_float(hi << 16));
+}
+
+template <typename T, int MODE, int BLK, int HD>
 __global__ __launch_bounds__(kPoolThreads) void pool_keys(const T* __restrict__ K,
-                                                          float* __restrict__ out, int N,
-                                                          int n, int span, size_t plane) {
+                                                          float* __restrict__ summ,
+                                                          uint16_t* __restrict__ bfp, int N,
+                                                          int n, int span, size_t plane,
+                                                          size_t kn_off) {
   constexpr int E = Vec16<T>::N;
-  const int bj = blockIdx.x;  // b * n + j
+  constexpr int LPH = HD / E;  // lanes per head (consecutive lanes of one wave)
+  const int bj = blockIdx.x;   // b * n + j
   const int b = bj / n, j = bj - b * n;
   const int e0 = (blockIdx.y * kPoolThreads + threadIdx.x) * E;
-  if (e0 >= span) return;
+  if (e0 >= span) return;  // whole heads drop out together: span is a multiple of HD
   const T* src = K + ((size_t)b * N + (size_t)j * BLK) * span + e0;
 
   float a[E], c[E];
@@ -79,18 +91,52 @@ __global__ __launch_bounds__(kPoolThreads) void pool_keys(const T* __restrict__ 
       }
     }
   }
-  float* dst = out + (size_t)bj * span + e0;
+  const size_t o = (size_t)bj * span + e0;
+  float ss = 0.0f;  // squared norm share of the block's scoring vector (for the prefilter bound)
   if (MODE == SA_KMEAN) {
     const float inv = 1.0f / (float)BLK;  // exact: BLK is a power of two
 #pragma unroll
-    for (int i = 0; i < E; ++i) dst[i] = a[i] * inv;
+    for (int i = 0; i < E; ++i) {
+      a[i] = a[i] * inv;
+      summ[o + i] = a[i];
+      ss = __builtin_fmaf(a[i], a[i], ss);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      dst[i] = canon(a[i]);
-      dst[plane + i] = canon(c[i]);
+      a[i] = canon(a[i]);
+      c[i] = canon(c[i]);
+      summ[o + i] = a[i];
+      summ[plane + o + i] = c[i];
+      ss = __builtin_fmaf(fmaxf(a[i] * a[i], c[i] * c[i]), 1.0f, ss);
     }
   }
+  // bf16 hi/lo planes: plane p's hi at bfp + 2p*plane, lo at bfp + (2p+1)*plane.
+#pragma unroll
+  for (int p = 0; p < (MODE == SA_KMEAN ? 1 : 2); ++p) {
+    const float* v = p == 0 ? a : c;
+    uint32_t hw[E / 2], lw[E / 2];
+#pragma unroll
+    for (int i = 0; i < E; i += 2) {
+      uint32_t h0, l0, h1, l1;
+      split_bf16(v[i], h0, l0);
+      split_bf16(v[i + 1], h1, l1);
+      hw[i / 2] = h0 | (h1 << 16);
+      lw[i / 2] = l0 | (l1 << 16);
+    }
+    uint16_t* hp = bfp + (size_t)(2 * p) * plane + o;
+    uint16_t* lp = bfp + (size_t)(2 * p + 1) * plane + o;
+    if (E == 8) {
+      *reinterpret_cast<uint4*>(hp) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4*>(lp) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    } else {
+      *reinterpret_cast<uint2*>(hp) = make_uint2(hw[0], hw[1]);
+      *reinterpret_cast<uint2*>(lp) = make_uint2(lw[0], lw[1]);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < LPH; off <<= 1) ss += __shfl_xor(ss, off);
+  if (e0 % HD == 0) summ[kn_off + (size_t)bj * (span / HD) + e0 / HD] = __builtin_sqrtf(ss);
 }
 
 template <typename T, int BLK, int D>
@@ -125,15 +171,22 @@ __global__ __launch_bounds__(kPoolThreads) void value_norms(const T* __restrict_
   }
 }
 
-template <typename T, int MODE, int BLK>
+template <typename T, int MODE, int BLK, int HD>
 hipError_t launch_keys(const Dims& D, const void* K, float* summ, hipStream_t s) {
+  const SummaryLayout L = summary_layout(D);
   const int span = D.Hkv * D.d;
   const int per_wg = kPoolThreads * Vec16<T>::N;
   dim3 grid((unsigned)(D.B * D.n), (unsigned)((span + per_wg - 1) / per_wg));
-  const size_t plane = (size_t)D.B * D.n * span;
-  hipLaunchKernelGGL((pool_keys<T, MODE, BLK>), grid, dim3(kPoolThreads), 0, s,
-                     static_cast<const T*>(K), summ, D.N, D.n, span, plane);
+  uint16_t* bfp = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(summ) + L.bf_byte);
+  hipLaunchKernelGGL((pool_keys<T, MODE, BLK, HD>), grid, dim3(kPoolThreads), 0, s,
+                     static_cast<const T*>(K), summ, bfp, D.N, D.n, span, L.plane, L.kn);
   return hipGetLastError();
+}
+
+template <typename T, int MODE, int BLK>
+hipError_t launch_keys_d(const Dims& D, const void* K, float* summ, hipStream_t s) {
+  return D.d == 64 ? launch_keys<T, MODE, BLK, 64>(D, K, summ, s)
+                   : launch_keys<T, MODE, BLK, 128>(D, K, summ, s);
 }
 
 template <typename T, int BLK, int HD>
@@ -150,14 +203,13 @@ hipError_t pool_dispatch(const Dims& D, const void* K, const void* V, float* sum
                          hipStream_t s) {
   hipError_t e;
   if (D.score_mode == SA_KMEAN)
-    e = D.blk == 64 ? launch_keys<T, SA_KMEAN, 64>(D, K, summ, s)
-                    : launch_keys<T, SA_KMEAN, 128>(D, K, summ, s);
+    e = D.blk == 64 ? launch_keys_d<T, SA_KMEAN, 64>(D, K, summ, s)
+                    : launch_keys_d<T, SA_KMEAN, 128>(D, K, summ, s);
   else
-    e = D.blk == 64 ? launch_keys<T, SA_KMINMAX, 64>(D, K, summ, s)
-                    : launch_keys<T, SA_KMINMAX, 128>(D, K, summ, s);
+    e = D.blk == 64 ? launch_keys_d<T, SA_KMINMAX, 64>(D, K, summ, s)
+                    : launch_keys_d<T, SA_KMINMAX, 128>(D, K, summ, s);
   if (e != hipSuccess || !D.oam) return e;
-  const size_t plane = (size_t)D.B * D.n * D.Hkv * D.d;
-  float* vn = summ + plane * (D.score_mode == SA_KMINMAX ? 2 : 1);
+  float* vn = summ + summary_layout(D).vn;
   if (D.blk == 64)
     return D.d == 64 ? launch_vn<T, 64, 64>(D, V, vn, s) : launch_vn<T, 64, 128>(D, V, vn, s);
   return D.d == 64 ? launch_vn<T, 128, 64>(D, V, vn, s) : launch_vn<T, 128, 128>(D, V, vn, s);

@@ -38,6 +38,9 @@
 namespace sa {
 namespace {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 __device__ __forceinline__ int budget_at(const BudgetDev& bd, int t, int n) {
   if (bd.kind == SA_K_CONST) return bd.k_max;
   const long long k = (long long)bd.k_max * (n - t) / n;
@@ -172,6 +175,216 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
   const int R = min(max(expanded(bd, kt), kt), nf);
   int* out = ranked + bht * bd.R;
   for (int r = threadIdx.x; r < R; r += NT) out[r] = (int)(0xffffffffu - (unsigned)keys[r]);
+  if (threadIdx.x == 0) {
+    const float s0 = order_key_inv((unsigned)(keys[0] >> 32));
+    const float sk1 = order_key_inv((unsigned)(keys[kt - 1] >> 32));
+    const float sk = order_key_inv((unsigned)(keys[kt] >> 32));
+    const float num = sk1 - sk;
+    const float den = s0 - sk;
+    sigma[bht] = den == 0.0f ? 0.0f : __fdiv_rn(num, den);
+  }
+}
+
+// ------------------------------------------------------------- score_rank (bf16 inputs)
+//
+// Same canonical scores as score_rank, computed where they matter.  For a block j the tile
+// score is max_i s_ij over the tile's rows; only the row that attains it needs the canonical
+// fp32 chain.  A matrix-core pass computes approximate scores for every (row, block):
+//   shat_ij = q_i . (hi_j + lo_j)   (bf16 MFMA, fp32 accumulation; hi/lo = bf16 split of
+//                                     the fp32 summary, so q_i . (hi + lo) misses at most
+//                                     2^-16 |q_i| |x_j|)
+// with |shat_ij - s_ij| <= E_j = c * max_i |q_i| * |x_j| (x_j the block's scoring vector;
+// c covers the canonical chain's own rounding, the split residual and the accumulation of
+// 4d products in fp32, with a margin of about 9x).  The row attaining max_i s_ij then
+// satisfies shat_ij >= max_i shat_ij - 2 E_j, so recomputing the canonical chain for exactly
+// those rows and taking their maximum gives the canonical tile score.  Almost always one row
+// per block qualifies, so the fp32 chain work falls by about the tile height.
+//
+// One workgroup (4 waves) per (b, h, t).  The tile's Q rows are staged in LDS as bf16 (for
+// the bound backbone as its positive and negative parts, so q+ . kmax + q- . kmin gives
+// the per-coordinate maximum); each wave takes 32-block chunks of the free blocks, holds a
+// 32-block x all-rows score tile in accumulators (lane = block, 16 rows per 32-row tile),
+// finds each block's candidate rows lane-locally, runs their canonical chains (q from LDS,
+// the fp32 summary from L2) and writes the block's order key.
+
+constexpr int kScoreThreads = 256;
+constexpr float kPrefilterC = 0x1p-11f;
+
+template <int MODE, int OAM, int D, int TILE>
+__global__ __launch_bounds__(kScoreThreads) void score_rank_mfma(
+    Dims dm, BudgetDev bd, const uint16_t* __restrict__ Q, const float* __restrict__ summ,
+    const uint16_t* __restrict__ bfp, int* __restrict__ ranked, float* __restrict__ sigma,
+    size_t plane, size_t vn_off, size_t kn_off) {
+  constexpr int NPL = MODE == SA_KMINMAX ? 2 : 1;  // staged Q planes (q, or q+ and q-)
+  constexpr int QS = D + 8;                        // LDS row stride (bf16 elements)
+  constexpr int RT = TILE / 32;                    // 32-row tiles
+  constexpr int KS = D / 16;                       // 16-coordinate MFMA steps
+  extern __shared__ __attribute__((aligned(16))) unsigned long long keys[];
+  __shared__ unsigned int qmax_bits;
+
+  int b, h, t;
+  decode_tile(dm, b, h, t);
+  const int n = dm.n;
+  const int g = h / dm.G;
+  const size_t bht = ((size_t)b * dm.Hq + h) * n + t;
+  const int kt = budget_at(bd, t, n);
+  const int nf = n_free(bd, t);
+  if (nf <= kt) {
+    if (threadIdx.x == 0) sigma[bht] = 1.0f;
+    return;
+  }
+  const int j0 = t < bd.n_sink ? t : bd.n_sink;
+  int P = 1;
+  while (P < nf) P <<= 1;
+  int Palloc = 1;
+  while (Palloc < n) Palloc <<= 1;
+  uint16_t* qs = reinterpret_cast<uint16_t*>(keys + Palloc);  // [NPL][TILE][QS]
+
+  for (int f = threadIdx.x; f < P; f += kScoreThreads)
+    keys[f] = f < nf ? (unsigned long long)(0xffffffffu - (unsigned)(j0 + f)) : 0ull;
+  if (threadIdx.x == 0) qmax_bits = 0u;
+  __syncthreads();
+
+  // Stage the tile's Q rows; row norms (any order: they only scale the bound) -> max.
+  {
+    constexpr int CH = TILE * D / 8;  // 16-byte chunks
+    constexpr int CPR = D / 8;        // chunks per row (consecutive threads)
+    const uint16_t* qsrc = Q + (((size_t)b * dm.N + (size_t)t * TILE) * dm.Hq + h) * D;
+    float rmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CH / kScoreThreads; ++i) {
+      const int c = threadIdx.x + i * kScoreThreads;
+      const int r = c / CPR, col = c - r * CPR;
+      uint4 v = *reinterpret_cast<const uint4*>(qsrc + (size_t)r * dm.Hq * D + col * 8);
+      float ss = 0.0f;
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lo = bf16_lo(w[k]), hi = bf16_hi(w[k]);
+        ss = __builtin_fmaf(lo, lo, ss);
+        ss = __builtin_fmaf(hi, hi, ss);
+      }
+#pragma unroll
+      for (int off = 1; off < CPR; off <<= 1) ss += __shfl_xor(ss, off);
+      rmax = fmaxf(rmax, ss);
+      if (MODE == SA_KMEAN) {
+        *reinterpret_cast<uint4*>(qs + r * QS + col * 8) = v;
+      } else {
+        uint32_t pw[4], nw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t neg = ((w[k] >> 15) & 0x00010001u) * 0xffffu;  // negative halves
+          pw[k] = w[k] & ~neg;
+          nw[k] = w[k] & neg;
+        }
+        *reinterpret_cast<uint4*>(qs + r * QS + col * 8) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+        *reinterpret_cast<uint4*>(qs + (TILE + r) * QS + col * 8) =
+            make_uint4(nw[0], nw[1], nw[2], nw[3]);
+      }
+    }
+    atomicMax(&qmax_bits, __float_as_uint(rmax));  // non-negative floats order as integers
+  }
+  __syncthreads();
+  const float qmax = __builtin_sqrtf(__uint_as_float(qmax_bits));
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const size_t kstride = (size_t)dm.Hkv * D;
+  const size_t kb0 = ((size_t)b * n * dm.Hkv + g) * D;  // element offset of block 0, kv head g
+  const int nchunks = (nf + 31) >> 5;
+
+  for (int ch = wv; ch < nchunks; ch += kScoreThreads / 64) {
+    const int j = j0 + ch * 32 + l32;  // this lane's block
+    const bool valid = j < t;
+    const size_t kofs = kb0 + (size_t)(valid ? j : j0) * kstride;
+
+    f32x16 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = (f32x16){};
+#pragma unroll
+    for (int pl = 0; pl < NPL; ++pl) {
+      // q . x with x = kmean; or q+ . kmax + q- . kmin (kmax is plane 1, kmin plane 0)
+      const int xp = MODE == SA_KMINMAX ? 1 - pl : 0;
+      const uint16_t* bh_ = bfp + (size_t)(2 * xp) * plane + kofs + 8 * hi;
+      const uint16_t* bl_ = bfp + (size_t)(2 * xp + 1) * plane + kofs + 8 * hi;
+      const uint16_t* ap = qs + (size_t)(pl * TILE + l32) * QS + 8 * hi;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 bhv = *reinterpret_cast<const bf16x8*>(bh_ + 16 * ks);
+        const bf16x8 blv = *reinterpret_cast<const bf16x8*>(bl_ + 16 * ks);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(ap + rt * 32 * QS + 16 * ks);
+          acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bhv, acc[rt], 0, 0, 0);
+          acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, blv, acc[rt], 0, 0, 0);
+        }
+      }
+    }
+    // Lane (l32, hi) holds block j's approximate scores of rows 32rt + 8i + 4hi + r.
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, acc[rt][v]);
+    const float M = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float kn = valid ? summ[kn_off + ((size_t)b * n + j) * dm.Hkv + g] : 0.0f;
+    const float thr = M - 2.0f * kPrefilterC * qmax * kn;
+    unsigned long long cand = 0ull;
+    if (valid) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (acc[rt][v] >= thr) cand |= 1ull << (rt * 16 + v);
+    }
+    // Canonical chains of the candidate rows.
+    float best = -INFINITY;
+    const float* xk = summ + kofs;  // kmean, or kmin (plane 0) / kmax (plane 1)
+    while (cand) {
+      const int bit = __builtin_ctzll(cand);
+      cand &= cand - 1;
+      const int row = 32 * (bit >> 4) + 8 * ((bit & 15) >> 2) + 4 * hi + (bit & 3);
+      const uint16_t* qr = qs + (size_t)row * QS;
+      const uint16_t* qn = qs + (size_t)(TILE + row) * QS;
+      float sv = 0.0f;
+#pragma unroll 2
+      for (int c0 = 0; c0 < D; c0 += 8) {
+        uint4 qv = *reinterpret_cast<const uint4*>(qr + c0);
+        if (MODE == SA_KMINMAX) {
+          const uint4 q2 = *reinterpret_cast<const uint4*>(qn + c0);
+          qv.x |= q2.x; qv.y |= q2.y; qv.z |= q2.z; qv.w |= q2.w;
+        }
+        const float4 x0 = *reinterpret_cast<const float4*>(xk + c0);
+        const float4 x1 = *reinterpret_cast<const float4*>(xk + c0 + 4);
+        const float q8[8] = {bf16_lo(qv.x), bf16_hi(qv.x), bf16_lo(qv.y), bf16_hi(qv.y),
+                             bf16_lo(qv.z), bf16_hi(qv.z), bf16_lo(qv.w), bf16_hi(qv.w)};
+        float xa[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        if (MODE == SA_KMINMAX) {
+          const float4 y0 = *reinterpret_cast<const float4*>(xk + plane + c0);
+          const float4 y1 = *reinterpret_cast<const float4*>(xk + plane + c0 + 4);
+          const float xb[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) xa[k] = q8[k] >= 0.0f ? xb[k] : xa[k];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sv = __builtin_fmaf(q8[k], xa[k], sv);
+      }
+      best = fmaxf(best, sv);
+    }
+    best = fmaxf(best, __shfl_xor(best, 32));
+    if (valid && hi == 0) {
+      float m = canon(best);
+      if (OAM) m = canon(m * summ[vn_off + ((size_t)b * n + j) * dm.Hkv + g]);
+      keys[j - j0] = ((unsigned long long)order_key(m) << 32) | (0xffffffffu - (unsigned)j);
+    }
+  }
+  __syncthreads();
+  bitonic_desc<kScoreThreads>(keys, P);
+
+  const int R = min(max(expanded(bd, kt), kt), nf);
+  int* out = ranked + bht * bd.R;
+  for (int r = threadIdx.x; r < R; r += kScoreThreads)
+    out[r] = (int)(0xffffffffu - (unsigned)keys[r]);
   if (threadIdx.x == 0) {
     const float s0 = order_key_inv((unsigned)(keys[0] >> 32));
     const float sk1 = order_key_inv((unsigned)(keys[kt - 1] >> 32));
@@ -349,6 +562,44 @@ hipError_t score_dispatch(const Dims& dm, const BudgetDev& bd, const void* Q, co
                 : score_by_shape<T, SA_KMINMAX, 0>(dm, bd, Q, summ, ranked, sigma, s);
 }
 
+template <int MODE, int OAM, int D, int TILE>
+hipError_t launch_score_mfma(const Dims& dm, const BudgetDev& bd, const void* Q,
+                             const float* summ, int* ranked, float* sigma, hipStream_t s) {
+  const SummaryLayout L = summary_layout(dm);
+  int P = 1;
+  while (P < dm.n) P <<= 1;
+  constexpr int NPL = MODE == SA_KMINMAX ? 2 : 1;
+  const size_t lds = sizeof(unsigned long long) * P + sizeof(uint16_t) * NPL * TILE * (D + 8);
+  hipError_t e = allow_lds(score_rank_mfma<MODE, OAM, D, TILE>, lds);
+  if (e != hipSuccess) return e;
+  const uint16_t* bfp =
+      reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(summ) + L.bf_byte);
+  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
+  hipLaunchKernelGGL((score_rank_mfma<MODE, OAM, D, TILE>), dim3(grid), dim3(kScoreThreads),
+                     lds, s, dm, bd, static_cast<const uint16_t*>(Q), summ, bfp, ranked, sigma,
+                     L.plane, L.vn, L.kn);
+  return hipGetLastError();
+}
+
+template <int MODE, int OAM>
+hipError_t score_mfma_shape(const Dims& dm, const BudgetDev& bd, const void* Q,
+                            const float* summ, int* ranked, float* sigma, hipStream_t s) {
+  if (dm.d == 64)
+    return dm.blk == 64 ? launch_score_mfma<MODE, OAM, 64, 64>(dm, bd, Q, summ, ranked, sigma, s)
+                        : launch_score_mfma<MODE, OAM, 64, 128>(dm, bd, Q, summ, ranked, sigma, s);
+  return dm.blk == 64 ? launch_score_mfma<MODE, OAM, 128, 64>(dm, bd, Q, summ, ranked, sigma, s)
+                      : launch_score_mfma<MODE, OAM, 128, 128>(dm, bd, Q, summ, ranked, sigma, s);
+}
+
+hipError_t score_mfma_dispatch(const Dims& dm, const BudgetDev& bd, const void* Q,
+                               const float* summ, int* ranked, float* sigma, hipStream_t s) {
+  if (dm.score_mode == SA_KMEAN)
+    return dm.oam ? score_mfma_shape<SA_KMEAN, 1>(dm, bd, Q, summ, ranked, sigma, s)
+                  : score_mfma_shape<SA_KMEAN, 0>(dm, bd, Q, summ, ranked, sigma, s);
+  return dm.oam ? score_mfma_shape<SA_KMINMAX, 1>(dm, bd, Q, summ, ranked, sigma, s)
+                : score_mfma_shape<SA_KMINMAX, 0>(dm, bd, Q, summ, ranked, sigma, s);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -375,9 +626,8 @@ hipError_t launch_select(const Dims& dm, const BudgetDev& bd, const void* Q, con
   if (!gate) gate = reinterpret_cast<uint8_t*>(ws + L.gate);
   if (!tau) tau = reinterpret_cast<float*>(ws + L.tau);
 
-  hipError_t e = dm.dtype == SA_BF16
-                     ? score_dispatch<uint16_t>(dm, bd, Q, summ, ranked, sigma, s)
-                     : score_dispatch<float>(dm, bd, Q, summ, ranked, sigma, s);
+  hipError_t e = dm.dtype == SA_BF16 ? score_mfma_dispatch(dm, bd, Q, summ, ranked, sigma, s)
+                                     : score_dispatch<float>(dm, bd, Q, summ, ranked, sigma, s);
   if (e != hipSuccess) return e;
 
   int P = 1;

@@ -85,10 +85,12 @@ typedef struct sa_budget {
 
 /*
  * Bytes of the block-summary buffer `sparse_attn_score` fills, for this problem.
- * Layout (all fp32, n = seqlen / block):
+ * It starts with (all fp32, n = seqlen / block):
  *   SA_KMEAN:   kmean [B, n, Hkv, d]
  *   SA_KMINMAX: kmin  [B, n, Hkv, d] followed by kmax [B, n, Hkv, d]
  *   then, if output_aware: vnorm [B, n, Hkv]
+ * and continues with auxiliary data for sparse_attn_select whose layout is private
+ * (a bf16 split of the planes above and per-block norms, about as large again).
  * Returns 0 for an invalid problem (see sparse_attn_last_error).
  */
 size_t sparse_attn_summary_bytes(const sa_problem* p);

@@ -39,7 +39,7 @@ def run_gpu(w: wl.Workload, inp, out_dtype=None, with_lse=False):
         "kA": summ[:plane].reshape(w.batch, n, w.n_kv_heads, w.head_dim),
         "kB": (summ[plane:2 * plane].reshape(w.batch, n, w.n_kv_heads, w.head_dim)
                if w.score_mode == wl.KMINMAX else None),
-        "vn": (summ[plane * (2 if w.score_mode == wl.KMINMAX else 1):]
+        "vn": (summ[plane * (2 if w.score_mode == wl.KMINMAX else 1):][:w.batch * n * w.n_kv_heads]
                .reshape(w.batch, n, w.n_kv_heads) if w.output_aware else None),
         "kv_idx": pf.kv_idx.cpu().numpy(), "kv_cnt": pf.kv_cnt.cpu().numpy(),
         "sigma": pf.sigma.cpu().numpy(), "sigma_bar": pf.sigma_bar.cpu().numpy(),

@@ -71,13 +71,21 @@ def _ok_budget():
 def test_sizes(lib):
     p, b = _ok_problem(), _ok_budget()
     assert api.index_width(p, b) == 65
-    assert api.summary_bytes(p) == 1 * 512 * 8 * 128 * 4
     assert api.select_workspace_bytes(p, b) >= 32 * 512 * 64 * 4
+
+    def expect(B, n, Hkv, d, nplanes, oam):
+        # public fp32 planes (+ vnorm), then knorm, then 256-aligned bf16 hi/lo planes
+        plane = B * n * Hkv * d
+        head = plane * nplanes * 4 + (B * n * Hkv * 4 if oam else 0) + B * n * Hkv * 4
+        head = (head + 255) // 256 * 256
+        return head + nplanes * 2 * plane * 2
+
+    assert api.summary_bytes(p) == expect(1, 512, 8, 128, 1, False)
     p5, b5 = api.problem(wl.WORKLOADS["stem_32k"]), api.budget(wl.WORKLOADS["stem_32k"])
-    assert api.summary_bytes(p5) == 4 * 512 * 8 * 128 * 4 + 4 * 512 * 8 * 4
+    assert api.summary_bytes(p5) == expect(4, 512, 8, 128, 1, True)
     assert api.index_width(p5, b5) == 131
     p4 = api.problem(wl.WORKLOADS["quest_64k"])
-    assert api.summary_bytes(p4) == 2 * 1024 * 8 * 128 * 4
+    assert api.summary_bytes(p4) == expect(1, 1024, 8, 128, 2, False)
 
 
 BAD_PROBLEMS = [

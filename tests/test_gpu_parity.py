@@ -131,13 +131,40 @@ EDGE = {
     "sinks_exceed": WL["stem_32k"].resized(batch=1, seqlen=640, n_q_heads=4, n_kv_heads=2,
                                            n_sink=12, k_max=4, k_min=2),
     "k1": WL["quest_64k"].resized(seqlen=1280, n_q_heads=8, n_kv_heads=8, k_max=1, k_min=1),
+    "tied_rows_kmean": WL["prefill_128k"].resized(seqlen=2048, n_q_heads=4, n_kv_heads=2,
+                                                  k_max=4, k_min=4, planted=False),
+    "tied_rows_quest": WL["quest_64k"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=2, k_max=4,
+                                               k_min=4, near_tie_keys=False),
+    "tied_blocks": WL["llama8b_32k"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=2, k_max=4,
+                                             k_min=4),
 }
+
+
+def _edge_inputs(name, w):
+    """Inputs of an edge case: the recipe's, or a tie-heavy variant of it."""
+    inp = wl.make_inputs(w)
+    if name.startswith("tied_rows"):
+        # every row of a query tile equal: every row ties for each block's maximum, so the
+        # prefilter keeps all of them as candidates
+        q = inp["Q"].clone()
+        T = w.block
+        for t in range(w.n_blocks):
+            q[:, t * T:(t + 1) * T] = q[:, t * T:t * T + 1]
+        inp["Q"] = q
+    if name == "tied_blocks":
+        # every key block identical: all tile scores of a tile tie, ranking falls to the index
+        k = inp["K"].clone()
+        T = w.block
+        for j in range(1, w.n_blocks):
+            k[:, j * T:(j + 1) * T] = k[:, :T]
+        inp["K"] = k
+    return inp
 
 
 @pytest.mark.parametrize("name", list(EDGE))
 def test_edge_cases(name):
     w = EDGE[name]
-    inp = wl.make_inputs(w)
+    inp = _edge_inputs(name, w)
     cfg = oracle.make_cfg(w)
     say(f"[{name}] oracle + GPU")
     o_sum = oracle.pool(cfg, inp["K"], inp["V"])
