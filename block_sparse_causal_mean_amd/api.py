@@ -29,7 +29,8 @@ SA_GATE_QUANTILE, SA_GATE_FIXED, SA_GATE_OFF = 0, 1, 2
 # Every function the header declares, checked by the tests against the built library.
 EXPORTS = ("sparse_attn_summary_bytes", "sparse_attn_select_workspace_bytes",
            "sparse_attn_index_width", "sparse_attn_score", "sparse_attn_select",
-           "sparse_attn_forward", "sparse_attn_last_error")
+           "sparse_attn_forward_workspace_bytes", "sparse_attn_forward",
+           "sparse_attn_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -70,8 +71,10 @@ def load() -> ctypes.CDLL:
     lib.sparse_attn_index_width.restype = ctypes.c_int32
     lib.sparse_attn_score.argtypes = [PP, P, P, P, P]
     lib.sparse_attn_select.argtypes = [PP, PB, P, P, P, ctypes.c_size_t, P, P, P, P, P, P, P]
+    lib.sparse_attn_forward_workspace_bytes.argtypes = [PP]
+    lib.sparse_attn_forward_workspace_bytes.restype = ctypes.c_size_t
     lib.sparse_attn_forward.argtypes = [PP, P, P, P, P, P, ctypes.c_int32, ctypes.c_float, P,
-                                        ctypes.c_int32, P, P]
+                                        ctypes.c_size_t, P, ctypes.c_int32, P, P]
     lib.sparse_attn_last_error.argtypes = []
     lib.sparse_attn_last_error.restype = ctypes.c_char_p
     for f in ("sparse_attn_score", "sparse_attn_select", "sparse_attn_forward"):
@@ -118,6 +121,11 @@ def index_width(p: Problem, b: Budget) -> int:
     w = load().sparse_attn_index_width(ctypes.byref(p), ctypes.byref(b))
     _check(min(w, 0))
     return w
+
+
+def forward_workspace_bytes(p: Problem) -> int:
+    """Scratch bytes sparse_attn_forward needs (0 for fp32 problems)."""
+    return load().sparse_attn_forward_workspace_bytes(ctypes.byref(p))
 
 
 def _ptr(t: Optional[torch.Tensor], name: str, nbytes: Optional[int] = None):
@@ -168,14 +176,18 @@ def select(p: Problem, b: Budget, Q: torch.Tensor, summaries: torch.Tensor, ws: 
 
 def forward(p: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
             kv_idx: torch.Tensor, kv_cnt: torch.Tensor, W: int, softmax_scale: float,
-            O: torch.Tensor, out_dtype: int, lse: Optional[torch.Tensor] = None, stream=None):
+            ws: Optional[torch.Tensor], O: torch.Tensor, out_dtype: int,
+            lse: Optional[torch.Tensor] = None, stream=None):
     n = p.seqlen // p.block
     q_bytes = p.batch * p.seqlen * p.n_q_heads * p.head_dim
     kv = p.batch * p.seqlen * p.n_kv_heads * p.head_dim * _elt(p)
+    need = forward_workspace_bytes(p)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().sparse_attn_forward(
         ctypes.byref(p), _ptr(Q, "Q", q_bytes * _elt(p)), _ptr(K, "K", kv), _ptr(V, "V", kv),
         _ptr(kv_idx, "kv_idx", p.batch * p.n_q_heads * n * W * 4),
         _ptr(kv_cnt, "kv_cnt", p.batch * p.n_q_heads * n * 4), W, softmax_scale,
+        _ptr(ws, "ws", need), ws_bytes,
         _ptr(O, "O", q_bytes * (4 if out_dtype == SA_F32 else 2)), out_dtype,
         _ptr(lse, "lse", p.batch * p.n_q_heads * p.seqlen * 4), _stream(stream)))
 
@@ -198,6 +210,8 @@ class Prefill:
         self.summ = torch.empty(summary_bytes(self.p) // 4, dtype=torch.float32, device=dev)
         self.ws = torch.empty(select_workspace_bytes(self.p, self.b), dtype=torch.uint8,
                               device=dev)
+        fwb = forward_workspace_bytes(self.p)
+        self.fws = torch.empty(max(fwb, 1), dtype=torch.uint8, device=dev) if fwb else None
         self.kv_idx = torch.empty((w.batch, w.n_q_heads, n, self.W), dtype=torch.int32,
                                   device=dev)
         self.kv_cnt = torch.empty((w.batch, w.n_q_heads, n), dtype=torch.int32, device=dev)
@@ -223,8 +237,8 @@ class Prefill:
                self.sigma_bar, self.gate, self.tau, stream)
 
     def forward(self, Q, K, V, stream=None):
-        forward(self.p, Q, K, V, self.kv_idx, self.kv_cnt, self.W, self.scale, self.O,
-                self.out_dtype, self.lse, stream)
+        forward(self.p, Q, K, V, self.kv_idx, self.kv_cnt, self.W, self.scale, self.fws,
+                self.O, self.out_dtype, self.lse, stream)
 
     def run(self, Q, K, V, stream=None):
         self.score(K, V, stream)

@@ -173,21 +173,30 @@ int sparse_attn_select(const sa_problem* p, const sa_budget* b, const void* Q,
                     "sparse_attn_select launch");
 }
 
+size_t sparse_attn_forward_workspace_bytes(const sa_problem* p) {
+  sa::Dims D;
+  if (check_problem(p, &D) != SA_OK) return 0;
+  return sa::forward_ws_bytes(D);
+}
+
 int sparse_attn_forward(const sa_problem* p, const void* Q, const void* K, const void* V,
                         const int32_t* kv_idx, const int32_t* kv_cnt, int32_t W,
-                        float softmax_scale, void* O, int32_t out_dtype, float* lse,
-                        void* stream) {
+                        float softmax_scale, void* ws, size_t ws_bytes, void* O,
+                        int32_t out_dtype, float* lse, void* stream) {
   sa::Dims D;
   int rc = check_problem(p, &D);
   if (rc != SA_OK) return rc;
   if (!Q || !K || !V || !kv_idx || !kv_cnt || !O)
     return fail(SA_ERR_INVALID, "Q, K, V, kv_idx, kv_cnt and O must be non-NULL");
+  const size_t need = sa::forward_ws_bytes(D);
+  if (need && (!ws || ws_bytes < need))
+    return fail(SA_ERR_INVALID, "forward workspace too small: %zu < %zu bytes", ws_bytes, need);
   if (W < 1) return fail(SA_ERR_INVALID, "W must be >= 1");
   if (out_dtype != SA_F32 && out_dtype != SA_BF16)
     return fail(SA_ERR_INVALID, "out_dtype must be SA_F32 or SA_BF16");
   if (!isfinite(softmax_scale)) return fail(SA_ERR_INVALID, "softmax_scale is not finite");
   g_err.clear();
-  return hip_status(sa::launch_forward(D, Q, K, V, kv_idx, kv_cnt, W, softmax_scale, O,
+  return hip_status(sa::launch_forward(D, Q, K, V, kv_idx, kv_cnt, W, softmax_scale, ws, O,
                                        out_dtype, lse, static_cast<hipStream_t>(stream)),
                     "sparse_attn_forward launch");
 }

@@ -6,25 +6,31 @@
 // softmax is invariant to the order of the KV blocks, and the causal mask is applied before
 // accumulation.
 //
-// bf16 kernel (attn_bf16): one workgroup per (batch, q head, query tile), BLK/32 waves, each
-// wave owns 32 query rows.  Per listed block the kernel computes S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 coordinates from LDS, B = the wave's Q
-// fragment kept in registers for the whole tile), so each lane's accumulator holds logits of
-// ONE query row for 16 keys.  That makes the row max and row sum lane-local (plus one swap
-// with the lane 32 apart), and the probabilities P^T are already laid out as the B operand
-// of the second product O^T += V^T P^T: the contraction index (keys) is permuted
-// consistently in the V^T operand instead of moving P through LDS.  K is staged in LDS
-// row-major and V transposed (both padded against bank conflicts); the next listed block is
-// prefetched into registers while the current one is computed.  fp32 accumulation
-// throughout.  The second product runs in fp16 (v_mfma_f32_32x32x16_f16): P in [0, 1] keeps
-// 11 significant bits instead of bf16's 8, and V converts from bf16 to fp16 exactly while it
-// is transposed into LDS (bf16 V must stay below 65504 in magnitude).
+// bf16 inputs (pack_v + attn_bf16):
+//   pack_v      once per call, V [B, N, Hkv, d] bf16 -> fp16 blocks [B, Hkv, n, d, BLK]:
+//               each block transposed (V^T, keys contiguous) and XOR-swizzled in 4-key
+//               granules, i.e. exactly the LDS image attn_bf16 wants.  Each V block is read
+//               by hundreds of tiles, so converting and transposing it once here takes that
+//               work out of the attention loop.  bf16 -> fp16 is exact for |v| in
+//               [2^-14, 65504]; smaller magnitudes keep an absolute error below 2^-25.
+//   attn_bf16   one workgroup per (batch, q head, query tile): BLK/32 query groups of 32 rows
+//               x 2 key halves, one wave each (two waves per SIMD).  Per listed block:
+//               S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 coordinates from
+//               LDS, B = the wave's Q fragment held in registers), so each lane's
+//               accumulator holds logits of ONE query row: row max and sum are lane-local
+//               plus one swap with the lane 32 apart, and P^T is already laid out as the B
+//               operand of O^T += V^T P^T (v_mfma_f32_32x32x16_f16; the key index is
+//               permuted consistently in the V^T operand instead of moving P through LDS).
+//               K and V^T blocks go from global memory straight into LDS (global_load_lds,
+//               no registers), double-buffered so the next block streams in while the
+//               current one is computed, with one workgroup barrier per block.  Both LDS
+//               images are XOR-swizzled so the operand reads are free of bank conflicts.
+//               The two key halves of a query group keep separate online-softmax states and
+//               merge once at the end.  fp32 accumulation throughout; P is rounded to fp16
+//               (11 significant bits) for the second product.
+// fp32 inputs (attn_f32): one thread per query row, fp32 VALU arithmetic, same online softmax.
 //
-// fp32 kernel (attn_f32): one thread per query row, fp32 VALU arithmetic with the same
-// online softmax; it serves fp32 inputs, where no bf16 rounding is acceptable.
-//
-// Launch order is latest tile first (late tiles carry the most blocks), with the q heads of
-// one kv head launched next to each other so their K/V blocks are shared through L2.
+// Launch order (decode_tile): one kv head's tiles, latest first, per XCD.
 
 #include "common.h"
 
@@ -52,97 +58,95 @@ __device__ __forceinline__ int next_entry(const int32_t* __restrict__ list, int 
   return -1;
 }
 
-union U4 {
-  uint4 v;
-  uint32_t w[4];
-};
+// ------------------------------------------------------------------ swizzled block images
+//
+// K block in LDS: BLK rows of D bf16; 16-byte chunk c of row r sits at chunk c ^ (r & 7).
+// V^T block (LDS and packed global copy): D rows of BLK fp16; 4-key granule g of row d sits
+// at granule g ^ (d & (BLK/4 - 1)).
+template <int D>
+__device__ __forceinline__ int k_chunk_pos(int r, int c) { return r * (D / 8) + (c ^ (r & 7)); }
+template <int BLK>
+__device__ __forceinline__ int v_gran_pos(int d, int g) {
+  return d * (BLK / 4) + (g ^ (d & (BLK / 4 - 1)));
+}
 
-// Work split of the bf16 kernel: BLK/32 query groups of 32 rows times 2 key halves, one wave
-// each.  The two waves of a query group keep separate online-softmax states over their key
-// halves and merge them once at the end, so two waves per SIMD interleave their matrix-core
-// and vector work.
+// ------------------------------------------------------------------------------ pack_v
+
+constexpr int kPackThreads = 256;
+
+template <int D, int BLK>
+__global__ __launch_bounds__(kPackThreads) void pack_v(Dims dm, const uint16_t* __restrict__ V,
+                                                       uint16_t* __restrict__ Vp) {
+  constexpr int RS = D + 2;  // LDS row stride (elements)
+  __shared__ uint16_t sv[BLK * RS];
+  const int id = (int)blockIdx.x;  // ((b * Hkv + g) * n + j)
+  const int j = id % dm.n;
+  const int bg = id / dm.n;
+  const int g = bg % dm.Hkv, b = bg / dm.Hkv;
+  const uint16_t* src = V + (((size_t)b * dm.N + (size_t)j * BLK) * dm.Hkv + g) * D;
+  for (int c = threadIdx.x; c < BLK * D / 8; c += kPackThreads) {
+    const int r = c / (D / 8), col = c - r * (D / 8);
+    const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)r * dm.Hkv * D + col * 8);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(sv + r * RS + col * 8);
+    dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+  }
+  __syncthreads();
+  uint2* out = reinterpret_cast<uint2*>(Vp + (size_t)id * D * BLK);
+  for (int i = threadIdx.x; i < D * BLK / 4; i += kPackThreads) {
+    const int d = i / (BLK / 4), p = i - d * (BLK / 4);
+    const int gk = p ^ (d & (BLK / 4 - 1));  // granule stored at position p
+    float x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = bf16_bits_to_f32(sv[(4 * gk + k) * RS + d]);
+    const f16x2 a = __builtin_convertvector((f32x2){x[0], x[1]}, f16x2);
+    const f16x2 c = __builtin_convertvector((f32x2){x[2], x[3]}, f16x2);
+    out[i] = make_uint2(*reinterpret_cast<const uint32_t*>(&a), *reinterpret_cast<const uint32_t*>(&c));
+  }
+}
+
+// --------------------------------------------------------------------------- attn_bf16
+
 template <int D, int BLK>
 struct Tiles {
-  static constexpr int QG = BLK / 32;              // query groups
-  static constexpr int NW = QG * 2;                // waves
-  static constexpr int NT = 64 * NW;               // threads (= 4 * BLK)
-  static constexpr int HK = BLK / 2;               // keys per wave per block
-  static constexpr int KT = HK / 32;               // 32-key tiles per wave per block
-  static constexpr int KS = D + 8;                 // LDS row stride of K (elements)
-  static constexpr int VS = BLK + 4;               // LDS row stride of V^T (elements)
-  static constexpr int KCH = BLK * D / 8;          // 16-byte chunks of a K block
-  static constexpr int KPT = (KCH + NT - 1) / NT;  // per thread
-  static constexpr int VMT = (BLK / 4) * (D / 8);  // 4-key x 8-coordinate micro tiles of V
-  static constexpr int VPT = (VMT + NT - 1) / NT;  // per thread
-  static constexpr size_t KV_LDS = sizeof(uint16_t) * ((size_t)BLK * KS + (size_t)D * VS);
-  static constexpr size_t MERGE_LDS = sizeof(float) * (size_t)QG * 64 * (D / 32 * 16 + 2);
-  static constexpr size_t LDS = KV_LDS > MERGE_LDS ? KV_LDS : MERGE_LDS;
+  static constexpr int QG = BLK / 32;          // query groups
+  static constexpr int NW = QG * 2;            // waves
+  static constexpr int NT = 64 * NW;           // threads (= 4 * BLK)
+  static constexpr int HK = BLK / 2;           // keys per wave per block
+  static constexpr int KT = HK / 32;           // 32-key tiles per wave per block
+  static constexpr int CHUNKS = BLK * D / 8;   // 16-byte chunks of one K (or V^T) block
+  static constexpr int LPT = CHUNKS / NT;      // direct loads per thread per block image
+  static constexpr size_t IMG = (size_t)BLK * D * 2;  // bytes of one block image
+  static constexpr size_t STAGE = 2 * IMG;            // K image + V^T image
+  static constexpr size_t MERGE = sizeof(float) * (size_t)QG * 64 * (D / 32 * 16 + 2);
+  static constexpr size_t LDS = 2 * STAGE > MERGE ? 2 * STAGE : MERGE;
+  static_assert(CHUNKS % NT == 0, "load split");
 };
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Issues the direct global->LDS loads of block j's K and V^T images into one stage.
 template <int D, int BLK>
-__device__ __forceinline__ void load_block(const uint16_t* __restrict__ K,
-                                           const uint16_t* __restrict__ V, size_t row0,
-                                           int rstride, U4 (&kr)[Tiles<D, BLK>::KPT],
-                                           U4 (&vr)[Tiles<D, BLK>::VPT][4]) {
+__device__ __forceinline__ void issue_block(const uint16_t* __restrict__ Kg,
+                                            const uint16_t* __restrict__ Vpg, int rstride,
+                                            int j, char* stage) {
   using TL = Tiles<D, BLK>;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint16_t* kb = Kg + (size_t)j * BLK * rstride;
+  const uint16_t* vb = Vpg + (size_t)j * D * BLK;
 #pragma unroll
-  for (int i = 0; i < TL::KPT; ++i) {
-    const int c = threadIdx.x + i * TL::NT;
-    if (TL::KCH % TL::NT == 0 || c < TL::KCH) {
-      const int r = c / (D / 8), col = c - r * (D / 8);
-      kr[i].v = *reinterpret_cast<const uint4*>(K + (row0 + r) * rstride + col * 8);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < TL::VPT; ++i) {
-    const int m = threadIdx.x + i * TL::NT;
-    if (TL::VMT % TL::NT == 0 || m < TL::VMT) {
-      const int kg = m / (D / 8), col = m - kg * (D / 8);
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        vr[i][k].v =
-            *reinterpret_cast<const uint4*>(V + (row0 + 4 * kg + k) * rstride + col * 8);
-    }
+  for (int i = 0; i < TL::LPT; ++i) {
+    const int region = wv + TL::NW * i;  // 64-chunk (1 KiB) LDS region
+    const int P = region * 64 + lane;    // LDS chunk this lane fills
+    const int r = P / (D / 8), pos = P - r * (D / 8);
+    const int c = pos ^ (r & 7);         // global chunk that belongs there
+    __builtin_amdgcn_global_load_lds(kb + (size_t)r * rstride + c * 8,
+                                     (lds_ptr)(stage + region * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + (size_t)P * 8,
+                                     (lds_ptr)(stage + TL::IMG + region * 1024), 16, 0, 0);
   }
 }
 
-template <int D, int BLK>
-__device__ __forceinline__ void store_block(uint16_t* Ks, uint16_t* Vt,
-                                            const U4 (&kr)[Tiles<D, BLK>::KPT],
-                                            const U4 (&vr)[Tiles<D, BLK>::VPT][4]) {
-  using TL = Tiles<D, BLK>;
-#pragma unroll
-  for (int i = 0; i < TL::KPT; ++i) {
-    const int c = threadIdx.x + i * TL::NT;
-    if (TL::KCH % TL::NT == 0 || c < TL::KCH) {
-      const int r = c / (D / 8), col = c - r * (D / 8);
-      *reinterpret_cast<uint4*>(Ks + r * TL::KS + col * 8) = kr[i].v;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < TL::VPT; ++i) {
-    const int m = threadIdx.x + i * TL::NT;
-    if (TL::VMT % TL::NT == 0 || m < TL::VMT) {
-      const int kg = m / (D / 8), col = m - kg * (D / 8);
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        // Coordinate col*8+dd of keys 4kg..4kg+3, bf16 -> fp32 (exact) -> fp16 (exact for
-        // |v| in [2^-14, 65504]; smaller magnitudes keep an absolute error below 2^-25).
-        const int wd = dd >> 1;
-        float x[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          x[k] = (dd & 1) ? bf16_hi(vr[i][k].w[wd]) : bf16_lo(vr[i][k].w[wd]);
-        const f16x2 p01 = __builtin_convertvector((f32x2){x[0], x[1]}, f16x2);
-        const f16x2 p23 = __builtin_convertvector((f32x2){x[2], x[3]}, f16x2);
-        uint2 pk;
-        pk.x = *reinterpret_cast<const uint32_t*>(&p01);
-        pk.y = *reinterpret_cast<const uint32_t*>(&p23);
-        *reinterpret_cast<uint2*>(Vt + (col * 8 + dd) * TL::VS + 4 * kg) = pk;
-      }
-    }
-  }
-}
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // A row's running maximum is only raised when a new logit exceeds it by more than this many
 // powers of two; until then probabilities may reach 2^kLazy, which fp16 P and the fp32
@@ -152,16 +156,14 @@ constexpr float kLazy = 8.0f;
 template <int D, int BLK>
 __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BLK>::NT
     Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, const int32_t* __restrict__ kv_idx,
+    const uint16_t* __restrict__ Vp, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, int W, float scale_log2, void* __restrict__ O,
     int out_f32, float* __restrict__ lse) {
   using TL = Tiles<D, BLK>;
   constexpr int KT = TL::KT;
   constexpr int DT = D / 32;  // 32-coordinate tiles of the output
   constexpr int DC = D / 16;  // 16-coordinate chunks of the QK^T contraction
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* Ks = smem;
-  uint16_t* Vt = smem + BLK * TL::KS;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   int b, h, t;
   decode_tile(dm, b, h, t);
@@ -175,6 +177,8 @@ __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BL
   const int qloc = qg * 32 + l32;  // this lane's query row within the tile
   const int qrow = t * BLK + qloc;
   const int rstride = dm.Hkv * D;
+  const uint16_t* Kg = K + ((size_t)b * dm.N * dm.Hkv + g) * D;
+  const uint16_t* Vpg = Vp + ((size_t)b * dm.Hkv + g) * dm.n * D * BLK;
 
   // Q fragment (B operand of S^T = K Q^T): lane holds coordinates 16c + 8*hi .. +7 of its row.
   bf16x8 qf[DC];
@@ -190,33 +194,28 @@ __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BL
   float m_run = -INFINITY;  // running max of raw logits (before scaling) for this lane's row
   float l_run = 0.0f;       // this lane's share of the row's softmax denominator
 
-  U4 kr[TL::KPT];
-  U4 vr[TL::VPT][4];
-  const size_t kvbase = (size_t)b * dm.N;
-  const uint16_t* Kg = K + (size_t)g * D;
-  const uint16_t* Vg = V + (size_t)g * D;
-
   int e = next_entry(list, cnt, 0, t);
-  if (e >= 0) {
-    load_block<D, BLK>(Kg, Vg, kvbase + (size_t)list[e] * BLK, rstride, kr, vr);
-    store_block<D, BLK>(Ks, Vt, kr, vr);
-  }
-  __syncthreads();
-
+  int st = 0;
+  if (e >= 0) issue_block<D, BLK>(Kg, Vpg, rstride, list[e], smem);
   while (e >= 0) {
     const int j = list[e];
     const int e2 = next_entry(list, cnt, e + 1, t);
-    if (e2 >= 0) load_block<D, BLK>(Kg, Vg, kvbase + (size_t)list[e2] * BLK, rstride, kr, vr);
+    wait_loads();     // this wave's share of block j has landed
+    __syncthreads();  // everyone's share has; stage st^1 is no longer read by anyone
+    if (e2 >= 0) issue_block<D, BLK>(Kg, Vpg, rstride, list[e2], smem + (st ^ 1) * TL::STAGE);
+    const char* Kst = smem + st * TL::STAGE;
+    const char* Vst = Kst + TL::IMG;
 
     // S^T = K Q^T over this wave's key half: KT tiles of 32 keys x 32 queries.
     f32x16 s[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       s[kt] = (f32x16){};
-      const uint16_t* kp = Ks + (kh * TL::HK + kt * 32 + l32) * TL::KS + 8 * hi;
+      const int r = kh * TL::HK + kt * 32 + l32;
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + 16 * c);
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(Kst + k_chunk_pos<D>(r, 2 * c + hi) * 16);
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kt], 0, 0, 0);
       }
     }
@@ -238,13 +237,12 @@ __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BL
 #pragma unroll
       for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[kt][v]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    // Raise the running max only when a logit exceeds it by more than 2^kLazy in
-    // probability; the first finite block always sets it.
-    const bool raise = mloc > m_run && (m_run == -INFINITY || (mloc - m_run) * scale_log2 > kLazy);
+    const bool raise =
+        mloc > m_run && (m_run == -INFINITY || (mloc - m_run) * scale_log2 > kLazy);
     if (__any(raise)) {
       const float m_new = raise ? mloc : m_run;
-      const float alpha = m_run == -INFINITY ? 0.0f
-                                             : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+      const float alpha =
+          m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -268,28 +266,26 @@ __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BL
     // kh*HK + kt*32 + 16*half + 8i' + 4*hi + r; the A operand reads V^T at the same keys.
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* vp = Vt + (dt * 32 + l32) * TL::VS + kh * TL::HK + 4 * hi;
+      const int d = dt * 32 + l32;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int k0 = kt * 32 + 16 * half;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vp + k0);
-          const uint2 up = *reinterpret_cast<const uint2*>(vp + k0 + 8);
+          const int g0 = (kh * TL::HK + kt * 32 + 16 * half) / 4 + hi;
+          const uint2 lo = *reinterpret_cast<const uint2*>(Vst + v_gran_pos<BLK>(d, g0) * 8);
+          const uint2 up = *reinterpret_cast<const uint2*>(Vst + v_gran_pos<BLK>(d, g0 + 2) * 8);
           const uint4 raw = make_uint4(lo.x, lo.y, up.x, up.y);
           const f16x8 a = *reinterpret_cast<const f16x8*>(&raw);
           acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[kt][half], acc_o[dt], 0, 0, 0);
         }
     }
-    __syncthreads();
-    if (e2 >= 0) store_block<D, BLK>(Ks, Vt, kr, vr);
-    __syncthreads();
+    st ^= 1;
     e = e2;
   }
+  __syncthreads();  // every wave is done with the K/V stages before they hold merge data
 
-  // Merge the two key halves of each query group through LDS (the K/V buffer is free now).
-  float* mrg = reinterpret_cast<float*>(smem);
-  float* mO = mrg + (size_t)qg * 64 * (DT * 16 + 2);  // [DT*16 values][64 lanes], then m, l
+  // Merge the two key halves of each query group through LDS.
+  float* mO = reinterpret_cast<float*>(smem) + (size_t)qg * 64 * (DT * 16 + 2);
   if (kh == 1) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -405,15 +401,19 @@ __global__ __launch_bounds__(BLK) void attn_f32(Dims dm, const float* __restrict
 template <int D, int BLK>
 hipError_t launch_bf16(const Dims& dm, const void* Q, const void* K, const void* V,
                        const int32_t* kv_idx, const int32_t* kv_cnt, int W, float scale,
-                       void* O, int out_dtype, float* lse, hipStream_t s) {
+                       void* ws, void* O, int out_dtype, float* lse, hipStream_t s) {
   using TL = Tiles<D, BLK>;
-  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
-  hipError_t e = allow_lds(attn_bf16<D, BLK>, TL::LDS);
+  uint16_t* Vp = static_cast<uint16_t*>(ws);
+  const unsigned nblk = (unsigned)((size_t)dm.B * dm.Hkv * dm.n);
+  hipLaunchKernelGGL((pack_v<D, BLK>), dim3(nblk), dim3(kPackThreads), 0, s, dm,
+                     static_cast<const uint16_t*>(V), Vp);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if ((e = allow_lds(attn_bf16<D, BLK>, TL::LDS)) != hipSuccess) return e;
+  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
   hipLaunchKernelGGL((attn_bf16<D, BLK>), dim3(grid), dim3(TL::NT), TL::LDS, s, dm,
-                     static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
-                     static_cast<const uint16_t*>(V), kv_idx, kv_cnt, W, scale * kLog2e, O,
-                     out_dtype == SA_F32 ? 1 : 0, lse);
+                     static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K), Vp,
+                     kv_idx, kv_cnt, W, scale * kLog2e, O, out_dtype == SA_F32 ? 1 : 0, lse);
   return hipGetLastError();
 }
 
@@ -434,17 +434,24 @@ hipError_t launch_f32(const Dims& dm, const void* Q, const void* K, const void* 
 
 }  // namespace
 
+size_t forward_ws_bytes(const Dims& dm) {
+  if (dm.dtype != SA_BF16) return 0;
+  return (size_t)dm.B * dm.Hkv * dm.n * dm.d * dm.blk * sizeof(uint16_t);
+}
+
 hipError_t launch_forward(const Dims& dm, const void* Q, const void* K, const void* V,
                           const int32_t* kv_idx, const int32_t* kv_cnt, int W, float scale,
-                          void* O, int out_dtype, float* lse, hipStream_t s) {
+                          void* ws, void* O, int out_dtype, float* lse, hipStream_t s) {
   if (dm.dtype == SA_BF16) {
     if (dm.d == 64)
-      return dm.blk == 64
-                 ? launch_bf16<64, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
-                 : launch_bf16<64, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s);
-    return dm.blk == 64
-               ? launch_bf16<128, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
-               : launch_bf16<128, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s);
+      return dm.blk == 64 ? launch_bf16<64, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
+                                                out_dtype, lse, s)
+                          : launch_bf16<64, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
+                                                 out_dtype, lse, s);
+    return dm.blk == 64 ? launch_bf16<128, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
+                                               out_dtype, lse, s)
+                        : launch_bf16<128, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
+                                                out_dtype, lse, s);
   }
   if (dm.d == 64)
     return dm.blk == 64

@@ -116,8 +116,9 @@ hipError_t launch_pool(const Dims& D, const void* K, const void* V, float* summ,
 hipError_t launch_select(const Dims& D, const BudgetDev& bd, const void* Q, const float* summ,
                          char* ws, int32_t* kv_idx, int32_t* kv_cnt, float* sigma,
                          float* sigma_bar, uint8_t* gate, float* tau, hipStream_t s);
+size_t forward_ws_bytes(const Dims& D);
 hipError_t launch_forward(const Dims& D, const void* Q, const void* K, const void* V,
                           const int32_t* kv_idx, const int32_t* kv_cnt, int W, float scale,
-                          void* O, int out_dtype, float* lse, hipStream_t s);
+                          void* ws, void* O, int out_dtype, float* lse, hipStream_t s);
 
 }  // namespace sa

@@ -138,6 +138,10 @@ int sparse_attn_select(const sa_problem* p, const sa_budget* b, const void* Q,
                        int32_t* kv_cnt, float* sigma, float* sigma_bar, uint8_t* gate,
                        float* tau, void* stream);
 
+/* Bytes of device workspace `sparse_attn_forward` needs (0 for fp32 problems, the size of V
+ * for bf16 ones).  0 also for an invalid problem (see sparse_attn_last_error). */
+size_t sparse_attn_forward_workspace_bytes(const sa_problem* p);
+
 /*
  * Sparse attention (Stem page, three-stage implementation; gated-selection page, step 5).
  *   Q, K, V        BSHD in p->dtype.
@@ -146,6 +150,8 @@ int sparse_attn_select(const sa_problem* p, const sa_budget* b, const void* Q,
  *                  entries must be distinct blocks <= t, others are skipped).
  *   W              row stride of kv_idx (its last dimension), >= 1.
  *   softmax_scale  logit scale, normally 1/sqrt(d).
+ *   ws             sparse_attn_forward_workspace_bytes(p) bytes of scratch (may be NULL when
+ *                  that is 0); its contents are ignored and overwritten.
  *   O              [B, N, Hq, d] in out_dtype (SA_BF16 or SA_F32), written.
  *   lse            optional fp32 [B, Hq, N]: natural-log log-sum-exp of the scaled logits.
  * Row i of tile t attends to every key of its listed blocks at a position <= i.
@@ -155,8 +161,8 @@ int sparse_attn_select(const sa_problem* p, const sa_budget* b, const void* Q,
  */
 int sparse_attn_forward(const sa_problem* p, const void* Q, const void* K, const void* V,
                         const int32_t* kv_idx, const int32_t* kv_cnt, int32_t W,
-                        float softmax_scale, void* O, int32_t out_dtype, float* lse,
-                        void* stream);
+                        float softmax_scale, void* ws, size_t ws_bytes, void* O,
+                        int32_t out_dtype, float* lse, void* stream);
 
 /* The calling thread's last error message ("" if none).  Valid until its next call. */
 const char* sparse_attn_last_error(void);

@@ -121,7 +121,7 @@ def test_invalid_problem_rejected_before_hip(lib, over, code):
     assert lib.sparse_attn_select(ctypes.byref(p), ctypes.byref(b), FAKE, FAKE, FAKE, 1 << 40,
                                   FAKE, FAKE, None, None, None, None, None) == code
     assert lib.sparse_attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 65, 0.1, FAKE,
-                                   api.SA_BF16, None, None) == code
+                                   1 << 40, FAKE, api.SA_BF16, None, None) == code
 
 
 @pytest.mark.parametrize("over", BAD_BUDGETS)
@@ -147,13 +147,20 @@ def test_null_pointers_and_small_buffers_rejected(lib):
     r = lib.sparse_attn_select(ctypes.byref(p), ctypes.byref(b), FAKE, FAKE, FAKE, need, None,
                                FAKE, None, None, None, None, None)
     assert r == api.SA_ERR_INVALID
+    big = 1 << 40
     assert lib.sparse_attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0.1, FAKE,
-                                   api.SA_BF16, None, None) == api.SA_ERR_INVALID
+                                   big, FAKE, api.SA_BF16, None, None) == api.SA_ERR_INVALID
     assert lib.sparse_attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 65, 0.1, FAKE,
-                                   5, None, None) == api.SA_ERR_INVALID
+                                   big, FAKE, 5, None, None) == api.SA_ERR_INVALID
     assert lib.sparse_attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 65,
-                                   float("inf"), FAKE, api.SA_BF16, None,
+                                   float("inf"), FAKE, big, FAKE, api.SA_BF16, None,
                                    None) == api.SA_ERR_INVALID
+    need = api.forward_workspace_bytes(p)
+    assert need == 1 * 32768 * 8 * 128 * 2
+    r = lib.sparse_attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 65, 0.1, FAKE,
+                                need - 1, FAKE, api.SA_BF16, None, None)
+    assert r == api.SA_ERR_INVALID and "workspace" in api.last_error()
+    assert api.forward_workspace_bytes(api.problem(wl.WORKLOADS["tiny_ref"])) == 0
     assert lib.sparse_attn_score(None, FAKE, FAKE, FAKE, None) == api.SA_ERR_INVALID
 
 

@@ -231,7 +231,7 @@ def test_forward_any_block_order_and_skipped_entries():
             wide[0, h, t, :len(row)] = torch.tensor(row, dtype=torch.int32)
             cnt2[0, h, t] = len(row) + 2  # count runs past the sentinel
     O2 = torch.empty_like(pf.O)
-    api.forward(pf.p, d["Q"], d["K"], d["V"], wide, cnt2, W2, pf.scale, O2, api.SA_F32)
+    api.forward(pf.p, d["Q"], d["K"], d["V"], wide, cnt2, W2, pf.scale, pf.fws, O2, api.SA_F32)
     torch.cuda.synchronize()
     check(O2, "skipped entries")
 
