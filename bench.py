@@ -137,6 +137,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=wl.HEADLINE, choices=wl.WORKLOAD_ORDER)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB, so a "
+                         "counter profile of this command can scale its byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
@@ -155,6 +158,14 @@ def main():
     Q, K, V = dev["Q"], dev["K"], dev["V"]
     pf = api.Prefill(w, keep_stats=True)
     s = torch.cuda.current_stream()
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
+        del src, dst
 
     for i in range(args.warmup):
         pf.run(Q, K, V)

@@ -60,14 +60,34 @@ __device__ __forceinline__ int next_entry(const int32_t* __restrict__ list, int 
 
 // ------------------------------------------------------------------ swizzled block images
 //
-// K block in LDS: BLK rows of D bf16; 16-byte chunk c of row r sits at chunk c ^ (r & 7).
-// V^T block (LDS and packed global copy): D rows of BLK fp16; 4-key granule g of row d sits
-// at granule g ^ (d & (BLK/4 - 1)).
+// K block in LDS: BLK rows of D bf16 (16-byte chunks); V^T block (LDS and the packed global
+// copy): D rows of BLK fp16 (8-byte granules of 4 keys).  Within a row, chunk/granule c sits
+// at c ^ key(row).  The keys make the 16 (b128 reads) or 32 (b64 reads) lanes of one LDS
+// phase, which read the same column of consecutive rows, land on distinct banks: rows are
+// 256 bytes (one full bank sweep) or 128 bytes (two rows per sweep) long.
 template <int D>
-__device__ __forceinline__ int k_chunk_pos(int r, int c) { return r * (D / 8) + (c ^ (r & 7)); }
+__device__ __forceinline__ int k_key(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int k_chunk_pos(int r, int c) { return r * (D / 8) + (c ^ k_key<D>(r)); }
+template <int BLK>
+__device__ __forceinline__ int v_key(int d) { return BLK == 128 ? (d & 31) : ((d >> 1) & 15); }
 template <int BLK>
 __device__ __forceinline__ int v_gran_pos(int d, int g) {
-  return d * (BLK / 4) + (g ^ (d & (BLK / 4 - 1)));
+  return d * (BLK / 4) + (g ^ v_key<BLK>(d));
+}
+
+// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap, no LDS traffic).  The swap
+// hands each lane its own value and its partner's, one in each result; both lanes of a pair
+// combine the same two values, so they get bit-identical results.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // ------------------------------------------------------------------------------ pack_v
@@ -94,7 +114,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_v(Dims dm, const uint16_t* 
   uint2* out = reinterpret_cast<uint2*>(Vp + (size_t)id * D * BLK);
   for (int i = threadIdx.x; i < D * BLK / 4; i += kPackThreads) {
     const int d = i / (BLK / 4), p = i - d * (BLK / 4);
-    const int gk = p ^ (d & (BLK / 4 - 1));  // granule stored at position p
+    const int gk = p ^ v_key<BLK>(d);  // granule stored at position p
     float x[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) x[k] = bf16_bits_to_f32(sv[(4 * gk + k) * RS + d]);
@@ -138,7 +158,7 @@ __device__ __forceinline__ void issue_block(const uint16_t* __restrict__ Kg,
     const int region = wv + TL::NW * i;  // 64-chunk (1 KiB) LDS region
     const int P = region * 64 + lane;    // LDS chunk this lane fills
     const int r = P / (D / 8), pos = P - r * (D / 8);
-    const int c = pos ^ (r & 7);         // global chunk that belongs there
+    const int c = pos ^ k_key<D>(r);     // global chunk that belongs there
     __builtin_amdgcn_global_load_lds(kb + (size_t)r * rstride + c * 8,
                                      (lds_ptr)(stage + region * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(vb + (size_t)P * 8,
@@ -206,7 +226,12 @@ __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BL
     const char* Kst = smem + st * TL::STAGE;
     const char* Vst = Kst + TL::IMG;
 
-    // S^T = K Q^T over this wave's key half: KT tiles of 32 keys x 32 queries.
+    // S^T = K Q^T over this wave's key half: KT tiles of 32 keys x 32 queries.  The two
+    // waves sharing a SIMD (same query group, both key halves) leave each barrier in step;
+    // the first key half issues its products at raised priority so it reaches its softmax
+    // while the other half's products still run, and the two then alternate between matrix
+    // and vector work instead of competing for the same unit.
+    if (kh == 0) __builtin_amdgcn_s_setprio(2);
     f32x16 s[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
@@ -219,6 +244,7 @@ __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BL
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kt], 0, 0, 0);
       }
     }
+    if (kh == 0) __builtin_amdgcn_s_setprio(0);
 
     // Online softmax.  Lane value (kt, i, r) is key kh*HK + kt*32 + 8i + 4*hi + r of the
     // block; the causal mask only touches the diagonal block.
@@ -236,7 +262,7 @@ __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BL
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[kt][v]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = pair_max(mloc);
     const bool raise =
         mloc > m_run && (m_run == -INFINITY || (mloc - m_run) * scale_log2 > kLazy);
     if (__any(raise)) {
@@ -302,7 +328,7 @@ __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BL
   const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_run - m) * scale_log2);
   const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
   const float l_lane = l_run * a0 + l1 * a1;
-  const float l_tot = l_lane + __shfl_xor(l_lane, 32);
+  const float l_tot = pair_sum(l_lane);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const size_t orow = (((size_t)b * dm.N + qrow) * dm.Hq + h) * D;
 #pragma unroll
