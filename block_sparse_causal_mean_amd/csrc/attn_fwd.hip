@@ -7,27 +7,28 @@
 // accumulation.
 //
 // bf16 inputs (pack_v + attn_bf16):
-//   pack_v      once per call, V [B, N, Hkv, d] bf16 -> fp16 blocks [B, Hkv, n, d, BLK]:
-//               each block transposed (V^T, keys contiguous) and XOR-swizzled in 4-key
-//               granules, i.e. exactly the LDS image attn_bf16 wants.  Each V block is read
+//   pack_v      once per call, V [B, N, Hkv, d] bf16 -> fp16 sub-block images (V^T, keys
+//               contiguous, rows padded): exactly the LDS image attn_bf16 wants.  Each V block is read
 //               by hundreds of tiles, so converting and transposing it once here takes that
 //               work out of the attention loop.  bf16 -> fp16 is exact for |v| in
 //               [2^-14, 65504]; smaller magnitudes keep an absolute error below 2^-25.
-//   attn_bf16   one workgroup per (batch, q head, query tile): BLK/32 query groups of 32 rows
-//               x 2 key halves, one wave each (two waves per SIMD).  Per listed block:
+//   attn_bf16   one workgroup per (batch, q head, query tile): one wave per 32-row query
+//               group, two workgroups per CU (independent barriers, so one computes while
+//               the other waits for memory).  Per 64-key (or 32-key) sub-block of a listed
+//               block:
 //               S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 coordinates from
 //               LDS, B = the wave's Q fragment held in registers), so each lane's
 //               accumulator holds logits of ONE query row: row max and sum are lane-local
 //               plus one swap with the lane 32 apart, and P^T is already laid out as the B
 //               operand of O^T += V^T P^T (v_mfma_f32_32x32x16_f16; the key index is
 //               permuted consistently in the V^T operand instead of moving P through LDS).
-//               K and V^T blocks go from global memory straight into LDS (global_load_lds,
-//               no registers), double-buffered so the next block streams in while the
-//               current one is computed, with one workgroup barrier per block.  Both LDS
-//               images are XOR-swizzled so the operand reads are free of bank conflicts.
-//               The two key halves of a query group keep separate online-softmax states and
-//               merge once at the end.  fp32 accumulation throughout; P is rounded to fp16
-//               (11 significant bits) for the second product.
+//               K and V^T sub-blocks go from global memory straight into LDS
+//               (global_load_lds, no registers), double-buffered so the next one streams in
+//               while the current one is computed, with one barrier per sub-block.  Both LDS
+//               images have padded rows, which keeps the operand reads free of bank
+//               conflicts at per-lane base + constant offsets.
+//               fp32 accumulation throughout; P is rounded to fp16 (11 significant bits)
+//               for the second product.
 // fp32 inputs (attn_f32): one thread per query row, fp32 VALU arithmetic, same online softmax.
 //
 // Launch order (decode_tile): one kv head's tiles, latest first, per XCD.
@@ -58,23 +59,51 @@ __device__ __forceinline__ int next_entry(const int32_t* __restrict__ list, int 
   return -1;
 }
 
-// ------------------------------------------------------------------ swizzled block images
+// A tile's block list held in registers, 64 entries at a time (lane i holds entry base + i),
+// read with readlane.  Keeping list reads off the scalar-memory path matters: a scalar load
+// in flight shares the LDS wait counter and would force every operand wait in the compute
+// loop to drain completely.
+struct ListWindow {
+  const int32_t* list;
+  int cnt, t, base, val;
+  __device__ __forceinline__ ListWindow(const int32_t* l, int c, int tt)
+      : list(l), cnt(c), t(tt), base(-64), val(-1) {}
+  __device__ __forceinline__ int get(int e) {  // e uniform, 0 <= e < cnt
+    if (e < base || e >= base + 64) {
+      base = e & ~63;
+      const int i = base + (int)(threadIdx.x & 63);
+      val = i < cnt ? list[i] : -1;
+    }
+    return __builtin_amdgcn_readlane(val, e - base);
+  }
+  // Next usable entry at or after e (same rules as next_entry), or -1.
+  __device__ __forceinline__ int next(int e) {
+    for (; e < cnt; ++e) {
+      const int j = get(e);
+      if (j < 0) return -1;
+      if (j <= t) return e;
+    }
+    return -1;
+  }
+};
+
+// ------------------------------------------------------------------ padded block images
 //
-// K block in LDS: BLK rows of D bf16 (16-byte chunks); V^T block (LDS and the packed global
-// copy): D rows of BLK fp16 (8-byte granules of 4 keys).  Within a row, chunk/granule c sits
-// at c ^ key(row).  The keys make the 16 (b128 reads) or 32 (b64 reads) lanes of one LDS
-// phase, which read the same column of consecutive rows, land on distinct banks: rows are
-// 256 bytes (one full bank sweep) or 128 bytes (two rows per sweep) long.
+// The attention loop streams each listed block in sub-blocks of SB = BLK/2 keys.  In LDS a K
+// sub-block is SB rows of D bf16 and a V^T sub-block is D rows of SB fp16, each row padded
+// (K by 16 bytes, V^T by 8) so that the lanes of one LDS phase, which read the same column
+// of consecutive rows, fall on distinct banks: the row strides are odd multiples of the read
+// width modulo the 256-byte bank sweep.  Padding rather than an address swizzle keeps every
+// operand read at a per-lane base plus a compile-time offset.
 template <int D>
-__device__ __forceinline__ int k_key(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-template <int D>
-__device__ __forceinline__ int k_chunk_pos(int r, int c) { return r * (D / 8) + (c ^ k_key<D>(r)); }
-template <int BLK>
-__device__ __forceinline__ int v_key(int d) { return BLK == 128 ? (d & 31) : ((d >> 1) & 15); }
-template <int BLK>
-__device__ __forceinline__ int v_gran_pos(int d, int g) {
-  return d * (BLK / 4) + (g ^ v_key<BLK>(d));
-}
+struct KImg {
+  static constexpr int RB = D * 2 + 16;  // row bytes
+  static constexpr int CPR = RB / 16;    // 16-byte chunks per row (last one is padding)
+};
+template <int SB>
+struct VImg {
+  static constexpr int RB = SB * 2 + 8;  // row bytes
+};
 
 // max / sum of x over lanes l and l ^ 32 (v_permlane32_swap, no LDS traffic).  The swap
 // hands each lane its own value and its partner's, one in each result; both lanes of a pair
@@ -94,10 +123,15 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 constexpr int kPackThreads = 256;
 
+// V [B, N, Hkv, D] bf16 -> fp16 sub-block images [B, Hkv, n, BLK/SB] x (D rows of
+// VImg<SB>::RB bytes: SB keys then zero padding) -- exactly the LDS image attn_bf16 uses.
 template <int D, int BLK>
 __global__ __launch_bounds__(kPackThreads) void pack_v(Dims dm, const uint16_t* __restrict__ V,
                                                        uint16_t* __restrict__ Vp) {
-  constexpr int RS = D + 2;  // LDS row stride (elements)
+  constexpr int SB = BLK / 2;
+  constexpr int RS = D + 2;                 // LDS row stride (elements)
+  constexpr int GR = VImg<SB>::RB / 8;      // 8-byte granules per image row (last: padding)
+  constexpr int IMG = D * VImg<SB>::RB / 2; // fp16 elements per sub-block image
   __shared__ uint16_t sv[BLK * RS];
   const int id = (int)blockIdx.x;  // ((b * Hkv + g) * n + j)
   const int j = id % dm.n;
@@ -111,13 +145,19 @@ __global__ __launch_bounds__(kPackThreads) void pack_v(Dims dm, const uint16_t* 
     dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
   }
   __syncthreads();
-  uint2* out = reinterpret_cast<uint2*>(Vp + (size_t)id * D * BLK);
-  for (int i = threadIdx.x; i < D * BLK / 4; i += kPackThreads) {
-    const int d = i / (BLK / 4), p = i - d * (BLK / 4);
-    const int gk = p ^ v_key<BLK>(d);  // granule stored at position p
+  uint2* out = reinterpret_cast<uint2*>(Vp + (size_t)id * (BLK / SB) * IMG);
+  for (int i = threadIdx.x; i < (BLK / SB) * D * GR; i += kPackThreads) {
+    const int sub = i / (D * GR);
+    const int w = i - sub * (D * GR);
+    const int d = w / GR, gk = w - d * GR;  // granule gk of row d
+    if (gk == GR - 1) {
+      out[i] = make_uint2(0u, 0u);
+      continue;
+    }
+    const int key0 = sub * SB + 4 * gk;
     float x[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) x[k] = bf16_bits_to_f32(sv[(4 * gk + k) * RS + d]);
+    for (int k = 0; k < 4; ++k) x[k] = bf16_bits_to_f32(sv[(key0 + k) * RS + d]);
     const f16x2 a = __builtin_convertvector((f32x2){x[0], x[1]}, f16x2);
     const f16x2 c = __builtin_convertvector((f32x2){x[2], x[3]}, f16x2);
     out[i] = make_uint2(*reinterpret_cast<const uint32_t*>(&a), *reinterpret_cast<const uint32_t*>(&c));
@@ -128,41 +168,46 @@ __global__ __launch_bounds__(kPackThreads) void pack_v(Dims dm, const uint16_t* 
 
 template <int D, int BLK>
 struct Tiles {
-  static constexpr int QG = BLK / 32;          // query groups
-  static constexpr int NW = QG * 2;            // waves
-  static constexpr int NT = 64 * NW;           // threads (= 4 * BLK)
-  static constexpr int HK = BLK / 2;           // keys per wave per block
-  static constexpr int KT = HK / 32;           // 32-key tiles per wave per block
-  static constexpr int CHUNKS = BLK * D / 8;   // 16-byte chunks of one K (or V^T) block
-  static constexpr int LPT = CHUNKS / NT;      // direct loads per thread per block image
-  static constexpr size_t IMG = (size_t)BLK * D * 2;  // bytes of one block image
-  static constexpr size_t STAGE = 2 * IMG;            // K image + V^T image
-  static constexpr size_t MERGE = sizeof(float) * (size_t)QG * 64 * (D / 32 * 16 + 2);
-  static constexpr size_t LDS = 2 * STAGE > MERGE ? 2 * STAGE : MERGE;
-  static_assert(CHUNKS % NT == 0, "load split");
+  static constexpr int NW = BLK / 32;          // waves = query groups of 32 rows
+  static constexpr int NT = 64 * NW;           // threads (= 2 * BLK)
+  static constexpr int SB = BLK / 2;           // keys per pipeline step (sub-block)
+  static constexpr int NSB = BLK / SB;         // sub-blocks per block
+  static constexpr int KT = SB / 32;           // 32-key tiles per step
+  static constexpr int KB = SB * KImg<D>::RB;  // bytes of a K image
+  static constexpr int VB = D * VImg<SB>::RB;  // bytes of a V^T image
+  static constexpr int KCH = KB / 16, VCH = VB / 16;  // 16-byte chunks
+  static constexpr int STAGE = KB + VB;
+  static constexpr int VSUB = VB / 2;          // fp16 elements per packed V^T image
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// Issues the direct global->LDS loads of block j's K and V^T images into one stage.
+// Issues the direct global->LDS loads of sub-block `sub` of block j into one stage: lane i
+// of a wave's load lands at the 1 KiB region base + 16 i, so each lane fetches the global
+// chunk that belongs at its slot (K padding slots refetch the row's first chunk).
 template <int D, int BLK>
-__device__ __forceinline__ void issue_block(const uint16_t* __restrict__ Kg,
-                                            const uint16_t* __restrict__ Vpg, int rstride,
-                                            int j, char* stage) {
+__device__ __forceinline__ void issue_step(const uint16_t* __restrict__ Kg,
+                                           const uint16_t* __restrict__ Vpg, int rstride,
+                                           int j, int sub, char* kst, char* vst) {
   using TL = Tiles<D, BLK>;
+  constexpr int CPR = KImg<D>::CPR;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint16_t* kb = Kg + (size_t)j * BLK * rstride;
-  const uint16_t* vb = Vpg + (size_t)j * D * BLK;
+  const uint16_t* kb = Kg + ((size_t)j * BLK + (size_t)sub * TL::SB) * rstride;
+  const uint16_t* vb = Vpg + ((size_t)j * TL::NSB + sub) * TL::VSUB;
 #pragma unroll
-  for (int i = 0; i < TL::LPT; ++i) {
-    const int region = wv + TL::NW * i;  // 64-chunk (1 KiB) LDS region
-    const int P = region * 64 + lane;    // LDS chunk this lane fills
-    const int r = P / (D / 8), pos = P - r * (D / 8);
-    const int c = pos ^ k_key<D>(r);     // global chunk that belongs there
-    __builtin_amdgcn_global_load_lds(kb + (size_t)r * rstride + c * 8,
-                                     (lds_ptr)(stage + region * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vb + (size_t)P * 8,
-                                     (lds_ptr)(stage + TL::IMG + region * 1024), 16, 0, 0);
+  for (int region = wv; region * 64 < TL::KCH; region += TL::NW) {
+    const int P = region * 64 + lane;
+    const int r = P / CPR, c = P - r * CPR;
+    if (P < TL::KCH)
+      __builtin_amdgcn_global_load_lds(kb + (size_t)r * rstride + (c < CPR - 1 ? c : 0) * 8,
+                                       (lds_ptr)(kst + region * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int region = wv; region * 64 < TL::VCH; region += TL::NW) {
+    const int P = region * 64 + lane;
+    if (P < TL::VCH)
+      __builtin_amdgcn_global_load_lds(vb + (size_t)P * 8, (lds_ptr)(vst + region * 1024), 16,
+                                       0, 0);
   }
 }
 
@@ -173,23 +218,126 @@ __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)"
 // accumulators hold exactly enough, and the rescale of O is skipped.
 constexpr float kLazy = 8.0f;
 
+// Online-softmax state of one wave (32 query rows; each lane pair shares a row).
+template <int D>
+struct RowState {
+  f32x16 acc_o[D / 32];
+  float m_run, l_run;
+};
+
+// One pipeline step: S^T = K Q^T for SB keys, online softmax, O^T += V^T P^T.
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BLK>::NT
+__device__ __forceinline__ void compute_step(const char* __restrict__ kst,
+                                             const char* __restrict__ vst, const bf16x8 (&qf)[D / 16],
+                                             RowState<D>& rs, bool diag, int k0, int qloc,
+                                             int l32, int hi, float scale_log2) {
+  using TL = Tiles<D, BLK>;
+  constexpr int KT = TL::KT, SB = TL::SB, DT = D / 32, DC = D / 16;
+  constexpr int KRB = KImg<D>::RB, VRB = VImg<SB>::RB;
+  // S^T = K Q^T: KT tiles x DC coordinate chunks = NS products, their A operands read from
+  // LDS PD products ahead (scheduling fences keep the reads where they are written, so the
+  // matrix unit never waits on the full LDS latency).
+  constexpr int NS = KT * DC, PD = 4;
+  f32x16 s[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) s[kt] = (f32x16){};
+  const char* kp = kst + l32 * KRB + hi * 16;  // row l32 (+32 kt), coordinates 8*hi + 16c
+  auto kaddr = [&](int i) { return kp + (i / DC) * 32 * KRB + (i % DC) * 32; };
+  bf16x8 ka[PD];
+#pragma unroll
+  for (int i = 0; i < PD; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kaddr(i));
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    s[i / DC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % PD], qf[i % DC], s[i / DC], 0, 0, 0);
+    if (i + PD < NS) ka[i % PD] = *reinterpret_cast<const bf16x8*>(kaddr(i + PD));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // Lane value (kt, i, r) is key k0 + kt*32 + 8i + 4*hi + r of the block.
+  if (diag) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kloc = k0 + kt * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+        if (kloc > qloc) s[kt][v] = -INFINITY;
+      }
+  }
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[kt][v]);
+  mloc = pair_max(mloc);
+  const bool raise =
+      mloc > rs.m_run && (rs.m_run == -INFINITY || (mloc - rs.m_run) * scale_log2 > kLazy);
+  if (__any(raise)) {
+    const float m_new = raise ? mloc : rs.m_run;
+    const float alpha =
+        rs.m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((rs.m_run - m_new) * scale_log2);
+    rs.m_run = m_new;
+    rs.l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) rs.acc_o[dt] *= alpha;
+  }
+  const float mc = rs.m_run == -INFINITY ? 0.0f : -rs.m_run * scale_log2;
+  float psum = 0.0f;
+  f16x8 pf[KT][2];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], scale_log2, mc));
+      psum += p;
+      pf[kt][v >> 3][v & 7] = (_Float16)p;
+    }
+  rs.l_run += psum;
+  // O^T += V^T P^T.  B operand slot 8*hi + 4i' + r of pf[kt][half] is key
+  // kt*32 + 16*half + 8i' + 4*hi + r of the step; the A operand reads V^T at those keys.
+  // Products are ordered (dt, kt, half); operands are read PD products ahead.
+  constexpr int NP = DT * KT * 2;
+  const char* vp = vst + l32 * VRB + hi * 8;  // row d = dt*32 + l32, keys 4*hi + ...
+  auto vaddr = [&](int i) {
+    const int dt = i / (KT * 2), kt = (i / 2) % KT, half = i % 2;
+    return vp + dt * 32 * VRB + (kt * 32 + 16 * half) * 2;
+  };
+  auto vload = [&](int i) {
+    const char* q = vaddr(i);
+    const uint2 lo = *reinterpret_cast<const uint2*>(q);
+    const uint2 up = *reinterpret_cast<const uint2*>(q + 16);
+    const uint4 raw = make_uint4(lo.x, lo.y, up.x, up.y);
+    return *reinterpret_cast<const f16x8*>(&raw);
+  };
+  f16x8 va[PD];
+#pragma unroll
+  for (int i = 0; i < PD; ++i) va[i] = vload(i);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int dt = i / (KT * 2), kt = (i / 2) % KT, half = i % 2;
+    rs.acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i % PD], pf[kt][half], rs.acc_o[dt], 0, 0, 0);
+    if (i + PD < NP) va[i % PD] = vload(i + PD);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK * 2, 2) void attn_bf16(  // BLK*2 == Tiles::NT; 2 waves/SIMD
     Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vp, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, int W, float scale_log2, void* __restrict__ O,
     int out_f32, float* __restrict__ lse) {
   using TL = Tiles<D, BLK>;
-  constexpr int KT = TL::KT;
-  constexpr int DT = D / 32;  // 32-coordinate tiles of the output
-  constexpr int DC = D / 16;  // 16-coordinate chunks of the QK^T contraction
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  constexpr int SB = TL::SB, DT = D / 32, DC = D / 16;
+  // Two separate stage buffers: the loads in flight into one are then provably disjoint from
+  // the reads of the other, so reads never wait for them.
+  __shared__ __attribute__((aligned(1024))) char k0s[TL::KB], v0s[TL::VB];
+  __shared__ __attribute__((aligned(1024))) char k1s[TL::KB], v1s[TL::VB];
 
   int b, h, t;
   decode_tile(dm, b, h, t);
   const int g = h / dm.G;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int qg = wv % TL::QG, kh = wv / TL::QG;  // query group, key half
+  const int lane = threadIdx.x & 63, qg = threadIdx.x >> 6;  // wave = query group
   const int l32 = lane & 31, hi = lane >> 5;
   const size_t bht = ((size_t)b * dm.Hq + h) * dm.n + t;
   const int32_t* list = kv_idx + bht * W;
@@ -198,7 +346,7 @@ __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BL
   const int qrow = t * BLK + qloc;
   const int rstride = dm.Hkv * D;
   const uint16_t* Kg = K + ((size_t)b * dm.N * dm.Hkv + g) * D;
-  const uint16_t* Vpg = Vp + ((size_t)b * dm.Hkv + g) * dm.n * D * BLK;
+  const uint16_t* Vpg = Vp + ((size_t)b * dm.Hkv + g) * dm.n * TL::NSB * TL::VSUB;
 
   // Q fragment (B operand of S^T = K Q^T): lane holds coordinates 16c + 8*hi .. +7 of its row.
   bf16x8 qf[DC];
@@ -207,128 +355,58 @@ __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BL
 #pragma unroll
     for (int c = 0; c < DC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
   }
-
-  f32x16 acc_o[DT];
+  RowState<D> rs;
 #pragma unroll
-  for (int i = 0; i < DT; ++i) acc_o[i] = (f32x16){};
-  float m_run = -INFINITY;  // running max of raw logits (before scaling) for this lane's row
-  float l_run = 0.0f;       // this lane's share of the row's softmax denominator
+  for (int i = 0; i < DT; ++i) rs.acc_o[i] = (f32x16){};
+  rs.m_run = -INFINITY;
+  rs.l_run = 0.0f;
 
-  int e = next_entry(list, cnt, 0, t);
-  int st = 0;
-  if (e >= 0) issue_block<D, BLK>(Kg, Vpg, rstride, list[e], smem);
+  // Steps are (list entry, sub-block); stage 0 holds even steps, stage 1 odd ones.
+  ListWindow lw(list, cnt, t);
+  int e = lw.next(0), sub = 0;
+  int j = e >= 0 ? lw.get(e) : 0;
+  if (e >= 0) issue_step<D, BLK>(Kg, Vpg, rstride, j, 0, k0s, v0s);
   while (e >= 0) {
-    const int j = list[e];
-    const int e2 = next_entry(list, cnt, e + 1, t);
-    wait_loads();     // this wave's share of block j has landed
-    __syncthreads();  // everyone's share has; stage st^1 is no longer read by anyone
-    if (e2 >= 0) issue_block<D, BLK>(Kg, Vpg, rstride, list[e2], smem + (st ^ 1) * TL::STAGE);
-    const char* Kst = smem + st * TL::STAGE;
-    const char* Vst = Kst + TL::IMG;
-
-    // S^T = K Q^T over this wave's key half: KT tiles of 32 keys x 32 queries.  The two
-    // waves sharing a SIMD (same query group, both key halves) leave each barrier in step;
-    // the first key half issues its products at raised priority so it reaches its softmax
-    // while the other half's products still run, and the two then alternate between matrix
-    // and vector work instead of competing for the same unit.
-    if (kh == 0) __builtin_amdgcn_s_setprio(2);
-    f32x16 s[KT];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      s[kt] = (f32x16){};
-      const int r = kh * TL::HK + kt * 32 + l32;
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(Kst + k_chunk_pos<D>(r, 2 * c + hi) * 16);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kt], 0, 0, 0);
+    // even step: compute from stage 0, prefetch the next step into stage 1
+    {
+      int e2 = e, sub2 = sub + 1, j2 = j;
+      if (sub2 == TL::NSB) {
+        e2 = lw.next(e + 1);
+        sub2 = 0;
+        if (e2 >= 0) j2 = lw.get(e2);
       }
+      wait_loads();
+      __syncthreads();
+      if (e2 >= 0) issue_step<D, BLK>(Kg, Vpg, rstride, j2, sub2, k1s, v1s);
+      const int k0 = sub * SB;
+      if (!(j == t && k0 > qg * 32 + 31))
+        compute_step<D, BLK>(k0s, v0s, qf, rs, j == t, k0, qloc, l32, hi, scale_log2);
+      e = e2;
+      sub = sub2;
+      j = j2;
     }
-    if (kh == 0) __builtin_amdgcn_s_setprio(0);
-
-    // Online softmax.  Lane value (kt, i, r) is key kh*HK + kt*32 + 8i + 4*hi + r of the
-    // block; the causal mask only touches the diagonal block.
-    if (j >= t) {
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kloc = kh * TL::HK + kt * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-          if (j > t || kloc > qloc) s[kt][v] = -INFINITY;
-        }
-    }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[kt][v]);
-    mloc = pair_max(mloc);
-    const bool raise =
-        mloc > m_run && (m_run == -INFINITY || (mloc - m_run) * scale_log2 > kLazy);
-    if (__any(raise)) {
-      const float m_new = raise ? mloc : m_run;
-      const float alpha =
-          m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
-    }
-    const float mc = m_run == -INFINITY ? 0.0f : -m_run * scale_log2;
-
-    float psum = 0.0f;
-    f16x8 pf[KT][2];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], scale_log2, mc));
-        psum += p;
-        pf[kt][v >> 3][v & 7] = (_Float16)p;
+    if (e < 0) break;
+    // odd step: compute from stage 1, prefetch into stage 0
+    {
+      int e2 = e, sub2 = sub + 1, j2 = j;
+      if (sub2 == TL::NSB) {
+        e2 = lw.next(e + 1);
+        sub2 = 0;
+        if (e2 >= 0) j2 = lw.get(e2);
       }
-    l_run += psum;
-
-    // O^T += V^T P^T.  B operand slot 8*hi + 4i' + r of pf[kt][half] is key
-    // kh*HK + kt*32 + 16*half + 8i' + 4*hi + r; the A operand reads V^T at the same keys.
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = dt * 32 + l32;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int g0 = (kh * TL::HK + kt * 32 + 16 * half) / 4 + hi;
-          const uint2 lo = *reinterpret_cast<const uint2*>(Vst + v_gran_pos<BLK>(d, g0) * 8);
-          const uint2 up = *reinterpret_cast<const uint2*>(Vst + v_gran_pos<BLK>(d, g0 + 2) * 8);
-          const uint4 raw = make_uint4(lo.x, lo.y, up.x, up.y);
-          const f16x8 a = *reinterpret_cast<const f16x8*>(&raw);
-          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[kt][half], acc_o[dt], 0, 0, 0);
-        }
+      wait_loads();
+      __syncthreads();
+      if (e2 >= 0) issue_step<D, BLK>(Kg, Vpg, rstride, j2, sub2, k0s, v0s);
+      const int k0 = sub * SB;
+      if (!(j == t && k0 > qg * 32 + 31))
+        compute_step<D, BLK>(k1s, v1s, qf, rs, j == t, k0, qloc, l32, hi, scale_log2);
+      e = e2;
+      sub = sub2;
+      j = j2;
     }
-    st ^= 1;
-    e = e2;
   }
-  __syncthreads();  // every wave is done with the K/V stages before they hold merge data
 
-  // Merge the two key halves of each query group through LDS.
-  float* mO = reinterpret_cast<float*>(smem) + (size_t)qg * 64 * (DT * 16 + 2);
-  if (kh == 1) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mO[(dt * 16 + v) * 64 + lane] = acc_o[dt][v];
-    mO[DT * 16 * 64 + lane] = m_run;
-    mO[(DT * 16 + 1) * 64 + lane] = l_run;
-  }
-  __syncthreads();
-  if (kh == 1) return;
-  const float m1 = mO[DT * 16 * 64 + lane];
-  const float l1 = mO[(DT * 16 + 1) * 64 + lane];
-  const float m = fmaxf(m_run, m1);
-  const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_run - m) * scale_log2);
-  const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
-  const float l_lane = l_run * a0 + l1 * a1;
-  const float l_tot = pair_sum(l_lane);
+  const float l_tot = pair_sum(rs.l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const size_t orow = (((size_t)b * dm.N + qrow) * dm.Hq + h) * D;
 #pragma unroll
@@ -338,10 +416,7 @@ __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BL
       const int d0 = dt * 32 + 8 * i + 4 * hi;
       float o[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int v = 4 * i + r;
-        o[r] = (acc_o[dt][v] * a0 + mO[(dt * 16 + v) * 64 + lane] * a1) * inv;
-      }
+      for (int r = 0; r < 4; ++r) o[r] = rs.acc_o[dt][4 * i + r] * inv;
       if (out_f32) {
         *reinterpret_cast<float4*>(static_cast<float*>(O) + orow + d0) =
             make_float4(o[0], o[1], o[2], o[3]);
@@ -354,7 +429,7 @@ __global__ __launch_bounds__(BLK * 4) void attn_bf16(  // BLK * 4 == Tiles<D, BL
     }
   if (lse && hi == 0)
     lse[((size_t)b * dm.Hq + h) * dm.N + qrow] =
-        l_tot > 0.0f ? (m * scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+        l_tot > 0.0f ? (rs.m_run * scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------- fp32 (VALU) path
@@ -435,9 +510,8 @@ hipError_t launch_bf16(const Dims& dm, const void* Q, const void* K, const void*
                      static_cast<const uint16_t*>(V), Vp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((e = allow_lds(attn_bf16<D, BLK>, TL::LDS)) != hipSuccess) return e;
   const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
-  hipLaunchKernelGGL((attn_bf16<D, BLK>), dim3(grid), dim3(TL::NT), TL::LDS, s, dm,
+  hipLaunchKernelGGL((attn_bf16<D, BLK>), dim3(grid), dim3(TL::NT), 0, s, dm,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K), Vp,
                      kv_idx, kv_cnt, W, scale * kLog2e, O, out_dtype == SA_F32 ? 1 : 0, lse);
   return hipGetLastError();
@@ -462,7 +536,8 @@ hipError_t launch_f32(const Dims& dm, const void* Q, const void* K, const void* 
 
 size_t forward_ws_bytes(const Dims& dm) {
   if (dm.dtype != SA_BF16) return 0;
-  return (size_t)dm.B * dm.Hkv * dm.n * dm.d * dm.blk * sizeof(uint16_t);
+  // packed V^T images: per block, 2 sub-blocks of d rows x (blk/2 keys + 4 padding) fp16
+  return (size_t)dm.B * dm.Hkv * dm.n * 2 * dm.d * (dm.blk / 2 + 4) * sizeof(uint16_t);
 }
 
 hipError_t launch_forward(const Dims& dm, const void* Q, const void* K, const void* V,

@@ -202,10 +202,12 @@ def test_forward_any_block_order_and_skipped_entries():
     base = pf.O.clone()
 
     def check(O, label):
+        # Each order meets the bf16 bar against the oracle; between orders P is rounded to
+        # fp16 against different running maxima, so they agree to a few fp16 ulps of |V|.
         err = np.abs(O.cpu().numpy().astype(np.float64) - O_ref).max()
         say(f"  {label}: max|O - O_ref| = {err:.3e}")
         assert err <= 2e-2
-        assert (O - base).abs().max().item() <= 2e-3
+        assert (O - base).abs().max().item() <= 1e-2
 
     check(base, "ascending")
     rev = idx.clone()
