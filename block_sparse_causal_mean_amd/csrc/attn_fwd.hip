@@ -7,31 +7,33 @@
 // accumulation.
 //
 // bf16 inputs (pack_v + attn_bf16):
-//   pack_v      once per call, V [B, N, Hkv, d] bf16 -> fp16 sub-block images (V^T, keys
-//               contiguous, rows padded): exactly the LDS image attn_bf16 wants.  Each V block is read
-//               by hundreds of tiles, so converting and transposing it once here takes that
-//               work out of the attention loop.  bf16 -> fp16 is exact for |v| in
+//   pack_v      once per call, V [B, N, Hkv, d] bf16 -> fp16 V^T step images (32 keys each,
+//               dense, swizzled): exactly the LDS image attn_bf16 wants.  Each V block is
+//               read by hundreds of tiles, so converting and transposing it once here takes
+//               that work out of the attention loop.  bf16 -> fp16 is exact for |v| in
 //               [2^-14, 65504]; smaller magnitudes keep an absolute error below 2^-25.
-//   attn_bf16   one workgroup per (batch, q head, query tile): one wave per 32-row query
-//               group, two workgroups per CU (independent barriers, so one computes while
-//               the other waits for memory).  Per 64-key (or 32-key) sub-block of a listed
-//               block:
+//   attn_bf16   one workgroup per (batch, q head, query tile), one wave per 32 query rows
+//               (4 waves for 128-row tiles, 2 for 64-row tiles), two workgroups per CU.  The
+//               tile's blocks are consumed in steps of 32 keys:
 //               S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 coordinates from
-//               LDS, B = the wave's Q fragment held in registers), so each lane's
-//               accumulator holds logits of ONE query row: row max and sum are lane-local
-//               plus one swap with the lane 32 apart, and P^T is already laid out as the B
-//               operand of O^T += V^T P^T (v_mfma_f32_32x32x16_f16; the key index is
-//               permuted consistently in the V^T operand instead of moving P through LDS).
-//               K and V^T sub-blocks go from global memory straight into LDS
-//               (global_load_lds, no registers), double-buffered so the next one streams in
-//               while the current one is computed, with one barrier per sub-block.  Both LDS
-//               images have padded rows, which keeps the operand reads free of bank
-//               conflicts at per-lane base + constant offsets.
-//               fp32 accumulation throughout; P is rounded to fp16 (11 significant bits)
-//               for the second product.
+//               LDS, B = the wave's Q fragment held in registers), so each lane's accumulator
+//               holds logits of ONE query row: row max and sum are lane-local plus one swap
+//               with the lane 32 apart, and P^T is already laid out as the B operand of
+//               O^T += V^T P^T (v_mfma_f32_32x32x16_f16; the V^T image stores each lane's eight
+//               keys in exactly that order, so one 16-byte read feeds one product and P never
+//               moves through LDS).  fp32 accumulation throughout; P is rounded to fp16
+//               (11 significant bits) for the second product.
+//               K and V^T steps go from global memory straight into a ring of 4 LDS slots
+//               (global_load_lds, no registers), each refilled three steps ahead of use, with
+//               partial vector-memory waits so a step never waits for later steps' loads.
+//               The template also builds 64-row waves (QH = 2: one K read feeds two products),
+//               which halves LDS operand traffic but needs over 256 registers, i.e. one wave
+//               per SIMD; on gfx950 it measured slower, so the launcher uses QH = 1.
 // fp32 inputs (attn_f32): one thread per query row, fp32 VALU arithmetic, same online softmax.
 //
-// Launch order (decode_tile): one kv head's tiles, latest first, per XCD.
+// Launch order (decode_tile): one kv head at a time, its tiles latest first.
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -43,6 +45,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -59,52 +63,6 @@ __device__ __forceinline__ int next_entry(const int32_t* __restrict__ list, int 
   return -1;
 }
 
-// A tile's block list held in registers, 64 entries at a time (lane i holds entry base + i),
-// read with readlane.  Keeping list reads off the scalar-memory path matters: a scalar load
-// in flight shares the LDS wait counter and would force every operand wait in the compute
-// loop to drain completely.
-struct ListWindow {
-  const int32_t* list;
-  int cnt, t, base, val;
-  __device__ __forceinline__ ListWindow(const int32_t* l, int c, int tt)
-      : list(l), cnt(c), t(tt), base(-64), val(-1) {}
-  __device__ __forceinline__ int get(int e) {  // e uniform, 0 <= e < cnt
-    if (e < base || e >= base + 64) {
-      base = e & ~63;
-      const int i = base + (int)(threadIdx.x & 63);
-      val = i < cnt ? list[i] : -1;
-    }
-    return __builtin_amdgcn_readlane(val, e - base);
-  }
-  // Next usable entry at or after e (same rules as next_entry), or -1.
-  __device__ __forceinline__ int next(int e) {
-    for (; e < cnt; ++e) {
-      const int j = get(e);
-      if (j < 0) return -1;
-      if (j <= t) return e;
-    }
-    return -1;
-  }
-};
-
-// ------------------------------------------------------------------ padded block images
-//
-// The attention loop streams each listed block in sub-blocks of SB = BLK/2 keys.  In LDS a K
-// sub-block is SB rows of D bf16 and a V^T sub-block is D rows of SB fp16, each row padded
-// (K by 16 bytes, V^T by 8) so that the lanes of one LDS phase, which read the same column
-// of consecutive rows, fall on distinct banks: the row strides are odd multiples of the read
-// width modulo the 256-byte bank sweep.  Padding rather than an address swizzle keeps every
-// operand read at a per-lane base plus a compile-time offset.
-template <int D>
-struct KImg {
-  static constexpr int RB = D * 2 + 16;  // row bytes
-  static constexpr int CPR = RB / 16;    // 16-byte chunks per row (last one is padding)
-};
-template <int SB>
-struct VImg {
-  static constexpr int RB = SB * 2 + 8;  // row bytes
-};
-
 // max / sum of x over lanes l and l ^ 32 (v_permlane32_swap, no LDS traffic).  The swap
 // hands each lane its own value and its partner's, one in each result; both lanes of a pair
 // combine the same two values, so they get bit-identical results.
@@ -119,194 +77,234 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ------------------------------------------------------------------ step images
+//
+// A step is 32 consecutive keys of one block.  In LDS (and, for V, in the packed workspace):
+//   K image    32 key rows x D bf16, rows of 2D bytes, dense.  The 16-byte chunk q of row r
+//              (coordinates 8q .. 8q+7) sits at chunk position q ^ kswz(r).
+//   V^T image  D coordinate rows x 32 keys fp16, rows of 64 bytes, dense.  Row d holds four
+//              16-byte chunks; logical chunk c = 2h + u holds keys 16h + 4u + (0..3) followed
+//              by keys 16h + 8 + 4u + (0..3) (the eight keys one lane feeds to one P V^T
+//              product) and sits at chunk position c ^ vswz(d).
+// The swizzles make the 16-byte operand reads conflict-free: in a K read (chunk q of rows
+// 0..31, 256-byte rows) any 16 consecutive lanes hit 16 distinct 16-byte bank groups; in a V^T
+// read (chunk c of rows 0..31, 64-byte rows) any 8 consecutive lanes hit distinct groups of a
+// 128-byte bank sweep and any 16 consecutive lanes distinct groups of a 256-byte one.
+// Swizzling instead of padding keeps the images dense, so no padding bytes are streamed.
+constexpr int kStep = 32;
+
+#ifndef ATTN_QH
+#define ATTN_QH 1
+#endif
+
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return (r / (128 / D)) & (D / 8 - 1);
+}
+__device__ __forceinline__ int vswz(int d) { return (((d >> 1) ^ (d >> 3)) & 1) | (d & 4) >> 1; }
+
 // ------------------------------------------------------------------------------ pack_v
 
 constexpr int kPackThreads = 256;
 
-// V [B, N, Hkv, D] bf16 -> fp16 sub-block images [B, Hkv, n, BLK/SB] x (D rows of
-// VImg<SB>::RB bytes: SB keys then zero padding) -- exactly the LDS image attn_bf16 uses.
-template <int D, int BLK>
+// V [B, N, Hkv, D] bf16 -> fp16 V^T step images [B, Hkv, N / 32] x (D x 32), one workgroup
+// per step.
+template <int D>
 __global__ __launch_bounds__(kPackThreads) void pack_v(Dims dm, const uint16_t* __restrict__ V,
                                                        uint16_t* __restrict__ Vp) {
-  constexpr int SB = BLK / 2;
-  constexpr int RS = D + 2;                 // LDS row stride (elements)
-  constexpr int GR = VImg<SB>::RB / 8;      // 8-byte granules per image row (last: padding)
-  constexpr int IMG = D * VImg<SB>::RB / 2; // fp16 elements per sub-block image
-  __shared__ uint16_t sv[BLK * RS];
-  const int id = (int)blockIdx.x;  // ((b * Hkv + g) * n + j)
-  const int j = id % dm.n;
-  const int bg = id / dm.n;
+  constexpr int RS = D + 2;  // LDS row stride (elements)
+  __shared__ uint16_t sv[kStep * RS];
+  const int steps = dm.N / kStep;
+  const int id = (int)blockIdx.x;  // (b * Hkv + g) * steps + s
+  const int s = id % steps;
+  const int bg = id / steps;
   const int g = bg % dm.Hkv, b = bg / dm.Hkv;
-  const uint16_t* src = V + (((size_t)b * dm.N + (size_t)j * BLK) * dm.Hkv + g) * D;
-  for (int c = threadIdx.x; c < BLK * D / 8; c += kPackThreads) {
+  const uint16_t* src = V + (((size_t)b * dm.N + (size_t)s * kStep) * dm.Hkv + g) * D;
+  for (int c = threadIdx.x; c < kStep * D / 8; c += kPackThreads) {
     const int r = c / (D / 8), col = c - r * (D / 8);
     const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)r * dm.Hkv * D + col * 8);
     uint32_t* dst = reinterpret_cast<uint32_t*>(sv + r * RS + col * 8);
     dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
   }
   __syncthreads();
-  uint2* out = reinterpret_cast<uint2*>(Vp + (size_t)id * (BLK / SB) * IMG);
-  for (int i = threadIdx.x; i < (BLK / SB) * D * GR; i += kPackThreads) {
-    const int sub = i / (D * GR);
-    const int w = i - sub * (D * GR);
-    const int d = w / GR, gk = w - d * GR;  // granule gk of row d
-    if (gk == GR - 1) {
-      out[i] = make_uint2(0u, 0u);
-      continue;
-    }
-    const int key0 = sub * SB + 4 * gk;
-    float x[4];
+  uint4* out = reinterpret_cast<uint4*>(Vp + (size_t)id * D * kStep);
+  for (int i = threadIdx.x; i < D * 4; i += kPackThreads) {
+    const int d = i >> 2, pos = i & 3;
+    const int c = pos ^ vswz(d);
+    const int key0 = 16 * (c >> 1) + 4 * (c & 1);  // keys key0 + (0..3), key0 + 8 + (0..3)
+    float x[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) x[k] = bf16_bits_to_f32(sv[(key0 + k) * RS + d]);
-    const f16x2 a = __builtin_convertvector((f32x2){x[0], x[1]}, f16x2);
-    const f16x2 c = __builtin_convertvector((f32x2){x[2], x[3]}, f16x2);
-    out[i] = make_uint2(*reinterpret_cast<const uint32_t*>(&a), *reinterpret_cast<const uint32_t*>(&c));
+    for (int k = 0; k < 4; ++k) {
+      x[k] = bf16_bits_to_f32(sv[(key0 + k) * RS + d]);
+      x[4 + k] = bf16_bits_to_f32(sv[(key0 + 8 + k) * RS + d]);
+    }
+    uint32_t wv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f16x2 h2 = __builtin_convertvector((f32x2){x[2 * k], x[2 * k + 1]}, f16x2);
+      wv[k] = __builtin_bit_cast(uint32_t, h2);
+    }
+    out[i] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   }
 }
 
 // --------------------------------------------------------------------------- attn_bf16
 
-template <int D, int BLK>
-struct Tiles {
-  static constexpr int NW = BLK / 32;          // waves = query groups of 32 rows
-  static constexpr int NT = 64 * NW;           // threads (= 2 * BLK)
-  static constexpr int SB = BLK / 2;           // keys per pipeline step (sub-block)
-  static constexpr int NSB = BLK / SB;         // sub-blocks per block
-  static constexpr int KT = SB / 32;           // 32-key tiles per step
-  static constexpr int KB = SB * KImg<D>::RB;  // bytes of a K image
-  static constexpr int VB = D * VImg<SB>::RB;  // bytes of a V^T image
-  static constexpr int KCH = KB / 16, VCH = VB / 16;  // 16-byte chunks
-  static constexpr int STAGE = KB + VB;
-  static constexpr int VSUB = VB / 2;          // fp16 elements per packed V^T image
+// D head dim, QH 32-row query groups per wave, NW waves per workgroup.
+template <int D, int QH, int NW>
+struct Cfg {
+  static constexpr int BLK = 32 * QH * NW;     // query tile rows = block keys
+  static constexpr int NSUB = BLK / kStep;     // steps per block
+  static constexpr int DC = D / 16;            // 16-coordinate chunks of the S^T products
+  static constexpr int DT = D / 32;            // 32-coordinate tiles of O^T
+  static constexpr int KSLOT = kStep * D * 2;  // bytes of a K step image
+  static constexpr int VSLOT = D * kStep * 2;  // bytes of a V^T step image
+  static constexpr int NR = 4;                 // ring slots (a K and a V^T image each)
+  static constexpr int KREG = KSLOT / 1024;    // 1 KiB load regions per image
+  static constexpr int VREG = VSLOT / 1024;
+  static constexpr int LPW = (KREG + VREG) / NW;  // loads per wave per refill group
+  static_assert(KREG % NW == 0 && VREG % NW == 0, "load regions must split evenly");
+  static constexpr int LCAP = 512;             // list entries staged in LDS per segment
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// Issues the direct global->LDS loads of sub-block `sub` of block j into one stage: lane i
-// of a wave's load lands at the 1 KiB region base + 16 i, so each lane fetches the global
-// chunk that belongs at its slot (K padding slots refetch the row's first chunk).
-template <int D, int BLK>
-__device__ __forceinline__ void issue_step(const uint16_t* __restrict__ Kg,
-                                           const uint16_t* __restrict__ Vpg, int rstride,
-                                           int j, int sub, char* kst, char* vst) {
-  using TL = Tiles<D, BLK>;
-  constexpr int CPR = KImg<D>::CPR;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint16_t* kb = Kg + ((size_t)j * BLK + (size_t)sub * TL::SB) * rstride;
-  const uint16_t* vb = Vpg + ((size_t)j * TL::NSB + sub) * TL::VSUB;
-#pragma unroll
-  for (int region = wv; region * 64 < TL::KCH; region += TL::NW) {
-    const int P = region * 64 + lane;
-    const int r = P / CPR, c = P - r * CPR;
-    if (P < TL::KCH)
-      __builtin_amdgcn_global_load_lds(kb + (size_t)r * rstride + (c < CPR - 1 ? c : 0) * 8,
-                                       (lds_ptr)(kst + region * 1024), 16, 0, 0);
-  }
-#pragma unroll
-  for (int region = wv; region * 64 < TL::VCH; region += TL::NW) {
-    const int P = region * 64 + lane;
-    if (P < TL::VCH)
-      __builtin_amdgcn_global_load_lds(vb + (size_t)P * 8, (lds_ptr)(vst + region * 1024), 16,
-                                       0, 0);
-  }
+// LDS byte address of a pointer into a __shared__ object, and reads at a raw LDS address
+// (one address register per read, any constant offset folded into the instruction).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr)p;
+}
+template <typename T>
+__device__ __forceinline__ T lds_read(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>((uintptr_t)addr);
 }
 
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Direct global -> LDS load: lane i's 16 bytes at gbase + voff (bytes) land at LDS address
+// m0 + 16 i.  gbase and lds are wave-uniform.  Inline asm keeps these loads out of the
+// compiler's own wait insertion, which cannot tell which ring slot a later LDS read touches
+// and would drain every load in flight before it; each wait for them is explicit (wait_vm
+// followed by a barrier).  The s_nop gives the load the wait states it needs after M0 and
+// its scalar base are written.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left alone), as the builtin so that the compiler's
+// own wait insertion knows which earlier loads have completed.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+// Workgroup barrier without the full memory drain __syncthreads() implies: loads still in
+// flight into other ring slots stay in flight.  Every LDS read before it has been consumed
+// by then (its value fed a product that precedes the barrier).
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 // A row's running maximum is only raised when a new logit exceeds it by more than this many
 // powers of two; until then probabilities may reach 2^kLazy, which fp16 P and the fp32
 // accumulators hold exactly enough, and the rescale of O is skipped.
 constexpr float kLazy = 8.0f;
 
-// Online-softmax state of one wave (32 query rows; each lane pair shares a row).
-template <int D>
-struct RowState {
-  f32x16 acc_o[D / 32];
-  float m_run, l_run;
+template <int D, int QH>
+struct WaveState {
+  f32x16 acc_o[QH][D / 32];
+  float m_run[QH], l_run[QH];
 };
 
-// One pipeline step: S^T = K Q^T for SB keys, online softmax, O^T += V^T P^T.
-template <int D, int BLK>
-__device__ __forceinline__ void compute_step(const char* __restrict__ kst,
-                                             const char* __restrict__ vst, const bf16x8 (&qf)[D / 16],
-                                             RowState<D>& rs, bool diag, int k0, int qloc,
-                                             int l32, int hi, float scale_log2) {
-  using TL = Tiles<D, BLK>;
-  constexpr int KT = TL::KT, SB = TL::SB, DT = D / 32, DC = D / 16;
-  constexpr int KRB = KImg<D>::RB, VRB = VImg<SB>::RB;
-  // S^T = K Q^T: KT tiles x DC coordinate chunks = NS products, their A operands read from
-  // LDS PD products ahead (scheduling fences keep the reads where they are written, so the
-  // matrix unit never waits on the full LDS latency).
-  constexpr int NS = KT * DC, PD = 4;
-  f32x16 s[KT];
+// S^T for one step: QH accumulators of 32 keys x 32 query rows.  Each K chunk read from LDS
+// feeds QH products; reads run PD chunks ahead of their products.
+template <int D, int QH>
+__device__ __forceinline__ void step_scores(const uint32_t (&ka_addr)[D / 16],
+                                            const bf16x8 (&qf)[QH][D / 16], f32x16 (&s)[QH]) {
+  constexpr int DC = D / 16, PD = 3;
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) s[kt] = (f32x16){};
-  const char* kp = kst + l32 * KRB + hi * 16;  // row l32 (+32 kt), coordinates 8*hi + 16c
-  auto kaddr = [&](int i) { return kp + (i / DC) * 32 * KRB + (i % DC) * 32; };
+  for (int qh = 0; qh < QH; ++qh) s[qh] = (f32x16){};
   bf16x8 ka[PD];
 #pragma unroll
-  for (int i = 0; i < PD; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(kaddr(i));
+  for (int i = 0; i < PD; ++i) ka[i] = lds_read<bf16x8>(ka_addr[i]);
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
+  for (int c = 0; c < DC; ++c) {
     __builtin_amdgcn_sched_barrier(0);
-    s[i / DC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % PD], qf[i % DC], s[i / DC], 0, 0, 0);
-    if (i + PD < NS) ka[i % PD] = *reinterpret_cast<const bf16x8*>(kaddr(i + PD));
+#pragma unroll
+    for (int qh = 0; qh < QH; ++qh)
+      s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c % PD], qf[qh][c], s[qh], 0, 0, 0);
+    if (c + PD < DC) ka[c % PD] = lds_read<bf16x8>(ka_addr[c + PD]);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // Lane value (kt, i, r) is key k0 + kt*32 + 8i + 4*hi + r of the block.
+}
+
+// Online softmax of one step's logits (masked on the diagonal block) and O^T += V^T P^T.
+template <int D, int QH>
+__device__ __forceinline__ void step_softmax_pv(f32x16 (&s)[QH], const uint32_t (&va_addr)[2],
+                                                WaveState<D, QH>& st,
+                                                bool diag, int kbase, int qbase, int hi,
+                                                float scale_log2) {
+  constexpr int DT = D / 32;
+  // Lane value v of s[qh] is key kbase + 8 (v >> 2) + 4 hi + (v & 3) of the tile, query row
+  // qbase + 32 qh (+ lane % 32).
   if (diag) {
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int qh = 0; qh < QH; ++qh)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int kloc = k0 + kt * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-        if (kloc > qloc) s[kt][v] = -INFINITY;
+        const int kloc = kbase + 8 * (v >> 2) + 4 * hi + (v & 3);
+        if (kloc > qbase + 32 * qh) s[qh][v] = -INFINITY;
       }
   }
-  float mloc = -INFINITY;
+  float alpha[QH];
+  bool any_raise = false;
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt)
+  for (int qh = 0; qh < QH; ++qh) {
+    float mloc = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[kt][v]);
-  mloc = pair_max(mloc);
-  const bool raise =
-      mloc > rs.m_run && (rs.m_run == -INFINITY || (mloc - rs.m_run) * scale_log2 > kLazy);
-  if (__any(raise)) {
-    const float m_new = raise ? mloc : rs.m_run;
-    const float alpha =
-        rs.m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((rs.m_run - m_new) * scale_log2);
-    rs.m_run = m_new;
-    rs.l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) rs.acc_o[dt] *= alpha;
+    for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[qh][v]);
+    mloc = pair_max(mloc);
+    const float m = st.m_run[qh];
+    const bool raise = mloc > m && (m == -INFINITY || (mloc - m) * scale_log2 > kLazy);
+    const float m_new = raise ? mloc : m;
+    alpha[qh] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m - m_new) * scale_log2);
+    st.m_run[qh] = m_new;
+    any_raise |= raise;
   }
-  const float mc = rs.m_run == -INFINITY ? 0.0f : -rs.m_run * scale_log2;
-  float psum = 0.0f;
-  f16x8 pf[KT][2];
+  if (__any(any_raise)) {
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt)
+    for (int qh = 0; qh < QH; ++qh) {
+      st.l_run[qh] *= alpha[qh];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], scale_log2, mc));
-      psum += p;
-      pf[kt][v >> 3][v & 7] = (_Float16)p;
+      for (int dt = 0; dt < DT; ++dt) st.acc_o[qh][dt] *= alpha[qh];
     }
-  rs.l_run += psum;
-  // O^T += V^T P^T.  B operand slot 8*hi + 4i' + r of pf[kt][half] is key
-  // kt*32 + 16*half + 8i' + 4*hi + r of the step; the A operand reads V^T at those keys.
-  // Products are ordered (dt, kt, half); operands are read PD products ahead.
-  constexpr int NP = DT * KT * 2;
-  const char* vp = vst + l32 * VRB + hi * 8;  // row d = dt*32 + l32, keys 4*hi + ...
-  auto vaddr = [&](int i) {
-    const int dt = i / (KT * 2), kt = (i / 2) % KT, half = i % 2;
-    return vp + dt * 32 * VRB + (kt * 32 + 16 * half) * 2;
-  };
+  }
+  f16x8 pf[QH][2];
+#pragma unroll
+  for (int qh = 0; qh < QH; ++qh) {
+    const float m = st.m_run[qh];
+    const float mc = m == -INFINITY ? 0.0f : -m * scale_log2;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      pf[qh][v >> 3][v & 7] =
+          (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[qh][v], scale_log2, mc));
+    // Row sum of the fp16 probabilities the P V^T product uses, two per v_dot2_f32_f16 (the
+    // products by 1 are exact; the sum is accumulated in fp32).
+    float psum = st.l_run[qh];
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      const f16x2 pp = {pf[qh][v >> 3][v & 7], pf[qh][v >> 3][(v & 7) + 1]};
+      psum = __builtin_amdgcn_fdot2(pp, one, psum, false);
+    }
+    st.l_run[qh] = psum;
+  }
+  // O^T += V^T P^T.  B operand slot 8 hi + 4 i' + r of pf[qh][half] is key
+  // 16 half + 8 i' + 4 hi + r of the step; the A operand is chunk 2 half + hi of V^T row d,
+  // which holds exactly those keys in that order (read through va_addr[half]).
+  constexpr int NP = DT * 2, PD = 3;
   auto vload = [&](int i) {
-    const char* q = vaddr(i);
-    const uint2 lo = *reinterpret_cast<const uint2*>(q);
-    const uint2 up = *reinterpret_cast<const uint2*>(q + 16);
-    const uint4 raw = make_uint4(lo.x, lo.y, up.x, up.y);
-    return *reinterpret_cast<const f16x8*>(&raw);
+    const int dt = i >> 1, half = i & 1;
+    return lds_read<f16x8>(va_addr[half] + dt * 2048);
   };
   f16x8 va[PD];
 #pragma unroll
@@ -314,122 +312,218 @@ __device__ __forceinline__ void compute_step(const char* __restrict__ kst,
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     __builtin_amdgcn_sched_barrier(0);
-    const int dt = i / (KT * 2), kt = (i / 2) % KT, half = i % 2;
-    rs.acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i % PD], pf[kt][half], rs.acc_o[dt], 0, 0, 0);
+    const int dt = i >> 1, half = i & 1;
+#pragma unroll
+    for (int qh = 0; qh < QH; ++qh)
+      st.acc_o[qh][dt] =
+          __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i % PD], pf[qh][half], st.acc_o[qh][dt], 0, 0, 0);
     if (i + PD < NP) va[i % PD] = vload(i + PD);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2, 2) void attn_bf16(  // BLK*2 == Tiles::NT; 2 waves/SIMD
+template <int D, int QH, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_bf16(
     Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vp, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, int W, float scale_log2, void* __restrict__ O,
     int out_f32, float* __restrict__ lse) {
-  using TL = Tiles<D, BLK>;
-  constexpr int SB = TL::SB, DT = D / 32, DC = D / 16;
-  // Two separate stage buffers: the loads in flight into one are then provably disjoint from
-  // the reads of the other, so reads never wait for them.
-  __shared__ __attribute__((aligned(1024))) char k0s[TL::KB], v0s[TL::VB];
-  __shared__ __attribute__((aligned(1024))) char k1s[TL::KB], v1s[TL::VB];
+  using C = Cfg<D, QH, NW>;
+  constexpr int BLK = C::BLK, NSUB = C::NSUB, DC = C::DC, DT = C::DT, LPW = C::LPW;
+  // Ring of NR slots, each a K step image followed by a V^T step image.
+  constexpr int SLOT = C::KSLOT + C::VSLOT;
+  __shared__ __attribute__((aligned(1024))) char ring[C::NR * SLOT];
+  __shared__ int lst[C::LCAP];
+  __shared__ int seg_info[4];  // usable entries, diagonal position, next entry, done
 
   int b, h, t;
   decode_tile(dm, b, h, t);
   const int g = h / dm.G;
-  const int lane = threadIdx.x & 63, qg = threadIdx.x >> 6;  // wave = query group
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
   const int l32 = lane & 31, hi = lane >> 5;
   const size_t bht = ((size_t)b * dm.Hq + h) * dm.n + t;
   const int32_t* list = kv_idx + bht * W;
-  const int cnt = min(kv_cnt[bht], W);
-  const int qloc = qg * 32 + l32;  // this lane's query row within the tile
-  const int qrow = t * BLK + qloc;
+  const int cnt = max(0, min(kv_cnt[bht], W));
+  const int qbase = w * 32 * QH + l32;  // this lane's first query row within the tile
   const int rstride = dm.Hkv * D;
   const uint16_t* Kg = K + ((size_t)b * dm.N * dm.Hkv + g) * D;
-  const uint16_t* Vpg = Vp + ((size_t)b * dm.Hkv + g) * dm.n * TL::NSB * TL::VSUB;
+  const uint16_t* Vpg = Vp + ((size_t)b * dm.Hkv + g) * (size_t)dm.N * D;
 
-  // Q fragment (B operand of S^T = K Q^T): lane holds coordinates 16c + 8*hi .. +7 of its row.
-  bf16x8 qf[DC];
-  {
-    const uint16_t* qp = Q + (((size_t)b * dm.N + qrow) * dm.Hq + h) * D + 8 * hi;
+  // Q fragments (B operand of S^T = K Q^T): lane holds coordinates 16c + 8 hi .. +7 of row
+  // qbase + 32 qh.
+  bf16x8 qf[QH][DC];
 #pragma unroll
-    for (int c = 0; c < DC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
+  for (int qh = 0; qh < QH; ++qh) {
+    const uint16_t* qp =
+        Q + (((size_t)b * dm.N + (size_t)t * BLK + qbase + 32 * qh) * dm.Hq + h) * D + 8 * hi;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) qf[qh][c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
   }
-  RowState<D> rs;
+  // Use the fragments once here so that the compiler waits for them now, before the K/V
+  // stream is in flight, rather than draining that stream at the first product.
 #pragma unroll
-  for (int i = 0; i < DT; ++i) rs.acc_o[i] = (f32x16){};
-  rs.m_run = -INFINITY;
-  rs.l_run = 0.0f;
-
-  // Steps are (list entry, sub-block); stage 0 holds even steps, stage 1 odd ones.
-  ListWindow lw(list, cnt, t);
-  int e = lw.next(0), sub = 0;
-  int j = e >= 0 ? lw.get(e) : 0;
-  if (e >= 0) issue_step<D, BLK>(Kg, Vpg, rstride, j, 0, k0s, v0s);
-  while (e >= 0) {
-    // even step: compute from stage 0, prefetch the next step into stage 1
-    {
-      int e2 = e, sub2 = sub + 1, j2 = j;
-      if (sub2 == TL::NSB) {
-        e2 = lw.next(e + 1);
-        sub2 = 0;
-        if (e2 >= 0) j2 = lw.get(e2);
-      }
-      wait_loads();
-      __syncthreads();
-      if (e2 >= 0) issue_step<D, BLK>(Kg, Vpg, rstride, j2, sub2, k1s, v1s);
-      const int k0 = sub * SB;
-      if (!(j == t && k0 > qg * 32 + 31))
-        compute_step<D, BLK>(k0s, v0s, qf, rs, j == t, k0, qloc, l32, hi, scale_log2);
-      e = e2;
-      sub = sub2;
-      j = j2;
-    }
-    if (e < 0) break;
-    // odd step: compute from stage 1, prefetch into stage 0
-    {
-      int e2 = e, sub2 = sub + 1, j2 = j;
-      if (sub2 == TL::NSB) {
-        e2 = lw.next(e + 1);
-        sub2 = 0;
-        if (e2 >= 0) j2 = lw.get(e2);
-      }
-      wait_loads();
-      __syncthreads();
-      if (e2 >= 0) issue_step<D, BLK>(Kg, Vpg, rstride, j2, sub2, k0s, v0s);
-      const int k0 = sub * SB;
-      if (!(j == t && k0 > qg * 32 + 31))
-        compute_step<D, BLK>(k1s, v1s, qf, rs, j == t, k0, qloc, l32, hi, scale_log2);
-      e = e2;
-      sub = sub2;
-      j = j2;
-    }
+  for (int qh = 0; qh < QH; ++qh)
+#pragma unroll
+    for (int c = 0; c < DC; ++c) asm volatile("" ::"v"(qf[qh][c]));
+  WaveState<D, QH> st;
+#pragma unroll
+  for (int qh = 0; qh < QH; ++qh) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.acc_o[qh][dt] = (f32x16){};
+    st.m_run[qh] = -INFINITY;
+    st.l_run[qh] = 0.0f;
   }
 
-  const float l_tot = pair_sum(rs.l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const size_t orow = (((size_t)b * dm.N + qrow) * dm.Hq + h) * D;
+  // Per-lane LDS read offsets within a slot.
+  int koff[DC];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int c = 0; c < DC; ++c) koff[c] = l32 * 2 * D + 16 * ((2 * c + hi) ^ kswz<D>(l32));
+  int voff[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = dt * 32 + 8 * i + 4 * hi;
-      float o[4];
+  for (int hf = 0; hf < 2; ++hf) voff[hf] = l32 * 64 + 16 * ((2 * hf + hi) ^ vswz(l32));
+  // Per-lane source offsets (elements, relative to a step's first key row) of this wave's K
+  // regions: region w + NW k, lane i lands at image byte 1024 (w + NW k) + 16 i.
+  int kgo[C::KREG / NW];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = rs.acc_o[dt][4 * i + r] * inv;
-      if (out_f32) {
-        *reinterpret_cast<float4*>(static_cast<float*>(O) + orow + d0) =
-            make_float4(o[0], o[1], o[2], o[3]);
-      } else {
-        uint2 pk;
-        pk.x = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-        pk.y = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(O) + orow + d0) = pk;
+  for (int k = 0; k < C::KREG / NW; ++k) {
+    const int off = (w + NW * k) * 1024 + 16 * lane;
+    const int r = off / (2 * D), p = (off % (2 * D)) / 16;
+    kgo[k] = 2 * (r * rstride + 8 * (p ^ kswz<D>(r)));  // bytes
+  }
+  const uint32_t vlo = 16 * lane;  // V^T images are copied verbatim
+
+  int seg_start = 0;
+  for (;;) {
+    // Stage the next segment of usable entries (0 <= j <= t, before the first negative
+    // entry, at most LCAP of them) in LDS; wave 0 compacts, the workgroup waits.
+    if (w == 0) {
+      int u = 0, base = seg_start, diag = -1, next = cnt, done = 1;
+      while (base < cnt) {
+        const int e = base + lane;
+        const int x = e < cnt ? list[e] : 0;
+        const unsigned long long negm = __ballot(e < cnt && x < 0);
+        const int first_neg = negm ? __builtin_ctzll(negm) : 64;
+        const bool valid = e < cnt && lane < first_neg && x <= t;
+        const unsigned long long vm = __ballot(valid);
+        const int pre = __builtin_popcountll(vm & ((1ull << lane) - 1ull));
+        const int nv = __builtin_popcountll(vm);
+        const int fit = min(nv, C::LCAP - u);
+        if (valid && pre < fit) lst[u + pre] = x;
+        // entries are distinct, so at most one lane holds the diagonal block
+        const unsigned long long dm_ = __ballot(valid && pre < fit && x == t);
+        if (dm_) diag = u + (int)__builtin_popcountll(vm & ((1ull << __builtin_ctzll(dm_)) - 1ull));
+        u += fit;
+        if (fit < nv) {  // LDS full: continue from the first entry that did not fit
+          const unsigned long long om = __ballot(valid && pre == fit);
+          next = base + __builtin_ctzll(om);
+          done = 0;
+          break;
+        }
+        if (negm) break;
+        base += 64;
+      }
+      if (lane == 0) {
+        seg_info[0] = u;
+        seg_info[1] = diag;
+        seg_info[2] = next;
+        seg_info[3] = done;
       }
     }
-  if (lse && hi == 0)
-    lse[((size_t)b * dm.Hq + h) * dm.N + qrow] =
-        l_tot > 0.0f ? (rs.m_run * scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+    __syncthreads();
+    const int U = seg_info[0], diag_e = seg_info[1], next_start = seg_info[2];
+    const int seg_done = seg_info[3];
+    const int nsteps = U * NSUB;
+
+    if (nsteps > 0) {
+      // Refill group m: K step m and V step m into ring slot m % NR.  Steps past the end reload
+      // the last step (valid memory, into a slot nobody reads again) so that every group
+      // issues the same LPW loads per wave, which the partial waits below count on.
+      const uint32_t ring_lds = lds_addr(ring);
+      auto entry_of = [&](int m) { return lst[min(m, nsteps - 1) / NSUB]; };
+      auto issue = [&](int m, int jv) {
+        const int a = min(m, nsteps - 1);
+        const int j = __builtin_amdgcn_readfirstlane(jv);  // uniform: SGPR base
+        const int sub = a % NSUB;
+        const uint16_t* kb = Kg + ((size_t)j * BLK + sub * kStep) * rstride;
+        const uint16_t* vb = Vpg + ((size_t)j * NSUB + sub) * (D * kStep) + 512 * w;
+        const uint32_t dst = ring_lds + (m % C::NR) * SLOT + w * 1024;
+#pragma unroll
+        for (int k = 0; k < C::KREG / NW; ++k) dma16(kb, kgo[k], dst + NW * k * 1024);
+#pragma unroll
+        for (int k = 0; k < C::VREG / NW; ++k)
+          dma16(vb + 512 * NW * k, vlo, dst + C::KSLOT + NW * k * 1024);
+      };
+#pragma unroll
+      for (int m = 0; m < C::NR - 1; ++m) issue(m, entry_of(m));
+      int jn = entry_of(C::NR - 1);  // block of the next group, read one step early
+
+      // Step i (slot i % NR): wait until group i has landed (groups i+1 .. i+NR-2 may still be
+      // in flight), barrier (every wave's part of group i is in, and every wave is done with
+      // step i-1, whose slot the new group overwrites), issue group i+NR-1, then compute step i.
+      for (int i = 0; i < nsteps; ++i) {
+        wait_vm<(C::NR - 2) * LPW>();
+        barrier_only();
+        issue(i + C::NR - 1, jn);
+        jn = entry_of(i + C::NR);
+        const uint32_t slot = ring_lds + (i % C::NR) * SLOT;
+        uint32_t ka_addr[DC], va_addr[2];
+        // One add per address register per step; the empty asm keeps the compiler from
+        // re-deriving each read's address from its parts.
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          ka_addr[c] = slot + koff[c];
+          asm volatile("" : "+v"(ka_addr[c]));
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          va_addr[c] = slot + C::KSLOT + voff[c];
+          asm volatile("" : "+v"(va_addr[c]));
+        }
+        const int e = i / NSUB, sub = i - e * NSUB;
+        const bool diag = e == diag_e;
+        // On the diagonal block, a step whose first key lies after this wave's last row is
+        // fully masked for the wave: skip it.
+        if (diag && sub >= QH * (w + 1)) continue;
+        f32x16 sc[QH];
+        step_scores<D, QH>(ka_addr, qf, sc);
+        step_softmax_pv<D, QH>(sc, va_addr, st, diag, sub * kStep, qbase, hi, scale_log2);
+      }
+      wait_vm<0>();  // dummy refills still in flight must land before the slots are reused
+    }
+    __syncthreads();
+    if (seg_done) break;
+    seg_start = next_start;
+  }
+
+#pragma unroll
+  for (int qh = 0; qh < QH; ++qh) {
+    const float l_tot = pair_sum(st.l_run[qh]);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const int qrow = t * BLK + qbase + 32 * qh;
+    const size_t orow = (((size_t)b * dm.N + qrow) * dm.Hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = dt * 32 + 8 * i + 4 * hi;
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = st.acc_o[qh][dt][4 * i + r] * inv;
+        if (out_f32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(O) + orow + d0) =
+              make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+          uint2 pk;
+          pk.x = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+          pk.y = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(O) + orow + d0) = pk;
+        }
+      }
+    if (lse && hi == 0)
+      lse[((size_t)b * dm.Hq + h) * dm.N + qrow] =
+          l_tot > 0.0f ? (st.m_run[qh] * scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
 }
 
 // ---------------------------------------------------------------------- fp32 (VALU) path
@@ -499,19 +593,18 @@ __global__ __launch_bounds__(BLK) void attn_f32(Dims dm, const float* __restrict
     lse[((size_t)b * dm.Hq + h) * dm.N + qrow] = l > 0.0f ? m + __logf(l) : -INFINITY;
 }
 
-template <int D, int BLK>
+template <int D, int QH, int NW>
 hipError_t launch_bf16(const Dims& dm, const void* Q, const void* K, const void* V,
                        const int32_t* kv_idx, const int32_t* kv_cnt, int W, float scale,
                        void* ws, void* O, int out_dtype, float* lse, hipStream_t s) {
-  using TL = Tiles<D, BLK>;
   uint16_t* Vp = static_cast<uint16_t*>(ws);
-  const unsigned nblk = (unsigned)((size_t)dm.B * dm.Hkv * dm.n);
-  hipLaunchKernelGGL((pack_v<D, BLK>), dim3(nblk), dim3(kPackThreads), 0, s, dm,
+  const unsigned nsteps = (unsigned)((size_t)dm.B * dm.Hkv * (dm.N / kStep));
+  hipLaunchKernelGGL((pack_v<D>), dim3(nsteps), dim3(kPackThreads), 0, s, dm,
                      static_cast<const uint16_t*>(V), Vp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
-  hipLaunchKernelGGL((attn_bf16<D, BLK>), dim3(grid), dim3(TL::NT), 0, s, dm,
+  hipLaunchKernelGGL((attn_bf16<D, QH, NW>), dim3(grid), dim3(64 * NW), 0, s, dm,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K), Vp,
                      kv_idx, kv_cnt, W, scale * kLog2e, O, out_dtype == SA_F32 ? 1 : 0, lse);
   return hipGetLastError();
@@ -536,8 +629,8 @@ hipError_t launch_f32(const Dims& dm, const void* Q, const void* K, const void* 
 
 size_t forward_ws_bytes(const Dims& dm) {
   if (dm.dtype != SA_BF16) return 0;
-  // packed V^T images: per block, 2 sub-blocks of d rows x (blk/2 keys + 4 padding) fp16
-  return (size_t)dm.B * dm.Hkv * dm.n * 2 * dm.d * (dm.blk / 2 + 4) * sizeof(uint16_t);
+  // packed V^T step images: the size of V
+  return (size_t)dm.B * dm.N * dm.Hkv * dm.d * sizeof(uint16_t);
 }
 
 hipError_t launch_forward(const Dims& dm, const void* Q, const void* K, const void* V,
@@ -545,14 +638,16 @@ hipError_t launch_forward(const Dims& dm, const void* Q, const void* K, const vo
                           void* ws, void* O, int out_dtype, float* lse, hipStream_t s) {
   if (dm.dtype == SA_BF16) {
     if (dm.d == 64)
-      return dm.blk == 64 ? launch_bf16<64, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
-                                                out_dtype, lse, s)
-                          : launch_bf16<64, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
-                                                 out_dtype, lse, s);
-    return dm.blk == 64 ? launch_bf16<128, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
-                                               out_dtype, lse, s)
-                        : launch_bf16<128, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
-                                                out_dtype, lse, s);
+      return dm.blk == 64 ? launch_bf16<64, 1, 2>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
+                                                  out_dtype, lse, s)
+                          : launch_bf16<64, ATTN_QH, 4 / ATTN_QH>(dm, Q, K, V, kv_idx, kv_cnt,
+                                                                   W, scale, ws, O, out_dtype,
+                                                                   lse, s);
+    return dm.blk == 64 ? launch_bf16<128, 1, 2>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
+                                                 out_dtype, lse, s)
+                        : launch_bf16<128, ATTN_QH, 4 / ATTN_QH>(dm, Q, K, V, kv_idx, kv_cnt, W,
+                                                                  scale, ws, O, out_dtype, lse,
+                                                                  s);
   }
   if (dm.d == 64)
     return dm.blk == 64

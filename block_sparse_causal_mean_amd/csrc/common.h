@@ -78,14 +78,14 @@ inline SummaryLayout summary_layout(const Dims& D) {
 }
 
 // Maps a workgroup id to (b, h, t).  Logical order: (batch, kv head) outermost, then tiles
-// latest first (late tiles carry the most blocks), then the q heads of the kv head.
-// Workgroups are dealt to the 8 XCDs round-robin by id, so when the count divides evenly the
-// id is remapped to give each XCD a contiguous range of that order: one XCD then works on one
-// kv head's tiles at a time and its L2 holds the blocks (and block summaries) they share.
+// latest first (late tiles carry the most blocks), then the q heads of the kv head.  The
+// hardware deals consecutive ids to the 8 XCDs in turn, so at any moment every XCD works on the
+// same kv head's nearby tiles: the blocks they share are then fetched once into the last-level
+// cache that all XCDs see, rather than each XCD streaming a different head.  (Giving each XCD
+// its own kv head instead was measured slower: the concurrent working set of 8 heads does not
+// fit in that cache.)
 __device__ __forceinline__ void decode_tile(const Dims& dm, int& b, int& h, int& t) {
-  const int U = dm.B * dm.Hq * dm.n;
-  int id = (int)blockIdx.x;
-  if ((U & 7) == 0) id = (id & 7) * (U >> 3) + (id >> 3);
+  const int id = (int)blockIdx.x;
   const int per_pair = dm.n * dm.G;  // tiles x q heads of one (batch, kv head)
   const int pair = id / per_pair;
   const int rest = id - pair * per_pair;
