@@ -224,6 +224,7 @@ def main():
                      "flops_per_launch": flops, "ms_per_launch": ms_fwd},
         "score_roofline": {"bound": "hbm", "achieved": score_gbs, "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": score_gbs / PEAK_HBM_GBS,
+                           "traffic": traffic_from_profiles("pool_keys_" + w.name),
                            "bytes_per_launch": score_bytes, "ms_per_launch_cold": ms_cold,
                            "kernel": "pool_keys (sparse_attn_score)"},
         "stages_ms": {"score": ms_score, "select": ms_select, "forward": ms_fwd},
