@@ -66,12 +66,18 @@ def effective_flops(w: wl.Workload, kv_cnt: torch.Tensor) -> float:
 
 
 def time_score_cold(pf: api.Prefill, K, V, reps: int = 10) -> float:
-    """Mean duration (ms) of the summary kernel(s) with the caches evicted before each run."""
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    """Mean duration (ms) of the summary kernel(s) with the caches evicted before each run.
+
+    The eviction READS a 1 GiB buffer (4x the last-level cache), so K cannot be served from any
+    cache and no dirty lines are left behind: evicting by writing leaves write-backs that share
+    HBM with the timed kernel and measured at half the read bandwidth of a clean eviction."""
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
     s = torch.cuda.current_stream()
     total = 0.0
     for _ in range(reps):
-        flush.fill_(1)
+        torch.sum(flush, dim=0, out=sink)
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(s)
         pf.score(K, V)

@@ -9,13 +9,12 @@
 //
 // Both kernels stream their input exactly once and are bound by HBM bandwidth.
 //
-// pool_keys: one workgroup per (batch, block, slice of the Hkv*d row span).  A key row
-//   [Hkv, d] is contiguous, so each thread owns 16 bytes of the span and walks the block's
-//   rows in order: every load instruction of a wave reads 1 KiB contiguous, and the fp32
-//   accumulation per coordinate runs in row order (the fixed reduction order the selection
-//   relies on for reproducible results).  It also writes, for the selection's matrix-core
-//   prefilter, each summary's bf16 hi/lo split and the block's L2 norm (an upper bound
-//   ingredient only: it never decides a selection by itself).
+// pool_keys: one workgroup per (batch, block, kv head).  The block's key tile is copied to
+//   LDS with all of its loads in flight at once, then one thread per coordinate accumulates
+//   the rows in order (the fixed reduction order the selection relies on for reproducible
+//   results).  It also writes, for the selection's matrix-core prefilter, each summary's bf16
+//   hi/lo split and the block's L2 norm (an upper-bound ingredient only: it never decides a
+//   selection by itself).
 // value_norms: one workgroup per (batch, block).  Each (row, kv head) pair's squared norm is
 //   a fused multiply-add chain over the d coordinates in order, by one thread; the square
 //   roots go to LDS and one thread per kv head sums them in row order.
@@ -32,18 +31,23 @@ struct Vec16;  // 16 bytes of elements, converted exactly to fp32
 template <>
 struct Vec16<uint16_t> {
   static constexpr int N = 8;
-  __device__ __forceinline__ static void load(const uint16_t* p, float* x) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
+  __device__ __forceinline__ static void cvt(const uint4& v, float* x) {
     x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
     x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+  }
+  __device__ __forceinline__ static void load(const uint16_t* p, float* x) {
+    cvt(*reinterpret_cast<const uint4*>(p), x);
   }
 };
 template <>
 struct Vec16<float> {
   static constexpr int N = 4;
+  __device__ __forceinline__ static void cvt(const uint4& v, float* x) {
+    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+  }
   __device__ __forceinline__ static void load(const float* p, float* x) {
-    float4 v = *reinterpret_cast<const float4*>(p);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    cvt(*reinterpret_cast<const uint4*>(p), x);
   }
 };
 
@@ -54,89 +58,94 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) 
   lo = f32_to_bf16_bits(x - __uint_as_float(hi << 16));
 }
 
+// pool_keys: one workgroup per (batch, block, kv head).  The block's BLK x HD key tile is
+// first copied into LDS with every 16-byte load issued at once (8 per thread for bf16 at
+// BLK = HD = 128), so the memory system sees the whole tile in flight; then thread c sums
+// coordinate c over the rows in order from LDS (the fixed reduction order), writes the
+// summary, its bf16 hi/lo split, and the block's L2 norm (a workgroup reduction in any order:
+// it only scales the prefilter's error bound).
 template <typename T, int MODE, int BLK, int HD>
 __global__ __launch_bounds__(kPoolThreads) void pool_keys(const T* __restrict__ K,
                                                           float* __restrict__ summ,
                                                           uint16_t* __restrict__ bfp, int N,
-                                                          int n, int span, size_t plane,
+                                                          int n, int Hkv, size_t plane,
                                                           size_t kn_off) {
-  constexpr int E = Vec16<T>::N;
-  constexpr int LPH = HD / E;  // lanes per head (consecutive lanes of one wave)
-  const int bj = blockIdx.x;   // b * n + j
+  constexpr int E = Vec16<T>::N;   // elements per 16-byte chunk
+  constexpr int CPR = HD / E;      // chunks per row
+  constexpr int NCH = BLK * CPR;   // chunks in the tile
+  static_assert(NCH % kPoolThreads == 0, "tile chunks must split evenly over the threads");
+  static_assert(HD <= kPoolThreads, "one thread per coordinate");
+  __shared__ uint4 tile[NCH];
+  __shared__ float red[kPoolThreads / 64];
+  const int id = (int)blockIdx.x;  // (b * n + j) * Hkv + g
+  const int g = id % Hkv;
+  const int bj = id / Hkv;
   const int b = bj / n, j = bj - b * n;
-  const int e0 = (blockIdx.y * kPoolThreads + threadIdx.x) * E;
-  if (e0 >= span) return;  // whole heads drop out together: span is a multiple of HD
-  const T* src = K + ((size_t)b * N + (size_t)j * BLK) * span + e0;
-
-  float a[E], c[E];
-  float x[E];
-  Vec16<T>::load(src, x);
-  if (MODE == SA_KMEAN) {
+  const int span = Hkv * HD;
+  const T* src = K + ((size_t)b * N + (size_t)j * BLK) * span + (size_t)g * HD;
+  {
+    uint4 v[NCH / kPoolThreads];
 #pragma unroll
-    for (int i = 0; i < E; ++i) a[i] = 0.0f + x[i];
-  } else {
+    for (int k = 0; k < NCH / kPoolThreads; ++k) {
+      const int c = threadIdx.x + k * kPoolThreads;
+      v[k] = *reinterpret_cast<const uint4*>(src + (size_t)(c / CPR) * span + (c % CPR) * E);
+    }
 #pragma unroll
-    for (int i = 0; i < E; ++i) a[i] = c[i] = x[i];
+    for (int k = 0; k < NCH / kPoolThreads; ++k) tile[threadIdx.x + k * kPoolThreads] = v[k];
   }
+  __syncthreads();
+  float ss = 0.0f;
+  const int c = threadIdx.x;
+  if (c < HD) {
+    const T* tv = reinterpret_cast<const T*>(tile);
+    float a = 0.0f, mx = 0.0f;
 #pragma unroll 16
-  for (int r = 1; r < BLK; ++r) {
-    Vec16<T>::load(src + (size_t)r * span, x);
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
+    for (int r = 0; r < BLK; ++r) {
+      float x;
+      if constexpr (sizeof(T) == 2) x = bf16_bits_to_f32(tv[r * HD + c]);
+      else x = tv[r * HD + c];
       if (MODE == SA_KMEAN) {
-        a[i] = a[i] + x[i];
+        a = (r == 0 ? 0.0f : a) + x;
+      } else if (r == 0) {
+        a = mx = x;
       } else {
-        a[i] = x[i] < a[i] ? x[i] : a[i];
-        c[i] = x[i] > c[i] ? x[i] : c[i];
+        a = x < a ? x : a;
+        mx = x > mx ? x : mx;
       }
     }
-  }
-  const size_t o = (size_t)bj * span + e0;
-  float ss = 0.0f;  // squared norm share of the block's scoring vector (for the prefilter bound)
-  if (MODE == SA_KMEAN) {
-    const float inv = 1.0f / (float)BLK;  // exact: BLK is a power of two
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      a[i] = a[i] * inv;
-      summ[o + i] = a[i];
-      ss = __builtin_fmaf(a[i], a[i], ss);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      a[i] = canon(a[i]);
-      c[i] = canon(c[i]);
-      summ[o + i] = a[i];
-      summ[plane + o + i] = c[i];
-      ss = __builtin_fmaf(fmaxf(a[i] * a[i], c[i] * c[i]), 1.0f, ss);
-    }
-  }
-  // bf16 hi/lo planes: plane p's hi at bfp + 2p*plane, lo at bfp + (2p+1)*plane.
-#pragma unroll
-  for (int p = 0; p < (MODE == SA_KMEAN ? 1 : 2); ++p) {
-    const float* v = p == 0 ? a : c;
-    uint32_t hw[E / 2], lw[E / 2];
-#pragma unroll
-    for (int i = 0; i < E; i += 2) {
-      uint32_t h0, l0, h1, l1;
-      split_bf16(v[i], h0, l0);
-      split_bf16(v[i + 1], h1, l1);
-      hw[i / 2] = h0 | (h1 << 16);
-      lw[i / 2] = l0 | (l1 << 16);
-    }
-    uint16_t* hp = bfp + (size_t)(2 * p) * plane + o;
-    uint16_t* lp = bfp + (size_t)(2 * p + 1) * plane + o;
-    if (E == 8) {
-      *reinterpret_cast<uint4*>(hp) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint4*>(lp) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    const size_t o = ((size_t)bj * Hkv + g) * HD + c;
+    uint32_t hi, lo;
+    if (MODE == SA_KMEAN) {
+      a = a * (1.0f / (float)BLK);  // exact: BLK is a power of two
+      summ[o] = a;
+      ss = a * a;
+      split_bf16(a, hi, lo);
+      bfp[o] = (uint16_t)hi;
+      bfp[plane + o] = (uint16_t)lo;
     } else {
-      *reinterpret_cast<uint2*>(hp) = make_uint2(hw[0], hw[1]);
-      *reinterpret_cast<uint2*>(lp) = make_uint2(lw[0], lw[1]);
+      a = canon(a);
+      mx = canon(mx);
+      summ[o] = a;
+      summ[plane + o] = mx;
+      ss = fmaxf(a * a, mx * mx);
+      split_bf16(a, hi, lo);
+      bfp[o] = (uint16_t)hi;
+      bfp[plane + o] = (uint16_t)lo;
+      split_bf16(mx, hi, lo);
+      bfp[2 * plane + o] = (uint16_t)hi;
+      bfp[3 * plane + o] = (uint16_t)lo;
     }
   }
 #pragma unroll
-  for (int off = 1; off < LPH; off <<= 1) ss += __shfl_xor(ss, off);
-  if (e0 % HD == 0) summ[kn_off + (size_t)bj * (span / HD) + e0 / HD] = __builtin_sqrtf(ss);
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kPoolThreads / 64; ++w) t += red[w];
+    summ[kn_off + (size_t)bj * Hkv + g] = __builtin_sqrtf(t);
+  }
 }
 
 template <typename T, int BLK, int D>
@@ -174,12 +183,10 @@ __global__ __launch_bounds__(kPoolThreads) void value_norms(const T* __restrict_
 template <typename T, int MODE, int BLK, int HD>
 hipError_t launch_keys(const Dims& D, const void* K, float* summ, hipStream_t s) {
   const SummaryLayout L = summary_layout(D);
-  const int span = D.Hkv * D.d;
-  const int per_wg = kPoolThreads * Vec16<T>::N;
-  dim3 grid((unsigned)(D.B * D.n), (unsigned)((span + per_wg - 1) / per_wg));
   uint16_t* bfp = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(summ) + L.bf_byte);
-  hipLaunchKernelGGL((pool_keys<T, MODE, BLK, HD>), grid, dim3(kPoolThreads), 0, s,
-                     static_cast<const T*>(K), summ, bfp, D.N, D.n, span, L.plane, L.kn);
+  hipLaunchKernelGGL((pool_keys<T, MODE, BLK, HD>), dim3((unsigned)(D.B * D.n * D.Hkv)),
+                     dim3(kPoolThreads), 0, s, static_cast<const T*>(K), summ, bfp, D.N, D.n,
+                     D.Hkv, L.plane, L.kn);
   return hipGetLastError();
 }
 
