@@ -55,15 +55,26 @@ struct BudgetDev {
 // Layout of the block-summary buffer.  The public part (documented in the header) comes
 // first: the fp32 planes [B, n, Hkv, d] (kmean, or kmin then kmax) and, when output-aware,
 // vnorm [B, n, Hkv].  The library-private part follows: knorm [B, n, Hkv] (fp32 L2 norm of
-// each block's scoring vector) and, 256-byte aligned, a bf16 hi and lo split of every fp32
-// plane (hi = bf16(x), lo = bf16(x - hi)) used by the matrix-core score prefilter.
+// each block's scoring vector), then two copies of the planes in "chunk-major" order, grouped
+// by 32-block chunks per (batch, kv head), for the selection kernel:
+//   bfc  bf16 hi/lo split of each plane (hi = bf16(x), lo = bf16(x - hi)), the matrix-core
+//        prefilter's B operands: per chunk [plane][hi, lo][d/16 steps][64 lanes][8], lane
+//        (i, u) holding coordinates 16 step + 8u .. +7 of block 32 chunk + i, so every operand
+//        load of a wave reads 1 KiB contiguous;
+//   xc   fp32 values for the exact score chains: per chunk [plane][d/8 groups][32 blocks][8],
+//        so a wave reading coordinates 8g .. 8g+7 of its 32 blocks reads 1 KiB contiguous.
+// Both private copies are 256-byte aligned; chunks past n are padding.
 struct SummaryLayout {
-  size_t plane;    // elements of one [B, n, Hkv, d] plane
-  int nplanes;     // 1 (kmean) or 2 (kmin, kmax)
-  size_t vn;       // float offset of vnorm (valid when output-aware)
-  size_t kn;       // float offset of knorm
-  size_t bf_byte;  // byte offset of the bf16 planes: hi(0), lo(0), hi(1), lo(1)
-  size_t bytes;    // total
+  size_t plane;      // elements of one [B, n, Hkv, d] plane
+  int nplanes;       // 1 (kmean) or 2 (kmin, kmax)
+  size_t vn;         // float offset of vnorm (valid when output-aware)
+  size_t kn;         // float offset of knorm
+  int ncb;           // 32-block chunks per (batch, kv head)
+  size_t bfc_byte;   // byte offset of the bf16 chunk-major copy
+  size_t bfc_chunk;  // bf16 elements per (batch, kv head, chunk)
+  size_t xc_byte;    // byte offset of the fp32 chunk-major copy
+  size_t xc_chunk;   // floats per (batch, kv head, chunk)
+  size_t bytes;      // total
 };
 inline SummaryLayout summary_layout(const Dims& D) {
   SummaryLayout L;
@@ -72,8 +83,13 @@ inline SummaryLayout summary_layout(const Dims& D) {
   const size_t blocks = (size_t)D.B * D.n * D.Hkv;
   L.vn = L.plane * L.nplanes;
   L.kn = L.vn + (D.oam ? blocks : 0);
-  L.bf_byte = ((L.kn + blocks) * sizeof(float) + 255) & ~(size_t)255;
-  L.bytes = L.bf_byte + (size_t)L.nplanes * 2 * L.plane * sizeof(uint16_t);
+  L.ncb = (D.n + 31) / 32;
+  const size_t chunks = (size_t)D.B * D.Hkv * L.ncb;
+  L.bfc_chunk = (size_t)L.nplanes * 2 * D.d * 32;  // [plane][hi, lo][d/16][64][8]
+  L.xc_chunk = (size_t)L.nplanes * D.d * 32;       // [plane][d/8][32][8]
+  L.bfc_byte = ((L.kn + blocks) * sizeof(float) + 255) & ~(size_t)255;
+  L.xc_byte = (L.bfc_byte + chunks * L.bfc_chunk * sizeof(uint16_t) + 255) & ~(size_t)255;
+  L.bytes = L.xc_byte + chunks * L.xc_chunk * sizeof(float);
   return L;
 }
 

@@ -12,9 +12,9 @@
 // pool_keys: one workgroup per (batch, block, kv head).  The block's key tile is copied to
 //   LDS with all of its loads in flight at once, then one thread per coordinate accumulates
 //   the rows in order (the fixed reduction order the selection relies on for reproducible
-//   results).  It also writes, for the selection's matrix-core prefilter, each summary's bf16
-//   hi/lo split and the block's L2 norm (an upper-bound ingredient only: it never decides a
-//   selection by itself).
+//   results).  It also writes the selection kernel's private copies of the summaries (bf16
+//   hi/lo split and fp32, in chunk-major order: see common.h) and the block's L2 norm (an
+//   upper-bound ingredient only: it never decides a selection by itself).
 // value_norms: one workgroup per (batch, block).  Each (row, kv head) pair's squared norm is
 //   a fused multiply-add chain over the d coordinates in order, by one thread; the square
 //   roots go to LDS and one thread per kv head sums them in row order.
@@ -67,12 +67,14 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) 
 template <typename T, int MODE, int BLK, int HD>
 __global__ __launch_bounds__(kPoolThreads) void pool_keys(const T* __restrict__ K,
                                                           float* __restrict__ summ,
-                                                          uint16_t* __restrict__ bfp, int N,
-                                                          int n, int Hkv, size_t plane,
-                                                          size_t kn_off) {
+                                                          uint16_t* __restrict__ bfc,
+                                                          float* __restrict__ xc, int N, int n,
+                                                          int Hkv, size_t plane, size_t kn_off,
+                                                          int ncb) {
   constexpr int E = Vec16<T>::N;   // elements per 16-byte chunk
   constexpr int CPR = HD / E;      // chunks per row
   constexpr int NCH = BLK * CPR;   // chunks in the tile
+  constexpr int NPL = MODE == SA_KMINMAX ? 2 : 1;
   static_assert(NCH % kPoolThreads == 0, "tile chunks must split evenly over the threads");
   static_assert(HD <= kPoolThreads, "one thread per coordinate");
   __shared__ uint4 tile[NCH];
@@ -98,7 +100,10 @@ __global__ __launch_bounds__(kPoolThreads) void pool_keys(const T* __restrict__ 
   const int c = threadIdx.x;
   if (c < HD) {
     const T* tv = reinterpret_cast<const T*>(tile);
-    float a = 0.0f, mx = 0.0f;
+    float v[NPL];
+    float& a = v[0];
+    float mx = 0.0f;
+    a = 0.0f;
 #pragma unroll 16
     for (int r = 0; r < BLK; ++r) {
       float x;
@@ -114,26 +119,31 @@ __global__ __launch_bounds__(kPoolThreads) void pool_keys(const T* __restrict__ 
       }
     }
     const size_t o = ((size_t)bj * Hkv + g) * HD + c;
-    uint32_t hi, lo;
     if (MODE == SA_KMEAN) {
       a = a * (1.0f / (float)BLK);  // exact: BLK is a power of two
       summ[o] = a;
       ss = a * a;
-      split_bf16(a, hi, lo);
-      bfp[o] = (uint16_t)hi;
-      bfp[plane + o] = (uint16_t)lo;
     } else {
       a = canon(a);
-      mx = canon(mx);
+      v[NPL - 1] = canon(mx);
       summ[o] = a;
-      summ[plane + o] = mx;
-      ss = fmaxf(a * a, mx * mx);
-      split_bf16(a, hi, lo);
-      bfp[o] = (uint16_t)hi;
-      bfp[plane + o] = (uint16_t)lo;
-      split_bf16(mx, hi, lo);
-      bfp[2 * plane + o] = (uint16_t)hi;
-      bfp[3 * plane + o] = (uint16_t)lo;
+      summ[plane + o] = v[NPL - 1];
+      ss = fmaxf(a * a, v[NPL - 1] * v[NPL - 1]);
+    }
+    // Chunk-major copies for the selection kernel (layout in common.h).
+    const int cb = j >> 5, jl = j & 31;
+    const size_t chunk = ((size_t)b * Hkv + g) * ncb + cb;
+    uint16_t* bc = bfc + chunk * (size_t)(NPL * 2 * HD * 32);
+    float* xcp = xc + chunk * (size_t)(NPL * HD * 32);
+    const int ks = c >> 4, u = (c >> 3) & 1, e = c & 7;
+    const int lane = jl + 32 * u;
+#pragma unroll
+    for (int p = 0; p < NPL; ++p) {
+      uint32_t hi, lo;
+      split_bf16(v[p], hi, lo);
+      bc[((p * 2 + 0) * (HD / 16) + ks) * 512 + lane * 8 + e] = (uint16_t)hi;
+      bc[((p * 2 + 1) * (HD / 16) + ks) * 512 + lane * 8 + e] = (uint16_t)lo;
+      xcp[(p * (HD / 8) + (c >> 3)) * 256 + jl * 8 + e] = v[p];
     }
   }
 #pragma unroll
@@ -183,10 +193,12 @@ __global__ __launch_bounds__(kPoolThreads) void value_norms(const T* __restrict_
 template <typename T, int MODE, int BLK, int HD>
 hipError_t launch_keys(const Dims& D, const void* K, float* summ, hipStream_t s) {
   const SummaryLayout L = summary_layout(D);
-  uint16_t* bfp = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(summ) + L.bf_byte);
+  char* base = reinterpret_cast<char*>(summ);
   hipLaunchKernelGGL((pool_keys<T, MODE, BLK, HD>), dim3((unsigned)(D.B * D.n * D.Hkv)),
-                     dim3(kPoolThreads), 0, s, static_cast<const T*>(K), summ, bfp, D.N, D.n,
-                     D.Hkv, L.plane, L.kn);
+                     dim3(kPoolThreads), 0, s, static_cast<const T*>(K), summ,
+                     reinterpret_cast<uint16_t*>(base + L.bfc_byte),
+                     reinterpret_cast<float*>(base + L.xc_byte), D.N, D.n, D.Hkv, L.plane, L.kn,
+                     L.ncb);
   return hipGetLastError();
 }
 

@@ -202,10 +202,13 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
 //
 // One workgroup (4 waves) per (b, h, t).  The tile's Q rows are staged in LDS as bf16 (for
 // the bound backbone as its positive and negative parts, so q+ . kmax + q- . kmin gives
-// the per-coordinate maximum); each wave takes 32-block chunks of the free blocks, holds a
-// 32-block x all-rows score tile in accumulators (lane = block, 16 rows per 32-row tile),
-// finds each block's candidate rows lane-locally, runs their canonical chains (q from LDS,
-// the fp32 summary from L2) and writes the block's order key.
+// the per-coordinate maximum); each wave takes aligned 32-block chunks covering the free
+// blocks, holds a 32-block x all-rows score tile in accumulators (lane = block, 16 rows per
+// 32-row tile), finds each block's candidate rows lane-locally, runs their canonical chains
+// (q from LDS, the fp32 summary from L2) and writes the block's order key.  Both the bf16
+// operands and the fp32 summaries come from the chunk-major copies the summary kernel writes
+// (common.h), so every one of these loads reads 1 KiB contiguous instead of 16-32 bytes from
+// each of 32 blocks.
 
 constexpr int kScoreThreads = 256;
 constexpr float kPrefilterC = 0x1p-11f;
@@ -213,8 +216,8 @@ constexpr float kPrefilterC = 0x1p-11f;
 template <int MODE, int OAM, int D, int TILE>
 __global__ __launch_bounds__(kScoreThreads) void score_rank_mfma(
     Dims dm, BudgetDev bd, const uint16_t* __restrict__ Q, const float* __restrict__ summ,
-    const uint16_t* __restrict__ bfp, int* __restrict__ ranked, float* __restrict__ sigma,
-    size_t plane, size_t vn_off, size_t kn_off) {
+    const uint16_t* __restrict__ bfc, const float* __restrict__ xc, int* __restrict__ ranked,
+    float* __restrict__ sigma, size_t vn_off, size_t kn_off, int ncb) {
   constexpr int NPL = MODE == SA_KMINMAX ? 2 : 1;  // staged Q planes (q, or q+ and q-)
   constexpr int QS = D + 8;                        // LDS row stride (bf16 elements)
   constexpr int RT = TILE / 32;                    // 32-row tiles
@@ -289,14 +292,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_rank_mfma(
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const size_t kstride = (size_t)dm.Hkv * D;
-  const size_t kb0 = ((size_t)b * n * dm.Hkv + g) * D;  // element offset of block 0, kv head g
-  const int nchunks = (nf + 31) >> 5;
+  // 32-block chunks of this (batch, kv head) covering the free blocks [j0, t).
+  const size_t chunk0 = ((size_t)b * dm.Hkv + g) * ncb;
+  constexpr size_t BFC = (size_t)NPL * 2 * D * 32, XC = (size_t)NPL * D * 32;
 
-  for (int ch = wv; ch < nchunks; ch += kScoreThreads / 64) {
-    const int j = j0 + ch * 32 + l32;  // this lane's block
-    const bool valid = j < t;
-    const size_t kofs = kb0 + (size_t)(valid ? j : j0) * kstride;
+  for (int ch = (j0 >> 5) + wv; ch * 32 < t; ch += kScoreThreads / 64) {
+    const int j = ch * 32 + l32;  // this lane's block
+    const bool valid = j >= j0 && j < t;
+    const uint16_t* bc = bfc + (chunk0 + ch) * BFC + lane * 8;
 
     f32x16 acc[RT];
 #pragma unroll
@@ -305,13 +308,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_rank_mfma(
     for (int pl = 0; pl < NPL; ++pl) {
       // q . x with x = kmean; or q+ . kmax + q- . kmin (kmax is plane 1, kmin plane 0)
       const int xp = MODE == SA_KMINMAX ? 1 - pl : 0;
-      const uint16_t* bh_ = bfp + (size_t)(2 * xp) * plane + kofs + 8 * hi;
-      const uint16_t* bl_ = bfp + (size_t)(2 * xp + 1) * plane + kofs + 8 * hi;
+      const uint16_t* bh_ = bc + (size_t)(2 * xp) * (KS * 512);
+      const uint16_t* bl_ = bc + (size_t)(2 * xp + 1) * (KS * 512);
       const uint16_t* ap = qs + (size_t)(pl * TILE + l32) * QS + 8 * hi;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 bhv = *reinterpret_cast<const bf16x8*>(bh_ + 16 * ks);
-        const bf16x8 blv = *reinterpret_cast<const bf16x8*>(bl_ + 16 * ks);
+        const bf16x8 bhv = *reinterpret_cast<const bf16x8*>(bh_ + 512 * ks);
+        const bf16x8 blv = *reinterpret_cast<const bf16x8*>(bl_ + 512 * ks);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(ap + rt * 32 * QS + 16 * ks);
@@ -339,7 +342,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_rank_mfma(
     }
     // Canonical chains of the candidate rows.
     float best = -INFINITY;
-    const float* xk = summ + kofs;  // kmean, or kmin (plane 0) / kmax (plane 1)
+    // kmean, or kmin (plane 0) / kmax (plane 1): coordinates 8c .. 8c+7 of this lane's block
+    // at xk + (plane * D/8 + c) * 256
+    const float* xk = xc + (chunk0 + ch) * XC + l32 * 8;
     while (cand) {
       const int bit = __builtin_ctzll(cand);
       cand &= cand - 1;
@@ -354,14 +359,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_rank_mfma(
           const uint4 q2 = *reinterpret_cast<const uint4*>(qn + c0);
           qv.x |= q2.x; qv.y |= q2.y; qv.z |= q2.z; qv.w |= q2.w;
         }
-        const float4 x0 = *reinterpret_cast<const float4*>(xk + c0);
-        const float4 x1 = *reinterpret_cast<const float4*>(xk + c0 + 4);
+        const float4 x0 = *reinterpret_cast<const float4*>(xk + (c0 / 8) * 256);
+        const float4 x1 = *reinterpret_cast<const float4*>(xk + (c0 / 8) * 256 + 4);
         const float q8[8] = {bf16_lo(qv.x), bf16_hi(qv.x), bf16_lo(qv.y), bf16_hi(qv.y),
                              bf16_lo(qv.z), bf16_hi(qv.z), bf16_lo(qv.w), bf16_hi(qv.w)};
         float xa[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         if (MODE == SA_KMINMAX) {
-          const float4 y0 = *reinterpret_cast<const float4*>(xk + plane + c0);
-          const float4 y1 = *reinterpret_cast<const float4*>(xk + plane + c0 + 4);
+          const float4 y0 = *reinterpret_cast<const float4*>(xk + (D / 8 + c0 / 8) * 256);
+          const float4 y1 = *reinterpret_cast<const float4*>(xk + (D / 8 + c0 / 8) * 256 + 4);
           const float xb[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
 #pragma unroll
           for (int k = 0; k < 8; ++k) xa[k] = q8[k] >= 0.0f ? xb[k] : xa[k];
@@ -572,12 +577,13 @@ hipError_t launch_score_mfma(const Dims& dm, const BudgetDev& bd, const void* Q,
   const size_t lds = sizeof(unsigned long long) * P + sizeof(uint16_t) * NPL * TILE * (D + 8);
   hipError_t e = allow_lds(score_rank_mfma<MODE, OAM, D, TILE>, lds);
   if (e != hipSuccess) return e;
-  const uint16_t* bfp =
-      reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(summ) + L.bf_byte);
+  const char* base = reinterpret_cast<const char*>(summ);
   const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
   hipLaunchKernelGGL((score_rank_mfma<MODE, OAM, D, TILE>), dim3(grid), dim3(kScoreThreads),
-                     lds, s, dm, bd, static_cast<const uint16_t*>(Q), summ, bfp, ranked, sigma,
-                     L.plane, L.vn, L.kn);
+                     lds, s, dm, bd, static_cast<const uint16_t*>(Q), summ,
+                     reinterpret_cast<const uint16_t*>(base + L.bfc_byte),
+                     reinterpret_cast<const float*>(base + L.xc_byte), ranked, sigma, L.vn, L.kn,
+                     L.ncb);
   return hipGetLastError();
 }
 

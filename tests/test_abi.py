@@ -74,11 +74,15 @@ def test_sizes(lib):
     assert api.select_workspace_bytes(p, b) >= 32 * 512 * 64 * 4
 
     def expect(B, n, Hkv, d, nplanes, oam):
-        # public fp32 planes (+ vnorm), then knorm, then 256-aligned bf16 hi/lo planes
+        # public fp32 planes (+ vnorm), then knorm, then 256-aligned private copies in 32-block
+        # chunks: bf16 hi/lo of every plane, then fp32 of every plane
         plane = B * n * Hkv * d
         head = plane * nplanes * 4 + (B * n * Hkv * 4 if oam else 0) + B * n * Hkv * 4
         head = (head + 255) // 256 * 256
-        return head + nplanes * 2 * plane * 2
+        chunks = B * Hkv * ((n + 31) // 32)
+        bfc = chunks * nplanes * 2 * d * 32 * 2
+        xc_off = (head + bfc + 255) // 256 * 256
+        return xc_off + chunks * nplanes * d * 32 * 4
 
     assert api.summary_bytes(p) == expect(1, 512, 8, 128, 1, False)
     p5, b5 = api.problem(wl.WORKLOADS["stem_32k"]), api.budget(wl.WORKLOADS["stem_32k"])
