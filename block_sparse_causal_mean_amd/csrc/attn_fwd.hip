@@ -13,7 +13,7 @@
 //               that work out of the attention loop.  bf16 -> fp16 is exact for |v| in
 //               [2^-14, 65504]; smaller magnitudes keep an absolute error below 2^-25.
 //   attn_bf16   one workgroup per (batch, q head, query tile), one wave per 32 query rows
-//               (4 waves for 128-row tiles, 2 for 64-row tiles), two workgroups per CU.  The
+//               (4 waves for 128-row tiles, 2 for 64-row tiles), three workgroups per CU.  The
 //               tile's blocks are consumed in steps of 32 keys:
 //               S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 coordinates from
 //               LDS, B = the wave's Q fragment held in registers), so each lane's accumulator
@@ -23,15 +23,19 @@
 //               keys in exactly that order, so one 16-byte read feeds one product and P never
 //               moves through LDS).  fp32 accumulation throughout; P is rounded to fp16
 //               (11 significant bits) for the second product.
-//               K and V^T steps go from global memory straight into a ring of 4 LDS slots
-//               (global_load_lds, no registers), each refilled three steps ahead of use, with
+//               K and V^T steps go from global memory straight into a ring of 3 LDS slots
+//               (global_load_lds, no registers), each refilled two steps ahead of use, with
 //               partial vector-memory waits so a step never waits for later steps' loads.
+//               (A 3-slot ring fits three workgroups per CU, three waves per SIMD: measured
+//               5% faster than a 4-slot ring at two workgroups per CU.)
 //               The template also builds 64-row waves (QH = 2: one K read feeds two products),
 //               which halves LDS operand traffic but needs over 256 registers, i.e. one wave
 //               per SIMD; on gfx950 it measured slower, so the launcher uses QH = 1.
 // fp32 inputs (attn_f32): one thread per query row, fp32 VALU arithmetic, same online softmax.
 //
-// Launch order (decode_tile): one kv head at a time, its tiles latest first.
+// Launch order (decode_tile_grouped): one kv head at a time, its tiles latest first, the
+// query heads of a tile on one XCD; each tile's blocks are visited shared-first
+// (reorder_shared) so that those heads hit each other's blocks in L2.
 
 #include <type_traits>
 
@@ -159,7 +163,7 @@ struct Cfg {
   static constexpr int DT = D / 32;            // 32-coordinate tiles of O^T
   static constexpr int KSLOT = kStep * D * 2;  // bytes of a K step image
   static constexpr int VSLOT = D * kStep * 2;  // bytes of a V^T step image
-  static constexpr int NR = 4;                 // ring slots (a K and a V^T image each)
+  static constexpr int NR = 3;                 // ring slots (a K and a V^T image each)
   static constexpr int KREG = KSLOT / 1024;    // 1 KiB load regions per image
   static constexpr int VREG = VSLOT / 1024;
   static constexpr int LPW = (KREG + VREG) / NW;  // loads per wave per refill group
@@ -220,7 +224,7 @@ struct WaveState {
 template <int D, int QH>
 __device__ __forceinline__ void step_scores(const uint32_t (&ka_addr)[D / 16],
                                             const bf16x8 (&qf)[QH][D / 16], f32x16 (&s)[QH]) {
-  constexpr int DC = D / 16, PD = 3;
+  constexpr int DC = D / 16, PD = 4;
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh) s[qh] = (f32x16){};
   bf16x8 ka[PD];
@@ -301,7 +305,7 @@ __device__ __forceinline__ void step_softmax_pv(f32x16 (&s)[QH], const uint32_t 
   // O^T += V^T P^T.  B operand slot 8 hi + 4 i' + r of pf[qh][half] is key
   // 16 half + 8 i' + 4 hi + r of the step; the A operand is chunk 2 half + hi of V^T row d,
   // which holds exactly those keys in that order (read through va_addr[half]).
-  constexpr int NP = DT * 2, PD = 3;
+  constexpr int NP = DT * 2, PD = 4;
   auto vload = [&](int i) {
     const int dt = i >> 1, half = i & 1;
     return lds_read<f16x8>(va_addr[half] + dt * 2048);
@@ -322,8 +326,79 @@ __device__ __forceinline__ void step_softmax_pv(f32x16 (&s)[QH], const uint32_t 
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Run by one wave.  lst[0 .. U) holds this tile's usable blocks (U = seg_info[0] <= 256);
+// reorders them by (number of the kv head's query heads whose list for this tile contains the
+// block) descending, then block index ascending, and updates the diagonal's position
+// (seg_info[1]).  The other heads' lists are copied to `scratch` first; membership is a binary
+// search, which assumes ascending lists (as sparse_attn_select writes them): other orders give
+// another, still valid, order.
+__device__ void reorder_shared(const int32_t* __restrict__ list, const int32_t* __restrict__ kv_cnt,
+                               size_t bht, const Dims& dm, int h, int t, int W, int* lst,
+                               int* seg_info, int* scratch) {
+  const int lane = threadIdx.x & 63;
+  const int U = seg_info[0];
+  const int g0 = (h / dm.G) * dm.G;
+  // other heads' lists: scratch[k * W ..], lengths in cl[k]
+  int cl[8];
+  int no = 0;
+  for (int hh = g0; hh < g0 + dm.G && no < 8; ++hh) {
+    if (hh == h) continue;
+    const long long d = ((long long)hh - h) * dm.n * W;  // same (b, t), other head
+    const int c = max(0, min(kv_cnt[(size_t)((long long)bht + ((long long)hh - h) * dm.n)], W));
+    for (int e = lane; e < c; e += 64) scratch[no * W + e] = list[d + e];
+    cl[no++] = c;
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  int P = 1;
+  while (P < U) P <<= 1;
+  unsigned* key = reinterpret_cast<unsigned*>(scratch + no * W);
+  for (int i = lane; i < P; i += 64) {
+    unsigned k = 0xffffffffu;  // padding sorts last
+    if (i < U) {
+      const int x = lst[i];
+      int count = 1;
+      for (int o = 0; o < no; ++o) {
+        const int* sl = scratch + o * W;
+        int lo = 0, hi = cl[o];
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (sl[mid] < x) lo = mid + 1; else hi = mid;
+        }
+        count += lo < cl[o] && sl[lo] == x;
+      }
+      k = ((unsigned)(dm.G - count) << 24) | (unsigned)x;
+    }
+    key[i] = k;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // ascending bitonic sort of key[0 .. P) by this wave (its LDS accesses execute in order)
+  for (int k = 2; k <= P; k <<= 1)
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = lane; i < (P >> 1); i += 64) {
+        const int lo = ((i & ~(jj - 1)) << 1) | (i & (jj - 1));
+        const int hi = lo + jj;
+        const unsigned a = key[lo], b = key[hi];
+        const bool up = (lo & k) == 0;
+        if (up ? (a > b) : (a < b)) {
+          key[lo] = b;
+          key[hi] = a;
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  int diag = -1;
+  for (int i = lane; i < U; i += 64) {
+    const int x = (int)(key[i] & 0xffffffu);
+    lst[i] = x;
+    const unsigned long long dm_ = __ballot(x == t);
+    if (dm_) diag = (i - lane) + __builtin_ctzll(dm_);
+  }
+  if (lane == 0) seg_info[1] = diag;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 template <int D, int QH, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void attn_bf16(
+__global__ __launch_bounds__(64 * NW, 3) void attn_bf16(
     Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vp, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, int W, float scale_log2, void* __restrict__ O,
@@ -337,7 +412,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16(
   __shared__ int seg_info[4];  // usable entries, diagonal position, next entry, done
 
   int b, h, t;
-  decode_tile(dm, b, h, t);
+  decode_tile_grouped(dm, b, h, t);
   const int g = h / dm.G;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
@@ -431,6 +506,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bf16(
       }
     }
     __syncthreads();
+    // Order the tile's blocks so that blocks listed by more of the kv head's query heads come
+    // first (ties by index): the G workgroups of this tile run together on one XCD and then
+    // request their shared blocks at the same steps.  Attention does not depend on the order.
+    // Done for single-segment lists only (the ring is still free and serves as scratch).
+    if (dm.G > 1 && seg_start == 0 && seg_info[3] && seg_info[0] > 1 && seg_info[0] <= 256 &&
+        (dm.G - 1) * W + 256 <= C::NR * SLOT / 4) {
+      if (w == 0) reorder_shared(list, kv_cnt, bht, dm, h, t, W, lst, seg_info,
+                                 reinterpret_cast<int*>(ring));
+      __syncthreads();
+    }
     const int U = seg_info[0], diag_e = seg_info[1], next_start = seg_info[2];
     const int seg_done = seg_info[3];
     const int nsteps = U * NSUB;

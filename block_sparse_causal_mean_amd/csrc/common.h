@@ -111,6 +111,30 @@ __device__ __forceinline__ void decode_tile(const Dims& dm, int& b, int& h, int&
   h = (pair - b * dm.Hkv) * dm.G + r;
 }
 
+// The attention kernel's order: as decode_tile, but the G query heads of one tile are dealt
+// to the same XCD (consecutive tiles still go to consecutive XCDs).  Those G workgroups run
+// together and read the same kv head; with their lists ordered so that blocks shared by
+// more heads come first, they request the shared blocks at the same steps and all but the
+// first find them in that XCD's L2.  Falls back to decode_tile's order when the counts do
+// not divide evenly.
+__device__ __forceinline__ void decode_tile_grouped(const Dims& dm, int& b, int& h, int& t) {
+  const int U = dm.B * dm.Hq * dm.n;
+  const int p = (int)blockIdx.x;
+  int id = p;
+  if (U % (8 * dm.G) == 0) {
+    const int x = p & 7, y = p >> 3;
+    const int z = y / dm.G, hq = y - z * dm.G;
+    id = (8 * z + x) * dm.G + hq;
+  }
+  const int per_pair = dm.n * dm.G;
+  const int pair = id / per_pair;
+  const int rest = id - pair * per_pair;
+  t = dm.n - 1 - rest / dm.G;
+  const int r = rest - (rest / dm.G) * dm.G;
+  b = pair / dm.Hkv;
+  h = (pair - b * dm.Hkv) * dm.G + r;
+}
+
 // Workspace layout of sparse_attn_select (byte offsets, 256-byte aligned).
 struct SelectWs {
   size_t ranked, sigma, sigma_bar, gate, tau, total;
