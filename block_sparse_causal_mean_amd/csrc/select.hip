@@ -300,6 +300,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_rank_mfma(
     const int j = ch * 32 + l32;  // this lane's block
     const bool valid = j >= j0 && j < t;
     const uint16_t* bc = bfc + (chunk0 + ch) * BFC + lane * 8;
+    // kmean, or kmin (plane 0) / kmax (plane 1): coordinates 8c .. 8c+7 of this lane's block
+    // at xk + (plane * D/8 + c) * 256
+    const float* xk = xc + (chunk0 + ch) * XC + l32 * 8;
+    // Mean-pooled backbone: this lane's half of the block's fp32 summary (coordinates
+    // D/2 * hi .. +D/2), requested now so it arrives while the matrix products run.
+    float xh[MODE == SA_KMEAN ? D / 2 : 1];
+    if constexpr (MODE == SA_KMEAN) {
+#pragma unroll
+      for (int c8 = 0; c8 < D / 16; ++c8) {
+        const float4 x0 = *reinterpret_cast<const float4*>(xk + (hi * (D / 16) + c8) * 256);
+        const float4 x1 = *reinterpret_cast<const float4*>(xk + (hi * (D / 16) + c8) * 256 + 4);
+        xh[8 * c8 + 0] = x0.x; xh[8 * c8 + 1] = x0.y; xh[8 * c8 + 2] = x0.z; xh[8 * c8 + 3] = x0.w;
+        xh[8 * c8 + 4] = x1.x; xh[8 * c8 + 5] = x1.y; xh[8 * c8 + 6] = x1.z; xh[8 * c8 + 7] = x1.w;
+      }
+    }
 
     f32x16 acc[RT];
 #pragma unroll
@@ -342,9 +357,58 @@ __global__ __launch_bounds__(kScoreThreads) void score_rank_mfma(
     }
     // Canonical chains of the candidate rows.
     float best = -INFINITY;
-    // kmean, or kmin (plane 0) / kmax (plane 1): coordinates 8c .. 8c+7 of this lane's block
-    // at xk + (plane * D/8 + c) * 256
-    const float* xk = xc + (chunk0 + ch) * XC + l32 * 8;
+    if constexpr (MODE == SA_KMEAN) {
+      // The two lanes of block j run each candidate's chain as a two-stage pipeline: lane
+      // hi = 0 does coordinates 0 .. D/2-1 of candidate k while lane hi = 1 finishes
+      // coordinates D/2 .. D-1 of candidate k-1 from the partial sum handed over by
+      // v_permlane32_swap.  Same fused multiply-adds in the same order as one lane's chain.
+      // The pair's candidates are lane 0's rows, then lane 1's.
+      // v_permlane32_swap(x, x): the first result holds the partner's value in lanes 32-63,
+      // the second in lanes 0-31.
+      const auto swl = __builtin_amdgcn_permlane32_swap((unsigned)cand, (unsigned)cand, false,
+                                                        false);
+      const auto swh = __builtin_amdgcn_permlane32_swap((unsigned)(cand >> 32),
+                                                        (unsigned)(cand >> 32), false, false);
+      const unsigned long long other =
+          ((unsigned long long)(hi ? swh[0] : swh[1]) << 32) | (unsigned)(hi ? swl[0] : swl[1]);
+      const unsigned long long c0m = hi ? other : cand;  // lane 0's candidates
+      const unsigned long long c1m = hi ? cand : other;  // lane 1's candidates
+      const int n0 = __builtin_popcountll(c0m), ncand = n0 + __builtin_popcountll(c1m);
+      unsigned long long rem0 = c0m, rem1 = c1m;
+      int prow = 0;        // row whose second half this lane (hi = 1) finishes next
+      float part = 0.0f;   // partial sum handed from lane 0 to lane 1
+      for (int k = 0; k <= ncand; ++k) {
+        // row of candidate k (lane 0 starts it) and of candidate k-1 (lane 1 finishes it)
+        int row = 0;
+        if (k < ncand) {
+          unsigned long long& rm = k < n0 ? rem0 : rem1;
+          const int bit = __builtin_ctzll(rm);
+          rm &= rm - 1;
+          row = 32 * (bit >> 4) + 8 * ((bit & 15) >> 2) + 4 * (k < n0 ? 0 : 1) + (bit & 3);
+        }
+        const int r_here = hi ? prow : row;
+        const bool active = hi ? (k >= 1) : (k < ncand);
+        float sv = hi ? part : 0.0f;
+        if (active) {
+          const uint16_t* qr = qs + (size_t)r_here * QS + hi * (D / 2);
+#pragma unroll
+          for (int c0 = 0; c0 < D / 2; c0 += 8) {
+            const uint4 qv = *reinterpret_cast<const uint4*>(qr + c0);
+            const float q8[8] = {bf16_lo(qv.x), bf16_hi(qv.x), bf16_lo(qv.y), bf16_hi(qv.y),
+                                 bf16_lo(qv.z), bf16_hi(qv.z), bf16_lo(qv.w), bf16_hi(qv.w)};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sv = __builtin_fmaf(q8[e], xh[c0 + e], sv);
+          }
+          if (hi) best = fmaxf(best, sv);
+        }
+        // hand lane 0's partial to lane 1; lane 1 remembers the row it belongs to
+        const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(sv),
+                                                         __float_as_uint(sv), false, false);
+        part = __uint_as_float(hi ? ps[0] : ps[1]);  // lane 1 receives lane 0's partial
+        prow = row;
+      }
+      (void)prow;
+    } else {
     while (cand) {
       const int bit = __builtin_ctzll(cand);
       cand &= cand - 1;
@@ -375,6 +439,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_rank_mfma(
         for (int k = 0; k < 8; ++k) sv = __builtin_fmaf(q8[k], xa[k], sv);
       }
       best = fmaxf(best, sv);
+    }
     }
     best = fmaxf(best, __shfl_xor(best, 32));
     if (valid && hi == 0) {
