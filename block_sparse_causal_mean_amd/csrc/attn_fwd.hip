@@ -187,10 +187,10 @@ __device__ __forceinline__ T lds_read(uint32_t addr) {
 // m0 + 16 i.  gbase and lds are wave-uniform.  Inline asm keeps these loads out of the
 // compiler's own wait insertion, which cannot tell which ring slot a later LDS read touches
 // and would drain every load in flight before it; each wait for them is explicit (wait_vm
-// followed by a barrier).  The s_nop gives the load the wait states it needs after M0 and
-// its scalar base are written.
+// followed by a barrier).  The s_nop is the one wait state an LDS-DMA load needs after M0
+// is written.
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(gbase), "s"(lds)
                : "memory", "m0");
@@ -397,6 +397,63 @@ __device__ void reorder_shared(const int32_t* __restrict__ list, const int32_t* 
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// Stages the next segment of a tile's list in LDS and orders it; run by the whole workgroup.
+// Usable entries are those with 0 <= j <= t before the first negative entry; at most LCAP of
+// them per segment (wave 0 compacts, the workgroup waits).  seg_info receives: usable entries,
+// position of the diagonal block (-1 if absent), the list position the next segment starts
+// at, and whether this segment ends the list.
+//
+// Single-segment lists are then ordered so that blocks listed by more of the kv head's query
+// heads come first (ties by index): the G workgroups of the tile run together on one XCD and
+// request their shared blocks at the same steps.  Attention does not depend on the order.
+// `scratch` (scratch_ints ints of LDS, free at this point) holds the other heads' lists.
+template <int LCAP>
+__device__ __forceinline__ void stage_segment(const int32_t* __restrict__ list,
+                                              const int32_t* __restrict__ kv_cnt, int cnt,
+                                              size_t bht, const Dims& dm, int h, int t, int W,
+                                              int seg_start, int w, int lane, int* lst,
+                                              int* seg_info, int* scratch, int scratch_ints) {
+  if (w == 0) {
+    int u = 0, base = seg_start, diag = -1, next = cnt, done = 1;
+    while (base < cnt) {
+      const int e = base + lane;
+      const int x = e < cnt ? list[e] : 0;
+      const unsigned long long negm = __ballot(e < cnt && x < 0);
+      const int first_neg = negm ? __builtin_ctzll(negm) : 64;
+      const bool valid = e < cnt && lane < first_neg && x <= t;
+      const unsigned long long vm = __ballot(valid);
+      const int pre = __builtin_popcountll(vm & ((1ull << lane) - 1ull));
+      const int nv = __builtin_popcountll(vm);
+      const int fit = min(nv, LCAP - u);
+      if (valid && pre < fit) lst[u + pre] = x;
+      // entries are distinct, so at most one lane holds the diagonal block
+      const unsigned long long dm_ = __ballot(valid && pre < fit && x == t);
+      if (dm_) diag = u + (int)__builtin_popcountll(vm & ((1ull << __builtin_ctzll(dm_)) - 1ull));
+      u += fit;
+      if (fit < nv) {  // LDS full: continue from the first entry that did not fit
+        const unsigned long long om = __ballot(valid && pre == fit);
+        next = base + __builtin_ctzll(om);
+        done = 0;
+        break;
+      }
+      if (negm) break;
+      base += 64;
+    }
+    if (lane == 0) {
+      seg_info[0] = u;
+      seg_info[1] = diag;
+      seg_info[2] = next;
+      seg_info[3] = done;
+    }
+  }
+  __syncthreads();
+  if (dm.G > 1 && seg_start == 0 && seg_info[3] && seg_info[0] > 1 && seg_info[0] <= 256 &&
+      (dm.G - 1) * W + 256 <= scratch_ints) {
+    if (w == 0) reorder_shared(list, kv_cnt, bht, dm, h, t, W, lst, seg_info, scratch);
+    __syncthreads();
+  }
+}
+
 template <int D, int QH, int NW>
 __global__ __launch_bounds__(64 * NW, 3) void attn_bf16(
     Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -470,52 +527,8 @@ __global__ __launch_bounds__(64 * NW, 3) void attn_bf16(
 
   int seg_start = 0;
   for (;;) {
-    // Stage the next segment of usable entries (0 <= j <= t, before the first negative
-    // entry, at most LCAP of them) in LDS; wave 0 compacts, the workgroup waits.
-    if (w == 0) {
-      int u = 0, base = seg_start, diag = -1, next = cnt, done = 1;
-      while (base < cnt) {
-        const int e = base + lane;
-        const int x = e < cnt ? list[e] : 0;
-        const unsigned long long negm = __ballot(e < cnt && x < 0);
-        const int first_neg = negm ? __builtin_ctzll(negm) : 64;
-        const bool valid = e < cnt && lane < first_neg && x <= t;
-        const unsigned long long vm = __ballot(valid);
-        const int pre = __builtin_popcountll(vm & ((1ull << lane) - 1ull));
-        const int nv = __builtin_popcountll(vm);
-        const int fit = min(nv, C::LCAP - u);
-        if (valid && pre < fit) lst[u + pre] = x;
-        // entries are distinct, so at most one lane holds the diagonal block
-        const unsigned long long dm_ = __ballot(valid && pre < fit && x == t);
-        if (dm_) diag = u + (int)__builtin_popcountll(vm & ((1ull << __builtin_ctzll(dm_)) - 1ull));
-        u += fit;
-        if (fit < nv) {  // LDS full: continue from the first entry that did not fit
-          const unsigned long long om = __ballot(valid && pre == fit);
-          next = base + __builtin_ctzll(om);
-          done = 0;
-          break;
-        }
-        if (negm) break;
-        base += 64;
-      }
-      if (lane == 0) {
-        seg_info[0] = u;
-        seg_info[1] = diag;
-        seg_info[2] = next;
-        seg_info[3] = done;
-      }
-    }
-    __syncthreads();
-    // Order the tile's blocks so that blocks listed by more of the kv head's query heads come
-    // first (ties by index): the G workgroups of this tile run together on one XCD and then
-    // request their shared blocks at the same steps.  Attention does not depend on the order.
-    // Done for single-segment lists only (the ring is still free and serves as scratch).
-    if (dm.G > 1 && seg_start == 0 && seg_info[3] && seg_info[0] > 1 && seg_info[0] <= 256 &&
-        (dm.G - 1) * W + 256 <= C::NR * SLOT / 4) {
-      if (w == 0) reorder_shared(list, kv_cnt, bht, dm, h, t, W, lst, seg_info,
-                                 reinterpret_cast<int*>(ring));
-      __syncthreads();
-    }
+    stage_segment<C::LCAP>(list, kv_cnt, cnt, bht, dm, h, t, W, seg_start, w, lane, lst, seg_info,
+                           reinterpret_cast<int*>(ring), C::NR * SLOT / 4);
     const int U = seg_info[0], diag_e = seg_info[1], next_start = seg_info[2];
     const int seg_done = seg_info[3];
     const int nsteps = U * NSUB;
@@ -728,11 +741,11 @@ hipError_t launch_forward(const Dims& dm, const void* Q, const void* K, const vo
                           : launch_bf16<64, ATTN_QH, 4 / ATTN_QH>(dm, Q, K, V, kv_idx, kv_cnt,
                                                                    W, scale, ws, O, out_dtype,
                                                                    lse, s);
-    return dm.blk == 64 ? launch_bf16<128, 1, 2>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
-                                                 out_dtype, lse, s)
-                        : launch_bf16<128, ATTN_QH, 4 / ATTN_QH>(dm, Q, K, V, kv_idx, kv_cnt, W,
-                                                                  scale, ws, O, out_dtype, lse,
-                                                                  s);
+    if (dm.blk == 64)
+      return launch_bf16<128, 1, 2>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O, out_dtype, lse,
+                                    s);
+    return launch_bf16<128, ATTN_QH, 4 / ATTN_QH>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
+                                                  out_dtype, lse, s);
   }
   if (dm.d == 64)
     return dm.blk == 64
