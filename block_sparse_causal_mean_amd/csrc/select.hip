@@ -78,6 +78,83 @@ __device__ void bitonic_desc(unsigned long long* keys, int P) {
   }
 }
 
+// The Rn largest of keys[0 .. nf) (distinct 64-bit keys; keys[nf .. P) hold 0), sorted
+// descending, by NT threads.  A radix select over 8-bit digits from the top finds the Rn-th
+// largest key (a 256-bin LDS histogram per digit); the keys at or above it, exactly Rn of
+// them, are gathered into `small` and only those are sorted.  When that would not shrink the
+// sort at least fourfold, all P keys are sorted in place instead.  Returns where the sorted
+// top keys are.  Every thread of the workgroup must call it.
+template <int NT>
+__device__ const unsigned long long* top_desc(unsigned long long* keys, int nf, int P, int Rn,
+                                              unsigned long long* small, int small_cap) {
+  __shared__ unsigned int hist[256];
+  __shared__ unsigned long long s_prefix;
+  __shared__ int s_need, s_done;
+  __shared__ unsigned int s_cnt;
+  int P2 = 1;
+  while (P2 < Rn) P2 <<= 1;
+  if (nf <= Rn || 4 * P2 > P || P2 > small_cap) {
+    bitonic_desc<NT>(keys, P);
+    return keys;
+  }
+  unsigned long long prefix = 0ull;
+  int need = Rn, shift = 56;
+  for (;;) {
+    for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0u;
+    __syncthreads();
+    const int hs = shift + 8;  // the digits above this one must match the prefix
+    for (int f = threadIdx.x; f < nf; f += NT) {
+      const unsigned long long key = keys[f];
+      if (hs == 64 || (key >> hs) == (prefix >> hs))
+        atomicAdd(&hist[(unsigned)(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane l holds digits 255 - 4l .. 252 - 4l; `above` counts the keys with a larger digit
+      const int lane = threadIdx.x;
+      unsigned c[4], tot = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[e] = hist[255 - 4 * lane - e];
+        tot += c[e];
+      }
+      unsigned incl = tot;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      unsigned above = incl - tot;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (above < (unsigned)need && above + c[e] >= (unsigned)need) {
+          s_prefix = prefix | ((unsigned long long)(255 - 4 * lane - e) << shift);
+          s_need = need - (int)above;
+          // done when this digit's whole bucket lies within the top Rn
+          s_done = above + c[e] == (unsigned)need || shift == 0;
+        }
+        above += c[e];
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    need = s_need;
+    if (s_done) break;
+    shift -= 8;
+  }
+  // exactly Rn keys have (key >> shift) >= (prefix >> shift)
+  if (threadIdx.x == 0) s_cnt = 0u;
+  for (int i = threadIdx.x; i < P2; i += NT) small[i] = 0ull;
+  __syncthreads();
+  for (int f = threadIdx.x; f < nf; f += NT) {
+    const unsigned long long key = keys[f];
+    if ((key >> shift) >= (prefix >> shift)) small[atomicAdd(&s_cnt, 1u)] = key;
+  }
+  __syncthreads();
+  bitonic_desc<NT>(small, P2);
+  return small;
+}
+
 template <typename T, int D>
 struct QRow;
 template <int D>
@@ -248,30 +325,33 @@ __global__ __launch_bounds__(kScoreThreads) void score_rank_mfma(
   if (threadIdx.x == 0) qmax_bits = 0u;
   __syncthreads();
 
-  // Stage the tile's Q rows; row norms (any order: they only scale the bound) -> max.
+  // Stage the tile's Q rows; row norms (any order: they only scale the bound) -> max.  Each
+  // thread takes a contiguous piece of one row (PPR pieces per row, all loads issued at
+  // once), so a row's sum of squares needs only PPR - 1 neighbouring-lane exchanges.
   {
-    constexpr int CH = TILE * D / 8;  // 16-byte chunks
-    constexpr int CPR = D / 8;        // chunks per row (consecutive threads)
-    const uint16_t* qsrc = Q + (((size_t)b * dm.N + (size_t)t * TILE) * dm.Hq + h) * D;
-    float rmax = 0.0f;
+    constexpr int EPT = TILE * D / kScoreThreads;  // elements per thread
+    constexpr int NV = EPT / 8;                    // 16-byte loads per thread
+    constexpr int PPR = D / EPT;                   // threads per row
+    static_assert(PPR == 2 || PPR == 4, "row pieces must pair within a lane quad");
+    const int r = threadIdx.x / PPR, piece = threadIdx.x % PPR;
+    const uint16_t* qsrc =
+        Q + (((size_t)b * dm.N + (size_t)t * TILE + r) * dm.Hq + h) * D + piece * EPT;
+    uint4 v[NV];
 #pragma unroll
-    for (int i = 0; i < CH / kScoreThreads; ++i) {
-      const int c = threadIdx.x + i * kScoreThreads;
-      const int r = c / CPR, col = c - r * CPR;
-      uint4 v = *reinterpret_cast<const uint4*>(qsrc + (size_t)r * dm.Hq * D + col * 8);
-      float ss = 0.0f;
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int i = 0; i < NV; ++i) v[i] = *reinterpret_cast<const uint4*>(qsrc + 8 * i);
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float lo = bf16_lo(w[k]), hi = bf16_hi(w[k]);
         ss = __builtin_fmaf(lo, lo, ss);
         ss = __builtin_fmaf(hi, hi, ss);
       }
-#pragma unroll
-      for (int off = 1; off < CPR; off <<= 1) ss += __shfl_xor(ss, off);
-      rmax = fmaxf(rmax, ss);
+      uint16_t* dst = qs + r * QS + piece * EPT + 8 * i;
       if (MODE == SA_KMEAN) {
-        *reinterpret_cast<uint4*>(qs + r * QS + col * 8) = v;
+        *reinterpret_cast<uint4*>(dst) = v[i];
       } else {
         uint32_t pw[4], nw[4];
 #pragma unroll
@@ -280,12 +360,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_rank_mfma(
           pw[k] = w[k] & ~neg;
           nw[k] = w[k] & neg;
         }
-        *reinterpret_cast<uint4*>(qs + r * QS + col * 8) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-        *reinterpret_cast<uint4*>(qs + (TILE + r) * QS + col * 8) =
-            make_uint4(nw[0], nw[1], nw[2], nw[3]);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+        *reinterpret_cast<uint4*>(dst + TILE * QS) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
       }
     }
-    atomicMax(&qmax_bits, __float_as_uint(rmax));  // non-negative floats order as integers
+#pragma unroll
+    for (int off = 1; off < PPR; off <<= 1) ss += __shfl_xor(ss, off);
+    float rmax = ss;
+#pragma unroll
+    for (int off = PPR; off < 64; off <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, off));
+    if ((threadIdx.x & 63) == 0)
+      atomicMax(&qmax_bits, __float_as_uint(rmax));  // non-negative floats order as integers
   }
   __syncthreads();
   const float qmax = __builtin_sqrtf(__uint_as_float(qmax_bits));
@@ -449,16 +534,19 @@ __global__ __launch_bounds__(kScoreThreads) void score_rank_mfma(
     }
   }
   __syncthreads();
-  bitonic_desc<kScoreThreads>(keys, P);
-
+  // Only the top R keys (and key kt, for sigma) are used: select them, then sort those.  The
+  // Q staging area is free by now and holds the selected keys.
   const int R = min(max(expanded(bd, kt), kt), nf);
+  const unsigned long long* top = top_desc<kScoreThreads>(
+      keys, nf, P, min(max(R, kt + 1), nf), reinterpret_cast<unsigned long long*>(qs),
+      NPL * TILE * QS * (int)sizeof(uint16_t) / (int)sizeof(unsigned long long));
   int* out = ranked + bht * bd.R;
   for (int r = threadIdx.x; r < R; r += kScoreThreads)
-    out[r] = (int)(0xffffffffu - (unsigned)keys[r]);
+    out[r] = (int)(0xffffffffu - (unsigned)top[r]);
   if (threadIdx.x == 0) {
-    const float s0 = order_key_inv((unsigned)(keys[0] >> 32));
-    const float sk1 = order_key_inv((unsigned)(keys[kt - 1] >> 32));
-    const float sk = order_key_inv((unsigned)(keys[kt] >> 32));
+    const float s0 = order_key_inv((unsigned)(top[0] >> 32));
+    const float sk1 = order_key_inv((unsigned)(top[kt - 1] >> 32));
+    const float sk = order_key_inv((unsigned)(top[kt] >> 32));
     const float num = sk1 - sk;
     const float den = s0 - sk;
     sigma[bht] = den == 0.0f ? 0.0f : __fdiv_rn(num, den);
