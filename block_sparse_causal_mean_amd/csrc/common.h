@@ -57,10 +57,10 @@ struct BudgetDev {
 // vnorm [B, n, Hkv].  The library-private part follows: knorm [B, n, Hkv] (fp32 L2 norm of
 // each block's scoring vector), then two copies of the planes in "chunk-major" order, grouped
 // by 32-block chunks per (batch, kv head), for the selection kernel:
-//   bfc  bf16 hi/lo split of each plane (hi = bf16(x), lo = bf16(x - hi)), the matrix-core
-//        prefilter's B operands: per chunk [plane][hi, lo][d/16 steps][64 lanes][8], lane
-//        (i, u) holding coordinates 16 step + 8u .. +7 of block 32 chunk + i, so every operand
-//        load of a wave reads 1 KiB contiguous;
+//   bfc  each plane rounded to bf16 (round to nearest even), the matrix-core prefilter's B
+//        operands: per chunk [plane][d/16 steps][64 lanes][8], lane (i, u) holding
+//        coordinates 16 step + 8u .. +7 of block 32 chunk + i, so every operand load of a
+//        wave reads 1 KiB contiguous;
 //   xc   fp32 values for the exact score chains: per chunk [plane][d/8 groups][32 blocks][8],
 //        so a wave reading coordinates 8g .. 8g+7 of its 32 blocks reads 1 KiB contiguous.
 // Both private copies are 256-byte aligned; chunks past n are padding.
@@ -85,7 +85,7 @@ inline SummaryLayout summary_layout(const Dims& D) {
   L.kn = L.vn + (D.oam ? blocks : 0);
   L.ncb = (D.n + 31) / 32;
   const size_t chunks = (size_t)D.B * D.Hkv * L.ncb;
-  L.bfc_chunk = (size_t)L.nplanes * 2 * D.d * 32;  // [plane][hi, lo][d/16][64][8]
+  L.bfc_chunk = (size_t)L.nplanes * D.d * 32;  // [plane][d/16][64][8]
   L.xc_chunk = (size_t)L.nplanes * D.d * 32;       // [plane][d/8][32][8]
   L.bfc_byte = ((L.kn + blocks) * sizeof(float) + 255) & ~(size_t)255;
   L.xc_byte = (L.bfc_byte + chunks * L.bfc_chunk * sizeof(uint16_t) + 255) & ~(size_t)255;

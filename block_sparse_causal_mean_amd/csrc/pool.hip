@@ -13,7 +13,7 @@
 //   LDS with all of its loads in flight at once, then one thread per coordinate accumulates
 //   the rows in order (the fixed reduction order the selection relies on for reproducible
 //   results).  It also writes the selection kernel's private copies of the summaries (bf16
-//   hi/lo split and fp32, in chunk-major order: see common.h) and the block's L2 norm (an
+//   and fp32, in chunk-major order: see common.h) and the block's L2 norm (an
 //   upper-bound ingredient only: it never decides a selection by itself).
 // value_norms: one workgroup per (batch, block).  Each (row, kv head) pair's squared norm is
 //   a fused multiply-add chain over the d coordinates in order, by one thread; the square
@@ -51,19 +51,12 @@ struct Vec16<float> {
   }
 };
 
-// Splits x into bf16 hi = RN(x) and lo = RN(x - hi) (x - hi is exact in fp32), packed as
-// bf16 bits into the low halves of the returned pair.
-__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
-  hi = f32_to_bf16_bits(x);
-  lo = f32_to_bf16_bits(x - __uint_as_float(hi << 16));
-}
-
 // pool_keys: one workgroup per (batch, block, kv head).  The block's BLK x HD key tile is
 // first copied into LDS with every 16-byte load issued at once (8 per thread for bf16 at
 // BLK = HD = 128), so the memory system sees the whole tile in flight; then thread c sums
 // coordinate c over the rows in order from LDS (the fixed reduction order), writes the
-// summary, its bf16 hi/lo split, and the block's L2 norm (a workgroup reduction in any order:
-// it only scales the prefilter's error bound).
+// summary, its bf16 rounding, and the block's L2 norm (a workgroup reduction in any order: it
+// only scales the prefilter's error bound).
 template <typename T, int MODE, int BLK, int HD>
 __global__ __launch_bounds__(kPoolThreads) void pool_keys(const T* __restrict__ K,
                                                           float* __restrict__ summ,
@@ -133,16 +126,13 @@ __global__ __launch_bounds__(kPoolThreads) void pool_keys(const T* __restrict__ 
     // Chunk-major copies for the selection kernel (layout in common.h).
     const int cb = j >> 5, jl = j & 31;
     const size_t chunk = ((size_t)b * Hkv + g) * ncb + cb;
-    uint16_t* bc = bfc + chunk * (size_t)(NPL * 2 * HD * 32);
+    uint16_t* bc = bfc + chunk * (size_t)(NPL * HD * 32);
     float* xcp = xc + chunk * (size_t)(NPL * HD * 32);
     const int ks = c >> 4, u = (c >> 3) & 1, e = c & 7;
     const int lane = jl + 32 * u;
 #pragma unroll
     for (int p = 0; p < NPL; ++p) {
-      uint32_t hi, lo;
-      split_bf16(v[p], hi, lo);
-      bc[((p * 2 + 0) * (HD / 16) + ks) * 512 + lane * 8 + e] = (uint16_t)hi;
-      bc[((p * 2 + 1) * (HD / 16) + ks) * 512 + lane * 8 + e] = (uint16_t)lo;
+      bc[(p * (HD / 16) + ks) * 512 + lane * 8 + e] = (uint16_t)f32_to_bf16_bits(v[p]);
       xcp[(p * (HD / 8) + (c >> 3)) * 256 + jl * 8 + e] = v[p];
     }
   }

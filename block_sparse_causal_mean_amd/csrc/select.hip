@@ -267,15 +267,16 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
 // Same canonical scores as score_rank, computed where they matter.  For a block j the tile
 // score is max_i s_ij over the tile's rows; only the row that attains it needs the canonical
 // fp32 chain.  A matrix-core pass computes approximate scores for every (row, block):
-//   shat_ij = q_i . (hi_j + lo_j)   (bf16 MFMA, fp32 accumulation; hi/lo = bf16 split of
-//                                     the fp32 summary, so q_i . (hi + lo) misses at most
-//                                     2^-16 |q_i| |x_j|)
-// with |shat_ij - s_ij| <= E_j = c * max_i |q_i| * |x_j| (x_j the block's scoring vector;
-// c covers the canonical chain's own rounding, the split residual and the accumulation of
-// 4d products in fp32, with a margin of about 9x).  The row attaining max_i s_ij then
-// satisfies shat_ij >= max_i shat_ij - 2 E_j, so recomputing the canonical chain for exactly
-// those rows and taking their maximum gives the canonical tile score.  Almost always one row
-// per block qualifies, so the fp32 chain work falls by about the tile height.
+//   shat_ij = q_i . bf16(x_j)   (bf16 MFMA, fp32 accumulation; bf16(x) is the fp32 summary
+//                                 rounded to nearest, within 2^-8 |x| per coordinate, so
+//                                 the rounding moves the product by at most 2^-8 |q_i| |x_j|)
+// with |shat_ij - s_ij| <= E_j = c * max_i |q_i| * |x_j| (x_j the block's scoring vector).
+// c = 1.125 * 2^-8 covers that rounding plus the fp32 accumulation of at most 2d products and
+// the canonical chain's own rounding, each below 2^-16 |q_i| |x_j|.  The row attaining
+// max_i s_ij then satisfies shat_ij >= max_i shat_ij - 2 E_j, so recomputing the canonical
+// chain for exactly those rows and taking their maximum gives the canonical tile score.
+// Usually one row per block qualifies (1.3 on average at 128K), so the fp32 chain work falls
+// by about the tile height.
 //
 // One workgroup (4 waves) per (b, h, t).  The tile's Q rows are staged in LDS as bf16 (for
 // the bound backbone as its positive and negative parts, so q+ . kmax + q- . kmin gives
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
 // each of 32 blocks.
 
 constexpr int kScoreThreads = 256;
-constexpr float kPrefilterC = 0x1p-11f;
+constexpr float kPrefilterC = 0x1.2p-8f;
 
 template <int MODE, int OAM, int D, int TILE>
 // Three waves per SIMD (at most 168 registers): as many workgroups as the LDS allows (three
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
   const int l32 = lane & 31, hi = lane >> 5;
   // 32-block chunks of this (batch, kv head) covering the free blocks [j0, t).
   const size_t chunk0 = ((size_t)b * dm.Hkv + g) * ncb;
-  constexpr size_t BFC = (size_t)NPL * 2 * D * 32, XC = (size_t)NPL * D * 32;
+  constexpr size_t BFC = (size_t)NPL * D * 32, XC = (size_t)NPL * D * 32;
 
   for (int ch = (j0 >> 5) + wv; ch * 32 < t; ch += kScoreThreads / 64) {
     const int j = ch * 32 + l32;  // this lane's block
@@ -410,18 +411,15 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     for (int pl = 0; pl < NPL; ++pl) {
       // q . x with x = kmean; or q+ . kmax + q- . kmin (kmax is plane 1, kmin plane 0)
       const int xp = MODE == SA_KMINMAX ? 1 - pl : 0;
-      const uint16_t* bh_ = bc + (size_t)(2 * xp) * (KS * 512);
-      const uint16_t* bl_ = bc + (size_t)(2 * xp + 1) * (KS * 512);
+      const uint16_t* bh_ = bc + (size_t)xp * (KS * 512);
       const uint16_t* ap = qs + (size_t)(pl * TILE + l32) * QS + 8 * hi;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 bhv = *reinterpret_cast<const bf16x8*>(bh_ + 512 * ks);
-        const bf16x8 blv = *reinterpret_cast<const bf16x8*>(bl_ + 512 * ks);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(ap + rt * 32 * QS + 16 * ks);
           acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bhv, acc[rt], 0, 0, 0);
-          acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, blv, acc[rt], 0, 0, 0);
         }
       }
     }

@@ -90,8 +90,8 @@ typedef struct sa_budget {
  *   SA_KMINMAX: kmin  [B, n, Hkv, d] followed by kmax [B, n, Hkv, d]
  *   then, if output_aware: vnorm [B, n, Hkv]
  * and continues with auxiliary data for sparse_attn_select whose layout is private
- * (per-block norms, and bf16-split and fp32 copies of the planes above in a blocked order:
- * about twice as large again).
+ * (per-block norms, and bf16 and fp32 copies of the planes above in a blocked order: about
+ * one and a half times as large again).
  * Returns 0 for an invalid problem (see sparse_attn_last_error).
  */
 size_t sparse_attn_summary_bytes(const sa_problem* p);

@@ -75,12 +75,12 @@ def test_sizes(lib):
 
     def expect(B, n, Hkv, d, nplanes, oam):
         # public fp32 planes (+ vnorm), then knorm, then 256-aligned private copies in 32-block
-        # chunks: bf16 hi/lo of every plane, then fp32 of every plane
+        # chunks: bf16 of every plane, then fp32 of every plane
         plane = B * n * Hkv * d
         head = plane * nplanes * 4 + (B * n * Hkv * 4 if oam else 0) + B * n * Hkv * 4
         head = (head + 255) // 256 * 256
         chunks = B * Hkv * ((n + 31) // 32)
-        bfc = chunks * nplanes * 2 * d * 32 * 2
+        bfc = chunks * nplanes * d * 32 * 2
         xc_off = (head + bfc + 255) // 256 * 256
         return xc_off + chunks * nplanes * d * 32 * 4
 
