@@ -245,3 +245,62 @@ def test_runs_are_deterministic():
     b = run_gpu(w, inp)
     for k in ("kA", "vn", "kv_idx", "kv_cnt", "sigma", "sigma_bar", "gate", "tau", "O"):
         np.testing.assert_array_equal(a[k], b[k])
+
+
+@pytest.mark.parametrize("name", ["prefill_128k", "llama8b_32k"])
+def test_forward_long_lists_in_segments(name):
+    """Lists with more usable entries than the kernel stages in LDS at once (512) are consumed
+    in segments, with the online softmax carried across them (ART page, section 2.4).  Dense
+    causal lists of up to 1100 blocks, in three orders: ascending (diagonal last), descending
+    (diagonal first), and with blocks after the tile interleaved (skipped, so segment
+    boundaries fall elsewhere).  Sampled rows against the fp64 oracle."""
+    base = WL[name]
+    n = 1100
+    w = base.resized(seqlen=n * base.block, n_q_heads=2, n_kv_heads=1)
+    inp = wl.make_inputs(w)
+    d = {k: v.cuda() for k, v in inp.items()}
+    p = api.problem(w)
+    fws = torch.empty(max(api.forward_workspace_bytes(p), 1), dtype=torch.uint8, device="cuda")
+    cfg = oracle.make_cfg(w)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    tiles = [n - 1, 1000, 700, 520, 300]
+    rng = np.random.default_rng(11)
+    for order in ("ascending", "descending", "with_skipped"):
+        W = 2 * n
+        idx = np.full((1, 2, n, W), -1, np.int32)
+        cnt = np.zeros((1, 2, n), np.int32)
+        for h in range(2):
+            for t in tiles:
+                row = list(range(t + 1))
+                if order == "descending":
+                    row = row[::-1]
+                elif order == "with_skipped":
+                    # a block after the tile (skipped) before every third entry
+                    out = []
+                    for i, j in enumerate(row):
+                        if i % 3 == 0:
+                            out.append(min(n - 1, t + 1 + (i % 7)) if t + 1 < n else j)
+                        out.append(j)
+                    row = [j for j in out]
+                    if t + 1 >= n:  # the last tile has no block after it: plain order
+                        row = list(range(t + 1))
+                idx[0, h, t, :len(row)] = row
+                cnt[0, h, t] = len(row)
+        O = torch.empty(1, w.seqlen, 2, w.head_dim, dtype=torch.float32, device="cuda")
+        api.forward(p, d["Q"], d["K"], d["V"], torch.as_tensor(idx).cuda(),
+                    torch.as_tensor(cnt).cuda(), W, scale, fws, O, api.SA_F32)
+        torch.cuda.synchronize()
+        rows = []
+        for t in tiles:
+            for h in range(2):
+                for r in (0, w.block - 1, int(rng.integers(w.block))):
+                    rows.append((0, h, t * w.block + r))
+        rows = np.array(rows, np.int64)
+        O_ref, _ = oracle.forward(cfg, inp["Q"], inp["K"], inp["V"], idx, cnt, scale, rows=rows)
+        r = torch.as_tensor(rows, device="cuda")
+        got = O[r[:, 0], r[:, 2], r[:, 1]].cpu().numpy().astype(np.float64)
+        err = np.abs(got - O_ref).max()
+        say(f"[long lists {name} {order}] {len(rows)} rows, max|O - O_ref| = {err:.3e}")
+        assert err <= out_tol(w, api.SA_F32, O_ref)
+        # rows of tiles with empty lists are zero
+        assert float(O[0, 5 * w.block:6 * w.block].abs().max()) == 0.0
