@@ -195,6 +195,11 @@ int sparse_attn_forward(const sa_problem* p, const void* Q, const void* K, const
   if (out_dtype != SA_F32 && out_dtype != SA_BF16)
     return fail(SA_ERR_INVALID, "out_dtype must be SA_F32 or SA_BF16");
   if (!isfinite(softmax_scale)) return fail(SA_ERR_INVALID, "softmax_scale is not finite");
+  if (D.dtype == SA_BF16 && (unsigned long long)D.N * D.Hkv * D.d * 2 >= (1ull << 32))
+    return fail(SA_ERR_UNSUPPORTED,
+                "seqlen * n_kv_heads * head_dim * 2 = %llu bytes of K per batch element: the "
+                "bf16 kernel addresses a batch element's keys with 32-bit offsets (< 2^32)",
+                (unsigned long long)D.N * D.Hkv * D.d * 2);
   g_err.clear();
   return hip_status(sa::launch_forward(D, Q, K, V, kv_idx, kv_cnt, W, softmax_scale, ws, O,
                                        out_dtype, lse, static_cast<hipStream_t>(stream)),

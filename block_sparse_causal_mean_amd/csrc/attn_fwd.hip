@@ -173,6 +173,9 @@ struct Cfg {
   static constexpr int LPW = (KREG + VREG) / NW;  // loads per wave per refill group
   static_assert(KREG % NW == 0 && VREG % NW == 0, "load regions must split evenly");
   static constexpr int LCAP = 512;             // list entries staged in LDS per segment
+  // Waves per SIMD the register allocation must allow: three for 32-row waves in 4-wave
+  // workgroups (168 registers), two otherwise (256).
+  static constexpr int WPE = QH == 1 && NW == 4 ? 3 : 2;
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -223,12 +226,17 @@ struct WaveState {
   float m_run[QH], l_run[QH];
 };
 
+// Operand reads issued ahead of the products that use them: four when a read feeds one
+// product, two when it feeds two (fewer registers held for 64-row waves).
+template <int QH>
+constexpr int kReadAhead = QH == 1 ? 4 : 2;
+
 // S^T for one step: QH accumulators of 32 keys x 32 query rows.  Each K chunk read from LDS
-// feeds QH products; reads run PD chunks ahead of their products.
+// (ka_addr[c]: this lane's chunk 2c + hi) feeds QH products.
 template <int D, int QH>
 __device__ __forceinline__ void step_scores(const uint32_t (&ka_addr)[D / 16],
                                             const bf16x8 (&qf)[QH][D / 16], f32x16 (&s)[QH]) {
-  constexpr int DC = D / 16, PD = 4;
+  constexpr int DC = D / 16, PD = kReadAhead<QH>;
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh) s[qh] = (f32x16){};
   bf16x8 ka[PD];
@@ -309,7 +317,7 @@ __device__ __forceinline__ void step_softmax_pv(f32x16 (&s)[QH], const uint32_t 
   // O^T += V^T P^T.  B operand slot 8 hi + 4 i' + r of pf[qh][half] is key
   // 16 half + 8 i' + 4 hi + r of the step; the A operand is chunk 2 half + hi of V^T row d,
   // which holds exactly those keys in that order (read through va_addr[half]).
-  constexpr int NP = DT * 2, PD = 4;
+  constexpr int NP = DT * 2, PD = kReadAhead<QH>;
   auto vload = [&](int i) {
     const int dt = i >> 1, half = i & 1;
     return lds_read<f16x8>(va_addr[half] + dt * 2048);
@@ -459,7 +467,8 @@ __device__ __forceinline__ void stage_segment(const int32_t* __restrict__ list,
 }
 
 template <int D, int QH, int NW>
-__global__ __launch_bounds__(64 * NW, 3) void attn_bf16(
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW>::WPE))) void attn_bf16(
     Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vp, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, int W, float scale_log2, void* __restrict__ O,
@@ -511,13 +520,12 @@ __global__ __launch_bounds__(64 * NW, 3) void attn_bf16(
     st.l_run[qh] = 0.0f;
   }
 
-  // Per-lane LDS read offsets within a slot.
-  int koff[DC];
-#pragma unroll
-  for (int c = 0; c < DC; ++c) koff[c] = l32 * 2 * D + 16 * ((2 * c + hi) ^ kswz<D>(l32));
-  int voff[2];
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) voff[hf] = l32 * 64 + 16 * ((2 * hf + hi) ^ vswz(l32));
+  // Per-lane LDS read offsets within a slot: K chunk hi of row l32 and V^T chunk hi of row l32.
+  // Chunk positions are chunk indices XOR a per-row value (kswz, vswz), so chunk 2c + hi sits
+  // at koff ^ 32 c, and V^T chunk 2 + hi at voff ^ 32; slots are 1 KiB aligned, so the same
+  // holds for the LDS addresses.
+  const int koff = l32 * 2 * D + 16 * (hi ^ kswz<D>(l32));
+  const int voff = l32 * 64 + 16 * (hi ^ vswz(l32));
   // Per-lane source offsets (elements, relative to a step's first key row) of this wave's K
   // regions: region w + NW k, lane i lands at image byte 1024 (w + NW k) + 16 i.
   int kgo[C::KREG / NW];
@@ -541,48 +549,58 @@ __global__ __launch_bounds__(64 * NW, 3) void attn_bf16(
       // Refill group m: K step m and V step m into ring slot m % NR.  Steps past the end reload
       // the last step (valid memory, into a slot nobody reads again) so that every group
       // issues the same LPW loads per wave, which the partial waits below count on.
+      // Scalar address arithmetic is kept to 32-bit unsigned sums and shifts: byte offsets
+      // within this (batch, kv head)'s K rows and V^T images are below 2^32 (the host checks
+      // N * Hkv * d * 2 < 2^32), and the ring slots of a step are carried, not divided out.
       const uint32_t ring_lds = lds_addr(ring);
-      auto entry_of = [&](int m) { return lst[min(m, nsteps - 1) / NSUB]; };
-      auto issue = [&](int m, int jv) {
-        const int a = min(m, nsteps - 1);
-        const int j = __builtin_amdgcn_readfirstlane(jv);  // uniform: SGPR base
-        const int sub = a % NSUB;
-        const uint16_t* kb = Kg + ((size_t)j * BLK + sub * kStep) * rstride;
-        const uint16_t* vb = Vpg + ((size_t)j * NSUB + sub) * (D * kStep) + 512 * w;
-        const uint32_t dst = ring_lds + (m % C::NR) * SLOT + w * 1024;
+      const uint32_t last = (uint32_t)nsteps - 1;
+      const uint32_t kblk_bytes = (uint32_t)(BLK * rstride * 2);
+      const uint32_t kstep_bytes = (uint32_t)(kStep * rstride * 2);
+      const char* kbase = reinterpret_cast<const char*>(Kg);
+      const char* vbase = reinterpret_cast<const char*>(Vpg) + 1024 * w;
+      auto entry_of = [&](uint32_t m) { return lst[min(m, last) / NSUB]; };
+      auto issue = [&](uint32_t m, int jv, uint32_t slot_idx) {
+        const uint32_t a = min(m, last);
+        const uint32_t j = (uint32_t)__builtin_amdgcn_readfirstlane(jv);  // uniform: SGPR
+        const uint32_t sub = a % NSUB;
+        const char* kb = kbase + (j * kblk_bytes + sub * kstep_bytes);
+        const char* vb = vbase + (j * NSUB + sub) * (uint32_t)C::VSLOT;
+        const uint32_t dst = ring_lds + slot_idx * SLOT + w * 1024;
 #pragma unroll
         for (int k = 0; k < C::KREG / NW; ++k) dma16(kb, kgo[k], dst + NW * k * 1024);
 #pragma unroll
         for (int k = 0; k < C::VREG / NW; ++k)
-          dma16(vb + 512 * NW * k, vlo, dst + C::KSLOT + NW * k * 1024);
+          dma16(vb + NW * k * 1024, vlo, dst + C::KSLOT + NW * k * 1024);
       };
 #pragma unroll
-      for (int m = 0; m < C::NR - 1; ++m) issue(m, entry_of(m));
+      for (int m = 0; m < C::NR - 1; ++m) issue(m, entry_of(m), m);
       int jn = entry_of(C::NR - 1);  // block of the next group, read one step early
+      uint32_t rs = 0, is = C::NR - 1;  // ring slots read and refilled at step i
 
       // Step i (slot i % NR): wait until group i has landed (groups i+1 .. i+NR-2 may still be
       // in flight), barrier (every wave's part of group i is in, and every wave is done with
       // step i-1, whose slot the new group overwrites), issue group i+NR-1, then compute step i.
-      for (int i = 0; i < nsteps; ++i) {
+      for (uint32_t i = 0; i <= last; ++i) {
         wait_vm<(C::NR - 2) * LPW>();
         barrier_only();
-        issue(i + C::NR - 1, jn);
+        issue(i + C::NR - 1, jn, is);
         jn = entry_of(i + C::NR);
-        const uint32_t slot = ring_lds + (i % C::NR) * SLOT;
+        const uint32_t slot = ring_lds + rs * SLOT;
+        is = rs;  // step i + 1 refills the slot step i reads
+        rs = rs == C::NR - 1 ? 0 : rs + 1;
+        // All of the step's read addresses up front, so that no read waits for its address; the
+        // empty asm keeps the compiler from re-deriving them next to the reads.
         uint32_t ka_addr[DC], va_addr[2];
-        // One add per address register per step; the empty asm keeps the compiler from
-        // re-deriving each read's address from its parts.
+        const uint32_t ka0 = slot + koff, va0 = slot + C::KSLOT + voff;
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
-          ka_addr[c] = slot + koff[c];
+          ka_addr[c] = ka0 ^ (32u * c);
           asm volatile("" : "+v"(ka_addr[c]));
         }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          va_addr[c] = slot + C::KSLOT + voff[c];
-          asm volatile("" : "+v"(va_addr[c]));
-        }
-        const int e = i / NSUB, sub = i - e * NSUB;
+        va_addr[0] = va0;
+        va_addr[1] = va0 ^ 32u;
+        asm volatile("" : "+v"(va_addr[0]), "+v"(va_addr[1]));
+        const int e = (int)(i / NSUB), sub = (int)(i % NSUB);
         const bool diag = e == diag_e;
         // On the diagonal block, a step whose first key lies after this wave's last row is
         // fully masked for the wave: skip it.

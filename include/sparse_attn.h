@@ -159,6 +159,8 @@ size_t sparse_attn_forward_workspace_bytes(const sa_problem* p);
  * Precision: fp32 accumulation.  With bf16 inputs, Q K^T runs on bf16 matrix cores and P V on
  * fp16 ones (P rounded to fp16, V converted exactly from bf16), so bf16 V values must lie
  * below 65504 in magnitude.  fp32 inputs are computed in fp32 throughout.
+ * Limit: with bf16 inputs, seqlen * n_kv_heads * head_dim * 2 (the bytes of K per batch
+ * element) must be below 2^32, else SA_ERR_UNSUPPORTED.
  */
 int sparse_attn_forward(const sa_problem* p, const void* Q, const void* K, const void* V,
                         const int32_t* kv_idx, const int32_t* kv_cnt, int32_t W,

@@ -168,6 +168,18 @@ def test_null_pointers_and_small_buffers_rejected(lib):
     assert lib.sparse_attn_score(None, FAKE, FAKE, FAKE, None) == api.SA_ERR_INVALID
 
 
+def test_bf16_forward_rejects_more_than_4gib_of_keys_per_batch_element(lib):
+    # 1M tokens x 16 kv heads x 128 x 2 bytes = 4 GiB of K in one batch element: the bf16 kernel
+    # addresses a batch element's keys with 32-bit byte offsets, so the call must refuse it
+    # before any HIP call (FAKE pointers are never touched).
+    p = _ok_problem()
+    p.seqlen, p.n_q_heads, p.n_kv_heads = 1 << 20, 16, 16
+    big = 1 << 60
+    r = lib.sparse_attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 65, 0.1, FAKE,
+                                big, FAKE, api.SA_BF16, None, None)
+    assert r == api.SA_ERR_UNSUPPORTED and "32-bit" in api.last_error()
+
+
 def test_binding_refuses_host_tensors(lib):
     import torch
     w = wl.WORKLOADS["tiny_ref"]
