@@ -44,6 +44,9 @@ BUDGET_LINEAR_DECAY = 1
 GATE_QUANTILE = 0
 GATE_FIXED = 1
 GATE_OFF = 2
+OAM_OFF = 0
+OAM_PRODUCT = 1
+OAM_ADDITIVE = 2
 F32 = 0
 BF16 = 1
 
@@ -59,7 +62,8 @@ class Workload:
     block: int
     dtype: int              # F32 or BF16 for Q, K, V
     score_mode: int         # KMEAN or KMINMAX
-    output_aware: int       # 1: tile score x mean value-row L2 norm
+    output_aware: int       # OAM_OFF, OAM_PRODUCT (score x mean value-row L2 norm) or
+                            # OAM_ADDITIVE (score / sqrt(d) + oam_beta * max(0, ln vnorm^2))
     k_max: int
     k_min: int
     budget_kind: int
@@ -72,6 +76,7 @@ class Workload:
     near_tie_keys: bool = False # K = base + 0.05 noise
     gate_mode: int = GATE_QUANTILE
     tau_fixed: float = 0.0
+    oam_beta: float = 0.0       # beta of the additive output-aware form
 
     @property
     def tile(self) -> int:
@@ -117,6 +122,15 @@ WORKLOADS: Dict[str, Workload] = {
         block=64, dtype=BF16, score_mode=KMEAN, output_aware=1, k_max=64, k_min=8,
         budget_kind=BUDGET_LINEAR_DECAY, n_sink=2, rho=2.0, q=0.1, seed=1004,
         v_logn_sigma=1.0),
+    # The Stem page's own output-aware form (Metodologia B), additive on the logit scale,
+    # on stem_32k's shapes and data.  There, block scores / sqrt(d) spread by about 0.06
+    # across blocks and ln(vnorm^2) by about 0.33, so beta = 0.2 gives the two terms a
+    # similar say in the ranking.
+    "stem_additive_32k": Workload(
+        name="stem_additive_32k", batch=4, seqlen=32768, n_q_heads=32, n_kv_heads=8,
+        head_dim=128, block=64, dtype=BF16, score_mode=KMEAN, output_aware=2, k_max=64,
+        k_min=8, budget_kind=BUDGET_LINEAR_DECAY, n_sink=2, rho=2.0, q=0.1, seed=1005,
+        v_logn_sigma=1.0, oam_beta=0.2),
 }
 
 # Order used by reports: the small reference case first, the 128K prefill (the headline) third.

@@ -29,7 +29,7 @@ class OracleCfg(ctypes.Structure):
         ("in_dtype", ctypes.c_int32), ("score_mode", ctypes.c_int32),
         ("output_aware", ctypes.c_int32), ("k_max", ctypes.c_int32), ("k_min", ctypes.c_int32),
         ("budget_kind", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
-        ("tau_fixed", ctypes.c_float), ("pad_", ctypes.c_float), ("rho", ctypes.c_double),
+        ("tau_fixed", ctypes.c_float), ("oam_beta", ctypes.c_float), ("rho", ctypes.c_double),
         ("q", ctypes.c_double), ("width", ctypes.c_int32), ("pad2_", ctypes.c_int32),
     ]
 
@@ -70,7 +70,8 @@ def make_cfg(w, **over) -> OracleCfg:
         n_kv_heads=get("n_kv_heads"), head_dim=get("head_dim"), block=get("block"),
         in_dtype=get("dtype"), score_mode=get("score_mode"), output_aware=get("output_aware"),
         k_max=k_max, k_min=get("k_min"), budget_kind=get("budget_kind"), n_sink=n_sink,
-        gate_mode=get("gate_mode"), tau_fixed=float(get("tau_fixed")), pad_=0.0, rho=rho,
+        gate_mode=get("gate_mode"), tau_fixed=float(get("tau_fixed")),
+        oam_beta=float(over.get("oam_beta", getattr(w, "oam_beta", 0.0))), rho=rho,
         q=float(get("q")), width=width, pad2_=0)
 
 

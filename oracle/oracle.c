@@ -44,8 +44,12 @@
  *   - row score s_ij = fmaf chain over c in order of q_ic * x_jc, where x = kmean, or for
  *     the bound x_c = (q_ic >= 0 ? kmax_c : kmin_c); no 1/sqrt(d) (ranking and sigma are
  *     invariant to a positive scale)
- *   - tile score S_tj = canon(max over the tile's rows of s_ij); output-aware:
- *     S_tj = canon(S_tj * vnorm_j)
+ *   - tile score S_tj = canon(max over the tile's rows of s_ij); output-aware, product form
+ *     (output_aware = 1): S_tj = canon(S_tj * vnorm_j); additive form (output_aware = 2,
+ *     Stem page, Metodologia B: score plus beta * max(0, log ||V_j||^2)):
+ *     S_tj = canon(fmaf(S_tj, scale, bonus_j)), scale = (float)(1 / sqrt(d)) puts the score
+ *     on the logit scale, bonus_j = (float)(beta * max(0, ln(vnorm_j^2))) with the logarithm,
+ *     the square and the product taken in fp64
  *   - sigma: two fp32 subtractions and one IEEE division; sigma_bar: fp32 sum over heads in
  *     order, divided by the head count; the quantile rank ceil(q*M) in fp64.
  *
@@ -73,12 +77,12 @@ typedef struct {
   int32_t batch, seqlen, n_q_heads, n_kv_heads, head_dim, block; /* query tile == block */
   int32_t in_dtype;     /* 0: float32 arrays, 1: bfloat16 bit patterns (uint16) */
   int32_t score_mode;   /* 0: mean-pooled keys, 1: per-coordinate min/max bound */
-  int32_t output_aware; /* 1: tile score times mean value-row L2 norm */
+  int32_t output_aware; /* 1: tile score times mean value-row L2 norm; 2: additive form */
   int32_t k_max, k_min, budget_kind; /* budget_kind 0: constant k_max, 1: linear decay */
   int32_t n_sink;       /* first n_sink blocks are always kept */
   int32_t gate_mode;    /* 0: per-call quantile, 1: fixed threshold, 2: no gate */
   float tau_fixed;
-  float pad_;
+  float oam_beta;       /* beta of the additive output-aware form */
   double rho, q;
   int32_t width;        /* entries per padded list */
   int32_t pad2_;
@@ -182,7 +186,14 @@ static float row_score(const oc_inputs* in, int b, int64_t pos, int h, int j) {
   return s;
 }
 
-/* Tile score S_tj: maximum over the tile's rows, then the output-aware factor. */
+/* Additive output-aware term of block j (Stem page, Metodologia B): beta times the positive
+ * part of the natural log of the squared value norm, in fp64, rounded once to fp32. */
+static float oam_bonus(float vnorm, float beta) {
+  const double l = log((double)vnorm * (double)vnorm);
+  return (float)((double)beta * (l > 0.0 ? l : 0.0));
+}
+
+/* Tile score S_tj: maximum over the tile's rows, then the output-aware factor or term. */
 static float tile_score(const oc_inputs* in, int b, int h, int t, int j) {
   const oc_cfg* c = in->c;
   float m = row_score(in, b, (int64_t)t * c->block, h, j);
@@ -194,7 +205,14 @@ static float tile_score(const oc_inputs* in, int b, int h, int t, int j) {
   if (c->output_aware) {
     const int n = c->seqlen / c->block;
     const int g = h / (c->n_q_heads / c->n_kv_heads);
-    m = canon(m * in->vn[((int64_t)b * n + j) * c->n_kv_heads + g]);
+    const float v = in->vn[((int64_t)b * n + j) * c->n_kv_heads + g];
+    if (c->output_aware == 1) {
+      m = canon(m * v);
+    } else {
+      /* the score on the logit scale (1/sqrt(d), as the attention's softmax sees it) */
+      const float scale = (float)(1.0 / sqrt((double)c->head_dim));
+      m = canon(fmaf(m, scale, oam_bonus(v, c->oam_beta)));
+    }
   }
   return m;
 }

@@ -479,3 +479,46 @@ def test_attention_invariants():
     Os, _ = oracle.forward(cfg, Q, K, V, out["kv_idx"], out["kv_cnt"], 0.25, rows=rows)
     for r, (b, h, p) in enumerate(rows):
         np.testing.assert_array_equal(Os[r], O[b, p, h])
+
+
+# ------------------------------------------------------- additive output-aware metric
+
+def test_additive_output_aware_golden():
+    """Stem page, Metodologia B: hand-worked ranking and cut margins (tests/golden)."""
+    g = json.load(open(os.path.join(GOLDEN, "additive_oam.json")))
+    w = _small(seqlen=512, n_q_heads=1, n_kv_heads=1, head_dim=64, block=64, k_max=g["k"],
+               k_min=g["k"], output_aware=2, gate_mode=wl.GATE_OFF)
+    Q = np.zeros((1, 512, 1, 64), np.float32)
+    Q[0, :, 0, 0] = 1.0
+    K = np.zeros((1, 512, 1, 64), np.float32)
+    V = np.zeros_like(K)
+    for j in range(8):
+        K[0, j * 64:(j + 1) * 64, 0, 0] = g["c"][j]
+        V[0, j * 64:(j + 1) * 64, 0, 5] = g["v"][j]
+    cfg = oracle.make_cfg(w, oam_beta=g["beta"])
+    assert cfg.output_aware == 2 and cfg.oam_beta == np.float32(g["beta"])
+    s = oracle.pool(cfg, torch.from_numpy(K), torch.from_numpy(V))
+    np.testing.assert_array_equal(s["vn"][0, :, 0], np.abs(np.array(g["v"], np.float32)))
+    out = oracle.select(cfg, torch.from_numpy(Q), s)
+    for t, want in g["tiles"].items():
+        t = int(t)
+        cnt = int(out["kv_cnt"][0, 0, t])
+        assert list(out["kv_idx"][0, 0, t, :cnt]) == want["list"], t
+        assert abs(float(out["sigma"][0, 0, t]) - want["sigma"]) <= g["sigma_tolerance"], t
+    assert not out["gate"].any()
+
+
+def test_additive_output_aware_with_small_value_norms_equals_plain_selection():
+    """Value-row norms <= 1 make max(0, ln ||V||^2) = 0, so the additive metric is the block
+    score times 1/8 (d = 64), an exact power-of-two scaling: selections and sigma must equal
+    the plain ones bit for bit."""
+    w, cfg, Q, K, V, s = _random_case(701, seqlen=768, head_dim=64, block=32, k_max=3, k_min=3,
+                                      n_q_heads=2, n_kv_heads=1)
+    plain = oracle.select(cfg, Q, s)
+    V2 = V / (V.norm(dim=-1, keepdim=True) * 1.01)
+    cfg2 = oracle.make_cfg(w, output_aware=2, oam_beta=0.7)
+    s2 = oracle.pool(cfg2, K, V2)
+    assert (s2["vn"] <= 1.0).all()
+    add = oracle.select(cfg2, Q, s2)
+    for key in ("kv_idx", "kv_cnt", "sigma", "sigma_bar", "gate", "tau"):
+        np.testing.assert_array_equal(add[key], plain[key])
