@@ -141,7 +141,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=wl.HEADLINE, choices=wl.WORKLOAD_ORDER)
+    ap.add_argument("--workload", default=wl.HEADLINE, choices=list(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB, so a "
@@ -221,7 +221,9 @@ def main():
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "block": w.block, "tile": w.tile,
                    "score_mode": "kminmax" if w.score_mode == wl.KMINMAX else "kmean",
-                   "output_aware": bool(w.output_aware), "k_max": w.k_max, "k_min": w.k_min,
+                   "output_aware": ["off", "product", "additive"][w.output_aware],
+                   **({"oam_beta": w.oam_beta} if w.output_aware == wl.OAM_ADDITIVE else {}),
+                   "k_max": w.k_max, "k_min": w.k_min,
                    "budget": "linear_decay" if w.budget_kind else "const", "n_sink": w.n_sink,
                    "rho": w.rho, "q": w.q, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,

@@ -25,6 +25,7 @@ SA_F32, SA_BF16 = 0, 1
 SA_KMEAN, SA_KMINMAX = 0, 1
 SA_K_CONST, SA_K_LINEAR_DECAY = 0, 1
 SA_GATE_QUANTILE, SA_GATE_FIXED, SA_GATE_OFF = 0, 1, 2
+SA_OAM_OFF, SA_OAM_PRODUCT, SA_OAM_ADDITIVE = 0, 1, 2
 
 # Every function the header declares, checked by the tests against the built library.
 EXPORTS = ("sparse_attn_summary_bytes", "sparse_attn_select_workspace_bytes",
@@ -36,7 +37,7 @@ EXPORTS = ("sparse_attn_summary_bytes", "sparse_attn_select_workspace_bytes",
 class Problem(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int32) for f in (
         "batch", "seqlen", "n_q_heads", "n_kv_heads", "head_dim", "block", "tile", "dtype",
-        "score_mode", "output_aware")]
+        "score_mode", "output_aware")] + [("oam_beta", ctypes.c_float)]
 
 
 class Budget(ctypes.Structure):
@@ -95,7 +96,8 @@ def _check(rc: int):
 def problem(w: wl.Workload) -> Problem:
     return Problem(batch=w.batch, seqlen=w.seqlen, n_q_heads=w.n_q_heads,
                    n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, block=w.block, tile=w.tile,
-                   dtype=w.dtype, score_mode=w.score_mode, output_aware=w.output_aware)
+                   dtype=w.dtype, score_mode=w.score_mode, output_aware=w.output_aware,
+                   oam_beta=getattr(w, "oam_beta", 0.0))
 
 
 def budget(w: wl.Workload) -> Budget:
@@ -245,3 +247,21 @@ class Prefill:
         self.select(Q, stream)
         self.forward(Q, K, V, stream)
         return self.O
+
+    def calibrate_tau(self, Q, K, V=None) -> float:
+        """A threshold for SA_GATE_FIXED from calibration inputs (the Stem page pairs its
+        output-aware metric with a fixed, per-layer threshold; the gated-selection page's
+        per-call quantile is what calibrates it here): runs the summaries and the selection
+        with the quantile gate, whatever this object's gate mode, and returns the mean of
+        the per-batch-element thresholds, leaving out batch elements where nothing can trip
+        (-inf if none remain).  Overwrites this object's lists and statistics; synchronizes.
+        """
+        b = budget(self.w)
+        b.gate_mode = SA_GATE_QUANTILE
+        tau = torch.empty((self.w.batch,), dtype=torch.float32, device=self.summ.device)
+        self.score(K, V)
+        select(self.p, b, Q, self.summ, self.ws, self.kv_idx, self.kv_cnt, self.sigma,
+               self.sigma_bar, self.gate, tau, None)
+        torch.cuda.synchronize()
+        t = tau[torch.isfinite(tau)]
+        return float(t.double().mean()) if t.numel() else float("-inf")

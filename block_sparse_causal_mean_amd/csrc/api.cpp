@@ -37,8 +37,11 @@ int check_problem(const sa_problem* p, sa::Dims* D) {
     return fail(SA_ERR_INVALID, "dtype must be SA_BF16 or SA_F32");
   if (p->score_mode != SA_KMEAN && p->score_mode != SA_KMINMAX)
     return fail(SA_ERR_INVALID, "score_mode must be SA_KMEAN or SA_KMINMAX");
-  if (p->output_aware != 0 && p->output_aware != 1)
-    return fail(SA_ERR_INVALID, "output_aware must be 0 or 1");
+  if (p->output_aware != SA_OAM_OFF && p->output_aware != SA_OAM_PRODUCT &&
+      p->output_aware != SA_OAM_ADDITIVE)
+    return fail(SA_ERR_INVALID, "output_aware must be SA_OAM_OFF, SA_OAM_PRODUCT or SA_OAM_ADDITIVE");
+  if (p->output_aware == SA_OAM_ADDITIVE && !(isfinite(p->oam_beta) && p->oam_beta >= 0.0f))
+    return fail(SA_ERR_INVALID, "oam_beta must be finite and >= 0 for SA_OAM_ADDITIVE");
   if (p->block < 1 || p->tile < 1) return fail(SA_ERR_INVALID, "block and tile must be >= 1");
   if (p->seqlen % p->block)
     return fail(SA_ERR_INVALID, "seqlen (%d) must be a multiple of block (%d)", p->seqlen,
@@ -66,6 +69,8 @@ int check_problem(const sa_problem* p, sa::Dims* D) {
     D->dtype = p->dtype;
     D->score_mode = p->score_mode;
     D->oam = p->output_aware;
+    D->oam_beta = p->output_aware == SA_OAM_ADDITIVE ? p->oam_beta : 0.0f;
+    D->oam_scale = (float)(1.0 / sqrt((double)p->head_dim));
   }
   return SA_OK;
 }

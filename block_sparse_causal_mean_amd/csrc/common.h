@@ -41,7 +41,8 @@ __device__ __forceinline__ float order_key_inv(uint32_t k) {
 
 struct Dims {
   int B, N, Hq, Hkv, G, d, blk, n;  // n = N / blk tiles (= blocks)
-  int dtype, score_mode, oam;
+  int dtype, score_mode, oam;     // oam: SA_OAM_OFF, SA_OAM_PRODUCT or SA_OAM_ADDITIVE
+  float oam_beta, oam_scale;      // additive form: beta and (float)(1 / sqrt(d))
 };
 
 struct BudgetDev {

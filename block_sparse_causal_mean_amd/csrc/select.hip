@@ -187,6 +187,21 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Output-aware tile score from the canonical tile score m and the block's mean value-row norm
+// v.  Product form: m * v.  Additive form (Stem page, Metodologia B: the score plus
+// beta * max(0, log ||V_j||^2)): the score on the logit scale, fmaf(m, 1/sqrt(d), bonus),
+// with bonus = beta * max(0, ln v^2) evaluated in fp64 and rounded once to fp32.
+template <int OAM>
+__device__ __forceinline__ float oam_combine(float m, float v, const Dims& dm) {
+  if (OAM == SA_OAM_PRODUCT) return canon(m * v);
+  if (OAM == SA_OAM_ADDITIVE) {
+    const double l = log((double)v * (double)v);
+    const float bonus = (float)((double)dm.oam_beta * (l > 0.0 ? l : 0.0));
+    return canon(__builtin_fmaf(m, dm.oam_scale, bonus));
+  }
+  return m;
+}
+
 // ----------------------------------------------------------------------- score_rank
 
 template <typename T, int MODE, int OAM, int D, int TILE>
@@ -239,7 +254,7 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
       for (int c = 0; c < D; ++c) s = __builtin_fmaf(q[c], q[c] >= 0.0f ? kx[c] : kb[c], s);
     }
     float m = canon(wave_max(s));
-    if (OAM) m = canon(m * vn[(size_t)j * dm.Hkv]);
+    m = oam_combine<OAM>(m, OAM ? vn[(size_t)j * dm.Hkv] : 0.0f, dm);
     if (lead) {
       const unsigned long long key =
           ((unsigned long long)order_key(m) << 32) | (0xffffffffu - (unsigned)j);
@@ -529,7 +544,7 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     best = fmaxf(best, __shfl_xor(best, 32));
     if (valid && hi == 0) {
       float m = canon(best);
-      if (OAM) m = canon(m * summ[vn_off + ((size_t)b * n + j) * dm.Hkv + g]);
+      m = oam_combine<OAM>(m, OAM ? summ[vn_off + ((size_t)b * n + j) * dm.Hkv + g] : 0.0f, dm);
       keys[j - j0] = ((unsigned long long)order_key(m) << 32) | (0xffffffffu - (unsigned)j);
     }
   }
@@ -710,14 +725,22 @@ hipError_t score_by_shape(const Dims& dm, const BudgetDev& bd, const void* Q, co
                       : launch_score<T, MODE, OAM, 128, 128>(dm, bd, Q, summ, ranked, sigma, s);
 }
 
+template <typename T, int MODE>
+hipError_t score_by_oam(const Dims& dm, const BudgetDev& bd, const void* Q, const float* summ,
+                        int* ranked, float* sigma, hipStream_t s) {
+  if (dm.oam == SA_OAM_PRODUCT)
+    return score_by_shape<T, MODE, SA_OAM_PRODUCT>(dm, bd, Q, summ, ranked, sigma, s);
+  if (dm.oam == SA_OAM_ADDITIVE)
+    return score_by_shape<T, MODE, SA_OAM_ADDITIVE>(dm, bd, Q, summ, ranked, sigma, s);
+  return score_by_shape<T, MODE, SA_OAM_OFF>(dm, bd, Q, summ, ranked, sigma, s);
+}
+
 template <typename T>
 hipError_t score_dispatch(const Dims& dm, const BudgetDev& bd, const void* Q, const float* summ,
                           int* ranked, float* sigma, hipStream_t s) {
   if (dm.score_mode == SA_KMEAN)
-    return dm.oam ? score_by_shape<T, SA_KMEAN, 1>(dm, bd, Q, summ, ranked, sigma, s)
-                  : score_by_shape<T, SA_KMEAN, 0>(dm, bd, Q, summ, ranked, sigma, s);
-  return dm.oam ? score_by_shape<T, SA_KMINMAX, 1>(dm, bd, Q, summ, ranked, sigma, s)
-                : score_by_shape<T, SA_KMINMAX, 0>(dm, bd, Q, summ, ranked, sigma, s);
+    return score_by_oam<T, SA_KMEAN>(dm, bd, Q, summ, ranked, sigma, s);
+  return score_by_oam<T, SA_KMINMAX>(dm, bd, Q, summ, ranked, sigma, s);
 }
 
 template <int MODE, int OAM, int D, int TILE>
@@ -750,13 +773,21 @@ hipError_t score_mfma_shape(const Dims& dm, const BudgetDev& bd, const void* Q,
                       : launch_score_mfma<MODE, OAM, 128, 128>(dm, bd, Q, summ, ranked, sigma, s);
 }
 
+template <int MODE>
+hipError_t score_mfma_oam(const Dims& dm, const BudgetDev& bd, const void* Q,
+                          const float* summ, int* ranked, float* sigma, hipStream_t s) {
+  if (dm.oam == SA_OAM_PRODUCT)
+    return score_mfma_shape<MODE, SA_OAM_PRODUCT>(dm, bd, Q, summ, ranked, sigma, s);
+  if (dm.oam == SA_OAM_ADDITIVE)
+    return score_mfma_shape<MODE, SA_OAM_ADDITIVE>(dm, bd, Q, summ, ranked, sigma, s);
+  return score_mfma_shape<MODE, SA_OAM_OFF>(dm, bd, Q, summ, ranked, sigma, s);
+}
+
 hipError_t score_mfma_dispatch(const Dims& dm, const BudgetDev& bd, const void* Q,
                                const float* summ, int* ranked, float* sigma, hipStream_t s) {
   if (dm.score_mode == SA_KMEAN)
-    return dm.oam ? score_mfma_shape<SA_KMEAN, 1>(dm, bd, Q, summ, ranked, sigma, s)
-                  : score_mfma_shape<SA_KMEAN, 0>(dm, bd, Q, summ, ranked, sigma, s);
-  return dm.oam ? score_mfma_shape<SA_KMINMAX, 1>(dm, bd, Q, summ, ranked, sigma, s)
-                : score_mfma_shape<SA_KMINMAX, 0>(dm, bd, Q, summ, ranked, sigma, s);
+    return score_mfma_oam<SA_KMEAN>(dm, bd, Q, summ, ranked, sigma, s);
+  return score_mfma_oam<SA_KMINMAX>(dm, bd, Q, summ, ranked, sigma, s);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

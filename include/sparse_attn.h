@@ -53,6 +53,7 @@ enum { SA_F32 = 0, SA_BF16 = 1 };                            /* element types */
 enum { SA_KMEAN = 0, SA_KMINMAX = 1 };                       /* block score backbones */
 enum { SA_K_CONST = 0, SA_K_LINEAR_DECAY = 1 };              /* budget schedules */
 enum { SA_GATE_QUANTILE = 0, SA_GATE_FIXED = 1, SA_GATE_OFF = 2 }; /* gate threshold source */
+enum { SA_OAM_OFF = 0, SA_OAM_PRODUCT = 1, SA_OAM_ADDITIVE = 2 };   /* output-aware scoring */
 
 /* Shapes and scoring mode. */
 typedef struct sa_problem {
@@ -65,7 +66,11 @@ typedef struct sa_problem {
   int32_t tile;         /* query tile size: must equal block */
   int32_t dtype;        /* SA_BF16 or SA_F32, for Q, K and V */
   int32_t score_mode;   /* SA_KMEAN: mean-pooled keys; SA_KMINMAX: per-coordinate bound */
-  int32_t output_aware; /* 1: tile score times the block's mean value-row L2 norm */
+  int32_t output_aware; /* SA_OAM_OFF; SA_OAM_PRODUCT: tile score times the block's mean
+                           value-row L2 norm vnorm; SA_OAM_ADDITIVE (Stem page, Metodologia B):
+                           fmaf(tile score, (float)(1/sqrt(d)), bonus) with
+                           bonus = (float)(oam_beta * max(0, ln(vnorm^2))) in fp64 */
+  float oam_beta;       /* beta of SA_OAM_ADDITIVE: finite, >= 0; ignored otherwise */
 } sa_problem;
 
 /* Budget, forced blocks and gate.  n = seqlen / block tiles (= blocks) per sequence. */
@@ -88,7 +93,7 @@ typedef struct sa_budget {
  * It starts with (all fp32, n = seqlen / block):
  *   SA_KMEAN:   kmean [B, n, Hkv, d]
  *   SA_KMINMAX: kmin  [B, n, Hkv, d] followed by kmax [B, n, Hkv, d]
- *   then, if output_aware: vnorm [B, n, Hkv]
+ *   then, if output_aware != SA_OAM_OFF: vnorm [B, n, Hkv]
  * and continues with auxiliary data for sparse_attn_select whose layout is private
  * (per-block norms, and bf16 and fp32 copies of the planes above in a blocked order: about
  * one and a half times as large again).

@@ -47,8 +47,9 @@ def test_struct_layout_matches_header(tmp_path):
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "sparse_attn.h"\n'
         "int main(void){\n"
-        'printf("%zu %zu %zu %zu %zu\\n", sizeof(sa_problem), sizeof(sa_budget),'
-        " offsetof(sa_budget, tau_fixed), offsetof(sa_budget, rho), offsetof(sa_budget, q));\n"
+        'printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(sa_problem), sizeof(sa_budget),'
+        " offsetof(sa_budget, tau_fixed), offsetof(sa_budget, rho), offsetof(sa_budget, q),"
+        " offsetof(sa_problem, oam_beta));\n"
         "return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
@@ -56,7 +57,8 @@ def test_struct_layout_matches_header(tmp_path):
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
                                           check=True).stdout.split()]
     want = [ctypes.sizeof(api.Problem), ctypes.sizeof(api.Budget),
-            api.Budget.tau_fixed.offset, api.Budget.rho.offset, api.Budget.q.offset]
+            api.Budget.tau_fixed.offset, api.Budget.rho.offset, api.Budget.q.offset,
+            api.Problem.oam_beta.offset]
     assert got == want
 
 
@@ -102,6 +104,8 @@ BAD_PROBLEMS = [
     (dict(dtype=7), api.SA_ERR_INVALID),
     (dict(score_mode=2), api.SA_ERR_INVALID),
     (dict(output_aware=3), api.SA_ERR_INVALID),
+    (dict(output_aware=2, oam_beta=-0.5), api.SA_ERR_INVALID),
+    (dict(output_aware=2, oam_beta=float("nan")), api.SA_ERR_INVALID),
     (dict(seqlen=64 * 16385), api.SA_ERR_UNSUPPORTED),
 ]
 

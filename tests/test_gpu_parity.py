@@ -39,6 +39,13 @@ SMALL = {
     "f32_d128_blk128": WL["tiny_ref"].resized(seqlen=2048, block=128, n_q_heads=4,
                                                n_kv_heads=2, head_dim=128, k_max=3, k_min=3,
                                                output_aware=1, score_mode=wl.KMINMAX),
+    # the additive output-aware metric: bf16 (matrix-core prefilter path) and fp32 (VALU path)
+    "stem_additive_b2_n32": WL["stem_additive_32k"].resized(batch=2, seqlen=2048, k_max=16,
+                                                            k_min=4),
+    "f32_additive_d64_quest": WL["tiny_ref"].resized(seqlen=2048, n_q_heads=4, n_kv_heads=2,
+                                                      k_max=3, k_min=3, score_mode=wl.KMINMAX,
+                                                      output_aware=wl.OAM_ADDITIVE,
+                                                      oam_beta=0.3, v_logn_sigma=1.0),
 }
 
 MAX_ORACLE_ROWS = 6000
@@ -304,3 +311,23 @@ def test_forward_long_lists_in_segments(name):
         assert err <= out_tol(w, api.SA_F32, O_ref)
         # rows of tiles with empty lists are zero
         assert float(O[0, 5 * w.block:6 * w.block].abs().max()) == 0.0
+
+
+def test_fixed_gate_with_calibrated_tau_reproduces_the_quantile_gate():
+    """A fixed threshold calibrated on an input (the per-call quantile's tau) gives that
+    input the same gate, lists and counts as the quantile gate; the fixed-gate run also
+    matches the oracle with that threshold bit for bit."""
+    w = WL["stem_additive_32k"].resized(batch=1, seqlen=2048, k_max=16, k_min=4)
+    inp = wl.make_inputs(w)
+    say("[calibrated tau] quantile run + calibration")
+    q_run = run_gpu(w, inp, out_dtype=api.SA_F32)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    tau = api.Prefill(w).calibrate_tau(dev["Q"], dev["K"], dev["V"])
+    assert tau == float(q_run["tau"][0])
+    wf = w.resized(gate_mode=wl.GATE_FIXED, tau_fixed=tau)
+    f_run = run_gpu(wf, inp, out_dtype=api.SA_F32)
+    for key in ("gate", "kv_idx", "kv_cnt", "sigma", "sigma_bar"):
+        np.testing.assert_array_equal(f_run[key], q_run[key], err_msg=key)
+    cfg = oracle.make_cfg(wf)
+    o_sel = oracle.select(cfg, inp["Q"], oracle.pool(cfg, inp["K"], inp["V"]))
+    assert_selection_equal(f_run, o_sel)
