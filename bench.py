@@ -70,15 +70,18 @@ def time_score_cold(pf: api.Prefill, K, V, reps: int = 10) -> float:
 
     The eviction READS a 1 GiB buffer (4x the last-level cache), so K cannot be served from any
     cache and no dirty lines are left behind: evicting by writing leaves write-backs that share
-    HBM with the timed kernel and measured at half the read bandwidth of a clean eviction."""
+    HBM with the timed kernel and measured at half the read bandwidth of a clean eviction.
+    Eviction, start event, kernel and end event are enqueued back to back, so the start event
+    completes when the eviction does and the kernel is already queued behind it: the interval
+    holds the kernel, not the host's launch latency."""
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
     s = torch.cuda.current_stream()
     total = 0.0
     for _ in range(reps):
-        torch.sum(flush, dim=0, out=sink)
-        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.sum(flush, dim=0, out=sink)
         e0.record(s)
         pf.score(K, V)
         e1.record(s)
