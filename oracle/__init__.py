@@ -55,6 +55,7 @@ def _load():
     lib.oracle_forward.argtypes = [cfgp, P, P, P, P, P, ctypes.c_int, ctypes.c_float,
                                    ctypes.c_int64, P, P, P]
     lib.oracle_budget.argtypes = [cfgp, ctypes.c_int]
+    lib.oracle_vs_lists.argtypes = [cfgp, P, ctypes.c_int, P, ctypes.c_int, P, P, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -210,6 +211,25 @@ def forward(cfg: OracleCfg, Q, K, V, kv_idx, kv_cnt, softmax_scale: float, rows=
     if rows is None:
         return O.reshape(B, N, Hq, d), lse.reshape(B, N, Hq)
     return O, lse
+
+
+def vs_lists(cfg: OracleCfg, vert, slash):
+    """Per-tile block lists of a vertical-slash index (oracle.c, oracle_vs_lists): vert
+    [B, Hq, NV] key blocks and slash [B, Hq, NS] block offsets, each ending at its first
+    negative entry.  Returns (kv_idx [B, Hq, n, W], kv_cnt [B, Hq, n]) with W = NV + NS + 1."""
+    lib = _load()
+    _check(cfg)
+    B, Hq, n = cfg.batch, cfg.n_q_heads, cfg.seqlen // cfg.block
+    v = np.ascontiguousarray(vert, dtype=np.int32).reshape(B, Hq, -1)
+    s = np.ascontiguousarray(slash, dtype=np.int32).reshape(B, Hq, -1)
+    NV, NS = v.shape[-1], s.shape[-1]
+    W = NV + NS + 1
+    idx = np.zeros((B, Hq, n, W), np.int32)
+    cnt = np.zeros((B, Hq, n), np.int32)
+    rc = lib.oracle_vs_lists(ctypes.byref(cfg), _p(v), NV, _p(s), NS, _p(idx), _p(cnt), W)
+    if rc != 0:
+        raise RuntimeError(f"oracle_vs_lists failed ({rc})")
+    return idx, cnt
 
 
 def threads() -> int:

@@ -513,6 +513,61 @@ int oracle_forward(const oc_cfg* c, const void* Q, const void* K, const void* V,
   return fail ? -1 : 0;
 }
 
+/* ------------------------------------------------------- vertical-slash index lists */
+
+/* VSPrefill page, Metodologia B.3: the sparse attention of query tile t reads the union of the
+ * selected vertical columns and the selected slash diagonals.  At block granularity (this
+ * build's reading): vertical entries are key-block indices, slash entries are block offsets
+ * delta, tile t reads block t - delta, and the diagonal block t is always read (as in every
+ * other list).  vert [B, Hq, NV] and slash [B, Hq, NS] end at their first negative entry;
+ * entries beyond the tile (a vertical block > t, an offset > t) are skipped.  Output: the
+ * union in ascending order, -1 padded to W entries, and its size. */
+int oracle_vs_lists(const oc_cfg* c, const int32_t* vert, int NV, const int32_t* slash, int NS,
+                    int32_t* kv_idx, int32_t* kv_cnt, int W) {
+  const int n = c->seqlen / c->block, Hq = c->n_q_heads;
+  int fail = 0;
+#pragma omp parallel
+  {
+    unsigned char* in = (unsigned char*)malloc((size_t)n);
+    if (!in) {
+#pragma omp atomic write
+      fail = 1;
+    }
+#pragma omp for collapse(2) schedule(static)
+    for (int bh = 0; bh < c->batch * Hq; ++bh)
+      for (int t = 0; t < n; ++t) {
+        if (!in) continue;
+        memset(in, 0, (size_t)(t + 1));
+        in[t] = 1;
+        for (int e = 0; e < NV; ++e) {
+          const int v = vert[(int64_t)bh * NV + e];
+          if (v < 0) break;
+          if (v <= t) in[v] = 1;
+        }
+        for (int e = 0; e < NS; ++e) {
+          const int dlt = slash[(int64_t)bh * NS + e];
+          if (dlt < 0) break;
+          if (dlt <= t) in[t - dlt] = 1;
+        }
+        int32_t* out = kv_idx + ((int64_t)bh * n + t) * W;
+        int m = 0;
+        for (int j = 0; j <= t; ++j)
+          if (in[j]) {
+            if (m < W) out[m] = j;
+            ++m;
+          }
+        if (m > W) {
+#pragma omp atomic write
+          fail = 2;
+        }
+        for (int e = m; e < W; ++e) out[e] = -1;
+        kv_cnt[(int64_t)bh * n + t] = m < W ? m : W;
+      }
+    free(in);
+  }
+  return fail ? -fail : 0;
+}
+
 /* Budget for tile t, exported so the tests can pin the schedule on its own. */
 int oracle_budget(const oc_cfg* c, int t) { return budget(c, t); }
 

@@ -522,3 +522,39 @@ def test_additive_output_aware_with_small_value_norms_equals_plain_selection():
     add = oracle.select(cfg2, Q, s2)
     for key in ("kv_idx", "kv_cnt", "sigma", "sigma_bar", "gate", "tau"):
         np.testing.assert_array_equal(add[key], plain[key])
+
+
+# ------------------------------------------------------------ vertical-slash index lists
+
+def test_vs_lists_golden():
+    """VSPrefill page, Metodologia B.3: hand-worked union of vertical and slash indices."""
+    g = json.load(open(os.path.join(GOLDEN, "vs_lists.json")))
+    w = _small(seqlen=512, n_q_heads=2, n_kv_heads=1, head_dim=16, block=64)
+    cfg = oracle.make_cfg(w)
+    idx, cnt = oracle.vs_lists(cfg, np.array(g["vert"]), np.array(g["slash"]))
+    assert idx.shape == (1, 2, 8, 9)
+    for h in range(2):
+        for t in range(8):
+            want = g["lists"][0][h][t]
+            assert int(cnt[0, h, t]) == len(want), (h, t)
+            assert list(idx[0, h, t, :len(want)]) == want, (h, t)
+            assert (idx[0, h, t, len(want):] == -1).all()
+
+
+def test_vs_lists_all_vertical_is_dense_causal_attention():
+    """Every block as a vertical column gives every tile all of its causal blocks, so the
+    attention equals dense causal attention (fp64 PyTorch on the CPU)."""
+    w = _small(seqlen=384, n_q_heads=4, n_kv_heads=2, head_dim=16, block=32)
+    cfg = oracle.make_cfg(w)
+    n = w.n_blocks
+    vert = np.tile(np.arange(n, dtype=np.int32), (1, 4, 1))
+    slash = np.full((1, 4, 1), -1, np.int32)
+    idx, cnt = oracle.vs_lists(cfg, vert, slash)
+    np.testing.assert_array_equal(cnt[0, 0], np.arange(1, n + 1))
+    Q = _randn((1, 384, 4, 16), 91)
+    K = _randn((1, 384, 2, 16), 92)
+    V = _randn((1, 384, 2, 16), 93)
+    scale = 1.0 / math.sqrt(16)
+    O, _ = oracle.forward(cfg, Q, K, V, idx, cnt, scale)
+    ref, _ = _dense_sdpa(Q, K, V, scale)
+    np.testing.assert_allclose(O, ref, atol=1e-12)
