@@ -65,6 +65,90 @@ def effective_flops(w: wl.Workload, kv_cnt: torch.Tensor) -> float:
     return 4.0 * w.tile * w.block * w.head_dim * float(kv_cnt.sum().item())
 
 
+def vs_block_counts(w: wl.Workload, vert: np.ndarray, slash: np.ndarray) -> np.ndarray:
+    """Blocks per (b, h, t) that the vertical-slash path reads (for its FLOP count): the
+    vertical blocks <= t, the blocks t - delta for the offsets delta <= t, and t."""
+    n = w.n_blocks
+    t = np.arange(n)[:, None]
+    cnt = np.zeros(vert.shape[:2] + (n,), np.int64)
+    for b in range(vert.shape[0]):
+        for h in range(vert.shape[1]):
+            m = np.zeros((n, n), bool)
+            m[np.arange(n), np.arange(n)] = True
+            v = vert[b, h]
+            v = v[:np.argmax(v < 0)] if (v < 0).any() else v
+            isv = np.zeros(n, bool)
+            isv[v[(v >= 0) & (v < n)]] = True
+            m |= isv[None, :] & (np.arange(n)[None, :] <= t)
+            s = slash[b, h]
+            s = s[:np.argmax(s < 0)] if (s < 0).any() else s
+            for dl in s:
+                r = np.arange(dl, n)
+                m[r, r - dl] = True
+            cnt[b, h] = m.sum(axis=1)
+    return cnt
+
+
+def bench_vs(args, w: wl.Workload, nv: int, ns: int):
+    """The vertical-slash path alone (sparse_attn_forward_vs), index given: the VSPrefill
+    page's fused kernel fed by the stand-in index of workloads.vs_index (the trained indexer
+    is not available).  One step = one call on inputs resident in HBM."""
+    log(f"[bench vs] workload {w.name}: generating inputs")
+    ex = {}
+    inp = wl.make_inputs(w, extras=ex)
+    vert, slash = wl.vs_index(w, nv, ns, anchors=ex.get("anchors"))
+    torch.cuda.set_device(0)
+    dev = {k: v.cuda() for k, v in inp.items()}
+    p = api.problem(w)
+    ws = torch.empty(api.forward_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    O = torch.empty((w.batch, w.seqlen, w.n_q_heads, w.head_dim), dtype=torch.bfloat16,
+                    device="cuda")
+    vt, st = torch.from_numpy(vert).cuda(), torch.from_numpy(slash).cuda()
+    scale = 1.0 / math.sqrt(w.head_dim)
+    call = lambda: api.forward_vs(p, dev["Q"], dev["K"], dev["V"], vt, st, scale, ws, O,
+                                  api.SA_BF16)
+    for _ in range(args.warmup):
+        call()
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(s)
+        call()
+        e1.record(s)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    cnt = vs_block_counts(w, vert, slash)
+    flops = 4.0 * w.tile * w.block * w.head_dim * float(cnt.sum())
+    achieved = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "vertical-slash sparse attention tokens/s (1 GPU, index given)",
+        "value": w.batch * w.seqlen * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen,
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "block": w.block, "index": "vertical-slash",
+                   "n_vertical": nv, "n_slash": ns,
+                   "index_source": "planted anchors + slash period" if "anchors" in ex
+                   else "seeded random columns + local window",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "attn_bf16 (sparse_attn_forward_vs)",
+                     "flops_per_launch": flops, "ms_per_launch": ms},
+        "selection": {"mean_blocks_per_tile": float(cnt.mean()),
+                      "density_of_causal": float(cnt.sum()) / (w.batch * w.n_q_heads *
+                                                               w.n_blocks * (w.n_blocks + 1) / 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def time_score_cold(pf: api.Prefill, K, V, reps: int = 10) -> float:
     """Mean duration (ms) of the summary kernel(s) with the caches evicted before each run.
 
@@ -146,6 +230,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=wl.HEADLINE, choices=list(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--vs", default=None, metavar="NV,NS",
+                    help="time the vertical-slash path instead (NV vertical blocks and NS slash "
+                         "offsets per head from the stand-in index)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB, so a "
                          "counter profile of this command can scale its byte counters")
@@ -158,6 +245,10 @@ def main():
     rank = int(os.environ.get("RANK", "0"))
 
     w = wl.WORKLOADS[args.workload]
+    if args.vs:
+        nv, ns = (int(x) for x in args.vs.split(","))
+        bench_vs(args, w, nv, ns)
+        return
     log(f"[bench] workload {w.name}: generating inputs")
     t0 = time.perf_counter()
     inp = wl.make_inputs(w)

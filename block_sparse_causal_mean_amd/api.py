@@ -31,7 +31,7 @@ SA_OAM_OFF, SA_OAM_PRODUCT, SA_OAM_ADDITIVE = 0, 1, 2
 EXPORTS = ("sparse_attn_summary_bytes", "sparse_attn_select_workspace_bytes",
            "sparse_attn_index_width", "sparse_attn_score", "sparse_attn_select",
            "sparse_attn_forward_workspace_bytes", "sparse_attn_forward",
-           "sparse_attn_last_error")
+           "sparse_attn_forward_vs", "sparse_attn_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -76,9 +76,13 @@ def load() -> ctypes.CDLL:
     lib.sparse_attn_forward_workspace_bytes.restype = ctypes.c_size_t
     lib.sparse_attn_forward.argtypes = [PP, P, P, P, P, P, ctypes.c_int32, ctypes.c_float, P,
                                         ctypes.c_size_t, P, ctypes.c_int32, P, P]
+    lib.sparse_attn_forward_vs.argtypes = [PP, P, P, P, P, ctypes.c_int32, P, ctypes.c_int32,
+                                           ctypes.c_float, P, ctypes.c_size_t, P,
+                                           ctypes.c_int32, P, P]
     lib.sparse_attn_last_error.argtypes = []
     lib.sparse_attn_last_error.restype = ctypes.c_char_p
-    for f in ("sparse_attn_score", "sparse_attn_select", "sparse_attn_forward"):
+    for f in ("sparse_attn_score", "sparse_attn_select", "sparse_attn_forward",
+              "sparse_attn_forward_vs"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -191,6 +195,31 @@ def forward(p: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
         _ptr(kv_cnt, "kv_cnt", p.batch * p.n_q_heads * n * 4), W, softmax_scale,
         _ptr(ws, "ws", need), ws_bytes,
         _ptr(O, "O", q_bytes * (4 if out_dtype == SA_F32 else 2)), out_dtype,
+        _ptr(lse, "lse", p.batch * p.n_q_heads * p.seqlen * 4), _stream(stream)))
+
+
+def forward_vs(p: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+               vertical: torch.Tensor, slash: torch.Tensor, softmax_scale: float,
+               ws: torch.Tensor, O: torch.Tensor, out_dtype: int,
+               lse: Optional[torch.Tensor] = None, stream=None):
+    """Sparse attention over a vertical-slash index (sparse_attn_forward_vs): vertical int32
+    [B, Hq, NV] key blocks and slash int32 [B, Hq, NS] block offsets, ascending, distinct,
+    ending at the first negative entry."""
+    B, Hq = p.batch, p.n_q_heads
+    for name, t in (("vertical", vertical), ("slash", slash)):
+        if t.dtype != torch.int32 or t.dim() != 3 or tuple(t.shape[:2]) != (B, Hq):
+            raise ValueError(f"{name} must be int32 [B, Hq, n]")
+    nv, ns = vertical.shape[2], slash.shape[2]
+    q_bytes = p.batch * p.seqlen * p.n_q_heads * p.head_dim
+    kv = p.batch * p.seqlen * p.n_kv_heads * p.head_dim * _elt(p)
+    need = forward_workspace_bytes(p)
+    osz = 4 if out_dtype == SA_F32 else 2
+    _check(load().sparse_attn_forward_vs(
+        ctypes.byref(p), _ptr(Q, "Q", q_bytes * _elt(p)), _ptr(K, "K", kv), _ptr(V, "V", kv),
+        _ptr(vertical, "vertical", B * Hq * nv * 4) if nv else None, nv,
+        _ptr(slash, "slash", B * Hq * ns * 4) if ns else None, ns, float(softmax_scale),
+        _ptr(ws, "ws", need), 0 if ws is None else ws.numel() * ws.element_size(),
+        _ptr(O, "O", q_bytes * osz), out_dtype,
         _ptr(lse, "lse", p.batch * p.n_q_heads * p.seqlen * 4), _stream(stream)))
 
 

@@ -211,6 +211,45 @@ int sparse_attn_forward(const sa_problem* p, const void* Q, const void* K, const
                     "sparse_attn_forward launch");
 }
 
+int sparse_attn_forward_vs(const sa_problem* p, const void* Q, const void* K, const void* V,
+                           const int32_t* vertical, int32_t n_vertical, const int32_t* slash,
+                           int32_t n_slash, float softmax_scale, void* ws, size_t ws_bytes,
+                           void* O, int32_t out_dtype, float* lse, void* stream) {
+  sa::Dims D;
+  int rc = check_problem(p, &D);
+  if (rc != SA_OK) return rc;
+  if (D.dtype != SA_BF16)
+    return fail(SA_ERR_UNSUPPORTED, "the vertical-slash path takes bf16 inputs");
+  if (!Q || !K || !V || !O) return fail(SA_ERR_INVALID, "Q, K, V and O must be non-NULL");
+  if (n_vertical < 0 || n_slash < 0)
+    return fail(SA_ERR_INVALID, "n_vertical and n_slash must be >= 0");
+  if ((n_vertical > 0 && !vertical) || (n_slash > 0 && !slash))
+    return fail(SA_ERR_INVALID, "a non-empty index needs a non-NULL pointer");
+  if (n_vertical + n_slash > sa::kVsMaxEntries)
+    return fail(SA_ERR_UNSUPPORTED, "n_vertical + n_slash = %d exceeds %d",
+                n_vertical + n_slash, sa::kVsMaxEntries);
+  const size_t need = sa::forward_ws_bytes(D);
+  if (!ws || ws_bytes < need)
+    return fail(SA_ERR_INVALID, "forward workspace too small: %zu < %zu bytes", ws_bytes, need);
+  if (out_dtype != SA_F32 && out_dtype != SA_BF16)
+    return fail(SA_ERR_INVALID, "out_dtype must be SA_F32 or SA_BF16");
+  if (!isfinite(softmax_scale)) return fail(SA_ERR_INVALID, "softmax_scale is not finite");
+  if ((unsigned long long)D.N * D.Hkv * D.d * 2 >= (1ull << 32))
+    return fail(SA_ERR_UNSUPPORTED,
+                "seqlen * n_kv_heads * head_dim * 2 = %llu bytes of K per batch element: the "
+                "bf16 kernel addresses a batch element's keys with 32-bit offsets (< 2^32)",
+                (unsigned long long)D.N * D.Hkv * D.d * 2);
+  g_err.clear();
+  sa::VsIndex vs;
+  vs.vert = vertical;
+  vs.slash = slash;
+  vs.nv = n_vertical;
+  vs.ns = n_slash;
+  return hip_status(sa::launch_forward_vs(D, Q, K, V, vs, softmax_scale, ws, O, out_dtype, lse,
+                                          static_cast<hipStream_t>(stream)),
+                    "sparse_attn_forward_vs launch");
+}
+
 const char* sparse_attn_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"

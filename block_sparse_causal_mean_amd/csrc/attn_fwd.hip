@@ -466,13 +466,102 @@ __device__ __forceinline__ void stage_segment(const int32_t* __restrict__ list,
   }
 }
 
-template <int D, int QH, int NW>
+// Appends to out the entries of row[0 .. len) before its first negative one that lie in
+// [0, t], mapped by f, in row order; returns their number.  Run by one wave.
+template <typename F>
+__device__ __forceinline__ int compact_row(const int32_t* __restrict__ row, int len, int t,
+                                           int* out, int lane, F f) {
+  int n = 0;
+  for (int base = 0; base < len; base += 64) {
+    const int e = base + lane;
+    const int x = e < len ? row[e] : -1;
+    const unsigned long long negm = __ballot(e < len && x < 0);
+    const int first_neg = negm ? __builtin_ctzll(negm) : 64;
+    const bool valid = e < len && lane < first_neg && x <= t;
+    const unsigned long long vm = __ballot(valid);
+    if (valid) out[n + __builtin_popcountll(vm & ((1ull << lane) - 1ull))] = f(x);
+    n += __builtin_popcountll(vm);
+    if (negm) break;
+  }
+  return n;
+}
+
+// Stages query tile t's list from a vertical-slash index (VSPrefill page, Metodologia B.3:
+// the fused kernel merges the vertical and the slash indices on the fly, with Merge Path, and
+// never materialises per-tile lists).  Run by wave 0; the workgroup waits afterwards.
+//   A = the vertical blocks <= t, ascending (vrow is ascending);
+//   B = t - delta for the slash offsets delta <= t, kept in descending order (srow is
+//       ascending);
+// each element's place in the merged order is its index plus its co-rank (the number of
+// smaller elements of the other list, a binary search), so a block present in both lists
+// lands on two adjacent places; those and any entry outside [0, t] (only possible when the
+// inputs break the ascending-and-distinct contract) are dropped, and the diagonal block t is
+// appended when neither list holds it.  `scratch` holds 2 (nv + ns) ints.
+__device__ void stage_vs(const int32_t* __restrict__ vrow, int nv,
+                         const int32_t* __restrict__ srow, int ns, int t, int w, int lane,
+                         int* lst, int* seg_info, int* scratch) {
+  if (w == 0) {
+    int* A = scratch;
+    int* Bd = scratch + nv;
+    int* M = scratch + nv + ns;
+    const int na = compact_row(vrow, nv, t, A, lane, [](int x) { return x; });
+    const int nb = compact_row(srow, ns, t, Bd, lane, [t](int x) { return t - x; });
+    for (int p = lane; p < na + nb; p += 64) M[p] = -1;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    for (int i = lane; i < na; i += 64) {  // A[i]: i + #{B < a}
+      const int a = A[i];
+      int lo = 0, hi = nb;  // first k with Bd[k] < a (Bd descending)
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (Bd[mid] < a) hi = mid; else lo = mid + 1;
+      }
+      M[i + (nb - lo)] = a;
+    }
+    for (int k = lane; k < nb; k += 64) {  // Bd[k] (ascending place nb-1-k): + #{A <= b}
+      const int b = Bd[k];
+      int lo = 0, hi = na;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (A[mid] <= b) lo = mid + 1; else hi = mid;
+      }
+      M[(nb - 1 - k) + lo] = b;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    int u = 0;
+    for (int base = 0; base < na + nb; base += 64) {
+      const int p = base + lane;
+      const int x = p < na + nb ? M[p] : -1;
+      const int prev = p > 0 && p < na + nb ? M[p - 1] : -1;
+      const bool keep = x >= 0 && x <= t && x != prev;
+      const unsigned long long km = __ballot(keep);
+      if (keep) lst[u + __builtin_popcountll(km & ((1ull << lane) - 1ull))] = x;
+      u += __builtin_popcountll(km);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int lastv = u > 0 ? lst[u - 1] : -1;
+    if (lastv != t) {
+      if (lane == 0) lst[u] = t;
+      ++u;
+    }
+    if (lane == 0) {
+      seg_info[0] = u;
+      seg_info[1] = u - 1;  // the diagonal is the last (largest) block
+      seg_info[2] = 0;
+      seg_info[3] = 1;
+    }
+  }
+  __syncthreads();
+}
+
+// D head dim, QH 32-row query groups per wave, NW waves per workgroup; VS: the tile's list
+// comes from a vertical-slash index (stage_vs) instead of kv_idx / kv_cnt.
+template <int D, int QH, int NW, bool VS>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW>::WPE))) void attn_bf16(
     Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vp, const int32_t* __restrict__ kv_idx,
-    const int32_t* __restrict__ kv_cnt, int W, float scale_log2, void* __restrict__ O,
-    int out_f32, float* __restrict__ lse) {
+    const int32_t* __restrict__ kv_cnt, int W, VsIndex vs, float scale_log2,
+    void* __restrict__ O, int out_f32, float* __restrict__ lse) {
   using C = Cfg<D, QH, NW>;
   constexpr int BLK = C::BLK, NSUB = C::NSUB, DC = C::DC, DT = C::DT, LPW = C::LPW;
   // Ring of NR slots, each a K step image followed by a V^T step image.
@@ -488,8 +577,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW>::WPE))) void attn_bf16(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
   const int l32 = lane & 31, hi = lane >> 5;
   const size_t bht = ((size_t)b * dm.Hq + h) * dm.n + t;
-  const int32_t* list = kv_idx + bht * W;
-  const int cnt = max(0, min(kv_cnt[bht], W));
+  const int32_t* list = VS ? nullptr : kv_idx + bht * W;
+  const int cnt = VS ? 0 : max(0, min(kv_cnt[bht], W));
   const int qbase = w * 32 * QH + l32;  // this lane's first query row within the tile
   const int rstride = dm.Hkv * D;
   const uint16_t* Kg = K + ((size_t)b * dm.N * dm.Hkv + g) * D;
@@ -539,8 +628,14 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW>::WPE))) void attn_bf16(
 
   int seg_start = 0;
   for (;;) {
-    stage_segment<C::LCAP>(list, kv_cnt, cnt, bht, dm, h, t, W, seg_start, w, lane, lst, seg_info,
-                           reinterpret_cast<int*>(ring), C::NR * SLOT / 4);
+    if constexpr (VS) {
+      const size_t bh = (size_t)b * dm.Hq + h;
+      stage_vs(vs.vert + bh * vs.nv, vs.nv, vs.slash + bh * vs.ns, vs.ns, t, w, lane, lst,
+               seg_info, reinterpret_cast<int*>(ring));
+    } else {
+      stage_segment<C::LCAP>(list, kv_cnt, cnt, bht, dm, h, t, W, seg_start, w, lane, lst,
+                             seg_info, reinterpret_cast<int*>(ring), C::NR * SLOT / 4);
+    }
     const int U = seg_info[0], diag_e = seg_info[1], next_start = seg_info[2];
     const int seg_done = seg_info[3];
     const int nsteps = U * NSUB;
@@ -713,10 +808,11 @@ __global__ __launch_bounds__(BLK) void attn_f32(Dims dm, const float* __restrict
     lse[((size_t)b * dm.Hq + h) * dm.N + qrow] = l > 0.0f ? m + __logf(l) : -INFINITY;
 }
 
-template <int D, int QH, int NW>
+template <int D, int QH, int NW, bool VS>
 hipError_t launch_bf16(const Dims& dm, const void* Q, const void* K, const void* V,
-                       const int32_t* kv_idx, const int32_t* kv_cnt, int W, float scale,
-                       void* ws, void* O, int out_dtype, float* lse, hipStream_t s) {
+                       const int32_t* kv_idx, const int32_t* kv_cnt, int W, const VsIndex& vs,
+                       float scale, void* ws, void* O, int out_dtype, float* lse,
+                       hipStream_t s) {
   uint16_t* Vp = static_cast<uint16_t*>(ws);
   const unsigned nsteps = (unsigned)((size_t)dm.B * dm.Hkv * (dm.N / kStep));
   hipLaunchKernelGGL((pack_v<D>), dim3(nsteps), dim3(kPackThreads), 0, s, dm,
@@ -724,9 +820,10 @@ hipError_t launch_bf16(const Dims& dm, const void* Q, const void* K, const void*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
-  hipLaunchKernelGGL((attn_bf16<D, QH, NW>), dim3(grid), dim3(64 * NW), 0, s, dm,
+  hipLaunchKernelGGL((attn_bf16<D, QH, NW, VS>), dim3(grid), dim3(64 * NW), 0, s, dm,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K), Vp,
-                     kv_idx, kv_cnt, W, scale * kLog2e, O, out_dtype == SA_F32 ? 1 : 0, lse);
+                     kv_idx, kv_cnt, W, vs, scale * kLog2e, O, out_dtype == SA_F32 ? 1 : 0,
+                     lse);
   return hipGetLastError();
 }
 
@@ -745,6 +842,23 @@ hipError_t launch_f32(const Dims& dm, const void* Q, const void* K, const void* 
   return hipGetLastError();
 }
 
+template <bool VS>
+hipError_t launch_bf16_shape(const Dims& dm, const void* Q, const void* K, const void* V,
+                             const int32_t* kv_idx, const int32_t* kv_cnt, int W,
+                             const VsIndex& vs, float scale, void* ws, void* O, int out_dtype,
+                             float* lse, hipStream_t s) {
+  if (dm.d == 64)
+    return dm.blk == 64 ? launch_bf16<64, 1, 2, VS>(dm, Q, K, V, kv_idx, kv_cnt, W, vs, scale,
+                                                      ws, O, out_dtype, lse, s)
+                        : launch_bf16<64, ATTN_QH, 4 / ATTN_QH, VS>(
+                              dm, Q, K, V, kv_idx, kv_cnt, W, vs, scale, ws, O, out_dtype, lse, s);
+  if (dm.blk == 64)
+    return launch_bf16<128, 1, 2, VS>(dm, Q, K, V, kv_idx, kv_cnt, W, vs, scale, ws, O,
+                                      out_dtype, lse, s);
+  return launch_bf16<128, ATTN_QH, 4 / ATTN_QH, VS>(dm, Q, K, V, kv_idx, kv_cnt, W, vs, scale, ws,
+                                                    O, out_dtype, lse, s);
+}
+
 }  // namespace
 
 size_t forward_ws_bytes(const Dims& dm) {
@@ -756,19 +870,9 @@ size_t forward_ws_bytes(const Dims& dm) {
 hipError_t launch_forward(const Dims& dm, const void* Q, const void* K, const void* V,
                           const int32_t* kv_idx, const int32_t* kv_cnt, int W, float scale,
                           void* ws, void* O, int out_dtype, float* lse, hipStream_t s) {
-  if (dm.dtype == SA_BF16) {
-    if (dm.d == 64)
-      return dm.blk == 64 ? launch_bf16<64, 1, 2>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
-                                                  out_dtype, lse, s)
-                          : launch_bf16<64, ATTN_QH, 4 / ATTN_QH>(dm, Q, K, V, kv_idx, kv_cnt,
-                                                                   W, scale, ws, O, out_dtype,
-                                                                   lse, s);
-    if (dm.blk == 64)
-      return launch_bf16<128, 1, 2>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O, out_dtype, lse,
-                                    s);
-    return launch_bf16<128, ATTN_QH, 4 / ATTN_QH>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, ws, O,
-                                                  out_dtype, lse, s);
-  }
+  if (dm.dtype == SA_BF16)
+    return launch_bf16_shape<false>(dm, Q, K, V, kv_idx, kv_cnt, W, VsIndex{}, scale, ws, O,
+                                    out_dtype, lse, s);
   if (dm.d == 64)
     return dm.blk == 64
                ? launch_f32<64, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
@@ -776,6 +880,13 @@ hipError_t launch_forward(const Dims& dm, const void* Q, const void* K, const vo
   return dm.blk == 64
              ? launch_f32<128, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
              : launch_f32<128, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s);
+}
+
+hipError_t launch_forward_vs(const Dims& dm, const void* Q, const void* K, const void* V,
+                             const VsIndex& vs, float scale, void* ws, void* O, int out_dtype,
+                             float* lse, hipStream_t s) {
+  return launch_bf16_shape<true>(dm, Q, K, V, nullptr, nullptr, 1, vs, scale, ws, O, out_dtype,
+                                 lse, s);
 }
 
 }  // namespace sa

@@ -157,9 +157,21 @@ hipError_t launch_pool(const Dims& D, const void* K, const void* V, float* summ,
 hipError_t launch_select(const Dims& D, const BudgetDev& bd, const void* Q, const float* summ,
                          char* ws, int32_t* kv_idx, int32_t* kv_cnt, float* sigma,
                          float* sigma_bar, uint8_t* gate, float* tau, hipStream_t s);
+// Vertical-slash index of the forward pass (per query head: vertical key blocks, ascending;
+// slash block offsets, ascending; each list ends at its first negative entry).
+struct VsIndex {
+  const int32_t* vert = nullptr;
+  const int32_t* slash = nullptr;
+  int nv = 0, ns = 0;
+};
+constexpr int kVsMaxEntries = 511;  // nv + ns: the merged list plus the diagonal fit in LDS
+
 size_t forward_ws_bytes(const Dims& D);
 hipError_t launch_forward(const Dims& D, const void* Q, const void* K, const void* V,
                           const int32_t* kv_idx, const int32_t* kv_cnt, int W, float scale,
                           void* ws, void* O, int out_dtype, float* lse, hipStream_t s);
+hipError_t launch_forward_vs(const Dims& D, const void* Q, const void* K, const void* V,
+                             const VsIndex& vs, float scale, void* ws, void* O, int out_dtype,
+                             float* lse, hipStream_t s);
 
 }  // namespace sa

@@ -146,10 +146,13 @@ def _unit(v: np.ndarray) -> np.ndarray:
     return v / np.linalg.norm(v)
 
 
-def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
+def make_inputs(w: Workload, seed: Optional[int] = None,
+                extras: Optional[dict] = None) -> Dict[str, torch.Tensor]:
     """Draw Q [B,N,Hq,d], K [B,N,Hkv,d], V [B,N,Hkv,d] (contiguous BSHD, CPU tensors).
 
-    The tensors hold values exactly representable in the workload dtype.
+    The tensors hold values exactly representable in the workload dtype.  If `extras` is a
+    dict, planted workloads also leave their anchor positions there ("anchors": int64
+    [B, Hkv, 64]).
     """
     rng = np.random.default_rng(w.seed if seed is None else seed)
     B, N, Hq, Hkv, d = w.batch, w.seqlen, w.n_q_heads, w.n_kv_heads, w.head_dim
@@ -167,6 +170,7 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tens
         scale = rng.lognormal(0.0, w.v_logn_sigma, size=(B, N, Hkv, 1)).astype(np.float32)
         v *= scale
 
+    anchor_pos = np.zeros((B, Hkv, min(64, N)), np.int64)
     if w.planted:
         # Vertical stripes: per (batch, kv head) a unit direction u and 64 distinct anchor
         # positions; anchors' keys and every query of the group get +4u, which adds +16 to
@@ -183,6 +187,7 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tens
                 e2 = e2 - (e2 @ u) * u - (e2 @ e1) * e1
                 e2 = _unit(e2)
                 anchors = rng.choice(N, size=min(64, N), replace=False)
+                anchor_pos[b, g] = anchors
                 k[b, anchors, g, :] += (4.0 * u).astype(np.float32)
                 slash = (4.0 * (np.cos(theta)[:, None] * e1[None, :]
                                 + np.sin(theta)[:, None] * e2[None, :])).astype(np.float32)
@@ -191,7 +196,45 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tens
                     h = g * G + r
                     q[b, :, h, :] += (4.0 * u).astype(np.float32)[None, :] + slash
 
+    if extras is not None and w.planted:
+        extras["anchors"] = anchor_pos
     return {"Q": _to_dtype(q, dt), "K": _to_dtype(k, dt), "V": _to_dtype(v, dt)}
+
+
+SLASH_PERIOD = 256  # tokens: the planted slash pattern's period
+
+
+def vs_index(w: Workload, n_vertical: int, n_slash: int, anchors: Optional[np.ndarray] = None,
+             seed: int = 0):
+    """A stand-in for the VSPrefill page's trained indexer (unavailable here): seeded
+    vertical-slash indices for the vertical-slash attention path, int32 [B, Hq, n_vertical]
+    key blocks and [B, Hq, n_slash] block offsets, each ascending, distinct, -1 padded.
+
+    With the planted workload's anchor positions (make_inputs' extras): a head's vertical
+    blocks are the blocks holding its kv group's anchors (the smallest n_vertical of them), and
+    its slash offsets are 0 and 1 (the local window) followed by multiples of the planted
+    slash period in blocks.  Without: n_vertical distinct blocks drawn per head, and the local
+    window 0 .. n_slash - 1.
+    """
+    B, Hq, n, G = w.batch, w.n_q_heads, w.n_blocks, w.n_q_heads // w.n_kv_heads
+    vert = np.full((B, Hq, max(n_vertical, 1)), -1, np.int32)[..., :n_vertical]
+    slash = np.full((B, Hq, max(n_slash, 1)), -1, np.int32)[..., :n_slash]
+    rng = np.random.default_rng(seed)
+    for b in range(B):
+        for h in range(Hq):
+            if anchors is not None:
+                blocks = np.unique(anchors[b, h // G] // w.block)[:n_vertical]
+            else:
+                blocks = np.sort(rng.choice(n, size=min(n_vertical, n), replace=False))
+            vert[b, h, :len(blocks)] = blocks
+            if anchors is not None and SLASH_PERIOD % w.block == 0:
+                p = SLASH_PERIOD // w.block
+                offs = [0, 1] + [p * i for i in range(1, n) if p * i > 1]
+            else:
+                offs = list(range(n))
+            offs = sorted(set(o for o in offs if o < n))[:n_slash]
+            slash[b, h, :len(offs)] = offs
+    return np.ascontiguousarray(vert), np.ascontiguousarray(slash)
 
 
 def tensor_digest(t: torch.Tensor) -> str:

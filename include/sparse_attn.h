@@ -172,6 +172,28 @@ int sparse_attn_forward(const sa_problem* p, const void* Q, const void* K, const
                         float softmax_scale, void* ws, size_t ws_bytes, void* O,
                         int32_t out_dtype, float* lse, void* stream);
 
+/*
+ * Sparse attention over a vertical-slash index (VSPrefill page, Metodologia B.3: the fused
+ * kernel merges the vertical and the slash indices on the fly, with Merge Path, instead of
+ * reading per-tile lists).  Block granularity: query tile t reads
+ *   the vertical key blocks v <= t,  the blocks t - delta for the slash offsets delta <= t,
+ *   and its diagonal block t,
+ * each block once, then attends exactly as sparse_attn_forward does over that list.
+ *   vertical   int32 [B, Hq, n_vertical]: key-block indices per query head, ascending and
+ *              distinct; the list ends at n_vertical or at its first negative entry.
+ *   slash      int32 [B, Hq, n_slash]: block offsets >= 0 per query head, ascending and
+ *              distinct; same end rule.  (Offset 0, the diagonal, is implied.)
+ *   n_vertical, n_slash >= 0 with n_vertical + n_slash <= 511, else SA_ERR_UNSUPPORTED.
+ *   Other arguments as for sparse_attn_forward; ws is required.
+ * bf16 inputs only (SA_ERR_UNSUPPORTED otherwise).  Indices that break the ascending-and-
+ * distinct contract give wrong lists, never an access outside the tile's causal blocks.
+ * The indices come from the caller (the pages' trained indexer, or any other source).
+ */
+int sparse_attn_forward_vs(const sa_problem* p, const void* Q, const void* K, const void* V,
+                           const int32_t* vertical, int32_t n_vertical, const int32_t* slash,
+                           int32_t n_slash, float softmax_scale, void* ws, size_t ws_bytes,
+                           void* O, int32_t out_dtype, float* lse, void* stream);
+
 /* The calling thread's last error message ("" if none).  Valid until its next call. */
 const char* sparse_attn_last_error(void);
 

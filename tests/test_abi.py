@@ -190,3 +190,23 @@ def test_binding_refuses_host_tensors(lib):
     x = torch.zeros(4)
     with pytest.raises(ValueError):
         api.score(api.problem(w), x, None, x)
+
+
+def test_forward_vs_validation(lib):
+    p = _ok_problem()
+    big = 1 << 40
+    ok_ws = api.forward_workspace_bytes(p)
+
+    def call(prob=p, vert=FAKE, nv=4, slash=FAKE, ns=4, ws_bytes=ok_ws, out=api.SA_BF16):
+        return lib.sparse_attn_forward_vs(ctypes.byref(prob), FAKE, FAKE, FAKE, vert, nv, slash,
+                                          ns, 0.1, FAKE, ws_bytes, FAKE, out, None, None)
+
+    f32 = api.problem(wl.WORKLOADS["tiny_ref"])
+    assert call(prob=f32, ws_bytes=big) == api.SA_ERR_UNSUPPORTED
+    assert "bf16" in api.last_error()
+    assert call(nv=300, ns=212) == api.SA_ERR_UNSUPPORTED
+    assert call(nv=-1) == api.SA_ERR_INVALID
+    assert call(vert=None) == api.SA_ERR_INVALID
+    assert call(slash=None, ns=2) == api.SA_ERR_INVALID
+    assert call(ws_bytes=ok_ws - 1) == api.SA_ERR_INVALID
+    assert call(out=7) == api.SA_ERR_INVALID
