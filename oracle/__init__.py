@@ -56,6 +56,8 @@ def _load():
                                    ctypes.c_int64, P, P, P]
     lib.oracle_budget.argtypes = [cfgp, ctypes.c_int]
     lib.oracle_vs_lists.argtypes = [cfgp, P, ctypes.c_int, P, ctypes.c_int, P, P, ctypes.c_int]
+    lib.oracle_decode_art.argtypes = [cfgp, P, P, P, ctypes.c_double, ctypes.c_int,
+                                      ctypes.c_double, ctypes.c_double, ctypes.c_int, P, P, P, P]
     _lib = lib
     return lib
 
@@ -230,6 +232,50 @@ def vs_lists(cfg: OracleCfg, vert, slash):
     if rc != 0:
         raise RuntimeError(f"oracle_vs_lists failed ({rc})")
     return idx, cnt
+
+
+def decode_art(cfg: OracleCfg, Q, K, V, softmax_scale: float, probe: int, tau: float,
+               phi: float, patience: int, keep_partials: bool = True) -> dict:
+    """Decode attention with run-time termination (oracle.c, oracle_decode_art), fp64.
+    Q [B, Hq, d] (one token per sequence and head), K, V [B, N, Hkv, d].  Returns dscale,
+    ddir [B, Hq, n] (the probe's norm and direction changes per step of the traversal order),
+    stop [B, Hq] (blocks processed under the rule) and, if keep_partials, Opart
+    [B, Hq, n, d] (the normalised partial output after each step)."""
+    lib = _load()
+    B, Hq, n, d = cfg.batch, cfg.n_q_heads, cfg.seqlen // cfg.block, cfg.head_dim
+    Qa = _arr(Q, cfg)
+    if Qa.size != B * Hq * d:
+        raise ValueError("Q must hold B * Hq * d elements")
+    dsc = np.zeros((B, Hq, n), np.float64)
+    ddr = np.zeros((B, Hq, n), np.float64)
+    Op = np.zeros((B, Hq, n, d), np.float64) if keep_partials else None
+    stop = np.zeros((B, Hq), np.int32)
+    rc = lib.oracle_decode_art(ctypes.byref(cfg), _p(Qa), _p(_arr(K, cfg)), _p(_arr(V, cfg)),
+                               float(softmax_scale), int(probe), float(tau), float(phi),
+                               int(patience), _p(dsc), _p(ddr), _p(Op), _p(stop))
+    if rc != 0:
+        raise RuntimeError(f"oracle_decode_art failed ({rc})")
+    return {"dscale": dsc, "ddir": ddr, "stop": stop, "Opart": Op}
+
+
+def art_stop(dscale, ddir, tau: float, phi: float, patience: int):
+    """The stopping rule applied to given per-step metrics (the same rule oracle.c applies):
+    blocks processed per (b, h)."""
+    B, Hq, n = dscale.shape
+    out = np.full((B, Hq), n, np.int32)
+    if patience <= 0:
+        return out
+    stable = (dscale < tau) & (ddir < phi)
+    stable[..., 0] = False
+    for b in range(B):
+        for h in range(Hq):
+            run = 0
+            for k in range(1, n):
+                run = run + 1 if stable[b, h, k] else 0
+                if run >= patience:
+                    out[b, h] = k + 1
+                    break
+    return out
 
 
 def threads() -> int:

@@ -568,6 +568,104 @@ int oracle_vs_lists(const oc_cfg* c, const int32_t* vert, int NV, const int32_t*
   return fail ? -fail : 0;
 }
 
+/* ------------------------------------------- decode with run-time termination (ART) */
+
+/* ART page, sections 2.1-2.4: a decode query attends to the K/V cache block by block with an
+ * online softmax; after each block the partial output's probe vector is compared with the
+ * previous one, and the traversal stops once both the change of its L2 norm (below tau) and
+ * its change of direction, 1 - cosine similarity (below phi), have held for `patience`
+ * consecutive blocks.  Block 0 (the attention sink) is always evaluated first; the other
+ * blocks follow recency-first (n-1, n-2, ..., 1), an order the online softmax is invariant to.
+ * This build's readings: the probe is the partial output's first `probe` coordinates; the
+ * stability of step k >= 1 compares steps k and k-1; stopping after step k (k >= patience)
+ * keeps O^(k), the normalised output over the first k + 1 blocks of the order; patience 0
+ * never stops.
+ *
+ * Q [B, Hq, d] (the decode tokens), K, V [B, N, Hkv, d]; the query attends to keys 0 .. N-1.
+ * Everything in fp64.  Outputs per (b, h): dscale[k], ddir[k] for k = 0 .. n-1 (step 0 has
+ * no predecessor: 0 and 0), the partial outputs O^(k) [n][d] when Opart is not NULL, and
+ * stop = the number of blocks the rule processes (n when it never stops). */
+int oracle_decode_art(const oc_cfg* c, const void* Q, const void* K, const void* V,
+                      double softmax_scale, int probe, double tau, double phi, int patience,
+                      double* dscale, double* ddir, double* Opart, int32_t* stop) {
+  const int N = c->seqlen, blk = c->block, n = N / blk, d = c->head_dim;
+  const int Hq = c->n_q_heads, Hkv = c->n_kv_heads, G = Hq / Hkv;
+  if (probe < 1 || probe > d) return -2;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+    double* prev = (double*)malloc(sizeof(double) * (size_t)probe);
+    double* s = (double*)malloc(sizeof(double) * (size_t)blk);
+    if (!acc || !prev || !s) {
+#pragma omp atomic write
+      fail = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int bh = 0; bh < c->batch * Hq; ++bh) {
+      if (!acc || !prev || !s) continue;
+      const int b = bh / Hq, h = bh % Hq, g = h / G;
+      double m = -INFINITY, l = 0.0;
+      for (int ch = 0; ch < d; ++ch) acc[ch] = 0.0;
+      for (int i = 0; i < probe; ++i) prev[i] = 0.0;
+      int run = 0, stopped = n;
+      for (int k = 0; k < n; ++k) {
+        const int j = k == 0 ? 0 : n - k; /* block 0, then n-1, n-2, ..., 1 */
+        double bm = -INFINITY;
+        for (int r = 0; r < blk; ++r) {
+          const int64_t pos = (int64_t)j * blk + r;
+          double dot = 0.0;
+          for (int ch = 0; ch < d; ++ch)
+            dot += (double)elem(Q, c->in_dtype, ((int64_t)b * Hq + h) * d + ch) *
+                   (double)elem(K, c->in_dtype, bshd(c, b, pos, g, Hkv, ch));
+          s[r] = dot * softmax_scale;
+          if (s[r] > bm) bm = s[r];
+        }
+        const double mn = bm > m ? bm : m;
+        const double a = exp(m - mn);
+        l *= a;
+        for (int ch = 0; ch < d; ++ch) acc[ch] *= a;
+        for (int r = 0; r < blk; ++r) {
+          const double w = exp(s[r] - mn);
+          l += w;
+          const int64_t pos = (int64_t)j * blk + r;
+          for (int ch = 0; ch < d; ++ch)
+            acc[ch] += w * (double)elem(V, c->in_dtype, bshd(c, b, pos, g, Hkv, ch));
+        }
+        m = mn;
+        double nx = 0.0, np = 0.0, dp = 0.0;
+        for (int i = 0; i < probe; ++i) {
+          const double x = acc[i] / l;
+          nx += x * x;
+          np += prev[i] * prev[i];
+          dp += x * prev[i];
+        }
+        nx = sqrt(nx);
+        np = sqrt(np);
+        double dsc = 0.0, ddr = 0.0;
+        if (k > 0) {
+          dsc = fabs(nx - np);
+          ddr = (nx > 0.0 && np > 0.0) ? 1.0 - dp / (nx * np) : 1.0;
+        }
+        dscale[(int64_t)bh * n + k] = dsc;
+        ddir[(int64_t)bh * n + k] = ddr;
+        for (int i = 0; i < probe; ++i) prev[i] = acc[i] / l;
+        if (Opart)
+          for (int ch = 0; ch < d; ++ch) Opart[((int64_t)bh * n + k) * d + ch] = acc[ch] / l;
+        if (k > 0 && stopped == n && patience > 0) {
+          run = (dsc < tau && ddr < phi) ? run + 1 : 0;
+          if (run >= patience) stopped = k + 1;
+        }
+      }
+      stop[bh] = stopped;
+    }
+    free(acc);
+    free(prev);
+    free(s);
+  }
+  return fail ? -1 : 0;
+}
+
 /* Budget for tile t, exported so the tests can pin the schedule on its own. */
 int oracle_budget(const oc_cfg* c, int t) { return budget(c, t); }
 

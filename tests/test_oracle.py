@@ -558,3 +558,61 @@ def test_vs_lists_all_vertical_is_dense_causal_attention():
     O, _ = oracle.forward(cfg, Q, K, V, idx, cnt, scale)
     ref, _ = _dense_sdpa(Q, K, V, scale)
     np.testing.assert_allclose(O, ref, atol=1e-12)
+
+
+# ------------------------------------------------- decode with run-time termination (ART)
+
+def _art_case(tau=1.0, phi=1.0, patience=0, d=64):
+    w = _small(seqlen=512, n_q_heads=1, n_kv_heads=1, head_dim=d, block=64)
+    cfg = oracle.make_cfg(w)
+    Q = np.zeros((1, 1, d), np.float32)
+    K = _randn((1, 512, 1, d), 81).numpy()
+    V = np.zeros((1, 512, 1, d), np.float32)
+    V[0, :, 0, 0] = 4.0
+    V[0, 7 * 64:8 * 64, 0, 1] = 4.0
+    return cfg, Q, K, V
+
+
+def test_art_golden():
+    """ART page, sections 2.2-2.4: hand-worked probe metrics and stopping points."""
+    g = json.load(open(os.path.join(GOLDEN, "art_decode.json")))
+    cfg, Q, K, V = _art_case()
+    for case in g["cases"]:
+        r = oracle.decode_art(cfg, Q, K, V, 0.125, 16, case["tau"], case["phi"],
+                              case["patience"])
+        np.testing.assert_allclose(r["dscale"][0, 0], g["dscale"], atol=g["metric_tolerance"])
+        np.testing.assert_allclose(r["ddir"][0, 0], g["ddir"], atol=g["metric_tolerance"])
+        assert int(r["stop"][0, 0]) == case["stop"], case
+        assert int(oracle.art_stop(r["dscale"], r["ddir"], case["tau"], case["phi"],
+                                   case["patience"])[0, 0]) == case["stop"]
+
+
+def test_art_full_traversal_is_dense_decode_attention():
+    """Without stopping, the last partial output is plain softmax attention of the decode
+    query over every cached key (fp64 PyTorch), whatever the traversal order."""
+    w = _small(batch=2, seqlen=640, n_q_heads=4, n_kv_heads=2, head_dim=32, block=64)
+    cfg = oracle.make_cfg(w)
+    Q = _randn((2, 4, 32), 83)
+    K = _randn((2, 640, 2, 32), 84)
+    V = _randn((2, 640, 2, 32), 85)
+    scale = 1.0 / math.sqrt(32)
+    r = oracle.decode_art(cfg, Q, K, V, scale, 16, 1.0, 1.0, 0)
+    assert (r["stop"] == 10).all()
+    q = Q.double()[:, :, None, :]                                  # [B, Hq, 1, d]
+    k = K.double().repeat_interleave(2, dim=2).permute(0, 2, 1, 3)   # [B, Hq, N, d]
+    v = V.double().repeat_interleave(2, dim=2).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale)[:, :, 0]
+    np.testing.assert_allclose(r["Opart"][:, :, -1], ref.numpy(), atol=1e-12)
+
+
+def test_art_constant_values_stop_after_patience():
+    """V constant: every partial output equals it, both changes are zero from the second
+    block on, so the rule stops after exactly patience + 1 blocks."""
+    w = _small(seqlen=1024, n_q_heads=2, n_kv_heads=1, head_dim=16, block=64)
+    cfg = oracle.make_cfg(w)
+    Q = _randn((1, 2, 16), 86)
+    K = _randn((1, 1024, 1, 16), 87)
+    V = torch.ones((1, 1024, 1, 16)) * 0.5
+    for p in (1, 3, 7):
+        r = oracle.decode_art(cfg, Q, K, V, 0.25, 16, 1e-9, 1e-9, p)
+        assert (r["stop"] == p + 1).all(), p
