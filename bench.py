@@ -149,6 +149,88 @@ def bench_vs(args, w: wl.Workload, nv: int, ns: int):
     print(json.dumps(out), flush=True)
 
 
+def bench_decode(args, w: wl.Workload):
+    """Decode with run-time termination (ART page), one step = one decode token per sequence
+    and query head over the resident K/V cache.  Times the rule's run and, for comparison, the
+    full traversal (patience 0).  HBM traffic = the K/V blocks each (sequence, kv head)
+    workgroup streams: up to the last of its query heads to stop."""
+    log(f"[bench decode] workload {w.name}: generating inputs")
+    t0 = time.perf_counter()
+    inp = wl.make_decode_inputs(w)
+    log(f"[bench decode] inputs ready in {time.perf_counter() - t0:.1f}s")
+    torch.cuda.set_device(0)
+    dev = {k: v.cuda() for k, v in inp.items()}
+    p = api.problem(w)
+    O = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    done = torch.empty((w.batch, w.n_q_heads), dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(w.head_dim)
+    s = torch.cuda.current_stream()
+
+    def timed(patience):
+        call = lambda: api.decode_art(p, dev["Q"], dev["K"], dev["V"], scale, w.art_tau,
+                                      w.art_phi, patience, O, api.SA_BF16, done)
+        for _ in range(args.warmup):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for e0, e1 in ev:
+            e0.record(s)
+            call()
+            e1.record(s)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t_start,
+                float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])))
+
+    el_full, ms_full = timed(0)
+    el, ms = timed(w.art_patience)
+    d = done.cpu().numpy()
+    G = w.n_q_heads // w.n_kv_heads
+    streamed = d.reshape(w.batch, w.n_kv_heads, G).max(axis=2)
+    n = w.seqlen // w.block
+    kv_block = w.block * w.head_dim * 2 * 2
+    bytes_art = float(streamed.sum()) * kv_block + 2 * w.batch * w.n_q_heads * w.head_dim * 2
+    bytes_full = float(w.batch * w.n_kv_heads * n) * kv_block + 2 * w.batch * w.n_q_heads * w.head_dim * 2
+    gbs = bytes_art / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "decode tokens/s with run-time termination (1 GPU)",
+        "value": w.batch * args.steps / el, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": el * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "cached_tokens": w.seqlen,
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "block": w.block, "tau": w.art_tau, "phi": w.art_phi,
+                   "patience": w.art_patience, "probe": 16, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "art_decode (sparse_attn_decode_art)", "bytes_per_launch": bytes_art,
+                     "ms_per_launch": ms},
+        "full_traversal": {"ms_per_launch": ms_full, "bytes_per_launch": bytes_full,
+                           "achieved_GBs": bytes_full / (ms_full * 1e-3) / 1e9,
+                           "tokens_per_s": w.batch * args.steps / el_full},
+        "termination": {"mean_blocks_per_head": float(d.mean()), "blocks": n,
+                        "mean_blocks_streamed_per_kv_head": float(streamed.mean()),
+                        "speedup_vs_full": ms_full / ms},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        nb = w.batch
+        wb = w.resized(batch=nb)
+        t0 = time.perf_counter()
+        oracle.decode_art(oracle.make_cfg(wb), inp["Q"][:nb], inp["K"][:nb], inp["V"][:nb], scale,
+                          16, w.art_tau, w.art_phi, w.art_patience, keep_partials=False)
+        sec = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": nb / sec, "unit": "tokens/s", "cores": oracle.threads(),
+                               "kind": "oracle",
+                               "sample": f"{nb} of {w.batch} sequences, all {w.n_q_heads} heads, "
+                                         f"the whole traversal in fp64 ({sec:.1f}s)"}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def time_score_cold(pf: api.Prefill, K, V, reps: int = 10) -> float:
     """Mean duration (ms) of the summary kernel(s) with the caches evicted before each run.
 
@@ -248,6 +330,9 @@ def main():
     if args.vs:
         nv, ns = (int(x) for x in args.vs.split(","))
         bench_vs(args, w, nv, ns)
+        return
+    if w.kind == "decode":
+        bench_decode(args, w)
         return
     log(f"[bench] workload {w.name}: generating inputs")
     t0 = time.perf_counter()

@@ -31,7 +31,7 @@ SA_OAM_OFF, SA_OAM_PRODUCT, SA_OAM_ADDITIVE = 0, 1, 2
 EXPORTS = ("sparse_attn_summary_bytes", "sparse_attn_select_workspace_bytes",
            "sparse_attn_index_width", "sparse_attn_score", "sparse_attn_select",
            "sparse_attn_forward_workspace_bytes", "sparse_attn_forward",
-           "sparse_attn_forward_vs", "sparse_attn_last_error")
+           "sparse_attn_forward_vs", "sparse_attn_decode_art", "sparse_attn_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -79,10 +79,13 @@ def load() -> ctypes.CDLL:
     lib.sparse_attn_forward_vs.argtypes = [PP, P, P, P, P, ctypes.c_int32, P, ctypes.c_int32,
                                            ctypes.c_float, P, ctypes.c_size_t, P,
                                            ctypes.c_int32, P, P]
+    lib.sparse_attn_decode_art.argtypes = [PP, P, P, P, ctypes.c_float, ctypes.c_float,
+                                           ctypes.c_float, ctypes.c_int32, P, ctypes.c_int32,
+                                           P, P]
     lib.sparse_attn_last_error.argtypes = []
     lib.sparse_attn_last_error.restype = ctypes.c_char_p
     for f in ("sparse_attn_score", "sparse_attn_select", "sparse_attn_forward",
-              "sparse_attn_forward_vs"):
+              "sparse_attn_forward_vs", "sparse_attn_decode_art"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -221,6 +224,23 @@ def forward_vs(p: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
         _ptr(ws, "ws", need), 0 if ws is None else ws.numel() * ws.element_size(),
         _ptr(O, "O", q_bytes * osz), out_dtype,
         _ptr(lse, "lse", p.batch * p.n_q_heads * p.seqlen * 4), _stream(stream)))
+
+
+def decode_art(p: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+               softmax_scale: float, tau: float, phi: float, patience: int, O: torch.Tensor,
+               out_dtype: int, blocks_done: torch.Tensor, stream=None):
+    """Decode attention with run-time termination (sparse_attn_decode_art): Q [B, Hq, d],
+    K, V [B, N, Hkv, d]; writes O [B, Hq, d] and blocks_done int32 [B, Hq]."""
+    B, Hq, d = p.batch, p.n_q_heads, p.head_dim
+    kv = p.batch * p.seqlen * p.n_kv_heads * d * _elt(p)
+    osz = 4 if out_dtype == SA_F32 else 2
+    if blocks_done.dtype != torch.int32:
+        raise ValueError("blocks_done must be int32")
+    _check(load().sparse_attn_decode_art(
+        ctypes.byref(p), _ptr(Q, "Q", B * Hq * d * _elt(p)), _ptr(K, "K", kv),
+        _ptr(V, "V", kv), float(softmax_scale), float(tau), float(phi), int(patience),
+        _ptr(O, "O", B * Hq * d * osz), out_dtype, _ptr(blocks_done, "blocks_done", B * Hq * 4),
+        _stream(stream)))
 
 
 class Prefill:

@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libsparse_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["pool.hip", "select.hip", "attn_fwd.hip", "api.cpp"]
+SOURCES = ["pool.hip", "select.hip", "attn_fwd.hip", "decode.hip", "api.cpp"]
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -250,6 +250,32 @@ int sparse_attn_forward_vs(const sa_problem* p, const void* Q, const void* K, co
                     "sparse_attn_forward_vs launch");
 }
 
+int sparse_attn_decode_art(const sa_problem* p, const void* Q, const void* K, const void* V,
+                           float softmax_scale, float tau, float phi, int32_t patience, void* O,
+                           int32_t out_dtype, int32_t* blocks_done, void* stream) {
+  sa::Dims D;
+  int rc = check_problem(p, &D);
+  if (rc != SA_OK) return rc;
+  if (D.dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "the decode path takes bf16 inputs");
+  if (D.blk != 64) return fail(SA_ERR_UNSUPPORTED, "the decode path uses blocks of 64 keys");
+  if (D.G > sa::kArtMaxHeadsPerKv)
+    return fail(SA_ERR_UNSUPPORTED, "n_q_heads / n_kv_heads = %d exceeds %d", D.G,
+                sa::kArtMaxHeadsPerKv);
+  if (!Q || !K || !V || !O || !blocks_done)
+    return fail(SA_ERR_INVALID, "Q, K, V, O and blocks_done must be non-NULL");
+  if (!(isfinite(tau) && tau >= 0.0f) || !(isfinite(phi) && phi >= 0.0f))
+    return fail(SA_ERR_INVALID, "tau and phi must be finite and >= 0");
+  if (patience < 0) return fail(SA_ERR_INVALID, "patience must be >= 0");
+  if (out_dtype != SA_F32 && out_dtype != SA_BF16)
+    return fail(SA_ERR_INVALID, "out_dtype must be SA_F32 or SA_BF16");
+  if (!isfinite(softmax_scale)) return fail(SA_ERR_INVALID, "softmax_scale is not finite");
+  g_err.clear();
+  return hip_status(sa::launch_decode_art(D, Q, K, V, softmax_scale, tau, phi, patience, O,
+                                          out_dtype, blocks_done,
+                                          static_cast<hipStream_t>(stream)),
+                    "sparse_attn_decode_art launch");
+}
+
 const char* sparse_attn_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"

@@ -174,4 +174,12 @@ hipError_t launch_forward_vs(const Dims& D, const void* Q, const void* K, const 
                              const VsIndex& vs, float scale, void* ws, void* O, int out_dtype,
                              float* lse, hipStream_t s);
 
+// Decode with run-time termination (decode.hip): blocks of 64 keys, probe of the first
+// kArtProbe output coordinates, at most kArtMaxHeadsPerKv query heads per kv head.
+constexpr int kArtProbe = 16;
+constexpr int kArtMaxHeadsPerKv = 4;
+hipError_t launch_decode_art(const Dims& D, const void* Q, const void* K, const void* V,
+                             float scale, float tau, float phi, int patience, void* O,
+                             int out_dtype, int32_t* done, hipStream_t s);
+
 }  // namespace sa

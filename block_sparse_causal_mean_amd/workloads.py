@@ -77,6 +77,10 @@ class Workload:
     gate_mode: int = GATE_QUANTILE
     tau_fixed: float = 0.0
     oam_beta: float = 0.0       # beta of the additive output-aware form
+    kind: str = "prefill"       # "prefill", or "decode" (one query token per sequence)
+    art_tau: float = 0.0        # decode: run-time termination thresholds and patience
+    art_phi: float = 0.0
+    art_patience: int = 0
 
     @property
     def tile(self) -> int:
@@ -132,6 +136,20 @@ WORKLOADS: Dict[str, Workload] = {
         k_min=8, budget_kind=BUDGET_LINEAR_DECAY, n_sink=2, rho=2.0, q=0.1, seed=1005,
         v_logn_sigma=1.0, oam_beta=0.2),
 }
+
+# Decode with run-time termination (ART page): one new token per sequence and head over a
+# 16K-token cache, 64 sequences (one workgroup per sequence and kv head: 512, two per CU; the
+# sequential traversal needs the second workgroup to keep HBM busy).  The selection fields are
+# unused.  tau = phi = 5e-3 and patience 4 stop these inputs' heads after about a third of
+# the cache (the pages give no values).
+DECODE_WORKLOADS: Dict[str, Workload] = {
+    "art_decode_16k": Workload(
+        name="art_decode_16k", batch=64, seqlen=16384, n_q_heads=32, n_kv_heads=8,
+        head_dim=128, block=64, dtype=BF16, score_mode=KMEAN, output_aware=0, k_max=1, k_min=1,
+        budget_kind=BUDGET_CONST, n_sink=0, rho=1.0, q=0.0, seed=1006, v_logn_sigma=0.5,
+        kind="decode", art_tau=5e-3, art_phi=5e-3, art_patience=4),
+}
+WORKLOADS.update(DECODE_WORKLOADS)
 
 # Order used by reports: the small reference case first, the 128K prefill (the headline) third.
 WORKLOAD_ORDER = ["tiny_ref", "llama8b_32k", "prefill_128k", "quest_64k", "stem_32k"]
@@ -199,6 +217,25 @@ def make_inputs(w: Workload, seed: Optional[int] = None,
     if extras is not None and w.planted:
         extras["anchors"] = anchor_pos
     return {"Q": _to_dtype(q, dt), "K": _to_dtype(k, dt), "V": _to_dtype(v, dt)}
+
+
+def make_decode_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Decode inputs: Q [B, Hq, d] (the new tokens), K, V [B, N, Hkv, d] (the cache), CPU
+    tensors in the workload dtype.  Q, K ~ N(0, 1); V ~ N(0, 1) times a per-token
+    LogNormal(0, v_logn_sigma) scale.  Drawn one sequence at a time (the caches are large)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    B, N, Hq, Hkv, d = w.batch, w.seqlen, w.n_q_heads, w.n_kv_heads, w.head_dim
+    dt = w.torch_dtype
+    q = rng.standard_normal((B, Hq, d), dtype=np.float32)
+    K = torch.empty((B, N, Hkv, d), dtype=dt)
+    V = torch.empty((B, N, Hkv, d), dtype=dt)
+    for b in range(B):
+        K[b] = _to_dtype(rng.standard_normal((N, Hkv, d), dtype=np.float32), dt)
+        v = rng.standard_normal((N, Hkv, d), dtype=np.float32)
+        if w.v_logn_sigma > 0:
+            v *= rng.lognormal(0.0, w.v_logn_sigma, size=(N, Hkv, 1)).astype(np.float32)
+        V[b] = _to_dtype(v, dt)
+    return {"Q": _to_dtype(q, dt), "K": K, "V": V}
 
 
 SLASH_PERIOD = 256  # tokens: the planted slash pattern's period

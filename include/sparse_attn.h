@@ -194,6 +194,30 @@ int sparse_attn_forward_vs(const sa_problem* p, const void* Q, const void* K, co
                            int32_t n_slash, float softmax_scale, void* ws, size_t ws_bytes,
                            void* O, int32_t out_dtype, float* lse, void* stream);
 
+/*
+ * Decode attention with run-time termination (ART page, sections 2.1-2.4).  One new query
+ * token per sequence and query head attends to the sequence's K/V cache (keys 0 .. seqlen-1)
+ * block by block, block 0 first, then the other blocks most recent first.  After each block
+ * the partial output's probe vector (its first 16 coordinates) is compared with the previous
+ * one; once the change of its L2 norm stays below tau and its change of direction
+ * (1 - cosine similarity) below phi for `patience` consecutive blocks, the traversal stops
+ * and the partial output (over the blocks seen) is the result.  patience = 0 never stops.
+ *   p            batch = sequences, seqlen = cached tokens, block = tile = 64 (the block the
+ *                rule works on), n_q_heads / n_kv_heads <= 4, dtype SA_BF16; score_mode and
+ *                output_aware are not used.
+ *   Q            [B, Hq, d] in p->dtype: the decode tokens.
+ *   K, V         [B, seqlen, Hkv, d] in p->dtype (the cache, BSHD as elsewhere).
+ *   tau, phi     finite, >= 0;  patience >= 0.
+ *   O            [B, Hq, d] in out_dtype, written.
+ *   blocks_done  int32 [B, Hq], written: blocks each head processed (seqlen / 64 if it never
+ *                stopped).
+ * The stop decision is taken in fp32; near a threshold it may differ from one taken in exact
+ * arithmetic.
+ */
+int sparse_attn_decode_art(const sa_problem* p, const void* Q, const void* K, const void* V,
+                           float softmax_scale, float tau, float phi, int32_t patience, void* O,
+                           int32_t out_dtype, int32_t* blocks_done, void* stream);
+
 /* The calling thread's last error message ("" if none).  Valid until its next call. */
 const char* sparse_attn_last_error(void);
 
