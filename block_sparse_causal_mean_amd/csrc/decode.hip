@@ -13,10 +13,11 @@
 // A head that stops freezes its output; the workgroup stops streaming when all have.  Each
 // block's K and V arrive in registers kArtPrefetch blocks ahead of their use (one register
 // slot per block in flight; the step loop is unrolled that many times so that the slots are
-// compile-time: with one workgroup per CU the registers are there, and the sequential
-// traversal needs the depth to cover memory latency), are stored to LDS, and
-// are read from there: K rows padded by 16 bytes so that 64 lanes reading 64 rows hit
-// distinct banks.  Scores: lane r = key r of the block, an fp32 dot product over d; softmax in
+// compile-time; the sequential traversal needs the depth to cover memory latency), are
+// stored to one of two LDS tile sets (alternating, so that one barrier per block suffices),
+// and are read from there: K rows padded by 16 bytes so that 64 lanes reading 64 rows hit
+// distinct banks.  Scores: lane r = key r of the block, a dot product over d with
+// v_dot2_f32_bf16 (two exact bf16 products per instruction, fp32 sums); softmax in
 // the log2 domain with exact rescaling; P V: lane i holds output coordinates E i .. E i + E-1.
 // Bound: HBM (the whole traversal streams K and V once); early termination is the saving.
 
@@ -26,6 +27,8 @@
 
 namespace sa {
 namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kArtBlk = 64;
 constexpr int kArtThreads = 256;
@@ -79,9 +82,9 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
     void* __restrict__ O, int out_f32, int32_t* __restrict__ done) {
   using C = ArtCfg<D>;
   constexpr int CH = C::CH, CPT = C::CPT, RS = C::RS, E = C::E;
-  __shared__ __attribute__((aligned(16))) char ktile[kArtBlk * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t vtile[kArtBlk * D];
-  __shared__ __attribute__((aligned(16))) float qs[kArtMaxG][D];
+  __shared__ __attribute__((aligned(16))) char ktiles[2][kArtBlk * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t vtiles[2][kArtBlk * D];
+  __shared__ __attribute__((aligned(16))) uint32_t qs[kArtMaxG][D / 2];  // bf16 pairs
   __shared__ __attribute__((aligned(16))) float ps[kArtMaxG][kArtBlk];
   __shared__ int live[kArtMaxG];
 
@@ -95,9 +98,9 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
   const bool active = w < G;  // this wave computes query head g * G + w
   const int h = g * G + w;
 
-  for (int i = threadIdx.x; i < G * D; i += kArtThreads) {
-    const int hh = i / D, c = i - hh * D;
-    qs[hh][c] = bf16_bits_to_f32(Q[((size_t)b * dm.Hq + g * G + hh) * D + c]);
+  for (int i = threadIdx.x; i < G * D / 2; i += kArtThreads) {
+    const int hh = i / (D / 2), c2 = i - hh * (D / 2);
+    qs[hh][c2] = reinterpret_cast<const uint32_t*>(Q + ((size_t)b * dm.Hq + g * G + hh) * D)[c2];
   }
   if (threadIdx.x < kArtMaxG) live[threadIdx.x] = (int)threadIdx.x < G ? 1 : 0;
 
@@ -119,15 +122,23 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
     }
   }
 
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f, nprev = 0.0f;  // nprev: the previous probe's norm
   float acc[E], prev[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = prev[e] = 0.0f;
   int run = 0, stopped = 0;  // stopped: blocks processed when this head stopped (0: running)
 
-  // One step of the traversal on the block whose chunks are in (kr, vr); refills them with
-  // block k + kArtPrefetch.  Returns whether any head of the group still runs.
+  // One step of the traversal on the block whose chunks are in (kr, vr), in tile set k & 1;
+  // refills the registers with block k + kArtPrefetch.  The barrier after the stores also
+  // means every wave is done with step k - 1 (whose tile set step k + 1 overwrites) and has
+  // posted its stop decision.  Stores, barrier and refill happen on every step, also past the
+  // end and after every head stopped (valid blocks, never used), so that each step's memory
+  // operations are the same and the compiler's waits stay partial: a step waits for its own
+  // block only, with the later blocks still in flight.  Returns whether any head ran before
+  // this step (decisions up to step k - 1).
   auto step = [&](int k, uint4 (&kr)[CPT], uint4 (&vr)[CPT]) -> bool {
+    char* ktile = ktiles[k & 1];
+    uint16_t* vtile = vtiles[k & 1];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int q = (int)threadIdx.x + i * kArtThreads;
@@ -136,30 +147,31 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
       *reinterpret_cast<uint4*>(vtile + r * D + cc * 8) = vr[i];
     }
     __syncthreads();
-    if (k + kArtPrefetch < n) {
-      const int jn = block_of(k + kArtPrefetch);
+    bool any = false;
+    for (int i = 0; i < G; ++i) any |= live[i] != 0;
+    {
+      const int jn = block_of(min(k + kArtPrefetch, n - 1));
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         kr[i] = chunk_src(Kb, jn, i);
         vr[i] = chunk_src(Vb, jn, i);
       }
     }
-    if (active && live[w]) {
+    if (k < n && active && live[w]) {
       // scores of key `lane`
       float s = 0.0f;
+      auto d2 = [](uint32_t a, uint32_t b2, float c) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                               __builtin_bit_cast(bf16x2, b2), c, false);
+      };
 #pragma unroll
       for (int cc = 0; cc < CH; ++cc) {
         const uint4 kv = *reinterpret_cast<const uint4*>(ktile + lane * RS + cc * 16);
-        const float4 q0 = *reinterpret_cast<const float4*>(&qs[w][cc * 8]);
-        const float4 q1 = *reinterpret_cast<const float4*>(&qs[w][cc * 8 + 4]);
-        s = __builtin_fmaf(q0.x, bf16_lo(kv.x), s);
-        s = __builtin_fmaf(q0.y, bf16_hi(kv.x), s);
-        s = __builtin_fmaf(q0.z, bf16_lo(kv.y), s);
-        s = __builtin_fmaf(q0.w, bf16_hi(kv.y), s);
-        s = __builtin_fmaf(q1.x, bf16_lo(kv.z), s);
-        s = __builtin_fmaf(q1.y, bf16_hi(kv.z), s);
-        s = __builtin_fmaf(q1.z, bf16_lo(kv.w), s);
-        s = __builtin_fmaf(q1.w, bf16_hi(kv.w), s);
+        const uint4 q4 = *reinterpret_cast<const uint4*>(&qs[w][cc * 4]);
+        s = d2(kv.x, q4.x, s);
+        s = d2(kv.y, q4.y, s);
+        s = d2(kv.z, q4.z, s);
+        s = d2(kv.w, q4.w, s);
       }
       s *= scale_log2;
       const float m_new = fmaxf(m_run, wmax(s));
@@ -190,20 +202,20 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
       }
       // probe: output coordinates 0 .. kArtProbe-1 (lanes 0 .. kArtProbe/E - 1)
       const float inv = 1.0f / l_run;
-      float nx = 0.0f, np = 0.0f, dp = 0.0f;
+      float nx = 0.0f, dp = 0.0f;
       if (lane < kArtProbe / E) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float x = acc[e] * inv;
           nx = __builtin_fmaf(x, x, nx);
-          np = __builtin_fmaf(prev[e], prev[e], np);
           dp = __builtin_fmaf(x, prev[e], dp);
           prev[e] = x;
         }
       }
       nx = __builtin_sqrtf(wsum(nx));
-      np = __builtin_sqrtf(wsum(np));
       dp = wsum(dp);
+      const float np = nprev;
+      nprev = nx;
       if (k > 0 && patience > 0) {
         const float dsc = fabsf(nx - np);
         const float ddr = (nx > 0.0f && np > 0.0f) ? 1.0f - dp / (nx * np) : 1.0f;
@@ -214,17 +226,16 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
         }
       }
     }
-    __syncthreads();
-    bool any = false;
-    for (int i = 0; i < G; ++i) any |= live[i] != 0;
     return any;
   };
 
-  bool go = true;
-  for (int k = 0; go && k < n; k += kArtPrefetch) {
+  // Rounds of kArtPrefetch steps; the traversal ends after the round in which the last head
+  // stopped (at most kArtPrefetch steps of loads later: no compute is spent on them).
+  for (int k = 0;; k += kArtPrefetch) {
+    bool any = true;
 #pragma unroll
-    for (int sl = 0; sl < kArtPrefetch; ++sl)
-      if (go && k + sl < n) go = step(k + sl, kr[sl], vr[sl]);
+    for (int sl = 0; sl < kArtPrefetch; ++sl) any = step(k + sl, kr[sl], vr[sl]);
+    if (!any || k + kArtPrefetch >= n) break;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // refills issued before the exit
   if (active) {
