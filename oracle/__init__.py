@@ -30,7 +30,7 @@ class OracleCfg(ctypes.Structure):
         ("output_aware", ctypes.c_int32), ("k_max", ctypes.c_int32), ("k_min", ctypes.c_int32),
         ("budget_kind", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
         ("tau_fixed", ctypes.c_float), ("oam_beta", ctypes.c_float), ("rho", ctypes.c_double),
-        ("q", ctypes.c_double), ("width", ctypes.c_int32), ("pad2_", ctypes.c_int32),
+        ("q", ctypes.c_double), ("width", ctypes.c_int32), ("select_unit", ctypes.c_int32),
     ]
 
 
@@ -75,7 +75,13 @@ def make_cfg(w, **over) -> OracleCfg:
         k_max=k_max, k_min=get("k_min"), budget_kind=get("budget_kind"), n_sink=n_sink,
         gate_mode=get("gate_mode"), tau_fixed=float(get("tau_fixed")),
         oam_beta=float(over.get("oam_beta", getattr(w, "oam_beta", 0.0))), rho=rho,
-        q=float(get("q")), width=width, pad2_=0)
+        q=float(get("q")), width=width,
+        select_unit=int(over.get("select_unit", getattr(w, "select_unit", 0))))
+
+
+def units(cfg: OracleCfg) -> int:
+    """Selection units per batch element: query heads, or kv heads for shared lists."""
+    return cfg.n_kv_heads if cfg.select_unit else cfg.n_q_heads
 
 
 def _arr(x, cfg: OracleCfg) -> np.ndarray:
@@ -130,10 +136,11 @@ def pool(cfg: OracleCfg, K, V=None) -> dict:
 
 
 def select(cfg: OracleCfg, Q, summ: dict) -> dict:
-    """Whole selection: kv_idx [B,Hq,n,W], kv_cnt, sigma [B,Hq,n], sigma_bar [B,n], gate, tau."""
+    """Whole selection: kv_idx [B,U,n,W], kv_cnt, sigma [B,U,n], sigma_bar [B,n], gate, tau
+    (U = units(cfg))."""
     lib = _load()
     _check(cfg)
-    B, Hq, n, W = cfg.batch, cfg.n_q_heads, cfg.seqlen // cfg.block, cfg.width
+    B, Hq, n, W = cfg.batch, units(cfg), cfg.seqlen // cfg.block, cfg.width
     out = {
         "kv_idx": np.zeros((B, Hq, n, W), np.int32), "kv_cnt": np.zeros((B, Hq, n), np.int32),
         "sigma": np.zeros((B, Hq, n), np.float32), "sigma_bar": np.zeros((B, n), np.float32),
@@ -150,10 +157,10 @@ def select(cfg: OracleCfg, Q, summ: dict) -> dict:
 
 
 def select_tile(cfg: OracleCfg, Q, summ: dict, b: int, t: int) -> dict:
-    """One tile: sigma per head, sigma_bar, eligibility, lists if untripped [0] / tripped [1]."""
+    """One tile: sigma per unit, sigma_bar, eligibility, lists if untripped [0] / tripped [1]."""
     lib = _load()
     _check(cfg)
-    Hq, W = cfg.n_q_heads, cfg.width
+    Hq, W = units(cfg), cfg.width
     sig = np.zeros((Hq,), np.float32)
     sbar = np.zeros((1,), np.float32)
     elig = np.zeros((1,), np.int32)

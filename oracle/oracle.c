@@ -65,6 +65,9 @@
  *     sigma_bar <= tau_b; ceil(q*M) = 0 trips nothing (tau reported as -inf).
  *   - Budget linear decay: k_t = max(k_min, floor(k_max * (n - t) / n)) in integers.
  *   - Lists are ascending block indices padded with -1; a count array comes with them.
+ *   - Group-shared selection (select_unit = 1; not on the pages, which select per query
+ *     head): one list per kv head, the tile score being the maximum over the tile's rows of
+ *     all that kv head's query heads; sigma per kv head, sigma_bar their mean.
  */
 
 #include <math.h>
@@ -85,7 +88,8 @@ typedef struct {
   float oam_beta;       /* beta of the additive output-aware form */
   double rho, q;
   int32_t width;        /* entries per padded list */
-  int32_t pad2_;
+  int32_t select_unit;  /* 0: one list per query head; 1: one list per kv head, shared by its
+                           query heads (see tile_score) */
 } oc_cfg;
 
 /* ---------------------------------------------------------------- element access */
@@ -163,6 +167,17 @@ int oracle_pool(const oc_cfg* c, const void* K, const void* V, float* kA, float*
 
 /* ---------------------------------------------------------------- 2. tile scores */
 
+/* Selection units.  The gated-selection page selects per query tile and head (Metodologia
+ * steps 2-3), one list per query head.  Its GQA form with one list per kv head, shared by that
+ * kv head's G query heads, is not on the pages; this oracle reads it as the same algorithm
+ * run on "the query rows of the tile in all G heads": the tile score of step 2 is the maximum
+ * of the row scores over those G x tile rows, and steps 3-5 then run per kv head exactly as
+ * they run per query head, sigma_bar averaging over the kv heads. */
+static int units(const oc_cfg* c) { return c->select_unit ? c->n_kv_heads : c->n_q_heads; }
+static int heads_per_unit(const oc_cfg* c) {
+  return c->select_unit ? c->n_q_heads / c->n_kv_heads : 1;
+}
+
 typedef struct {
   const oc_cfg* c;
   const void* Q;
@@ -193,18 +208,21 @@ static float oam_bonus(float vnorm, float beta) {
   return (float)((double)beta * (l > 0.0 ? l : 0.0));
 }
 
-/* Tile score S_tj: maximum over the tile's rows, then the output-aware factor or term. */
-static float tile_score(const oc_inputs* in, int b, int h, int t, int j) {
+/* Tile score S_tj of selection unit u: maximum over the tile's rows (of every query head of
+ * the unit), then the output-aware factor or term. */
+static float tile_score(const oc_inputs* in, int b, int u, int t, int j) {
   const oc_cfg* c = in->c;
-  float m = row_score(in, b, (int64_t)t * c->block, h, j);
-  for (int r = 1; r < c->block; ++r) {
-    float s = row_score(in, b, (int64_t)t * c->block + r, h, j);
-    if (s > m) m = s;
-  }
+  const int gs = heads_per_unit(c), h0 = u * gs;
+  float m = row_score(in, b, (int64_t)t * c->block, h0, j);
+  for (int h = h0; h < h0 + gs; ++h)
+    for (int r = 0; r < c->block; ++r) {
+      float s = row_score(in, b, (int64_t)t * c->block + r, h, j);
+      if (s > m) m = s;
+    }
   m = canon(m);
   if (c->output_aware) {
     const int n = c->seqlen / c->block;
-    const int g = h / (c->n_q_heads / c->n_kv_heads);
+    const int g = h0 / (c->n_q_heads / c->n_kv_heads);
     const float v = in->vn[((int64_t)b * n + j) * c->n_kv_heads + g];
     if (c->output_aware == 1) {
       m = canon(m * v);
@@ -246,12 +264,12 @@ static int by_rank(const void* pa, const void* pb) {
   return (a->j < b->j) ? -1 : (a->j > b->j);
 }
 
-/* Scores every free causal block of tile t for head h and ranks them; returns the count. */
-static int rank_free(const oc_inputs* in, int b, int h, int t, scored* out) {
+/* Scores every free causal block of tile t for unit u and ranks them; returns the count. */
+static int rank_free(const oc_inputs* in, int b, int u, int t, scored* out) {
   int m = 0;
   for (int j = 0; j <= t; ++j) {
     if (is_forced(in->c, t, j)) continue;
-    out[m].s = tile_score(in, b, h, t, j);
+    out[m].s = tile_score(in, b, u, t, j);
     out[m].j = j;
     ++m;
   }
@@ -332,12 +350,13 @@ static void gate_batch(const oc_cfg* c, const float* sbar, const int* elig, floa
 
 /* ------------------------------------------------------- whole selection (steps 2-7) */
 
-/* Q [B,N,Hq,d]; summaries from oracle_pool.  Outputs: kv_idx [B,Hq,n,W], kv_cnt [B,Hq,n],
- * sigma [B,Hq,n], sigma_bar [B,n], gate [B,n], tau [B]. */
+/* Q [B,N,Hq,d]; summaries from oracle_pool.  With U selection units (Hq, or Hkv when lists
+ * are per kv head), outputs: kv_idx [B,U,n,W], kv_cnt [B,U,n], sigma [B,U,n], sigma_bar [B,n],
+ * gate [B,n], tau [B]. */
 int oracle_select(const oc_cfg* c, const void* Q, const float* kA, const float* kB,
                   const float* vn, int32_t* kv_idx, int32_t* kv_cnt, float* sigma,
                   float* sigma_bar, unsigned char* gate, float* tau) {
-  const int n = c->seqlen / c->block, Hq = c->n_q_heads, W = c->width;
+  const int n = c->seqlen / c->block, Hq = units(c), W = c->width;
   oc_inputs in = {c, Q, kA, kB, vn};
   int Rmax = n; /* ranked entries kept per (b, h, t): all free blocks */
   scored* ranked = (scored*)malloc(sizeof(scored) * (size_t)c->batch * Hq * n * Rmax);
@@ -360,7 +379,7 @@ int oracle_select(const oc_cfg* c, const void* Q, const float* kA, const float* 
 
   for (int b = 0; b < c->batch; ++b) {
     for (int t = 0; t < n; ++t) {
-      float acc = 0.0f;
+      float acc = 0.0f; /* over the units: heads, or kv heads */
       for (int h = 0; h < Hq; ++h) acc = acc + sigma[((int64_t)b * Hq + h) * n + t];
       sigma_bar[(int64_t)b * n + t] = acc / (float)Hq;
     }
@@ -383,13 +402,13 @@ int oracle_select(const oc_cfg* c, const void* Q, const float* kA, const float* 
 }
 
 /* One tile (b, t) on its own, for checks at sizes where the whole selection is too slow:
- * sigma for every head [Hq], sigma_bar, eligibility, and for every head the list emitted if
- * the tile does not trip (lists[0][h][:], cnts[0][h]) and if it does (lists[1], cnts[1]).
- * The gate itself needs every tile of the batch element and is not computed here. */
+ * sigma for every selection unit [U], sigma_bar, eligibility, and for every unit the list
+ * emitted if the tile does not trip (lists[0][u][:], cnts[0][u]) and if it does (lists[1],
+ * cnts[1]).  The gate itself needs every tile of the batch element and is not computed here. */
 int oracle_select_tile(const oc_cfg* c, const void* Q, const float* kA, const float* kB,
                        const float* vn, int b, int t, float* sigma_h, float* sigma_bar,
                        int32_t* eligible, int32_t* lists, int32_t* cnts) {
-  const int n = c->seqlen / c->block, Hq = c->n_q_heads, W = c->width;
+  const int n = c->seqlen / c->block, Hq = units(c), W = c->width;
   oc_inputs in = {c, Q, kA, kB, vn};
   scored* ranked = (scored*)malloc(sizeof(scored) * (size_t)Hq * n);
   int* nfree = (int*)malloc(sizeof(int) * (size_t)Hq);
@@ -418,7 +437,7 @@ int oracle_select_tile(const oc_cfg* c, const void* Q, const float* kA, const fl
   return 0;
 }
 
-/* Tile scores of every block of tile t for head h (forced blocks are reported as NaN). */
+/* Tile scores of every block of tile t for selection unit h (forced blocks: NaN). */
 int oracle_tile_scores(const oc_cfg* c, const void* Q, const float* kA, const float* kB,
                        const float* vn, int b, int h, int t, float* S) {
   oc_inputs in = {c, Q, kA, kB, vn};
@@ -473,7 +492,8 @@ static void attend_row(const oc_cfg* c, const void* Q, const void* K, const void
 
 /* Rows to compute: rows[3*i .. 3*i+2] = (b, h, pos) for i < n_rows; rows == NULL means every
  * row, in [B, N, Hq] order.  O receives n_rows x d doubles, lse n_rows doubles (may be NULL).
- * The list of row (b, h, pos) is kv_idx[b, h, pos / block, :], with kv_cnt entries. */
+ * The list of row (b, h, pos) is kv_idx[b, u, pos / block, :], with kv_cnt entries, for the
+ * selection unit u of head h (h itself, or its kv head). */
 int oracle_forward(const oc_cfg* c, const void* Q, const void* K, const void* V,
                    const int32_t* kv_idx, const int32_t* kv_cnt, int W, float softmax_scale,
                    int64_t n_rows, const int64_t* rows, double* O, double* lse) {
@@ -502,7 +522,7 @@ int oracle_forward(const oc_cfg* c, const void* Q, const void* K, const void* V,
         b = (int)(i / ((int64_t)Hq * c->seqlen));
       }
       int t = (int)(pos / c->block);
-      int64_t bht = ((int64_t)b * Hq + h) * n + t;
+      int64_t bht = ((int64_t)b * units(c) + h / heads_per_unit(c)) * n + t;
       double l;
       attend_row(c, Q, K, V, kv_idx + bht * W, kv_cnt[bht], (double)softmax_scale, b, pos, h,
                  O + i * d, &l, z);

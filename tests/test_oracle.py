@@ -407,6 +407,95 @@ def test_output_aware_exact_scaling_leaves_selection_unchanged():
         np.testing.assert_array_equal(oam[key], plain[key])
 
 
+# ------------------------------------------------------- group-shared (per kv head) lists
+
+@pytest.mark.parametrize("oam", [0, 1])
+def test_group_selection_golden(oam):
+    g = json.load(open(os.path.join(GOLDEN, "group_selection.json")))
+    _, w, Q, K, V = _constructed(output_aware=oam, vscale=4.0)
+    cfg = oracle.make_cfg(w, select_unit=1)
+    assert oracle.units(cfg) == 1 and cfg.width == 5
+    s = oracle.pool(cfg, K, V)
+    for j in range(7):  # the group score is the larger of the two heads' exact scores
+        assert oracle.tile_scores(cfg, Q, s, 0, 0, 7)[j] == g["group_score"][j] * (4 if oam else 1)
+    out = oracle.select(cfg, Q, s)
+    want_sigma = np.array([[_f32(x) for x in row] for row in g["sigma"]], np.float32)
+    np.testing.assert_array_equal(out["sigma"][0].view(np.uint32), want_sigma.view(np.uint32))
+    want_sbar = np.array([_f32(x) for x in g["sigma_bar"]], np.float32)
+    np.testing.assert_array_equal(out["sigma_bar"][0].view(np.uint32), want_sbar.view(np.uint32))
+    assert out["tau"][0] == _f32(g["tau"])
+    np.testing.assert_array_equal(out["gate"][0], g["gate"])
+    np.testing.assert_array_equal(out["kv_idx"][0], g["kv_idx"])
+    np.testing.assert_array_equal(out["kv_cnt"][0], g["kv_cnt"])
+    for t in range(8):
+        one = oracle.select_tile(cfg, Q, s, 0, t)
+        tr = int(out["gate"][0, t])
+        np.testing.assert_array_equal(one["lists"][tr], out["kv_idx"][0, :, t])
+
+
+def test_group_selection_with_one_head_per_kv_head_is_per_head_selection():
+    w, cfg, Q, K, V, s = _random_case(810, seqlen=768, head_dim=16, block=32, k_max=3,
+                                      k_min=3, n_q_heads=3, n_kv_heads=3, q=0.3,
+                                      dtype=wl.BF16)
+    a = oracle.select(cfg, Q, s)
+    b = oracle.select(oracle.make_cfg(w, select_unit=1), Q, s)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("seed,kw", [
+    (820, dict(n_q_heads=4, n_kv_heads=2, q=0.3)),
+    (830, dict(n_q_heads=4, n_kv_heads=1, output_aware=1, n_sink=1, q=0.5,
+               score_mode=wl.KMINMAX, dtype=wl.BF16)),
+])
+def test_group_selection_is_brute_force_over_the_group(seed, kw):
+    """Group scores are the maximum of the group's heads' scores; the kept free blocks are
+    the top of a stable sort of those; sigma_bar averages over kv heads."""
+    w, cfg1, Q, K, V, s = _random_case(seed, seqlen=640, head_dim=16, block=32, k_max=3,
+                                       k_min=3, batch=2, **kw)
+    cfg = oracle.make_cfg(w, select_unit=1)
+    G = w.n_q_heads // w.n_kv_heads
+    out = oracle.select(cfg, Q, s)
+    assert out["kv_idx"].shape[1] == w.n_kv_heads
+    for b in range(w.batch):
+        for u in range(w.n_kv_heads):
+            for t in range(w.n_blocks):
+                per_head = [oracle.tile_scores(cfg1, Q, s, b, u * G + x, t) for x in range(G)]
+                S = np.maximum.reduce(per_head)
+                np.testing.assert_array_equal(
+                    oracle.tile_scores(cfg, Q, s, b, u, t)[np.isfinite(S)], S[np.isfinite(S)])
+                forced = {t} | set(range(min(w.n_sink, t)))
+                free = [j for j in range(t + 1) if j not in forced]
+                order = sorted(free, key=lambda j: (-S[j], j))
+                cnt = out["kv_cnt"][b, u, t]
+                keep = cnt - len(forced)
+                assert sorted(order[:keep] + sorted(forced)) == out["kv_idx"][b, u, t][:cnt].tolist()
+                if len(free) > 3:
+                    a0, a2, a3 = S[order[0]], S[order[2]], S[order[3]]
+                    want = np.float32(0) if a0 == a3 else np.float32(a2 - a3) / np.float32(a0 - a3)
+                    assert out["sigma"][b, u, t] == want
+        acc = np.zeros(w.n_blocks, np.float32)
+        for u in range(w.n_kv_heads):
+            acc = acc + out["sigma"][b, u]
+        np.testing.assert_array_equal(out["sigma_bar"][b], acc / np.float32(w.n_kv_heads))
+
+
+def test_group_lists_serve_every_head_of_the_kv_head():
+    """Attention with group-shared lists equals attention with each head given its kv head's
+    list explicitly."""
+    w, cfg1, Q, K, V, s = _random_case(840, seqlen=256, head_dim=16, block=32, k_max=2,
+                                       k_min=2, n_q_heads=4, n_kv_heads=2, q=0.5)
+    cfg = oracle.make_cfg(w, select_unit=1)
+    sel = oracle.select(cfg, Q, s)
+    G = w.n_q_heads // w.n_kv_heads
+    scale = 1.0 / math.sqrt(w.head_dim)
+    Og, lg = oracle.forward(cfg, Q, K, V, sel["kv_idx"], sel["kv_cnt"], scale)
+    Oh, lh = oracle.forward(cfg1, Q, K, V, np.repeat(sel["kv_idx"], G, axis=1),
+                            np.repeat(sel["kv_cnt"], G, axis=1), scale)
+    np.testing.assert_array_equal(Og, Oh)
+    np.testing.assert_array_equal(lg, lh)
+
+
 # --------------------------------------------------------------------------- attention
 
 def _dense_sdpa(Q, K, V, scale):
