@@ -62,7 +62,10 @@ def traffic_from_profiles(name: str):
 
 
 def effective_flops(w: wl.Workload, kv_cnt: torch.Tensor) -> float:
-    return 4.0 * w.tile * w.block * w.head_dim * float(kv_cnt.sum().item())
+    """4 T blk d per listed block and query head (a list shared by a kv head's query heads
+    counts once per head)."""
+    heads_per_list = w.n_q_heads // w.n_units
+    return 4.0 * w.tile * w.block * w.head_dim * heads_per_list * float(kv_cnt.sum().item())
 
 
 def vs_block_counts(w: wl.Workload, vert: np.ndarray, slash: np.ndarray) -> np.ndarray:
@@ -284,8 +287,8 @@ def cpu_baseline(w: wl.Workload, inp, budget_s: float = 15.0, max_tiles: int = 4
         t_sel += time.perf_counter() - t1
         rows = np.array([(b, h, p) for h in range(w.n_q_heads)
                          for p in range(t * w.tile, (t + 1) * w.tile)], np.int64)
-        idx = np.zeros((w.batch, w.n_q_heads, n, cfg.width), np.int32)
-        cnt = np.zeros((w.batch, w.n_q_heads, n), np.int32)
+        idx = np.zeros((w.batch, w.n_units, n, cfg.width), np.int32)
+        cnt = np.zeros((w.batch, w.n_units, n), np.int32)
         idx[b, :, t] = one["lists"][0]
         cnt[b, :, t] = one["cnts"][0]
         t1 = time.perf_counter()
@@ -389,7 +392,7 @@ def main():
     score_gbs = score_bytes / (ms_cold * 1e-3) / 1e9
 
     gate = pf.gate.float().mean().item()
-    density = float(pf.kv_cnt.sum().item()) / (w.batch * w.n_q_heads * w.n_blocks *
+    density = float(pf.kv_cnt.sum().item()) / (w.batch * w.n_units * w.n_blocks *
                                                (w.n_blocks + 1) / 2)
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
@@ -404,7 +407,9 @@ def main():
                    **({"oam_beta": w.oam_beta} if w.output_aware == wl.OAM_ADDITIVE else {}),
                    "k_max": w.k_max, "k_min": w.k_min,
                    "budget": "linear_decay" if w.budget_kind else "const", "n_sink": w.n_sink,
-                   "rho": w.rho, "q": w.q, "parallelism": "single GPU"},
+                   "rho": w.rho, "q": w.q,
+                   "lists": "per kv head" if w.select_unit else "per query head",
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "kernel": "attn_bf16 (sparse_attn_forward)",

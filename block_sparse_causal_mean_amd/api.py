@@ -26,6 +26,7 @@ SA_KMEAN, SA_KMINMAX = 0, 1
 SA_K_CONST, SA_K_LINEAR_DECAY = 0, 1
 SA_GATE_QUANTILE, SA_GATE_FIXED, SA_GATE_OFF = 0, 1, 2
 SA_OAM_OFF, SA_OAM_PRODUCT, SA_OAM_ADDITIVE = 0, 1, 2
+SA_SELECT_PER_Q_HEAD, SA_SELECT_PER_KV_HEAD = 0, 1
 
 # Every function the header declares, checked by the tests against the built library.
 EXPORTS = ("sparse_attn_summary_bytes", "sparse_attn_select_workspace_bytes",
@@ -37,7 +38,8 @@ EXPORTS = ("sparse_attn_summary_bytes", "sparse_attn_select_workspace_bytes",
 class Problem(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int32) for f in (
         "batch", "seqlen", "n_q_heads", "n_kv_heads", "head_dim", "block", "tile", "dtype",
-        "score_mode", "output_aware")] + [("oam_beta", ctypes.c_float)]
+        "score_mode", "output_aware")] + [("oam_beta", ctypes.c_float),
+                                          ("select_unit", ctypes.c_int32)]
 
 
 class Budget(ctypes.Structure):
@@ -104,7 +106,13 @@ def problem(w: wl.Workload) -> Problem:
     return Problem(batch=w.batch, seqlen=w.seqlen, n_q_heads=w.n_q_heads,
                    n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, block=w.block, tile=w.tile,
                    dtype=w.dtype, score_mode=w.score_mode, output_aware=w.output_aware,
-                   oam_beta=getattr(w, "oam_beta", 0.0))
+                   oam_beta=getattr(w, "oam_beta", 0.0),
+                   select_unit=getattr(w, "select_unit", SA_SELECT_PER_Q_HEAD))
+
+
+def units(p: Problem) -> int:
+    """Selection units per sequence (lists per batch element and tile): Hq, or Hkv."""
+    return p.n_kv_heads if p.select_unit == SA_SELECT_PER_KV_HEAD else p.n_q_heads
 
 
 def budget(w: wl.Workload) -> Budget:
@@ -171,7 +179,7 @@ def select(p: Problem, b: Budget, Q: torch.Tensor, summaries: torch.Tensor, ws: 
            kv_idx: torch.Tensor, kv_cnt: torch.Tensor, sigma=None, sigma_bar=None, gate=None,
            tau=None, stream=None):
     n = p.seqlen // p.block
-    bhn = p.batch * p.n_q_heads * n
+    bhn = p.batch * units(p) * n
     W = index_width(p, b)
     _check(load().sparse_attn_select(
         ctypes.byref(p), ctypes.byref(b),
@@ -194,8 +202,8 @@ def forward(p: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().sparse_attn_forward(
         ctypes.byref(p), _ptr(Q, "Q", q_bytes * _elt(p)), _ptr(K, "K", kv), _ptr(V, "V", kv),
-        _ptr(kv_idx, "kv_idx", p.batch * p.n_q_heads * n * W * 4),
-        _ptr(kv_cnt, "kv_cnt", p.batch * p.n_q_heads * n * 4), W, softmax_scale,
+        _ptr(kv_idx, "kv_idx", p.batch * units(p) * n * W * 4),
+        _ptr(kv_cnt, "kv_cnt", p.batch * units(p) * n * 4), W, softmax_scale,
         _ptr(ws, "ws", need), ws_bytes,
         _ptr(O, "O", q_bytes * (4 if out_dtype == SA_F32 else 2)), out_dtype,
         _ptr(lse, "lse", p.batch * p.n_q_heads * p.seqlen * 4), _stream(stream)))
@@ -263,11 +271,11 @@ class Prefill:
                               device=dev)
         fwb = forward_workspace_bytes(self.p)
         self.fws = torch.empty(max(fwb, 1), dtype=torch.uint8, device=dev) if fwb else None
-        self.kv_idx = torch.empty((w.batch, w.n_q_heads, n, self.W), dtype=torch.int32,
-                                  device=dev)
-        self.kv_cnt = torch.empty((w.batch, w.n_q_heads, n), dtype=torch.int32, device=dev)
+        U = units(self.p)
+        self.kv_idx = torch.empty((w.batch, U, n, self.W), dtype=torch.int32, device=dev)
+        self.kv_cnt = torch.empty((w.batch, U, n), dtype=torch.int32, device=dev)
         if keep_stats:
-            self.sigma = torch.empty((w.batch, w.n_q_heads, n), dtype=torch.float32, device=dev)
+            self.sigma = torch.empty((w.batch, U, n), dtype=torch.float32, device=dev)
             self.sigma_bar = torch.empty((w.batch, n), dtype=torch.float32, device=dev)
             self.gate = torch.empty((w.batch, n), dtype=torch.uint8, device=dev)
             self.tau = torch.empty((w.batch,), dtype=torch.float32, device=dev)

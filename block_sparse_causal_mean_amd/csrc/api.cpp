@@ -42,6 +42,8 @@ int check_problem(const sa_problem* p, sa::Dims* D) {
     return fail(SA_ERR_INVALID, "output_aware must be SA_OAM_OFF, SA_OAM_PRODUCT or SA_OAM_ADDITIVE");
   if (p->output_aware == SA_OAM_ADDITIVE && !(isfinite(p->oam_beta) && p->oam_beta >= 0.0f))
     return fail(SA_ERR_INVALID, "oam_beta must be finite and >= 0 for SA_OAM_ADDITIVE");
+  if (p->select_unit != SA_SELECT_PER_Q_HEAD && p->select_unit != SA_SELECT_PER_KV_HEAD)
+    return fail(SA_ERR_INVALID, "select_unit must be SA_SELECT_PER_Q_HEAD or SA_SELECT_PER_KV_HEAD");
   if (p->block < 1 || p->tile < 1) return fail(SA_ERR_INVALID, "block and tile must be >= 1");
   if (p->seqlen % p->block)
     return fail(SA_ERR_INVALID, "seqlen (%d) must be a multiple of block (%d)", p->seqlen,
@@ -71,6 +73,8 @@ int check_problem(const sa_problem* p, sa::Dims* D) {
     D->oam = p->output_aware;
     D->oam_beta = p->output_aware == SA_OAM_ADDITIVE ? p->oam_beta : 0.0f;
     D->oam_scale = (float)(1.0 / sqrt((double)p->head_dim));
+    D->gs = p->select_unit == SA_SELECT_PER_KV_HEAD ? D->G : 1;
+    D->Hu = D->Hq / D->gs;
   }
   return SA_OK;
 }

@@ -155,10 +155,13 @@ __global__ __launch_bounds__(kPackThreads) void pack_v(Dims dm, const uint16_t* 
 
 // --------------------------------------------------------------------------- attn_bf16
 
-// D head dim, QH 32-row query groups per wave, NW waves per workgroup.
-template <int D, int QH, int NW>
+// D head dim, QH 32-row query groups per wave, NW waves per workgroup, HPW query heads per
+// workgroup (two only with lists shared by a kv head's query heads: then one K/V stream feeds
+// both heads' waves).
+template <int D, int QH, int NW, int HPW = 1>
 struct Cfg {
-  static constexpr int BLK = 32 * QH * NW;     // query tile rows = block keys
+  static constexpr int BLK = 32 * QH * NW / HPW;  // query tile rows = block keys
+  static constexpr int WPH = NW / HPW;            // waves per query head
   static constexpr int NSUB = BLK / kStep;     // steps per block
   static constexpr int DC = D / 16;            // 16-coordinate chunks of the S^T products
   static constexpr int DT = D / 32;            // 32-coordinate tiles of O^T
@@ -459,7 +462,8 @@ __device__ __forceinline__ void stage_segment(const int32_t* __restrict__ list,
     }
   }
   __syncthreads();
-  if (dm.G > 1 && seg_start == 0 && seg_info[3] && seg_info[0] > 1 && seg_info[0] <= 256 &&
+  if (dm.G > 1 && dm.gs == 1 && seg_start == 0 && seg_info[3] && seg_info[0] > 1 &&
+      seg_info[0] <= 256 &&
       (dm.G - 1) * W + 256 <= scratch_ints) {
     if (w == 0) reorder_shared(list, kv_cnt, bht, dm, h, t, W, lst, seg_info, scratch);
     __syncthreads();
@@ -554,15 +558,17 @@ __device__ void stage_vs(const int32_t* __restrict__ vrow, int nv,
 }
 
 // D head dim, QH 32-row query groups per wave, NW waves per workgroup; VS: the tile's list
-// comes from a vertical-slash index (stage_vs) instead of kv_idx / kv_cnt.
-template <int D, int QH, int NW, bool VS>
+// comes from a vertical-slash index (stage_vs) instead of kv_idx / kv_cnt; HPW query heads
+// per workgroup (2: consecutive query heads of one kv head, which share their lists).
+template <int D, int QH, int NW, bool VS, int HPW>
 __global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW>::WPE))) void attn_bf16(
+__attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW>::WPE))) void attn_bf16(
     Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vp, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, int W, VsIndex vs, float scale_log2,
     void* __restrict__ O, int out_f32, float* __restrict__ lse) {
-  using C = Cfg<D, QH, NW>;
+  using C = Cfg<D, QH, NW, HPW>;
+  static_assert(HPW == 1 || !VS, "vertical-slash lists are per query head");
   constexpr int BLK = C::BLK, NSUB = C::NSUB, DC = C::DC, DT = C::DT, LPW = C::LPW;
   // Ring of NR slots, each a K step image followed by a V^T step image.
   constexpr int SLOT = C::KSLOT + C::VSLOT;
@@ -570,16 +576,27 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW>::WPE))) void attn_bf16(
   __shared__ int lst[C::LCAP];
   __shared__ int seg_info[4];  // usable entries, diagonal position, next entry, done
 
-  int b, h, t;
-  decode_tile_grouped(dm, b, h, t);
-  const int g = h / dm.G;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
+  const int wr = w % C::WPH;  // the wave's place among its head's waves
+  int b, h, t;
+  if constexpr (HPW == 1) {
+    decode_tile_grouped(dm, b, h, t);
+  } else {
+    // workgroups over (batch, pair of query heads, tile) in the same order
+    Dims dp = dm;
+    dp.G = dm.G / HPW;
+    dp.Hq = dm.Hq / HPW;
+    int hp;
+    decode_tile_grouped(dp, b, hp, t);
+    h = hp * HPW + w / C::WPH;
+  }
+  const int g = h / dm.G;
   const int l32 = lane & 31, hi = lane >> 5;
-  const size_t bht = ((size_t)b * dm.Hq + h) * dm.n + t;
+  const size_t bht = ((size_t)b * dm.Hu + h / dm.gs) * dm.n + t;  // the list's (b, unit, t)
   const int32_t* list = VS ? nullptr : kv_idx + bht * W;
   const int cnt = VS ? 0 : max(0, min(kv_cnt[bht], W));
-  const int qbase = w * 32 * QH + l32;  // this lane's first query row within the tile
+  const int qbase = wr * 32 * QH + l32;  // this lane's first query row within the tile
   const int rstride = dm.Hkv * D;
   const uint16_t* Kg = K + ((size_t)b * dm.N * dm.Hkv + g) * D;
   const uint16_t* Vpg = Vp + ((size_t)b * dm.Hkv + g) * (size_t)dm.N * D;
@@ -699,7 +716,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW>::WPE))) void attn_bf16(
         const bool diag = e == diag_e;
         // On the diagonal block, a step whose first key lies after this wave's last row is
         // fully masked for the wave: skip it.
-        if (diag && sub >= QH * (w + 1)) continue;
+        if (diag && sub >= QH * (wr + 1)) continue;
         f32x16 sc[QH];
         step_scores<D, QH>(ka_addr, qf, sc);
         step_softmax_pv<D, QH>(sc, va_addr, st, diag, sub * kStep, qbase, hi, scale_log2);
@@ -757,7 +774,7 @@ __global__ __launch_bounds__(BLK) void attn_f32(Dims dm, const float* __restrict
   int b, h, t;
   decode_tile(dm, b, h, t);
   const int g = h / dm.G;
-  const size_t bht = ((size_t)b * dm.Hq + h) * dm.n + t;
+  const size_t bht = ((size_t)b * dm.Hu + h / dm.gs) * dm.n + t;  // the list's (b, unit, t)
   const int32_t* list = kv_idx + bht * W;
   const int cnt = min(kv_cnt[bht], W);
   const int qrow = t * BLK + threadIdx.x;
@@ -808,7 +825,7 @@ __global__ __launch_bounds__(BLK) void attn_f32(Dims dm, const float* __restrict
     lse[((size_t)b * dm.Hq + h) * dm.N + qrow] = l > 0.0f ? m + __logf(l) : -INFINITY;
 }
 
-template <int D, int QH, int NW, bool VS>
+template <int D, int QH, int NW, bool VS, int HPW = 1>
 hipError_t launch_bf16(const Dims& dm, const void* Q, const void* K, const void* V,
                        const int32_t* kv_idx, const int32_t* kv_cnt, int W, const VsIndex& vs,
                        float scale, void* ws, void* O, int out_dtype, float* lse,
@@ -819,8 +836,8 @@ hipError_t launch_bf16(const Dims& dm, const void* Q, const void* K, const void*
                      static_cast<const uint16_t*>(V), Vp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
-  hipLaunchKernelGGL((attn_bf16<D, QH, NW, VS>), dim3(grid), dim3(64 * NW), 0, s, dm,
+  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq / HPW * dm.n);
+  hipLaunchKernelGGL((attn_bf16<D, QH, NW, VS, HPW>), dim3(grid), dim3(64 * NW), 0, s, dm,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K), Vp,
                      kv_idx, kv_cnt, W, vs, scale * kLog2e, O, out_dtype == SA_F32 ? 1 : 0,
                      lse);
@@ -847,6 +864,15 @@ hipError_t launch_bf16_shape(const Dims& dm, const void* Q, const void* K, const
                              const int32_t* kv_idx, const int32_t* kv_cnt, int W,
                              const VsIndex& vs, float scale, void* ws, void* O, int out_dtype,
                              float* lse, hipStream_t s) {
+  // 64-row tiles whose lists a kv head's query heads share (an even number of them): two
+  // heads per workgroup, so each K/V step in LDS feeds four waves instead of two.
+  if constexpr (!VS) {
+    if (dm.blk == 64 && dm.gs > 1 && dm.gs % 2 == 0)
+      return dm.d == 64 ? launch_bf16<64, 1, 4, false, 2>(dm, Q, K, V, kv_idx, kv_cnt, W, vs,
+                                                          scale, ws, O, out_dtype, lse, s)
+                        : launch_bf16<128, 1, 4, false, 2>(dm, Q, K, V, kv_idx, kv_cnt, W, vs,
+                                                           scale, ws, O, out_dtype, lse, s);
+  }
   if (dm.d == 64)
     return dm.blk == 64 ? launch_bf16<64, 1, 2, VS>(dm, Q, K, V, kv_idx, kv_cnt, W, vs, scale,
                                                       ws, O, out_dtype, lse, s)

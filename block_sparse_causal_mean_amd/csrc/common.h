@@ -41,6 +41,7 @@ __device__ __forceinline__ float order_key_inv(uint32_t k) {
 
 struct Dims {
   int B, N, Hq, Hkv, G, d, blk, n;  // n = N / blk tiles (= blocks)
+  int gs, Hu;  // query heads per selection unit (1, or G when lists are per kv head); units
   int dtype, score_mode, oam;     // oam: SA_OAM_OFF, SA_OAM_PRODUCT or SA_OAM_ADDITIVE
   float oam_beta, oam_scale;      // additive form: beta and (float)(1 / sqrt(d))
 };
@@ -110,6 +111,20 @@ __device__ __forceinline__ void decode_tile(const Dims& dm, int& b, int& h, int&
   const int r = rest - (rest / dm.G) * dm.G;
   b = pair / dm.Hkv;
   h = (pair - b * dm.Hkv) * dm.G + r;
+}
+
+// decode_tile over selection units instead of query heads: u is the unit (the query head,
+// or the kv head when one list serves all of a kv head's query heads).
+__device__ __forceinline__ void decode_unit(const Dims& dm, int& b, int& u, int& t) {
+  const int id = (int)blockIdx.x;
+  const int Gu = dm.G / dm.gs;  // units per kv head
+  const int per_pair = dm.n * Gu;
+  const int pair = id / per_pair;
+  const int rest = id - pair * per_pair;
+  t = dm.n - 1 - rest / Gu;
+  const int r = rest - (rest / Gu) * Gu;
+  b = pair / dm.Hkv;
+  u = (pair - b * dm.Hkv) * Gu + r;
 }
 
 // The attention kernel's order: as decode_tile, but the G query heads of one tile are dealt

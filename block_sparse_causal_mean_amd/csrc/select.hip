@@ -213,11 +213,11 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
   extern __shared__ unsigned long long keys[];
   constexpr int NT = TILE;  // one lane per query row
   const int n = dm.n;
-  const int BH = dm.B * dm.Hq;
+  const int BH = dm.B * dm.Hu;  // (batch, selection unit) pairs
   const int t = n - 1 - (int)(blockIdx.x / BH);
   const int bh = (int)(blockIdx.x % BH);
-  const int b = bh / dm.Hq, h = bh - b * dm.Hq;
-  const int g = h / dm.G;
+  const int b = bh / dm.Hu, u = bh - b * dm.Hu;
+  const int g = u * dm.gs / dm.G;
   const size_t bht = (size_t)bh * n + t;
 
   const int kt = budget_at(bd, t, n);
@@ -233,15 +233,17 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
   __syncthreads();
 
   const int row = t * TILE + threadIdx.x;
-  float q[D];
-  QRow<T, D>::load(Q + (((size_t)b * dm.N + row) * dm.Hq + h) * D, q);
-
   const size_t plane = (size_t)dm.B * n * dm.Hkv * D;
   const float* kbase = summ + (((size_t)b * n) * dm.Hkv + g) * D;
   const size_t kstride = (size_t)dm.Hkv * D;
   const float* vn = summ + plane * (MODE == SA_KMINMAX ? 2 : 1) + ((size_t)b * n) * dm.Hkv + g;
   const bool lead = (threadIdx.x & 63) == 0;
 
+  // The unit's query heads in turn; a block's key keeps the maximum over all of their rows
+  // (the output-aware combine and the order key are monotone, so the maximum commutes).
+  for (int h = u * dm.gs; h < (u + 1) * dm.gs; ++h) {
+  float q[D];
+  QRow<T, D>::load(Q + (((size_t)b * dm.N + row) * dm.Hq + h) * D, q);
   for (int j = j0; j < t; ++j) {
     const float* kb = kbase + (size_t)j * kstride;
     float s = 0.0f;
@@ -260,6 +262,7 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
           ((unsigned long long)order_key(m) << 32) | (0xffffffffu - (unsigned)j);
       atomicMax(&keys[j - j0], key);
     }
+  }
   }
   __syncthreads();
   bitonic_desc<NT>(keys, P);
@@ -318,13 +321,13 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
   constexpr int RT = TILE / 32;                    // 32-row tiles
   constexpr int KS = D / 16;                       // 16-coordinate MFMA steps
   extern __shared__ __attribute__((aligned(16))) unsigned long long keys[];
-  __shared__ unsigned int qmax_bits;
+  __shared__ float qmax_w[kScoreThreads / 64];
 
-  int b, h, t;
-  decode_tile(dm, b, h, t);
+  int b, u, t;
+  decode_unit(dm, b, u, t);
   const int n = dm.n;
-  const int g = h / dm.G;
-  const size_t bht = ((size_t)b * dm.Hq + h) * n + t;
+  const int g = u * dm.gs / dm.G;
+  const size_t bht = ((size_t)b * dm.Hu + u) * n + t;
   const int kt = budget_at(bd, t, n);
   const int nf = n_free(bd, t);
   if (nf <= kt) {
@@ -340,8 +343,18 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
 
   for (int f = threadIdx.x; f < P; f += kScoreThreads)
     keys[f] = f < nf ? (unsigned long long)(0xffffffffu - (unsigned)(j0 + f)) : 0ull;
-  if (threadIdx.x == 0) qmax_bits = 0u;
-  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  // 32-block chunks of this (batch, kv head) covering the free blocks [j0, t).
+  const size_t chunk0 = ((size_t)b * dm.Hkv + g) * ncb;
+  constexpr size_t BFC = (size_t)NPL * D * 32, XC = (size_t)NPL * D * 32;
+
+  // The unit's query heads in turn (one pass per head).  Each free block's key holds the
+  // largest tile score over the passes so far: the output-aware combine and the order key are
+  // monotone, so the maximum over all of the unit's rows is exact.
+  for (int h = u * dm.gs; h < (u + 1) * dm.gs; ++h) {
+  __syncthreads();  // the previous pass has finished reading qs and qmax_w
 
   // Stage the tile's Q rows; row norms (any order: they only scale the bound) -> max.  Each
   // thread takes a contiguous piece of one row (PPR pieces per row, all loads issued at
@@ -387,17 +400,13 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     float rmax = ss;
 #pragma unroll
     for (int off = PPR; off < 64; off <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, off));
-    if ((threadIdx.x & 63) == 0)
-      atomicMax(&qmax_bits, __float_as_uint(rmax));  // non-negative floats order as integers
+    if ((threadIdx.x & 63) == 0) qmax_w[threadIdx.x >> 6] = rmax;
   }
   __syncthreads();
-  const float qmax = __builtin_sqrtf(__uint_as_float(qmax_bits));
-
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int l32 = lane & 31, hi = lane >> 5;
-  // 32-block chunks of this (batch, kv head) covering the free blocks [j0, t).
-  const size_t chunk0 = ((size_t)b * dm.Hkv + g) * ncb;
-  constexpr size_t BFC = (size_t)NPL * D * 32, XC = (size_t)NPL * D * 32;
+  float qmax2 = qmax_w[0];
+#pragma unroll
+  for (int k = 1; k < kScoreThreads / 64; ++k) qmax2 = fmaxf(qmax2, qmax_w[k]);
+  const float qmax = __builtin_sqrtf(qmax2);
 
   for (int ch = (j0 >> 5) + wv; ch * 32 < t; ch += kScoreThreads / 64) {
     const int j = ch * 32 + l32;  // this lane's block
@@ -545,8 +554,12 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     if (valid && hi == 0) {
       float m = canon(best);
       m = oam_combine<OAM>(m, OAM ? summ[vn_off + ((size_t)b * n + j) * dm.Hkv + g] : 0.0f, dm);
-      keys[j - j0] = ((unsigned long long)order_key(m) << 32) | (0xffffffffu - (unsigned)j);
+      const unsigned long long key =
+          ((unsigned long long)order_key(m) << 32) | (0xffffffffu - (unsigned)j);
+      // one lane per block and pass, passes separated by barriers: a plain maximum
+      keys[j - j0] = key > keys[j - j0] ? key : keys[j - j0];
     }
+  }
   }
   __syncthreads();
   // Only the top R keys (and key kt, for sigma) are used: select them, then sort those.  The
@@ -586,8 +599,8 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(Dims dm, BudgetDev b
   __syncthreads();
   for (int t = threadIdx.x; t < n; t += kGateThreads) {
     float acc = 0.0f;
-    for (int h = 0; h < dm.Hq; ++h) acc = acc + sigma[((size_t)b * dm.Hq + h) * n + t];
-    const float sb = __fdiv_rn(acc, (float)dm.Hq);
+    for (int u = 0; u < dm.Hu; ++u) acc = acc + sigma[((size_t)b * dm.Hu + u) * n + t];
+    const float sb = __fdiv_rn(acc, (float)dm.Hu);
     sbar[t] = sb;
     sigma_bar[(size_t)b * n + t] = sb;
     if (n_free(bd, t) > budget_at(bd, t, n)) buf[atomicAdd(&M, 1)] = sb;
@@ -642,10 +655,10 @@ __global__ __launch_bounds__(64 * kEmitWaves) void emit_kernel(Dims dm, BudgetDe
   const int nwords = (n + 31) >> 5;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const size_t item = (size_t)blockIdx.x * kEmitWaves + w;
-  const size_t total = (size_t)dm.B * dm.Hq * n;
+  const size_t total = (size_t)dm.B * dm.Hu * n;
   const bool live = item < total;
   const int t = live ? (int)(item % n) : 0;
-  const int b = live ? (int)(item / ((size_t)dm.Hq * n)) : 0;
+  const int b = live ? (int)(item / ((size_t)dm.Hu * n)) : 0;
   unsigned int* bm = bits + w * nwords;
 
   const int kt = budget_at(bd, t, n);
@@ -707,7 +720,7 @@ hipError_t launch_score(const Dims& dm, const BudgetDev& bd, const void* Q, cons
   int P = 1;
   while (P < dm.n) P <<= 1;
   const size_t lds = sizeof(unsigned long long) * P;
-  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
+  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hu * dm.n);
   hipError_t e = allow_lds(score_rank<T, MODE, OAM, D, TILE>, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((score_rank<T, MODE, OAM, D, TILE>), dim3(grid), dim3(TILE), lds, s, dm,
@@ -754,7 +767,7 @@ hipError_t launch_score_mfma(const Dims& dm, const BudgetDev& bd, const void* Q,
   hipError_t e = allow_lds(score_rank_mfma<MODE, OAM, D, TILE>, lds);
   if (e != hipSuccess) return e;
   const char* base = reinterpret_cast<const char*>(summ);
-  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
+  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hu * dm.n);
   hipLaunchKernelGGL((score_rank_mfma<MODE, OAM, D, TILE>), dim3(grid), dim3(kScoreThreads),
                      lds, s, dm, bd, static_cast<const uint16_t*>(Q), summ,
                      reinterpret_cast<const uint16_t*>(base + L.bfc_byte),
@@ -796,7 +809,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 SelectWs select_ws_layout(const Dims& dm, const BudgetDev& bd) {
   SelectWs w;
-  const size_t bhn = (size_t)dm.B * dm.Hq * dm.n;
+  const size_t bhn = (size_t)dm.B * dm.Hu * dm.n;
   w.ranked = 0;
   w.sigma = align256(w.ranked + sizeof(int) * bhn * bd.R);
   w.sigma_bar = align256(w.sigma + sizeof(float) * bhn);
@@ -828,7 +841,7 @@ hipError_t launch_select(const Dims& dm, const BudgetDev& bd, const void* Q, con
                      sigma, sigma_bar, gate, tau);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  const size_t total = (size_t)dm.B * dm.Hq * dm.n;
+  const size_t total = (size_t)dm.B * dm.Hu * dm.n;
   const unsigned grid = (unsigned)((total + kEmitWaves - 1) / kEmitWaves);
   const size_t elds = sizeof(unsigned int) * kEmitWaves * (size_t)((dm.n + 31) / 32);
   hipLaunchKernelGGL(emit_kernel, dim3(grid), dim3(64 * kEmitWaves), elds, s, dm, bd, ranked,

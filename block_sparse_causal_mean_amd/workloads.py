@@ -47,6 +47,8 @@ GATE_OFF = 2
 OAM_OFF = 0
 OAM_PRODUCT = 1
 OAM_ADDITIVE = 2
+SELECT_PER_Q_HEAD = 0   # one block list per query head (the pages' per-head selection)
+SELECT_PER_KV_HEAD = 1  # one list per kv head, shared by its query heads
 F32 = 0
 BF16 = 1
 
@@ -81,6 +83,12 @@ class Workload:
     art_tau: float = 0.0        # decode: run-time termination thresholds and patience
     art_phi: float = 0.0
     art_patience: int = 0
+    select_unit: int = SELECT_PER_Q_HEAD
+
+    @property
+    def n_units(self) -> int:
+        """Selection units per sequence: query heads, or kv heads for shared lists."""
+        return self.n_kv_heads if self.select_unit == SELECT_PER_KV_HEAD else self.n_q_heads
 
     @property
     def tile(self) -> int:
@@ -136,6 +144,13 @@ WORKLOADS: Dict[str, Workload] = {
         k_min=8, budget_kind=BUDGET_LINEAR_DECAY, n_sink=2, rho=2.0, q=0.1, seed=1005,
         v_logn_sigma=1.0, oam_beta=0.2),
 }
+
+# One list per kv head, shared by its query heads (a GQA variant the pages do not describe):
+# the same shapes, method parameters and seeds (so the same inputs) as the per-head workloads.
+# On 64-key blocks the attention kernel then runs two query heads per workgroup.
+for _base in ("llama8b_32k", "prefill_128k", "stem_32k"):
+    WORKLOADS[_base + "_kvshared"] = dataclasses.replace(
+        WORKLOADS[_base], name=_base + "_kvshared", select_unit=SELECT_PER_KV_HEAD)
 
 # Decode with run-time termination (ART page): one new token per sequence and head over a
 # 16K-token cache, 64 sequences (one workgroup per sequence and kv head: 512, two per CU; the

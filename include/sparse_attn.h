@@ -54,6 +54,7 @@ enum { SA_KMEAN = 0, SA_KMINMAX = 1 };                       /* block score back
 enum { SA_K_CONST = 0, SA_K_LINEAR_DECAY = 1 };              /* budget schedules */
 enum { SA_GATE_QUANTILE = 0, SA_GATE_FIXED = 1, SA_GATE_OFF = 2 }; /* gate threshold source */
 enum { SA_OAM_OFF = 0, SA_OAM_PRODUCT = 1, SA_OAM_ADDITIVE = 2 };   /* output-aware scoring */
+enum { SA_SELECT_PER_Q_HEAD = 0, SA_SELECT_PER_KV_HEAD = 1 };       /* one list per ... */
 
 /* Shapes and scoring mode. */
 typedef struct sa_problem {
@@ -71,6 +72,13 @@ typedef struct sa_problem {
                            fmaf(tile score, (float)(1/sqrt(d)), bonus) with
                            bonus = (float)(oam_beta * max(0, ln(vnorm^2))) in fp64 */
   float oam_beta;       /* beta of SA_OAM_ADDITIVE: finite, >= 0; ignored otherwise */
+  int32_t select_unit;  /* SA_SELECT_PER_Q_HEAD: one list per query head (the gated-selection
+                           page's per-head selection, Metodologia steps 2-3).
+                           SA_SELECT_PER_KV_HEAD: one list per kv head, shared by its
+                           Hq / Hkv query heads (a GQA variant the pages do not describe): the
+                           tile score is the maximum over the tile's rows of all those heads;
+                           sigma is per kv head and sigma_bar their mean.  U below is the
+                           number of selection units per sequence: Hq, or Hkv. */
 } sa_problem;
 
 /* Budget, forced blocks and gate.  n = seqlen / block tiles (= blocks) per sequence. */
@@ -127,12 +135,13 @@ int sparse_attn_score(const sa_problem* p, const void* K, const void* V, void* s
  *   Q          [B, N, Hq, d] in p->dtype.
  *   summaries  from sparse_attn_score on the same problem.
  *   ws         sparse_attn_select_workspace_bytes(p, b) bytes of scratch, contents ignored.
- *   kv_idx     int32 [B, Hq, n, W], W = sparse_attn_index_width(p, b): tile t's kept blocks
- *              in ascending order (so the diagonal block t is last), then -1 sentinels.
- *   kv_cnt     int32 [B, Hq, n]: number of non-sentinel entries.
- *   sigma      optional (NULL to skip) fp32 [B, Hq, n]: cut margin per tile and head; 1.0
+ *   kv_idx     int32 [B, U, n, W], W = sparse_attn_index_width(p, b), U = Hq or Hkv (see
+ *              select_unit): tile t's kept blocks in ascending order (so the diagonal block t
+ *              is last), then -1 sentinels.
+ *   kv_cnt     int32 [B, U, n]: number of non-sentinel entries.
+ *   sigma      optional (NULL to skip) fp32 [B, U, n]: cut margin per tile and unit; 1.0
  *              for a tile with at most k_t free candidates (not eligible).
- *   sigma_bar  optional fp32 [B, n]: mean of sigma over the Hq heads.
+ *   sigma_bar  optional fp32 [B, n]: mean of sigma over the U units.
  *   gate       optional uint8 [B, n]: 1 where the tile tripped and kept floor(rho * k_t).
  *   tau        optional fp32 [B]: the threshold used (-inf when nothing can trip).
  * Free blocks of tile t are the causal blocks 0..t minus the forced ones (the diagonal t and
@@ -151,7 +160,9 @@ size_t sparse_attn_forward_workspace_bytes(const sa_problem* p);
 /*
  * Sparse attention (Stem page, three-stage implementation; gated-selection page, step 5).
  *   Q, K, V        BSHD in p->dtype.
- *   kv_idx, kv_cnt as written by sparse_attn_select (any order of blocks is accepted; the
+ *   kv_idx, kv_cnt [B, U, n, W] and [B, U, n] as written by sparse_attn_select for the same
+ *                  select_unit (query head h reads unit h, or its kv head h / (Hq / Hkv));
+ *                  any order of blocks is accepted; the
  *                  list of query tile t ends at kv_cnt or at the first negative entry;
  *                  entries must be distinct blocks <= t, others are skipped).
  *   W              row stride of kv_idx (its last dimension), >= 1.

@@ -47,9 +47,9 @@ def test_struct_layout_matches_header(tmp_path):
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "sparse_attn.h"\n'
         "int main(void){\n"
-        'printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(sa_problem), sizeof(sa_budget),'
+        'printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(sa_problem), sizeof(sa_budget),'
         " offsetof(sa_budget, tau_fixed), offsetof(sa_budget, rho), offsetof(sa_budget, q),"
-        " offsetof(sa_problem, oam_beta));\n"
+        " offsetof(sa_problem, oam_beta), offsetof(sa_problem, select_unit));\n"
         "return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
@@ -58,7 +58,7 @@ def test_struct_layout_matches_header(tmp_path):
                                           check=True).stdout.split()]
     want = [ctypes.sizeof(api.Problem), ctypes.sizeof(api.Budget),
             api.Budget.tau_fixed.offset, api.Budget.rho.offset, api.Budget.q.offset,
-            api.Problem.oam_beta.offset]
+            api.Problem.oam_beta.offset, api.Problem.select_unit.offset]
     assert got == want
 
 
@@ -106,6 +106,8 @@ BAD_PROBLEMS = [
     (dict(output_aware=3), api.SA_ERR_INVALID),
     (dict(output_aware=2, oam_beta=-0.5), api.SA_ERR_INVALID),
     (dict(output_aware=2, oam_beta=float("nan")), api.SA_ERR_INVALID),
+    (dict(select_unit=2), api.SA_ERR_INVALID),
+    (dict(select_unit=-1), api.SA_ERR_INVALID),
     (dict(seqlen=64 * 16385), api.SA_ERR_UNSUPPORTED),
 ]
 

@@ -1,6 +1,7 @@
 """Host-side logic of bench.py (CPU only)."""
 
 import numpy as np
+import torch
 
 import bench
 import oracle
@@ -18,3 +19,14 @@ def test_vs_block_counts_match_the_oracle_lists():
         slash[0, 2, 2:] = -1
         _, cnt = oracle.vs_lists(oracle.make_cfg(w), vert, slash)
         np.testing.assert_array_equal(bench.vs_block_counts(w, vert, slash), cnt)
+
+
+def test_effective_flops_count_shared_lists_once_per_head():
+    """A list shared by a kv head's G query heads is attended by all G of them."""
+    per_head = wl.WORKLOADS["llama8b_32k"].resized(seqlen=2048)
+    shared = wl.WORKLOADS["llama8b_32k_kvshared"].resized(seqlen=2048)
+    n = per_head.n_blocks
+    c_head = torch.full((1, per_head.n_q_heads, n), 3, dtype=torch.int32)
+    c_shared = torch.full((1, shared.n_kv_heads, n), 3, dtype=torch.int32)
+    assert bench.effective_flops(per_head, c_head) == bench.effective_flops(shared, c_shared)
+    assert bench.effective_flops(shared, c_shared) == 4.0 * 64 * 64 * 128 * 32 * n * 3

@@ -25,7 +25,8 @@ from parity import bits, check_structure, out_tol, say
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["llama8b_32k", "prefill_128k", "quest_64k", "stem_32k", "stem_additive_32k"]
+FULL = ["llama8b_32k", "prefill_128k", "quest_64k", "stem_32k", "stem_additive_32k",
+        "llama8b_32k_kvshared", "stem_32k_kvshared"]
 
 
 def _sample_tiles(n, gate_row, rng, extra=4):

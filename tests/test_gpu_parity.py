@@ -46,6 +46,20 @@ SMALL = {
                                                       k_max=3, k_min=3, score_mode=wl.KMINMAX,
                                                       output_aware=wl.OAM_ADDITIVE,
                                                       oam_beta=0.3, v_logn_sigma=1.0),
+    # one list per kv head, shared by its query heads: two heads per attention workgroup on
+    # 64-key blocks with an even group (d = 128 and 64), one head per workgroup otherwise
+    # (odd group, 128-key blocks, fp32)
+    "llama8b_n32_kvshared": WL["llama8b_32k_kvshared"].resized(seqlen=2048, k_max=8, k_min=8),
+    "stem_b2_n32_kvshared": WL["stem_32k_kvshared"].resized(batch=2, seqlen=2048, k_max=16,
+                                                            k_min=4),
+    "quest_d64_g2_kvshared": WL["quest_64k"].resized(seqlen=1280, n_q_heads=4, n_kv_heads=2,
+                                                      head_dim=64, k_max=3, k_min=3,
+                                                      select_unit=wl.SELECT_PER_KV_HEAD),
+    "ragged_g3_d64_kvshared": WL["llama8b_32k_kvshared"].resized(
+        batch=3, seqlen=832, n_q_heads=6, n_kv_heads=2, head_dim=64, k_max=3, k_min=3, q=0.3),
+    "prefill_n32_kvshared": WL["prefill_128k_kvshared"].resized(seqlen=4096, k_max=6, k_min=6),
+    "f32_kvshared": WL["tiny_ref"].resized(seqlen=1024, n_q_heads=4, n_kv_heads=2, k_max=3,
+                                           k_min=3, select_unit=wl.SELECT_PER_KV_HEAD),
 }
 
 MAX_ORACLE_ROWS = 6000
