@@ -84,6 +84,7 @@ class Workload:
     art_phi: float = 0.0
     art_patience: int = 0
     select_unit: int = SELECT_PER_Q_HEAD
+    q_tile: int = 0         # query tile rows; 0 = block (every workload of the pages)
 
     @property
     def n_units(self) -> int:
@@ -92,7 +93,11 @@ class Workload:
 
     @property
     def tile(self) -> int:
-        return self.block
+        return self.q_tile or self.block
+
+    @property
+    def n_tiles(self) -> int:
+        return self.seqlen // self.tile
 
     @property
     def n_blocks(self) -> int:
@@ -107,8 +112,11 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
     def index_width(self) -> int:
-        """Entries per sentinel-padded block list: forced blocks plus the expanded budget."""
-        return min(self.n_blocks, 1 + self.n_sink + int(math.floor(self.rho * self.k_max)))
+        """Entries per sentinel-padded block list: forced blocks (the tile's diagonal blocks
+        and the sinks) plus the expanded budget."""
+        n_diag = max(1, self.tile // self.block)
+        return min(self.n_blocks,
+                   n_diag + self.n_sink + int(math.floor(self.rho * self.k_max)))
 
 
 WORKLOADS: Dict[str, Workload] = {

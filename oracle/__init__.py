@@ -31,6 +31,7 @@ class OracleCfg(ctypes.Structure):
         ("budget_kind", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
         ("tau_fixed", ctypes.c_float), ("oam_beta", ctypes.c_float), ("rho", ctypes.c_double),
         ("q", ctypes.c_double), ("width", ctypes.c_int32), ("select_unit", ctypes.c_int32),
+        ("tile", ctypes.c_int32), ("pad3_", ctypes.c_int32),
     ]
 
 
@@ -55,6 +56,8 @@ def _load():
     lib.oracle_forward.argtypes = [cfgp, P, P, P, P, P, ctypes.c_int, ctypes.c_float,
                                    ctypes.c_int64, P, P, P]
     lib.oracle_budget.argtypes = [cfgp, ctypes.c_int]
+    lib.oracle_n_tiles.argtypes = [cfgp]
+    lib.oracle_diag_end.argtypes = [cfgp, ctypes.c_int]
     lib.oracle_vs_lists.argtypes = [cfgp, P, ctypes.c_int, P, ctypes.c_int, P, P, ctypes.c_int]
     lib.oracle_decode_art.argtypes = [cfgp, P, P, P, ctypes.c_double, ctypes.c_int,
                                       ctypes.c_double, ctypes.c_double, ctypes.c_int, P, P, P, P]
@@ -65,9 +68,11 @@ def _load():
 def make_cfg(w, **over) -> OracleCfg:
     """Oracle problem description from any object with the workload's attribute names."""
     get = lambda k: over.get(k, getattr(w, k))
-    n = get("seqlen") // get("block")
+    n, blk = get("seqlen") // get("block"), get("block")
+    T = int(over.get("tile", getattr(w, "tile", blk)))
     rho, k_max, n_sink = float(get("rho")), int(get("k_max")), int(get("n_sink"))
-    width = over.get("width", min(n, 1 + n_sink + int(math.floor(rho * k_max))))
+    n_diag = max(1, T // blk)  # diagonal blocks per tile
+    width = over.get("width", min(n, n_diag + n_sink + int(math.floor(rho * k_max))))
     return OracleCfg(
         batch=get("batch"), seqlen=get("seqlen"), n_q_heads=get("n_q_heads"),
         n_kv_heads=get("n_kv_heads"), head_dim=get("head_dim"), block=get("block"),
@@ -76,7 +81,12 @@ def make_cfg(w, **over) -> OracleCfg:
         gate_mode=get("gate_mode"), tau_fixed=float(get("tau_fixed")),
         oam_beta=float(over.get("oam_beta", getattr(w, "oam_beta", 0.0))), rho=rho,
         q=float(get("q")), width=width,
-        select_unit=int(over.get("select_unit", getattr(w, "select_unit", 0))))
+        select_unit=int(over.get("select_unit", getattr(w, "select_unit", 0))), tile=T)
+
+
+def n_tiles(cfg: OracleCfg) -> int:
+    """Query tiles per sequence: N / T."""
+    return cfg.seqlen // (cfg.tile or cfg.block)
 
 
 def units(cfg: OracleCfg) -> int:
@@ -118,6 +128,9 @@ def _check(cfg: OracleCfg):
         raise ValueError("need 1 <= k_min <= k_max")
     if cfg.seqlen % cfg.block or cfg.n_q_heads % cfg.n_kv_heads:
         raise ValueError("seqlen % block and n_q_heads % n_kv_heads must be 0")
+    T = cfg.tile or cfg.block
+    if cfg.seqlen % T or (T % cfg.block and cfg.block % T):
+        raise ValueError("seqlen % tile must be 0, and tile a multiple or divisor of block")
 
 
 def pool(cfg: OracleCfg, K, V=None) -> dict:
@@ -140,7 +153,7 @@ def select(cfg: OracleCfg, Q, summ: dict) -> dict:
     (U = units(cfg))."""
     lib = _load()
     _check(cfg)
-    B, Hq, n, W = cfg.batch, units(cfg), cfg.seqlen // cfg.block, cfg.width
+    B, Hq, n, W = cfg.batch, units(cfg), n_tiles(cfg), cfg.width
     out = {
         "kv_idx": np.zeros((B, Hq, n, W), np.int32), "kv_cnt": np.zeros((B, Hq, n), np.int32),
         "sigma": np.zeros((B, Hq, n), np.float32), "sigma_bar": np.zeros((B, n), np.float32),
@@ -177,8 +190,9 @@ def select_tile(cfg: OracleCfg, Q, summ: dict, b: int, t: int) -> dict:
 
 
 def tile_scores(cfg: OracleCfg, Q, summ: dict, b: int, h: int, t: int) -> np.ndarray:
+    """Scores of tile t's causal blocks (NaN for its forced ones), for selection unit h."""
     lib = _load()
-    S = np.zeros((t + 1,), np.float32)
+    S = np.zeros((lib.oracle_diag_end(ctypes.byref(cfg), t),), np.float32)
     Qa = _arr(Q, cfg)
     lib.oracle_tile_scores(ctypes.byref(cfg), _p(Qa), _p(summ["kA"]), _p(summ["kB"]),
                            _p(summ["vn"]), b, h, t, _p(S))
@@ -229,6 +243,8 @@ def vs_lists(cfg: OracleCfg, vert, slash):
     lib = _load()
     _check(cfg)
     B, Hq, n = cfg.batch, cfg.n_q_heads, cfg.seqlen // cfg.block
+    if (cfg.tile or cfg.block) != cfg.block:
+        raise ValueError("vertical-slash lists are defined for tile = block")
     v = np.ascontiguousarray(vert, dtype=np.int32).reshape(B, Hq, -1)
     s = np.ascontiguousarray(slash, dtype=np.int32).reshape(B, Hq, -1)
     NV, NS = v.shape[-1], s.shape[-1]

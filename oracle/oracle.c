@@ -65,6 +65,8 @@
  *     sigma_bar <= tau_b; ceil(q*M) = 0 trips nothing (tau reported as -inf).
  *   - Budget linear decay: k_t = max(k_min, floor(k_max * (n - t) / n)) in integers.
  *   - Lists are ascending block indices padded with -1; a count array comes with them.
+ *   - Tile != block: tile t's diagonal blocks are all blocks overlapping its rows (forced);
+ *     its free blocks are the earlier ones; the budget's position decay runs over tiles.
  *   - Group-shared selection (select_unit = 1; not on the pages, which select per query
  *     head): one list per kv head, the tile score being the maximum over the tile's rows of
  *     all that kv head's query heads; sigma per kv head, sigma_bar their mean.
@@ -77,7 +79,7 @@
 
 /* Problem description, mirrored field for field by a ctypes Structure in __init__.py. */
 typedef struct {
-  int32_t batch, seqlen, n_q_heads, n_kv_heads, head_dim, block; /* query tile == block */
+  int32_t batch, seqlen, n_q_heads, n_kv_heads, head_dim, block; /* block: keys per block */
   int32_t in_dtype;     /* 0: float32 arrays, 1: bfloat16 bit patterns (uint16) */
   int32_t score_mode;   /* 0: mean-pooled keys, 1: per-coordinate min/max bound */
   int32_t output_aware; /* 1: tile score times mean value-row L2 norm; 2: additive form */
@@ -90,6 +92,9 @@ typedef struct {
   int32_t width;        /* entries per padded list */
   int32_t select_unit;  /* 0: one list per query head; 1: one list per kv head, shared by its
                            query heads (see tile_score) */
+  int32_t tile;         /* query tile rows T (0: equal to block); a multiple of block, or a
+                           divisor of it */
+  int32_t pad3_;
 } oc_cfg;
 
 /* ---------------------------------------------------------------- element access */
@@ -167,6 +172,21 @@ int oracle_pool(const oc_cfg* c, const void* K, const void* V, float* kA, float*
 
 /* ---------------------------------------------------------------- 2. tile scores */
 
+/* Query tiles.  The pages' tile is a query block scored against key blocks (gated-selection
+ * page, Metodologia step 2); the workloads have tile = block.  A tile of T rows over blocks
+ * of blk keys reads as: tile t holds rows tT .. tT+T-1; its causal blocks are those starting
+ * at or before its last row, j < diag_end(t); the blocks overlapping its rows,
+ * diag_first(t) <= j < diag_end(t), are its diagonal blocks (forced, as the single diagonal
+ * block is when T = blk). */
+static int tile_rows(const oc_cfg* c) { return c->tile > 0 ? c->tile : c->block; }
+static int n_tiles(const oc_cfg* c) { return c->seqlen / tile_rows(c); }
+static int diag_first(const oc_cfg* c, int t) {
+  return (int)((int64_t)t * tile_rows(c) / c->block);
+}
+static int diag_end(const oc_cfg* c, int t) {
+  return (int)(((int64_t)(t + 1) * tile_rows(c) - 1) / c->block) + 1;
+}
+
 /* Selection units.  The gated-selection page selects per query tile and head (Metodologia
  * steps 2-3), one list per query head.  Its GQA form with one list per kv head, shared by that
  * kv head's G query heads, is not on the pages; this oracle reads it as the same algorithm
@@ -212,11 +232,11 @@ static float oam_bonus(float vnorm, float beta) {
  * the unit), then the output-aware factor or term. */
 static float tile_score(const oc_inputs* in, int b, int u, int t, int j) {
   const oc_cfg* c = in->c;
-  const int gs = heads_per_unit(c), h0 = u * gs;
-  float m = row_score(in, b, (int64_t)t * c->block, h0, j);
+  const int gs = heads_per_unit(c), h0 = u * gs, T = tile_rows(c);
+  float m = row_score(in, b, (int64_t)t * T, h0, j);
   for (int h = h0; h < h0 + gs; ++h)
-    for (int r = 0; r < c->block; ++r) {
-      float s = row_score(in, b, (int64_t)t * c->block + r, h, j);
+    for (int r = 0; r < T; ++r) {
+      float s = row_score(in, b, (int64_t)t * T + r, h, j);
       if (s > m) m = s;
     }
   m = canon(m);
@@ -237,14 +257,19 @@ static float tile_score(const oc_inputs* in, int b, int u, int t, int j) {
 
 /* ------------------------------------------------------------ 3. budget and forced set */
 
+/* Budget of tile t: the position decay runs over the tile index (tiles = n_tiles). */
 static int budget(const oc_cfg* c, int t) {
-  const int n = c->seqlen / c->block;
+  const int n = n_tiles(c);
   if (c->budget_kind == 0) return c->k_max;
   int64_t k = (int64_t)c->k_max * (n - t) / n;
   return k > c->k_min ? (int)k : c->k_min;
 }
 
-static int is_forced(const oc_cfg* c, int t, int j) { return j == t || j < c->n_sink; }
+/* Forced blocks of tile t: its diagonal blocks (every block that overlaps the tile's rows)
+ * and the sinks. */
+static int is_forced(const oc_cfg* c, int t, int j) {
+  return j >= diag_first(c, t) || j < c->n_sink;
+}
 
 static int expanded(const oc_cfg* c, int k) { return (int)floor(c->rho * (double)k); }
 
@@ -267,7 +292,7 @@ static int by_rank(const void* pa, const void* pb) {
 /* Scores every free causal block of tile t for unit u and ranks them; returns the count. */
 static int rank_free(const oc_inputs* in, int b, int u, int t, scored* out) {
   int m = 0;
-  for (int j = 0; j <= t; ++j) {
+  for (int j = 0; j < diag_end(in->c, t); ++j) {
     if (is_forced(in->c, t, j)) continue;
     out[m].s = tile_score(in, b, u, t, j);
     out[m].j = j;
@@ -302,7 +327,7 @@ static int cmp_int(const void* a, const void* b) {
 /* Forced blocks plus the first `keep` ranked free blocks, ascending, -1 padded. */
 static int emit_list(const oc_cfg* c, int t, const scored* r, int keep, int* list) {
   int cnt = 0;
-  for (int j = 0; j <= t; ++j)
+  for (int j = 0; j < diag_end(c, t); ++j)
     if (is_forced(c, t, j)) list[cnt++] = j;
   for (int e = 0; e < keep; ++e) list[cnt++] = r[e].j;
   qsort(list, (size_t)cnt, sizeof(int), cmp_int);
@@ -326,7 +351,7 @@ static int cmp_float(const void* a, const void* b) {
 /* Per batch element: tau from the eligible tiles' sigma_bar, and the gate bits. */
 static void gate_batch(const oc_cfg* c, const float* sbar, const int* elig, float* tau,
                        unsigned char* gate) {
-  const int n = c->seqlen / c->block;
+  const int n = n_tiles(c);
   float t_b = -INFINITY;
   if (c->gate_mode == 0) {
     float* vals = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
@@ -351,14 +376,14 @@ static void gate_batch(const oc_cfg* c, const float* sbar, const int* elig, floa
 /* ------------------------------------------------------- whole selection (steps 2-7) */
 
 /* Q [B,N,Hq,d]; summaries from oracle_pool.  With U selection units (Hq, or Hkv when lists
- * are per kv head), outputs: kv_idx [B,U,n,W], kv_cnt [B,U,n], sigma [B,U,n], sigma_bar [B,n],
- * gate [B,n], tau [B]. */
+ * are per kv head) and n = N / T tiles, outputs: kv_idx [B,U,n,W], kv_cnt [B,U,n],
+ * sigma [B,U,n], sigma_bar [B,n], gate [B,n], tau [B]. */
 int oracle_select(const oc_cfg* c, const void* Q, const float* kA, const float* kB,
                   const float* vn, int32_t* kv_idx, int32_t* kv_cnt, float* sigma,
                   float* sigma_bar, unsigned char* gate, float* tau) {
-  const int n = c->seqlen / c->block, Hq = units(c), W = c->width;
+  const int n = n_tiles(c), Hq = units(c), W = c->width;
   oc_inputs in = {c, Q, kA, kB, vn};
-  int Rmax = n; /* ranked entries kept per (b, h, t): all free blocks */
+  int Rmax = c->seqlen / c->block; /* ranked entries kept per (b, h, t): all free blocks */
   scored* ranked = (scored*)malloc(sizeof(scored) * (size_t)c->batch * Hq * n * Rmax);
   int* nfree = (int*)malloc(sizeof(int) * (size_t)c->batch * Hq * n);
   int* elig = (int*)malloc(sizeof(int) * (size_t)c->batch * n);
@@ -408,7 +433,7 @@ int oracle_select(const oc_cfg* c, const void* Q, const float* kA, const float* 
 int oracle_select_tile(const oc_cfg* c, const void* Q, const float* kA, const float* kB,
                        const float* vn, int b, int t, float* sigma_h, float* sigma_bar,
                        int32_t* eligible, int32_t* lists, int32_t* cnts) {
-  const int n = c->seqlen / c->block, Hq = units(c), W = c->width;
+  const int n = c->seqlen / c->block, Hq = units(c), W = c->width; /* n: blocks */
   oc_inputs in = {c, Q, kA, kB, vn};
   scored* ranked = (scored*)malloc(sizeof(scored) * (size_t)Hq * n);
   int* nfree = (int*)malloc(sizeof(int) * (size_t)Hq);
@@ -437,13 +462,19 @@ int oracle_select_tile(const oc_cfg* c, const void* Q, const float* kA, const fl
   return 0;
 }
 
-/* Tile scores of every block of tile t for selection unit h (forced blocks: NaN). */
+/* Tile scores of the causal blocks j < diag_end(t) of tile t for selection unit h (forced
+ * blocks: NaN); returns diag_end(t). */
 int oracle_tile_scores(const oc_cfg* c, const void* Q, const float* kA, const float* kB,
                        const float* vn, int b, int h, int t, float* S) {
   oc_inputs in = {c, Q, kA, kB, vn};
-  for (int j = 0; j <= t; ++j) S[j] = is_forced(c, t, j) ? NAN : tile_score(&in, b, h, t, j);
-  return 0;
+  const int e = diag_end(c, t);
+  for (int j = 0; j < e; ++j) S[j] = is_forced(c, t, j) ? NAN : tile_score(&in, b, h, t, j);
+  return e;
 }
+
+/* Tiles per sequence and the causal-block end of tile t, exported for the tests. */
+int oracle_n_tiles(const oc_cfg* c) { return n_tiles(c); }
+int oracle_diag_end(const oc_cfg* c, int t) { return diag_end(c, t); }
 
 /* Raw row score s_ij of query position pos against block j (one fmaf chain). */
 float oracle_row_score(const oc_cfg* c, const void* Q, const float* kA, const float* kB,
@@ -492,12 +523,12 @@ static void attend_row(const oc_cfg* c, const void* Q, const void* K, const void
 
 /* Rows to compute: rows[3*i .. 3*i+2] = (b, h, pos) for i < n_rows; rows == NULL means every
  * row, in [B, N, Hq] order.  O receives n_rows x d doubles, lse n_rows doubles (may be NULL).
- * The list of row (b, h, pos) is kv_idx[b, u, pos / block, :], with kv_cnt entries, for the
+ * The list of row (b, h, pos) is kv_idx[b, u, pos / T, :], with kv_cnt entries, for the
  * selection unit u of head h (h itself, or its kv head). */
 int oracle_forward(const oc_cfg* c, const void* Q, const void* K, const void* V,
                    const int32_t* kv_idx, const int32_t* kv_cnt, int W, float softmax_scale,
                    int64_t n_rows, const int64_t* rows, double* O, double* lse) {
-  const int n = c->seqlen / c->block, Hq = c->n_q_heads, d = c->head_dim;
+  const int n = n_tiles(c), Hq = c->n_q_heads, d = c->head_dim;
   if (rows == NULL) n_rows = (int64_t)c->batch * c->seqlen * Hq;
   int fail = 0;
 #pragma omp parallel
@@ -521,7 +552,7 @@ int oracle_forward(const oc_cfg* c, const void* Q, const void* K, const void* V,
         pos = (i / Hq) % c->seqlen;
         b = (int)(i / ((int64_t)Hq * c->seqlen));
       }
-      int t = (int)(pos / c->block);
+      int t = (int)(pos / tile_rows(c));
       int64_t bht = ((int64_t)b * units(c) + h / heads_per_unit(c)) * n + t;
       double l;
       attend_row(c, Q, K, V, kv_idx + bht * W, kv_cnt[bht], (double)softmax_scale, b, pos, h,
