@@ -271,7 +271,7 @@ def cpu_baseline(w: wl.Workload, inp, budget_s: float = 15.0, max_tiles: int = 4
     t0 = time.perf_counter()
     summ = oracle.pool(cfg, inp["K"], inp["V"])
     t_pool = time.perf_counter() - t0
-    n = w.n_blocks
+    n = w.n_tiles
     order = [int(x) for x in np.linspace(n // 4, n - 1, max_tiles)]
     rng = np.random.default_rng(0)
     order = list(rng.permutation(sorted(set(order))))
@@ -392,8 +392,10 @@ def main():
     score_gbs = score_bytes / (ms_cold * 1e-3) / 1e9
 
     gate = pf.gate.float().mean().item()
-    density = float(pf.kv_cnt.sum().item()) / (w.batch * w.n_units * w.n_blocks *
-                                               (w.n_blocks + 1) / 2)
+    # causal (tile, block) pairs: tile t has m (t + 1) causal blocks, m = tile / block
+    m = w.tile // w.block
+    density = float(pf.kv_cnt.sum().item()) / (w.batch * w.n_units * m * w.n_tiles *
+                                               (w.n_tiles + 1) / 2)
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,

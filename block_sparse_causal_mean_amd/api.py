@@ -178,7 +178,7 @@ def score(p: Problem, K: torch.Tensor, V: Optional[torch.Tensor], summaries: tor
 def select(p: Problem, b: Budget, Q: torch.Tensor, summaries: torch.Tensor, ws: torch.Tensor,
            kv_idx: torch.Tensor, kv_cnt: torch.Tensor, sigma=None, sigma_bar=None, gate=None,
            tau=None, stream=None):
-    n = p.seqlen // p.block
+    n = p.seqlen // p.tile  # query tiles
     bhn = p.batch * units(p) * n
     W = index_width(p, b)
     _check(load().sparse_attn_select(
@@ -195,7 +195,7 @@ def forward(p: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
             kv_idx: torch.Tensor, kv_cnt: torch.Tensor, W: int, softmax_scale: float,
             ws: Optional[torch.Tensor], O: torch.Tensor, out_dtype: int,
             lse: Optional[torch.Tensor] = None, stream=None):
-    n = p.seqlen // p.block
+    n = p.seqlen // p.tile  # query tiles
     q_bytes = p.batch * p.seqlen * p.n_q_heads * p.head_dim
     kv = p.batch * p.seqlen * p.n_kv_heads * p.head_dim * _elt(p)
     need = forward_workspace_bytes(p)
@@ -263,7 +263,7 @@ class Prefill:
         self.p = problem(w)
         self.b = budget(w)
         self.W = index_width(self.p, self.b)
-        n = w.n_blocks
+        n = w.n_tiles
         dev = torch.device(device)
         self.out_dtype = w.dtype if out_dtype is None else out_dtype
         self.summ = torch.empty(summary_bytes(self.p) // 4, dtype=torch.float32, device=dev)

@@ -52,11 +52,14 @@ int check_problem(const sa_problem* p, sa::Dims* D) {
     return fail(SA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", p->head_dim);
   if (p->block != 64 && p->block != 128)
     return fail(SA_ERR_UNSUPPORTED, "block %d unsupported (64 or 128)", p->block);
-  if (p->tile != p->block)
-    return fail(SA_ERR_UNSUPPORTED, "tile (%d) must equal block (%d)", p->tile, p->block);
+  if (p->tile != p->block && !(p->tile == 128 && p->block == 64))
+    return fail(SA_ERR_UNSUPPORTED, "tile (%d) must equal block (%d), or be 128 over block 64",
+                p->tile, p->block);
   const long long n = p->seqlen / p->block;
   if (n > kMaxTiles)
     return fail(SA_ERR_UNSUPPORTED, "seqlen / block = %lld tiles exceeds %d", n, kMaxTiles);
+  if (p->seqlen % p->tile)
+    return fail(SA_ERR_INVALID, "seqlen (%d) must be a multiple of tile (%d)", p->seqlen, p->tile);
   if ((long long)p->batch * p->n_q_heads * n > 0x7fffffffLL)
     return fail(SA_ERR_UNSUPPORTED, "batch * n_q_heads * tiles exceeds the launch grid");
   if (D) {
@@ -68,6 +71,9 @@ int check_problem(const sa_problem* p, sa::Dims* D) {
     D->d = p->head_dim;
     D->blk = p->block;
     D->n = (int)n;
+    D->T = p->tile;
+    D->nt = p->seqlen / p->tile;
+    D->m = p->tile / p->block;
     D->dtype = p->dtype;
     D->score_mode = p->score_mode;
     D->oam = p->output_aware;
@@ -108,9 +114,10 @@ int check_budget(const sa_budget* b, const sa::Dims& D, sa::BudgetDev* bd) {
     long long r = ex > b->k_max ? ex : b->k_max;
     if (r > D.n) r = D.n;
     bd->R = (int)(r > 0 ? r : 1);
-    long long w = 1 + (long long)b->n_sink + ex;
+    long long w = D.m + (long long)b->n_sink + ex;
     if (w > D.n) w = D.n;
     bd->W = (int)w;
+    bd->m = D.m;
   }
   return SA_OK;
 }
@@ -224,6 +231,7 @@ int sparse_attn_forward_vs(const sa_problem* p, const void* Q, const void* K, co
   if (rc != SA_OK) return rc;
   if (D.dtype != SA_BF16)
     return fail(SA_ERR_UNSUPPORTED, "the vertical-slash path takes bf16 inputs");
+  if (D.m != 1) return fail(SA_ERR_UNSUPPORTED, "the vertical-slash path needs tile = block");
   if (!Q || !K || !V || !O) return fail(SA_ERR_INVALID, "Q, K, V and O must be non-NULL");
   if (n_vertical < 0 || n_slash < 0)
     return fail(SA_ERR_INVALID, "n_vertical and n_slash must be >= 0");
@@ -261,7 +269,8 @@ int sparse_attn_decode_art(const sa_problem* p, const void* Q, const void* K, co
   int rc = check_problem(p, &D);
   if (rc != SA_OK) return rc;
   if (D.dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "the decode path takes bf16 inputs");
-  if (D.blk != 64) return fail(SA_ERR_UNSUPPORTED, "the decode path uses blocks of 64 keys");
+  if (D.blk != 64 || D.m != 1)
+    return fail(SA_ERR_UNSUPPORTED, "the decode path uses blocks (and tiles) of 64 keys");
   if (D.G > sa::kArtMaxHeadsPerKv)
     return fail(SA_ERR_UNSUPPORTED, "n_q_heads / n_kv_heads = %d exceeds %d", D.G,
                 sa::kArtMaxHeadsPerKv);

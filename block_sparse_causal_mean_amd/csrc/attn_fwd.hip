@@ -158,10 +158,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_v(Dims dm, const uint16_t* 
 // D head dim, QH 32-row query groups per wave, NW waves per workgroup, HPW query heads per
 // workgroup (two only with lists shared by a kv head's query heads: then one K/V stream feeds
 // both heads' waves).
-template <int D, int QH, int NW, int HPW = 1>
+template <int D, int QH, int NW, int HPW = 1, int KB = 0>
 struct Cfg {
-  static constexpr int BLK = 32 * QH * NW / HPW;  // query tile rows = block keys
-  static constexpr int WPH = NW / HPW;            // waves per query head
+  static constexpr int ROWS = 32 * QH * NW / HPW;  // query tile rows
+  static constexpr int BLK = KB ? KB : ROWS;       // keys per block (the tile's, or half)
+  static constexpr int WPH = NW / HPW;             // waves per query head
   static constexpr int NSUB = BLK / kStep;     // steps per block
   static constexpr int DC = D / 16;            // 16-coordinate chunks of the S^T products
   static constexpr int DT = D / 32;            // 32-coordinate tiles of O^T
@@ -358,8 +359,8 @@ __device__ void reorder_shared(const int32_t* __restrict__ list, const int32_t* 
   int no = 0;
   for (int hh = g0; hh < g0 + dm.G && no < 8; ++hh) {
     if (hh == h) continue;
-    const long long d = ((long long)hh - h) * dm.n * W;  // same (b, t), other head
-    const int c = max(0, min(kv_cnt[(size_t)((long long)bht + ((long long)hh - h) * dm.n)], W));
+    const long long d = ((long long)hh - h) * dm.nt * W;  // same (b, t), other head
+    const int c = max(0, min(kv_cnt[(size_t)((long long)bht + ((long long)hh - h) * dm.nt)], W));
     for (int e = lane; e < c; e += 64) scratch[no * W + e] = list[d + e];
     cl[no++] = c;
   }
@@ -401,14 +402,20 @@ __device__ void reorder_shared(const int32_t* __restrict__ list, const int32_t* 
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
-  int diag = -1;
+  int diag = -1, diag2 = -1;
+  const int d0 = dm.m * t;  // the tile's diagonal blocks d0 (and d0 + 1)
   for (int i = lane; i < U; i += 64) {
     const int x = (int)(key[i] & 0xffffffu);
     lst[i] = x;
-    const unsigned long long dm_ = __ballot(x == t);
+    const unsigned long long dm_ = __ballot(x == d0);
     if (dm_) diag = (i - lane) + __builtin_ctzll(dm_);
+    const unsigned long long dm2 = __ballot(dm.m > 1 && x == d0 + 1);
+    if (dm2) diag2 = (i - lane) + __builtin_ctzll(dm2);
   }
-  if (lane == 0) seg_info[1] = diag;
+  if (lane == 0) {
+    seg_info[1] = diag;
+    seg_info[4] = diag2;
+  }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
@@ -428,22 +435,26 @@ __device__ __forceinline__ void stage_segment(const int32_t* __restrict__ list,
                                               size_t bht, const Dims& dm, int h, int t, int W,
                                               int seg_start, int w, int lane, int* lst,
                                               int* seg_info, int* scratch, int scratch_ints) {
+  // the tile's diagonal blocks: d0 (and d0 + 1 for tiles of two blocks); causal ones < dend
+  const int d0 = dm.m * t, dend = d0 + dm.m;
   if (w == 0) {
-    int u = 0, base = seg_start, diag = -1, next = cnt, done = 1;
+    int u = 0, base = seg_start, diag = -1, diag2 = -1, next = cnt, done = 1;
     while (base < cnt) {
       const int e = base + lane;
       const int x = e < cnt ? list[e] : 0;
       const unsigned long long negm = __ballot(e < cnt && x < 0);
       const int first_neg = negm ? __builtin_ctzll(negm) : 64;
-      const bool valid = e < cnt && lane < first_neg && x <= t;
+      const bool valid = e < cnt && lane < first_neg && x < dend;
       const unsigned long long vm = __ballot(valid);
       const int pre = __builtin_popcountll(vm & ((1ull << lane) - 1ull));
       const int nv = __builtin_popcountll(vm);
       const int fit = min(nv, LCAP - u);
       if (valid && pre < fit) lst[u + pre] = x;
-      // entries are distinct, so at most one lane holds the diagonal block
-      const unsigned long long dm_ = __ballot(valid && pre < fit && x == t);
+      // entries are distinct, so at most one lane holds each diagonal block
+      const unsigned long long dm_ = __ballot(valid && pre < fit && x == d0);
       if (dm_) diag = u + (int)__builtin_popcountll(vm & ((1ull << __builtin_ctzll(dm_)) - 1ull));
+      const unsigned long long dm2 = __ballot(valid && pre < fit && x == d0 + 1);
+      if (dm2) diag2 = u + (int)__builtin_popcountll(vm & ((1ull << __builtin_ctzll(dm2)) - 1ull));
       u += fit;
       if (fit < nv) {  // LDS full: continue from the first entry that did not fit
         const unsigned long long om = __ballot(valid && pre == fit);
@@ -459,6 +470,7 @@ __device__ __forceinline__ void stage_segment(const int32_t* __restrict__ list,
       seg_info[1] = diag;
       seg_info[2] = next;
       seg_info[3] = done;
+      seg_info[4] = diag2;
     }
   }
   __syncthreads();
@@ -552,6 +564,7 @@ __device__ void stage_vs(const int32_t* __restrict__ vrow, int nv,
       seg_info[1] = u - 1;  // the diagonal is the last (largest) block
       seg_info[2] = 0;
       seg_info[3] = 1;
+      seg_info[4] = -1;
     }
   }
   __syncthreads();
@@ -560,21 +573,24 @@ __device__ void stage_vs(const int32_t* __restrict__ vrow, int nv,
 // D head dim, QH 32-row query groups per wave, NW waves per workgroup; VS: the tile's list
 // comes from a vertical-slash index (stage_vs) instead of kv_idx / kv_cnt; HPW query heads
 // per workgroup (2: consecutive query heads of one kv head, which share their lists).
-template <int D, int QH, int NW, bool VS, int HPW>
+template <int D, int QH, int NW, bool VS, int HPW, int KB>
 __global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW>::WPE))) void attn_bf16(
+__attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf16(
     Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vp, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, int W, VsIndex vs, float scale_log2,
     void* __restrict__ O, int out_f32, float* __restrict__ lse) {
-  using C = Cfg<D, QH, NW, HPW>;
+  using C = Cfg<D, QH, NW, HPW, KB>;
   static_assert(HPW == 1 || !VS, "vertical-slash lists are per query head");
-  constexpr int BLK = C::BLK, NSUB = C::NSUB, DC = C::DC, DT = C::DT, LPW = C::LPW;
+  static_assert(KB == 0 || !VS, "vertical-slash lists need tile = block");
+  constexpr int BLK = C::BLK, ROWS = C::ROWS, NSUB = C::NSUB, DC = C::DC, DT = C::DT;
+  constexpr int LPW = C::LPW;
   // Ring of NR slots, each a K step image followed by a V^T step image.
   constexpr int SLOT = C::KSLOT + C::VSLOT;
   __shared__ __attribute__((aligned(1024))) char ring[C::NR * SLOT];
   __shared__ int lst[C::LCAP];
-  __shared__ int seg_info[4];  // usable entries, diagonal position, next entry, done
+  // usable entries, position of diagonal block d0, next entry, done, position of d0 + 1
+  __shared__ int seg_info[5];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
@@ -593,7 +609,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW>::WPE))) void attn_bf16(
   }
   const int g = h / dm.G;
   const int l32 = lane & 31, hi = lane >> 5;
-  const size_t bht = ((size_t)b * dm.Hu + h / dm.gs) * dm.n + t;  // the list's (b, unit, t)
+  const size_t bht = ((size_t)b * dm.Hu + h / dm.gs) * dm.nt + t;  // the list's (b, unit, t)
   const int32_t* list = VS ? nullptr : kv_idx + bht * W;
   const int cnt = VS ? 0 : max(0, min(kv_cnt[bht], W));
   const int qbase = wr * 32 * QH + l32;  // this lane's first query row within the tile
@@ -607,7 +623,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW>::WPE))) void attn_bf16(
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh) {
     const uint16_t* qp =
-        Q + (((size_t)b * dm.N + (size_t)t * BLK + qbase + 32 * qh) * dm.Hq + h) * D + 8 * hi;
+        Q + (((size_t)b * dm.N + (size_t)t * ROWS + qbase + 32 * qh) * dm.Hq + h) * D + 8 * hi;
 #pragma unroll
     for (int c = 0; c < DC; ++c) qf[qh][c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
   }
@@ -654,6 +670,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW>::WPE))) void attn_bf16(
                              seg_info, reinterpret_cast<int*>(ring), C::NR * SLOT / 4);
     }
     const int U = seg_info[0], diag_e = seg_info[1], next_start = seg_info[2];
+    const int diag_e2 = KB ? seg_info[4] : -1;  // second diagonal block (128-row tiles)
     const int seg_done = seg_info[3];
     const int nsteps = U * NSUB;
 
@@ -713,13 +730,23 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW>::WPE))) void attn_bf16(
         va_addr[1] = va0 ^ 32u;
         asm volatile("" : "+v"(va_addr[0]), "+v"(va_addr[1]));
         const int e = (int)(i / NSUB), sub = (int)(i % NSUB);
-        const bool diag = e == diag_e;
-        // On the diagonal block, a step whose first key lies after this wave's last row is
+        // key offset of the step from the tile's first row, on the diagonal blocks (the
+        // second one starts BLK keys in); -1 elsewhere
+        int kofs;
+        bool diag;
+        if constexpr (KB == 0) {
+          diag = e == diag_e;
+          kofs = sub * kStep;
+        } else {
+          kofs = e == diag_e ? sub * kStep : (e == diag_e2 ? BLK + sub * kStep : -1);
+          diag = kofs >= 0;
+        }
+        // On a diagonal block, a step whose first key lies after this wave's last row is
         // fully masked for the wave: skip it.
-        if (diag && sub >= QH * (wr + 1)) continue;
+        if (diag && kofs >= kStep * QH * (wr + 1)) continue;
         f32x16 sc[QH];
         step_scores<D, QH>(ka_addr, qf, sc);
-        step_softmax_pv<D, QH>(sc, va_addr, st, diag, sub * kStep, qbase, hi, scale_log2);
+        step_softmax_pv<D, QH>(sc, va_addr, st, diag, kofs, qbase, hi, scale_log2);
       }
       wait_vm<0>();  // dummy refills still in flight must land before the slots are reused
     }
@@ -732,7 +759,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW>::WPE))) void attn_bf16(
   for (int qh = 0; qh < QH; ++qh) {
     const float l_tot = pair_sum(st.l_run[qh]);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const int qrow = t * BLK + qbase + 32 * qh;
+    const int qrow = t * ROWS + qbase + 32 * qh;
     const size_t orow = (((size_t)b * dm.N + qrow) * dm.Hq + h) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -760,8 +787,9 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW>::WPE))) void attn_bf16(
 
 // ---------------------------------------------------------------------- fp32 (VALU) path
 
-template <int D, int BLK>
-__global__ __launch_bounds__(BLK) void attn_f32(Dims dm, const float* __restrict__ Q,
+// One thread per query row of a TR-row tile; blocks of KB keys staged in LDS.
+template <int D, int TR, int KB>
+__global__ __launch_bounds__(TR) void attn_f32(Dims dm, const float* __restrict__ Q,
                                                 const float* __restrict__ K,
                                                 const float* __restrict__ V,
                                                 const int32_t* __restrict__ kv_idx,
@@ -769,15 +797,16 @@ __global__ __launch_bounds__(BLK) void attn_f32(Dims dm, const float* __restrict
                                                 float scale, void* __restrict__ O, int out_f32,
                                                 float* __restrict__ lse) {
   extern __shared__ float fsm[];
-  float* Kb = fsm;            // [BLK][D]
-  float* Vb = fsm + BLK * D;  // [BLK][D]
+  float* Kb = fsm;           // [KB][D]
+  float* Vb = fsm + KB * D;  // [KB][D]
   int b, h, t;
   decode_tile(dm, b, h, t);
   const int g = h / dm.G;
-  const size_t bht = ((size_t)b * dm.Hu + h / dm.gs) * dm.n + t;  // the list's (b, unit, t)
+  const size_t bht = ((size_t)b * dm.Hu + h / dm.gs) * dm.nt + t;  // the list's (b, unit, t)
   const int32_t* list = kv_idx + bht * W;
   const int cnt = min(kv_cnt[bht], W);
-  const int qrow = t * BLK + threadIdx.x;
+  const int qrow = t * TR + threadIdx.x;
+  const int jmax = dm.m * t + dm.m - 1;  // the tile's last causal block
   const int rstride = dm.Hkv * D;
 
   float q[D], o[D];
@@ -788,17 +817,17 @@ __global__ __launch_bounds__(BLK) void attn_f32(Dims dm, const float* __restrict
     o[c] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f;
-  for (int e = next_entry(list, cnt, 0, t); e >= 0; e = next_entry(list, cnt, e + 1, t)) {
+  for (int e = next_entry(list, cnt, 0, jmax); e >= 0; e = next_entry(list, cnt, e + 1, jmax)) {
     const int j = list[e];
-    const size_t row0 = (size_t)b * dm.N + (size_t)j * BLK;
-    for (int x = threadIdx.x; x < BLK * D; x += BLK) {
+    const size_t row0 = (size_t)b * dm.N + (size_t)j * KB;
+    for (int x = threadIdx.x; x < KB * D; x += TR) {
       const int r = x / D, c = x - r * D;
       Kb[x] = K[(row0 + r) * rstride + (size_t)g * D + c];
       Vb[x] = V[(row0 + r) * rstride + (size_t)g * D + c];
     }
     __syncthreads();
-    for (int r = 0; r < BLK; ++r) {
-      if ((size_t)j * BLK + r > (size_t)qrow) break;
+    for (int r = 0; r < KB; ++r) {
+      if ((size_t)j * KB + r > (size_t)qrow) break;
       float sdot = 0.0f;
 #pragma unroll
       for (int c = 0; c < D; ++c) sdot = __builtin_fmaf(q[c], Kb[r * D + c], sdot);
@@ -825,7 +854,7 @@ __global__ __launch_bounds__(BLK) void attn_f32(Dims dm, const float* __restrict
     lse[((size_t)b * dm.Hq + h) * dm.N + qrow] = l > 0.0f ? m + __logf(l) : -INFINITY;
 }
 
-template <int D, int QH, int NW, bool VS, int HPW = 1>
+template <int D, int QH, int NW, bool VS, int HPW = 1, int KB = 0>
 hipError_t launch_bf16(const Dims& dm, const void* Q, const void* K, const void* V,
                        const int32_t* kv_idx, const int32_t* kv_cnt, int W, const VsIndex& vs,
                        float scale, void* ws, void* O, int out_dtype, float* lse,
@@ -836,23 +865,23 @@ hipError_t launch_bf16(const Dims& dm, const void* Q, const void* K, const void*
                      static_cast<const uint16_t*>(V), Vp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq / HPW * dm.n);
-  hipLaunchKernelGGL((attn_bf16<D, QH, NW, VS, HPW>), dim3(grid), dim3(64 * NW), 0, s, dm,
+  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq / HPW * dm.nt);
+  hipLaunchKernelGGL((attn_bf16<D, QH, NW, VS, HPW, KB>), dim3(grid), dim3(64 * NW), 0, s, dm,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K), Vp,
                      kv_idx, kv_cnt, W, vs, scale * kLog2e, O, out_dtype == SA_F32 ? 1 : 0,
                      lse);
   return hipGetLastError();
 }
 
-template <int D, int BLK>
+template <int D, int TR, int KB>
 hipError_t launch_f32(const Dims& dm, const void* Q, const void* K, const void* V,
                       const int32_t* kv_idx, const int32_t* kv_cnt, int W, float scale,
                       void* O, int out_dtype, float* lse, hipStream_t s) {
-  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.n);
-  const size_t lds = sizeof(float) * 2 * BLK * D;
-  hipError_t e = allow_lds(attn_f32<D, BLK>, lds);
+  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq * dm.nt);
+  const size_t lds = sizeof(float) * 2 * KB * D;
+  hipError_t e = allow_lds(attn_f32<D, TR, KB>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_f32<D, BLK>), dim3(grid), dim3(BLK), lds, s, dm,
+  hipLaunchKernelGGL((attn_f32<D, TR, KB>), dim3(grid), dim3(TR), lds, s, dm,
                      static_cast<const float*>(Q), static_cast<const float*>(K),
                      static_cast<const float*>(V), kv_idx, kv_cnt, W, scale, O,
                      out_dtype == SA_F32 ? 1 : 0, lse);
@@ -864,9 +893,16 @@ hipError_t launch_bf16_shape(const Dims& dm, const void* Q, const void* K, const
                              const int32_t* kv_idx, const int32_t* kv_cnt, int W,
                              const VsIndex& vs, float scale, void* ws, void* O, int out_dtype,
                              float* lse, hipStream_t s) {
-  // 64-row tiles whose lists a kv head's query heads share (an even number of them): two
-  // heads per workgroup, so each K/V step in LDS feeds four waves instead of two.
   if constexpr (!VS) {
+    // 128-row tiles over 64-key blocks: four waves per tile, two steps per block.
+    if (dm.m == 2)
+      return dm.d == 64 ? launch_bf16<64, 1, 4, false, 1, 64>(dm, Q, K, V, kv_idx, kv_cnt, W,
+                                                              vs, scale, ws, O, out_dtype, lse, s)
+                        : launch_bf16<128, 1, 4, false, 1, 64>(dm, Q, K, V, kv_idx, kv_cnt, W,
+                                                               vs, scale, ws, O, out_dtype, lse,
+                                                               s);
+    // 64-row tiles whose lists a kv head's query heads share (an even number of them): two
+    // heads per workgroup, so each K/V step in LDS feeds four waves instead of two.
     if (dm.blk == 64 && dm.gs > 1 && dm.gs % 2 == 0)
       return dm.d == 64 ? launch_bf16<64, 1, 4, false, 2>(dm, Q, K, V, kv_idx, kv_cnt, W, vs,
                                                           scale, ws, O, out_dtype, lse, s)
@@ -899,13 +935,20 @@ hipError_t launch_forward(const Dims& dm, const void* Q, const void* K, const vo
   if (dm.dtype == SA_BF16)
     return launch_bf16_shape<false>(dm, Q, K, V, kv_idx, kv_cnt, W, VsIndex{}, scale, ws, O,
                                     out_dtype, lse, s);
+  if (dm.m == 2)  // 128-row tiles over 64-key blocks
+    return dm.d == 64
+               ? launch_f32<64, 128, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
+               : launch_f32<128, 128, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse,
+                                          s);
   if (dm.d == 64)
     return dm.blk == 64
-               ? launch_f32<64, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
-               : launch_f32<64, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s);
+               ? launch_f32<64, 64, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
+               : launch_f32<64, 128, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse,
+                                          s);
   return dm.blk == 64
-             ? launch_f32<128, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
-             : launch_f32<128, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s);
+             ? launch_f32<128, 64, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
+             : launch_f32<128, 128, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse,
+                                         s);
 }
 
 hipError_t launch_forward_vs(const Dims& dm, const void* Q, const void* K, const void* V,

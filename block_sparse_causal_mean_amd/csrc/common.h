@@ -40,7 +40,8 @@ __device__ __forceinline__ float order_key_inv(uint32_t k) {
 // ------------------------------------------------------------------ derived sizes
 
 struct Dims {
-  int B, N, Hq, Hkv, G, d, blk, n;  // n = N / blk tiles (= blocks)
+  int B, N, Hq, Hkv, G, d, blk, n;  // n = N / blk key blocks
+  int T, nt, m;  // query tile rows, tiles N / T, diagonal blocks per tile T / blk (1 or 2)
   int gs, Hu;  // query heads per selection unit (1, or G when lists are per kv head); units
   int dtype, score_mode, oam;     // oam: SA_OAM_OFF, SA_OAM_PRODUCT or SA_OAM_ADDITIVE
   float oam_beta, oam_scale;      // additive form: beta and (float)(1 / sqrt(d))
@@ -52,6 +53,7 @@ struct BudgetDev {
   double rho, q;
   int R;  // ranked entries stored per (b, h, t)
   int W;  // entries per padded list
+  int m;  // diagonal blocks per tile: tile t's are m t .. m t + m - 1, its free ones < m t
 };
 
 // Layout of the block-summary buffer.  The public part (documented in the header) comes
@@ -104,10 +106,10 @@ inline SummaryLayout summary_layout(const Dims& D) {
 // fit in that cache.)
 __device__ __forceinline__ void decode_tile(const Dims& dm, int& b, int& h, int& t) {
   const int id = (int)blockIdx.x;
-  const int per_pair = dm.n * dm.G;  // tiles x q heads of one (batch, kv head)
+  const int per_pair = dm.nt * dm.G;  // tiles x q heads of one (batch, kv head)
   const int pair = id / per_pair;
   const int rest = id - pair * per_pair;
-  t = dm.n - 1 - rest / dm.G;
+  t = dm.nt - 1 - rest / dm.G;
   const int r = rest - (rest / dm.G) * dm.G;
   b = pair / dm.Hkv;
   h = (pair - b * dm.Hkv) * dm.G + r;
@@ -118,10 +120,10 @@ __device__ __forceinline__ void decode_tile(const Dims& dm, int& b, int& h, int&
 __device__ __forceinline__ void decode_unit(const Dims& dm, int& b, int& u, int& t) {
   const int id = (int)blockIdx.x;
   const int Gu = dm.G / dm.gs;  // units per kv head
-  const int per_pair = dm.n * Gu;
+  const int per_pair = dm.nt * Gu;
   const int pair = id / per_pair;
   const int rest = id - pair * per_pair;
-  t = dm.n - 1 - rest / Gu;
+  t = dm.nt - 1 - rest / Gu;
   const int r = rest - (rest / Gu) * Gu;
   b = pair / dm.Hkv;
   u = (pair - b * dm.Hkv) * Gu + r;
@@ -134,7 +136,7 @@ __device__ __forceinline__ void decode_unit(const Dims& dm, int& b, int& u, int&
 // first find them in that XCD's L2.  Falls back to decode_tile's order when the counts do
 // not divide evenly.
 __device__ __forceinline__ void decode_tile_grouped(const Dims& dm, int& b, int& h, int& t) {
-  const int U = dm.B * dm.Hq * dm.n;
+  const int U = dm.B * dm.Hq * dm.nt;
   const int p = (int)blockIdx.x;
   int id = p;
   if (U % (8 * dm.G) == 0) {
@@ -142,10 +144,10 @@ __device__ __forceinline__ void decode_tile_grouped(const Dims& dm, int& b, int&
     const int z = y / dm.G, hq = y - z * dm.G;
     id = (8 * z + x) * dm.G + hq;
   }
-  const int per_pair = dm.n * dm.G;
+  const int per_pair = dm.nt * dm.G;
   const int pair = id / per_pair;
   const int rest = id - pair * per_pair;
-  t = dm.n - 1 - rest / dm.G;
+  t = dm.nt - 1 - rest / dm.G;
   const int r = rest - (rest / dm.G) * dm.G;
   b = pair / dm.Hkv;
   h = (pair - b * dm.Hkv) * dm.G + r;

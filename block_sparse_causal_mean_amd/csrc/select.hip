@@ -46,8 +46,10 @@ __device__ __forceinline__ int budget_at(const BudgetDev& bd, int t, int n) {
   const long long k = (long long)bd.k_max * (n - t) / n;
   return k > bd.k_min ? (int)k : bd.k_min;
 }
+// Free blocks of tile t: the blocks before its diagonal ones (m t), minus the sinks.
 __device__ __forceinline__ int n_free(const BudgetDev& bd, int t) {
-  return t - (t < bd.n_sink ? t : bd.n_sink);
+  const int d0 = bd.m * t;
+  return d0 - (d0 < bd.n_sink ? d0 : bd.n_sink);
 }
 __device__ __forceinline__ int expanded(const BudgetDev& bd, int k) {
   return (int)floor(bd.rho * (double)k);
@@ -212,21 +214,22 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
                                                    float* __restrict__ sigma) {
   extern __shared__ unsigned long long keys[];
   constexpr int NT = TILE;  // one lane per query row
-  const int n = dm.n;
+  const int n = dm.n, nt = dm.nt;  // blocks, tiles
   const int BH = dm.B * dm.Hu;  // (batch, selection unit) pairs
-  const int t = n - 1 - (int)(blockIdx.x / BH);
+  const int t = nt - 1 - (int)(blockIdx.x / BH);
   const int bh = (int)(blockIdx.x % BH);
   const int b = bh / dm.Hu, u = bh - b * dm.Hu;
   const int g = u * dm.gs / dm.G;
-  const size_t bht = (size_t)bh * n + t;
+  const size_t bht = (size_t)bh * nt + t;
 
-  const int kt = budget_at(bd, t, n);
+  const int kt = budget_at(bd, t, nt);
   const int nf = n_free(bd, t);
   if (nf <= kt) {  // not eligible: every free block is kept, nothing to rank
     if (threadIdx.x == 0) sigma[bht] = 1.0f;
     return;
   }
-  const int j0 = t < bd.n_sink ? t : bd.n_sink;  // first free block
+  const int d0 = bd.m * t;                          // first diagonal block
+  const int j0 = d0 < bd.n_sink ? d0 : bd.n_sink;  // first free block
   const int P = next_pow2(nf);
   for (int f = threadIdx.x; f < P; f += NT)
     keys[f] = f < nf ? (unsigned long long)(0xffffffffu - (unsigned)(j0 + f)) : 0ull;
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
   for (int h = u * dm.gs; h < (u + 1) * dm.gs; ++h) {
   float q[D];
   QRow<T, D>::load(Q + (((size_t)b * dm.N + row) * dm.Hq + h) * D, q);
-  for (int j = j0; j < t; ++j) {
+  for (int j = j0; j < d0; ++j) {
     const float* kb = kbase + (size_t)j * kstride;
     float s = 0.0f;
     if (MODE == SA_KMEAN) {
@@ -325,16 +328,17 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
 
   int b, u, t;
   decode_unit(dm, b, u, t);
-  const int n = dm.n;
+  const int n = dm.n;  // blocks
   const int g = u * dm.gs / dm.G;
-  const size_t bht = ((size_t)b * dm.Hu + u) * n + t;
-  const int kt = budget_at(bd, t, n);
+  const size_t bht = ((size_t)b * dm.Hu + u) * dm.nt + t;
+  const int kt = budget_at(bd, t, dm.nt);
   const int nf = n_free(bd, t);
   if (nf <= kt) {
     if (threadIdx.x == 0) sigma[bht] = 1.0f;
     return;
   }
-  const int j0 = t < bd.n_sink ? t : bd.n_sink;
+  const int d0 = bd.m * t;  // first diagonal block: the free blocks are [j0, d0)
+  const int j0 = d0 < bd.n_sink ? d0 : bd.n_sink;
   int P = 1;
   while (P < nf) P <<= 1;
   int Palloc = 1;
@@ -346,7 +350,7 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  // 32-block chunks of this (batch, kv head) covering the free blocks [j0, t).
+  // 32-block chunks of this (batch, kv head) covering the free blocks [j0, d0).
   const size_t chunk0 = ((size_t)b * dm.Hkv + g) * ncb;
   constexpr size_t BFC = (size_t)NPL * D * 32, XC = (size_t)NPL * D * 32;
 
@@ -408,9 +412,9 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
   for (int k = 1; k < kScoreThreads / 64; ++k) qmax2 = fmaxf(qmax2, qmax_w[k]);
   const float qmax = __builtin_sqrtf(qmax2);
 
-  for (int ch = (j0 >> 5) + wv; ch * 32 < t; ch += kScoreThreads / 64) {
+  for (int ch = (j0 >> 5) + wv; ch * 32 < d0; ch += kScoreThreads / 64) {
     const int j = ch * 32 + l32;  // this lane's block
-    const bool valid = j >= j0 && j < t;
+    const bool valid = j >= j0 && j < d0;
     const uint16_t* bc = bfc + (chunk0 + ch) * BFC + lane * 8;
     // kmean, or kmin (plane 0) / kmax (plane 1): coordinates 8c .. 8c+7 of this lane's block
     // at xk + (plane * D/8 + c) * 256
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(Dims dm, BudgetDev b
                                                             float* __restrict__ tau) {
   extern __shared__ float gsh[];  // sbar[n], then sort buffer [P]
   __shared__ int M;
-  const int n = dm.n, b = blockIdx.x;
+  const int n = dm.nt, b = blockIdx.x;  // tiles
   float* sbar = gsh;
   float* buf = gsh + n;
   if (threadIdx.x == 0) M = 0;
@@ -651,8 +655,8 @@ __global__ __launch_bounds__(64 * kEmitWaves) void emit_kernel(Dims dm, BudgetDe
                                                                int32_t* __restrict__ kv_idx,
                                                                int32_t* __restrict__ kv_cnt) {
   extern __shared__ unsigned int bits[];  // [kEmitWaves][nwords]
-  const int n = dm.n;
-  const int nwords = (n + 31) >> 5;
+  const int n = dm.nt;                 // tiles
+  const int nwords = (dm.n + 31) >> 5;  // bitmap words over the blocks
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const size_t item = (size_t)blockIdx.x * kEmitWaves + w;
   const size_t total = (size_t)dm.B * dm.Hu * n;
@@ -664,11 +668,12 @@ __global__ __launch_bounds__(64 * kEmitWaves) void emit_kernel(Dims dm, BudgetDe
   const int kt = budget_at(bd, t, n);
   const int nf = n_free(bd, t);
   const bool elig = live && nf > kt;
+  const int d0 = bd.m * t, dend = d0 + bd.m;  // the tile's diagonal blocks [d0, dend)
   int keep = 0;
   if (elig) {
     const bool tripped = gate[(size_t)b * n + t] != 0;
     keep = min(tripped ? expanded(bd, kt) : kt, nf);
-    for (int i = lane; i <= (t >> 5); i += 64) bm[i] = 0u;
+    for (int i = lane; i <= ((dend - 1) >> 5); i += 64) bm[i] = 0u;
   }
   __syncthreads();
   if (elig) {
@@ -677,18 +682,18 @@ __global__ __launch_bounds__(64 * kEmitWaves) void emit_kernel(Dims dm, BudgetDe
       const int j = rk[e];
       atomicOr(&bm[j >> 5], 1u << (j & 31));
     }
-    if (lane == 0) atomicOr(&bm[t >> 5], 1u << (t & 31));
+    if (lane < bd.m) atomicOr(&bm[(d0 + lane) >> 5], 1u << ((d0 + lane) & 31));
     for (int j = lane; j < bd.n_sink; j += 64) atomicOr(&bm[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
   if (!live) return;
   int32_t* out = kv_idx + item * bd.W;
   int cnt;
-  if (!elig) {  // every block 0..t is kept
-    cnt = t + 1;
+  if (!elig) {  // every causal block 0 .. dend-1 is kept
+    cnt = dend;
     for (int e = lane; e < cnt; e += 64) out[e] = e;
   } else {
-    const int nw = (t >> 5) + 1;
+    const int nw = ((dend - 1) >> 5) + 1;
     int base = 0;
     for (int w0 = 0; w0 < nw; w0 += 64) {
       const unsigned int word = (w0 + lane < nw) ? bm[w0 + lane] : 0u;
@@ -720,7 +725,7 @@ hipError_t launch_score(const Dims& dm, const BudgetDev& bd, const void* Q, cons
   int P = 1;
   while (P < dm.n) P <<= 1;
   const size_t lds = sizeof(unsigned long long) * P;
-  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hu * dm.n);
+  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hu * dm.nt);
   hipError_t e = allow_lds(score_rank<T, MODE, OAM, D, TILE>, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((score_rank<T, MODE, OAM, D, TILE>), dim3(grid), dim3(TILE), lds, s, dm,
@@ -732,9 +737,9 @@ template <typename T, int MODE, int OAM>
 hipError_t score_by_shape(const Dims& dm, const BudgetDev& bd, const void* Q, const float* summ,
                           int* ranked, float* sigma, hipStream_t s) {
   if (dm.d == 64)
-    return dm.blk == 64 ? launch_score<T, MODE, OAM, 64, 64>(dm, bd, Q, summ, ranked, sigma, s)
+    return dm.T == 64 ? launch_score<T, MODE, OAM, 64, 64>(dm, bd, Q, summ, ranked, sigma, s)
                         : launch_score<T, MODE, OAM, 64, 128>(dm, bd, Q, summ, ranked, sigma, s);
-  return dm.blk == 64 ? launch_score<T, MODE, OAM, 128, 64>(dm, bd, Q, summ, ranked, sigma, s)
+  return dm.T == 64 ? launch_score<T, MODE, OAM, 128, 64>(dm, bd, Q, summ, ranked, sigma, s)
                       : launch_score<T, MODE, OAM, 128, 128>(dm, bd, Q, summ, ranked, sigma, s);
 }
 
@@ -767,7 +772,7 @@ hipError_t launch_score_mfma(const Dims& dm, const BudgetDev& bd, const void* Q,
   hipError_t e = allow_lds(score_rank_mfma<MODE, OAM, D, TILE>, lds);
   if (e != hipSuccess) return e;
   const char* base = reinterpret_cast<const char*>(summ);
-  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hu * dm.n);
+  const unsigned grid = (unsigned)((size_t)dm.B * dm.Hu * dm.nt);
   hipLaunchKernelGGL((score_rank_mfma<MODE, OAM, D, TILE>), dim3(grid), dim3(kScoreThreads),
                      lds, s, dm, bd, static_cast<const uint16_t*>(Q), summ,
                      reinterpret_cast<const uint16_t*>(base + L.bfc_byte),
@@ -780,9 +785,9 @@ template <int MODE, int OAM>
 hipError_t score_mfma_shape(const Dims& dm, const BudgetDev& bd, const void* Q,
                             const float* summ, int* ranked, float* sigma, hipStream_t s) {
   if (dm.d == 64)
-    return dm.blk == 64 ? launch_score_mfma<MODE, OAM, 64, 64>(dm, bd, Q, summ, ranked, sigma, s)
+    return dm.T == 64 ? launch_score_mfma<MODE, OAM, 64, 64>(dm, bd, Q, summ, ranked, sigma, s)
                         : launch_score_mfma<MODE, OAM, 64, 128>(dm, bd, Q, summ, ranked, sigma, s);
-  return dm.blk == 64 ? launch_score_mfma<MODE, OAM, 128, 64>(dm, bd, Q, summ, ranked, sigma, s)
+  return dm.T == 64 ? launch_score_mfma<MODE, OAM, 128, 64>(dm, bd, Q, summ, ranked, sigma, s)
                       : launch_score_mfma<MODE, OAM, 128, 128>(dm, bd, Q, summ, ranked, sigma, s);
 }
 
@@ -809,12 +814,12 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 SelectWs select_ws_layout(const Dims& dm, const BudgetDev& bd) {
   SelectWs w;
-  const size_t bhn = (size_t)dm.B * dm.Hu * dm.n;
+  const size_t bhn = (size_t)dm.B * dm.Hu * dm.nt;
   w.ranked = 0;
   w.sigma = align256(w.ranked + sizeof(int) * bhn * bd.R);
   w.sigma_bar = align256(w.sigma + sizeof(float) * bhn);
-  w.gate = align256(w.sigma_bar + sizeof(float) * (size_t)dm.B * dm.n);
-  w.tau = align256(w.gate + (size_t)dm.B * dm.n);
+  w.gate = align256(w.sigma_bar + sizeof(float) * (size_t)dm.B * dm.nt);
+  w.tau = align256(w.gate + (size_t)dm.B * dm.nt);
   w.total = align256(w.tau + sizeof(float) * dm.B);
   return w;
 }
@@ -834,14 +839,14 @@ hipError_t launch_select(const Dims& dm, const BudgetDev& bd, const void* Q, con
   if (e != hipSuccess) return e;
 
   int P = 1;
-  while (P < dm.n) P <<= 1;
-  const size_t glds = sizeof(float) * ((size_t)dm.n + P);
+  while (P < dm.nt) P <<= 1;
+  const size_t glds = sizeof(float) * ((size_t)dm.nt + P);
   if ((e = allow_lds(gate_kernel, glds)) != hipSuccess) return e;
   hipLaunchKernelGGL(gate_kernel, dim3((unsigned)dm.B), dim3(kGateThreads), glds, s, dm, bd,
                      sigma, sigma_bar, gate, tau);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  const size_t total = (size_t)dm.B * dm.Hu * dm.n;
+  const size_t total = (size_t)dm.B * dm.Hu * dm.nt;
   const unsigned grid = (unsigned)((total + kEmitWaves - 1) / kEmitWaves);
   const size_t elds = sizeof(unsigned int) * kEmitWaves * (size_t)((dm.n + 31) / 32);
   hipLaunchKernelGGL(emit_kernel, dim3(grid), dim3(64 * kEmitWaves), elds, s, dm, bd, ranked,

@@ -160,6 +160,13 @@ for _base in ("llama8b_32k", "prefill_128k", "stem_32k"):
     WORKLOADS[_base + "_kvshared"] = dataclasses.replace(
         WORKLOADS[_base], name=_base + "_kvshared", select_unit=SELECT_PER_KV_HEAD)
 
+# Query tiles of 128 rows over key blocks of 64 (tile != block, not on the pages: a tile's two
+# diagonal blocks are both forced).  Same inputs as the per-head workloads; each K/V step then
+# feeds the four waves of a 128-row tile.
+for _base in ("llama8b_32k", "stem_32k"):
+    WORKLOADS[_base + "_t128"] = dataclasses.replace(
+        WORKLOADS[_base], name=_base + "_t128", q_tile=128)
+
 # Decode with run-time termination (ART page): one new token per sequence and head over a
 # 16K-token cache, 64 sequences (one workgroup per sequence and kv head: 512, two per CU; the
 # sequential traversal needs the second workgroup to keep HBM busy).  The selection fields are

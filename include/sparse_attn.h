@@ -29,7 +29,8 @@
  *   - Return value: SA_OK, or a negative status.  Arguments are validated on the host
  *     before any HIP call, so an invalid call enqueues nothing.  sparse_attn_last_error()
  *     gives the calling thread's last message.
- *   - Supported in this version: head_dim in {64, 128}; block == tile in {64, 128};
+ *   - Supported in this version: head_dim in {64, 128}; block == tile in {64, 128}, or
+ *     tile 128 over block 64;
  *     seqlen % block == 0; Hq % Hkv == 0; bf16 or fp32 inputs.
  */
 #ifndef SPARSE_ATTN_H_
@@ -64,7 +65,9 @@ typedef struct sa_problem {
   int32_t n_kv_heads;   /* Hkv >= 1 */
   int32_t head_dim;     /* d: 64 or 128 */
   int32_t block;        /* key block size: 64 or 128 */
-  int32_t tile;         /* query tile size: must equal block */
+  int32_t tile;         /* query tile rows T: equal to block, or 128 over blocks of 64 (then
+                           tile t's diagonal blocks 2t and 2t+1 are both forced, its free
+                           blocks are 0 .. 2t-1, and n below counts tiles, N / T) */
   int32_t dtype;        /* SA_BF16 or SA_F32, for Q, K and V */
   int32_t score_mode;   /* SA_KMEAN: mean-pooled keys; SA_KMINMAX: per-coordinate bound */
   int32_t output_aware; /* SA_OAM_OFF; SA_OAM_PRODUCT: tile score times the block's mean
@@ -81,7 +84,8 @@ typedef struct sa_problem {
                            number of selection units per sequence: Hq, or Hkv. */
 } sa_problem;
 
-/* Budget, forced blocks and gate.  n = seqlen / block tiles (= blocks) per sequence. */
+/* Budget, forced blocks and gate.  n = seqlen / tile query tiles per sequence (equal to the
+ * number of blocks when tile = block). */
 typedef struct sa_budget {
   int32_t k_max;     /* free blocks kept per tile (constant budget), or the decay's start */
   int32_t k_min;     /* floor of the decaying budget; 1 <= k_min <= k_max */
@@ -113,7 +117,8 @@ size_t sparse_attn_summary_bytes(const sa_problem* p);
 size_t sparse_attn_select_workspace_bytes(const sa_problem* p, const sa_budget* b);
 
 /*
- * W, the entries per padded list: min(n, 1 + n_sink + floor(rho * k_max)).
+ * W, the entries per padded list: min(seqlen / block, tile / block + n_sink +
+ * floor(rho * k_max)) (tile / block diagonal blocks).
  * Returns a negative status for invalid arguments.
  */
 int32_t sparse_attn_index_width(const sa_problem* p, const sa_budget* b);
@@ -136,16 +141,17 @@ int sparse_attn_score(const sa_problem* p, const void* K, const void* V, void* s
  *   summaries  from sparse_attn_score on the same problem.
  *   ws         sparse_attn_select_workspace_bytes(p, b) bytes of scratch, contents ignored.
  *   kv_idx     int32 [B, U, n, W], W = sparse_attn_index_width(p, b), U = Hq or Hkv (see
- *              select_unit): tile t's kept blocks in ascending order (so the diagonal block t
- *              is last), then -1 sentinels.
+ *              select_unit): tile t's kept blocks in ascending order (so its diagonal block or
+ *              blocks come last), then -1 sentinels.
  *   kv_cnt     int32 [B, U, n]: number of non-sentinel entries.
  *   sigma      optional (NULL to skip) fp32 [B, U, n]: cut margin per tile and unit; 1.0
  *              for a tile with at most k_t free candidates (not eligible).
  *   sigma_bar  optional fp32 [B, n]: mean of sigma over the U units.
  *   gate       optional uint8 [B, n]: 1 where the tile tripped and kept floor(rho * k_t).
  *   tau        optional fp32 [B]: the threshold used (-inf when nothing can trip).
- * Free blocks of tile t are the causal blocks 0..t minus the forced ones (the diagonal t and
- * the n_sink first blocks); they rank by tile score, ties to the lower index.  Scores are
+ * Free blocks of tile t are the blocks before its diagonal ones (block t, or blocks 2t and
+ * 2t+1 for 128-row tiles over 64-key blocks) minus the n_sink first blocks; they rank by
+ * tile score, ties to the lower index; the diagonal and sink blocks are always kept.  Scores are
  * fp32 with a fixed reduction order, so the lists are reproducible bit for bit.
  */
 int sparse_attn_select(const sa_problem* p, const sa_budget* b, const void* Q,
@@ -164,7 +170,8 @@ size_t sparse_attn_forward_workspace_bytes(const sa_problem* p);
  *                  select_unit (query head h reads unit h, or its kv head h / (Hq / Hkv));
  *                  any order of blocks is accepted; the
  *                  list of query tile t ends at kv_cnt or at the first negative entry;
- *                  entries must be distinct blocks <= t, others are skipped).
+ *                  entries must be distinct causal blocks of the tile (<= its last
+ *                  diagonal block), others are skipped).
  *   W              row stride of kv_idx (its last dimension), >= 1.
  *   softmax_scale  logit scale, normally 1/sqrt(d).
  *   ws             sparse_attn_forward_workspace_bytes(p) bytes of scratch (may be NULL when

@@ -97,7 +97,9 @@ def test_sizes(lib):
 BAD_PROBLEMS = [
     (dict(head_dim=96), api.SA_ERR_UNSUPPORTED),
     (dict(block=32, tile=32), api.SA_ERR_UNSUPPORTED),
-    (dict(tile=128), api.SA_ERR_UNSUPPORTED),
+    (dict(tile=256), api.SA_ERR_UNSUPPORTED),
+    (dict(block=128, tile=64), api.SA_ERR_UNSUPPORTED),
+    (dict(seqlen=64 * 511, tile=128), api.SA_ERR_INVALID),
     (dict(seqlen=1000), api.SA_ERR_INVALID),
     (dict(n_q_heads=30), api.SA_ERR_INVALID),
     (dict(batch=0), api.SA_ERR_INVALID),

@@ -26,7 +26,7 @@ from parity import bits, check_structure, out_tol, say
 pytestmark = pytest.mark.gpu
 
 FULL = ["llama8b_32k", "prefill_128k", "quest_64k", "stem_32k", "stem_additive_32k",
-        "llama8b_32k_kvshared", "stem_32k_kvshared"]
+        "llama8b_32k_kvshared", "stem_32k_kvshared", "llama8b_32k_t128", "stem_32k_t128"]
 
 
 def _sample_tiles(n, gate_row, rng, extra=4):
@@ -49,7 +49,7 @@ def test_full_size_sampled_parity(name):
     pf.run(d["Q"], d["K"], d["V"])
     torch.cuda.synchronize()
     say(f"[full] {name}: GPU pipeline done")
-    n, B, Hq, G = w.n_blocks, w.batch, w.n_q_heads, w.n_q_heads // w.n_kv_heads
+    n, B, Hq, G = w.n_tiles, w.batch, w.n_q_heads, w.n_q_heads // w.n_kv_heads
     kv_idx, kv_cnt = pf.kv_idx.cpu().numpy(), pf.kv_cnt.cpu().numpy()
     sigma, sigma_bar = pf.sigma.cpu().numpy(), pf.sigma_bar.cpu().numpy()
     gate, tau = pf.gate.cpu().numpy(), pf.tau.cpu().numpy()
@@ -62,7 +62,7 @@ def test_full_size_sampled_parity(name):
     # Summaries, in full.
     cfg = oracle.make_cfg(w)
     summ = oracle.pool(cfg, inp["K"], inp["V"])
-    plane = B * n * w.n_kv_heads * w.head_dim
+    plane = B * w.n_blocks * w.n_kv_heads * w.head_dim
     g_summ = pf.summ.cpu().numpy()
     np.testing.assert_array_equal(bits(g_summ[:plane]), bits(summ["kA"].reshape(-1)))
     off = plane
@@ -70,7 +70,7 @@ def test_full_size_sampled_parity(name):
         np.testing.assert_array_equal(bits(g_summ[plane:2 * plane]), bits(summ["kB"].reshape(-1)))
         off = 2 * plane
     if w.output_aware:
-        np.testing.assert_array_equal(bits(g_summ[off:off + B * n * w.n_kv_heads]),
+        np.testing.assert_array_equal(bits(g_summ[off:off + B * w.n_blocks * w.n_kv_heads]),
                                       bits(summ["vn"].reshape(-1)))
 
     # Selection of sampled tiles, every head.

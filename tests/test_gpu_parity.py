@@ -60,6 +60,20 @@ SMALL = {
     "prefill_n32_kvshared": WL["prefill_128k_kvshared"].resized(seqlen=4096, k_max=6, k_min=6),
     "f32_kvshared": WL["tiny_ref"].resized(seqlen=1024, n_q_heads=4, n_kv_heads=2, k_max=3,
                                            k_min=3, select_unit=wl.SELECT_PER_KV_HEAD),
+    # query tiles of 128 rows over blocks of 64 keys (two diagonal blocks per tile)
+    "llama8b_n16_t128": WL["llama8b_32k_t128"].resized(seqlen=2048, k_max=6, k_min=6),
+    "stem_b2_t128": WL["stem_32k_t128"].resized(batch=2, seqlen=2560, k_max=12, k_min=3,
+                                                n_sink=3),
+    "quest_d64_t128": WL["quest_64k"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=2,
+                                              head_dim=64, k_max=3, k_min=3, q_tile=128,
+                                              output_aware=1),
+    "t128_kvshared": WL["llama8b_32k_t128"].resized(seqlen=2048, k_max=5, k_min=5,
+                                                    select_unit=wl.SELECT_PER_KV_HEAD),
+    "f32_t128": WL["tiny_ref"].resized(seqlen=1024, n_q_heads=2, n_kv_heads=1, k_max=3,
+                                       k_min=3, q_tile=128),
+    "f32_t128_d128": WL["tiny_ref"].resized(seqlen=768, n_q_heads=2, n_kv_heads=2,
+                                            head_dim=128, k_max=2, k_min=2, q_tile=128,
+                                            score_mode=wl.KMINMAX),
 }
 
 MAX_ORACLE_ROWS = 6000
@@ -70,9 +84,9 @@ def sample_rows(w, rng, max_rows=MAX_ORACLE_ROWS):
     total = w.batch * w.seqlen * w.n_q_heads
     if total <= max_rows:
         return None
-    T = w.block
+    T = w.tile
     fixed = []
-    for t in (0, 1, w.n_blocks - 1):
+    for t in (0, 1, w.n_tiles - 1):
         for i in range(t * T, (t + 1) * T):
             fixed.append((0, 0, i))
     k = max_rows - len(fixed)
