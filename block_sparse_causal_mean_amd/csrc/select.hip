@@ -312,7 +312,9 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
 constexpr int kScoreThreads = 256;
 constexpr float kPrefilterC = 0x1.2p-8f;
 
-template <int MODE, int OAM, int D, int TILE>
+// GRP: selection units of several query heads (one list per kv head).  A separate
+// instantiation, because the loop over the unit's heads costs the one-head case registers.
+template <int MODE, int OAM, int D, int TILE, bool GRP>
 // Three waves per SIMD (at most 168 registers): as many workgroups as the LDS allows (three
 // per CU), measured 23% faster than the compiler's default of two waves per SIMD.
 __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
@@ -348,16 +350,11 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
   for (int f = threadIdx.x; f < P; f += kScoreThreads)
     keys[f] = f < nf ? (unsigned long long)(0xffffffffu - (unsigned)(j0 + f)) : 0ull;
 
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int l32 = lane & 31, hi = lane >> 5;
-  // 32-block chunks of this (batch, kv head) covering the free blocks [j0, d0).
-  const size_t chunk0 = ((size_t)b * dm.Hkv + g) * ncb;
-  constexpr size_t BFC = (size_t)NPL * D * 32, XC = (size_t)NPL * D * 32;
-
   // The unit's query heads in turn (one pass per head).  Each free block's key holds the
   // largest tile score over the passes so far: the output-aware combine and the order key are
   // monotone, so the maximum over all of the unit's rows is exact.
-  for (int h = u * dm.gs; h < (u + 1) * dm.gs; ++h) {
+  const int h_end = GRP ? (u + 1) * dm.gs : u + 1;
+  for (int h = GRP ? u * dm.gs : u; h < h_end; ++h) {
   __syncthreads();  // the previous pass has finished reading qs and qmax_w
 
   // Stage the tile's Q rows; row norms (any order: they only scale the bound) -> max.  Each
@@ -411,6 +408,12 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
 #pragma unroll
   for (int k = 1; k < kScoreThreads / 64; ++k) qmax2 = fmaxf(qmax2, qmax_w[k]);
   const float qmax = __builtin_sqrtf(qmax2);
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  // 32-block chunks of this (batch, kv head) covering the free blocks [j0, d0).
+  const size_t chunk0 = ((size_t)b * dm.Hkv + g) * ncb;
+  constexpr size_t BFC = (size_t)NPL * D * 32, XC = (size_t)NPL * D * 32;
 
   for (int ch = (j0 >> 5) + wv; ch * 32 < d0; ch += kScoreThreads / 64) {
     const int j = ch * 32 + l32;  // this lane's block
@@ -761,24 +764,32 @@ hipError_t score_dispatch(const Dims& dm, const BudgetDev& bd, const void* Q, co
   return score_by_oam<T, SA_KMINMAX>(dm, bd, Q, summ, ranked, sigma, s);
 }
 
-template <int MODE, int OAM, int D, int TILE>
-hipError_t launch_score_mfma(const Dims& dm, const BudgetDev& bd, const void* Q,
+template <int MODE, int OAM, int D, int TILE, bool GRP>
+hipError_t launch_score_mfma_g(const Dims& dm, const BudgetDev& bd, const void* Q,
                              const float* summ, int* ranked, float* sigma, hipStream_t s) {
   const SummaryLayout L = summary_layout(dm);
   int P = 1;
   while (P < dm.n) P <<= 1;
   constexpr int NPL = MODE == SA_KMINMAX ? 2 : 1;
   const size_t lds = sizeof(unsigned long long) * P + sizeof(uint16_t) * NPL * TILE * (D + 8);
-  hipError_t e = allow_lds(score_rank_mfma<MODE, OAM, D, TILE>, lds);
+  hipError_t e = allow_lds(score_rank_mfma<MODE, OAM, D, TILE, GRP>, lds);
   if (e != hipSuccess) return e;
   const char* base = reinterpret_cast<const char*>(summ);
   const unsigned grid = (unsigned)((size_t)dm.B * dm.Hu * dm.nt);
-  hipLaunchKernelGGL((score_rank_mfma<MODE, OAM, D, TILE>), dim3(grid), dim3(kScoreThreads),
+  hipLaunchKernelGGL((score_rank_mfma<MODE, OAM, D, TILE, GRP>), dim3(grid), dim3(kScoreThreads),
                      lds, s, dm, bd, static_cast<const uint16_t*>(Q), summ,
                      reinterpret_cast<const uint16_t*>(base + L.bfc_byte),
                      reinterpret_cast<const float*>(base + L.xc_byte), ranked, sigma, L.vn, L.kn,
                      L.ncb);
   return hipGetLastError();
+}
+
+template <int MODE, int OAM, int D, int TILE>
+hipError_t launch_score_mfma(const Dims& dm, const BudgetDev& bd, const void* Q,
+                             const float* summ, int* ranked, float* sigma, hipStream_t s) {
+  return dm.gs > 1 ? launch_score_mfma_g<MODE, OAM, D, TILE, true>(dm, bd, Q, summ, ranked, sigma, s)
+                   : launch_score_mfma_g<MODE, OAM, D, TILE, false>(dm, bd, Q, summ, ranked, sigma,
+                                                                    s);
 }
 
 template <int MODE, int OAM>
