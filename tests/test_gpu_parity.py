@@ -172,6 +172,22 @@ EDGE = {
                                                k_min=4, near_tie_keys=False),
     "tied_blocks": WL["llama8b_32k"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=2, k_max=4,
                                              k_min=4),
+    # 128-row tiles over 64-key blocks, and lists shared by a kv head's query heads
+    "t128_single_tile": WL["llama8b_32k_t128"].resized(seqlen=128, k_max=2, k_min=2),
+    "t128_dense_limit": WL["llama8b_32k_t128"].resized(seqlen=1024, n_q_heads=4, n_kv_heads=2,
+                                                       k_max=64, k_min=64),
+    "t128_q1_all_trip": WL["llama8b_32k_t128"].resized(seqlen=2048, n_q_heads=4, n_kv_heads=1,
+                                                       k_max=4, k_min=4, q=1.0),
+    "t128_fixed_gate_odd_sinks": WL["stem_32k_t128"].resized(
+        batch=1, seqlen=1280, n_q_heads=4, n_kv_heads=2, n_sink=5, k_max=4, k_min=2,
+        gate_mode=wl.GATE_FIXED, tau_fixed=0.3),
+    "tied_blocks_t128": WL["llama8b_32k_t128"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=2,
+                                                       k_max=4, k_min=4),
+    "kvshared_dense_limit": WL["llama8b_32k_kvshared"].resized(seqlen=1024, n_q_heads=4,
+                                                               n_kv_heads=2, k_max=64, k_min=64),
+    "tied_rows_kvshared": WL["prefill_128k_kvshared"].resized(seqlen=2048, n_q_heads=4,
+                                                              n_kv_heads=2, k_max=4, k_min=4,
+                                                              planted=False),
 }
 
 
@@ -182,11 +198,11 @@ def _edge_inputs(name, w):
         # every row of a query tile equal: every row ties for each block's maximum, so the
         # prefilter keeps all of them as candidates
         q = inp["Q"].clone()
-        T = w.block
-        for t in range(w.n_blocks):
+        T = w.tile
+        for t in range(w.n_tiles):
             q[:, t * T:(t + 1) * T] = q[:, t * T:t * T + 1]
         inp["Q"] = q
-    if name == "tied_blocks":
+    if name.startswith("tied_blocks"):
         # every key block identical: all tile scores of a tile tie, ranking falls to the index
         k = inp["K"].clone()
         T = w.block
@@ -210,12 +226,15 @@ def test_edge_cases(name):
     check_structure(w, g["kv_idx"], g["kv_cnt"], g["gate"], g["sigma"], g["sigma_bar"],
                     g["tau"])
     compare_outputs(w, g, inp, api.SA_F32, sample_rows(w, np.random.default_rng(1)))
-    if name == "dense_limit":
-        assert np.all(g["kv_cnt"] == np.arange(1, w.n_blocks + 1))
+    m = w.tile // w.block  # diagonal blocks per tile
+    t = np.arange(w.n_tiles)
+    if name.endswith("dense_limit"):  # every causal block of every tile
+        assert np.all(g["kv_cnt"] == m * (t + 1))
     if name == "q0_no_trips" or name == "gate_off":
         assert g["gate"].sum() == 0
-    if name == "q1_all_trip":  # tau is the largest eligible sigma_bar: every eligible tile trips
-        assert g["gate"].sum() == w.n_blocks - w.k_max - 1
+    if name.endswith("q1_all_trip"):  # tau = the largest eligible sigma_bar: every one trips
+        nfree = m * t - np.minimum(m * t, w.n_sink)
+        assert g["gate"].sum() == int((nfree > w.k_max).sum()) > 0
 
 
 def test_forward_any_block_order_and_skipped_entries():
