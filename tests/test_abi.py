@@ -214,3 +214,39 @@ def test_forward_vs_validation(lib):
     assert call(slash=None, ns=2) == api.SA_ERR_INVALID
     assert call(ws_bytes=ok_ws - 1) == api.SA_ERR_INVALID
     assert call(out=7) == api.SA_ERR_INVALID
+
+
+def test_sizes_per_kv_head_lists_and_wide_tiles(lib):
+    """Lists per kv head shrink the selection workspace by the group size; 128-row tiles over
+    64-key blocks add a second forced diagonal block to each list and halve the tile count."""
+    w = wl.WORKLOADS["llama8b_32k"]
+    p, b = api.problem(w), api.budget(w)
+    pk = api.problem(wl.WORKLOADS["llama8b_32k_kvshared"])
+    pt = api.problem(wl.WORKLOADS["llama8b_32k_t128"])
+    assert api.units(p) == 32 and api.units(pk) == 8
+    ws, wsk = api.select_workspace_bytes(p, b), api.select_workspace_bytes(pk, b)
+    assert wsk < ws and wsk >= 8 * 512 * 64 * 4  # ranked keys per (kv head, tile)
+    assert api.index_width(pt, b) == 2 + 0 + 64 == wl.WORKLOADS["llama8b_32k_t128"].index_width()
+    assert api.select_workspace_bytes(pt, b) < ws  # 256 tiles instead of 512
+    # the block summaries do not depend on the tile or the selection unit
+    assert api.summary_bytes(pk) == api.summary_bytes(pt) == api.summary_bytes(p)
+
+
+def test_wide_tiles_rejected_where_unsupported(lib):
+    """128-row tiles over 64-key blocks are a selection-and-prefill variant: the vertical-slash
+    path and decode reject them before any HIP call."""
+    pt = api.problem(wl.WORKLOADS["llama8b_32k_t128"])
+    ws = api.forward_workspace_bytes(pt)
+    rc = lib.sparse_attn_forward_vs(ctypes.byref(pt), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, 0.1,
+                                    FAKE, ws, FAKE, api.SA_BF16, None, None)
+    assert rc == api.SA_ERR_UNSUPPORTED and "tile" in api.last_error()
+    rc = lib.sparse_attn_decode_art(ctypes.byref(pt), FAKE, FAKE, FAKE, 0.1, 0.01, 0.01, 2, FAKE,
+                                    api.SA_BF16, FAKE, None)
+    assert rc == api.SA_ERR_UNSUPPORTED and "tile" in api.last_error()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess, sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0 and "one GPU" in (r.stdout + r.stderr)
