@@ -57,7 +57,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Index of the next usable list entry at or after e, or -1: the list ends at cnt or at the
-// first negative entry; entries after the tile (j > t) are skipped.
+// first negative entry; entries after the tile's last causal block (j > t) are skipped.
 __device__ __forceinline__ int next_entry(const int32_t* __restrict__ list, int cnt, int e,
                                           int t) {
   for (; e < cnt; ++e) {
@@ -420,10 +420,11 @@ __device__ void reorder_shared(const int32_t* __restrict__ list, const int32_t* 
 }
 
 // Stages the next segment of a tile's list in LDS and orders it; run by the whole workgroup.
-// Usable entries are those with 0 <= j <= t before the first negative entry; at most LCAP of
-// them per segment (wave 0 compacts, the workgroup waits).  seg_info receives: usable entries,
-// position of the diagonal block (-1 if absent), the list position the next segment starts
-// at, and whether this segment ends the list.
+// Usable entries are the tile's causal blocks (0 <= j < m (t + 1), m = 1 or 2 diagonal blocks
+// per tile) before the first negative entry; at most LCAP of them per segment (wave 0
+// compacts, the workgroup waits).  seg_info receives: usable entries, position of the first
+// diagonal block m t (-1 if absent), the list position the next segment starts at, whether
+// this segment ends the list, and the position of the second diagonal block m t + 1.
 //
 // Single-segment lists are then ordered so that blocks listed by more of the kv head's query
 // heads come first (ties by index): the G workgroups of the tile run together on one XCD and

@@ -51,7 +51,7 @@ struct BudgetDev {
   int k_max, k_min, kind, n_sink, gate_mode;
   float tau_fixed;
   double rho, q;
-  int R;  // ranked entries stored per (b, h, t)
+  int R;  // ranked entries stored per (b, unit, t)
   int W;  // entries per padded list
   int m;  // diagonal blocks per tile: tile t's are m t .. m t + m - 1, its free ones < m t
 };

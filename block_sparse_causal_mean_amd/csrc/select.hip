@@ -12,8 +12,12 @@
 // Stem page, Metodologia A: the budget k_t may decay linearly with the tile's position, and
 // early blocks act as anchors (here: n_sink blocks always kept).
 //
+// Selection runs per (batch, unit, tile): the unit is a query head, or a kv head whose query
+// heads share one list (the tile score then being the maximum over all of their rows).  A
+// tile of 128 rows over 64-key blocks has two diagonal blocks, both forced.
+//
 // Three stream-ordered launches, no host synchronisation:
-//   score_rank  one workgroup per (b, h, t), tiles launched latest-first (they carry the most
+//   score_rank  one workgroup per (b, unit, t), tiles launched latest-first (they carry the most
 //               blocks).  One wave per 64 query rows; lane = query row, with the row held in
 //               registers as fp32.  Each block summary is read by the whole wave at one
 //               uniform address (scalar loads), so every fused multiply-add takes one operand
@@ -21,16 +25,16 @@
 //               chains in coordinate order.  The wave's maximum over rows goes to LDS as an
 //               order-preserving 64-bit key (score, then lower index first), merged across
 //               the tile's waves with an LDS atomic max, then sorted by a bitonic network.
-//   gate        one workgroup per batch element: head mean, eligible count, the quantile's
-//               order statistic (bitonic sort of the eligible sigma_bar), gate bits.
-//   emit        one wave per (b, h, t): forced blocks and the kept ranked blocks marked in
+//   gate        one workgroup per batch element: mean over units, eligible count, the
+//               quantile's order statistic (bitonic sort of the eligible sigma_bar), gate bits.
+//   emit        one wave per (b, unit, t): forced blocks and the kept ranked blocks marked in
 //               an LDS bitmap, then written out in ascending order with a wave prefix sum.
 //
 // The arithmetic that decides selections is IEEE fp32 with a fixed order (compiled without
 // contraction): row score = fused multiply-add chain over coordinates in order, starting at
 // +0; tile score = maximum over rows, with -0 mapped to +0, times the value norm when the
 // score is output-aware; sigma = two subtractions and a correctly rounded division;
-// sigma_bar = sum over heads in order divided by the head count; the quantile rank
+// sigma_bar = sum over units in order divided by their count; the quantile rank
 // ceil(q * M) in fp64.
 
 #include "common.h"
@@ -299,7 +303,8 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
 // Usually one row per block qualifies (1.3 on average at 128K), so the fp32 chain work falls
 // by about the tile height.
 //
-// One workgroup (4 waves) per (b, h, t).  The tile's Q rows are staged in LDS as bf16 (for
+// One workgroup (4 waves) per (b, unit, t); a unit of several query heads takes one pass per
+// head, each block keeping its largest score.  The tile's Q rows are staged in LDS as bf16 (for
 // the bound backbone as its positive and negative parts, so q+ . kmax + q- . kmin gives
 // the per-coordinate maximum); each wave takes aligned 32-block chunks covering the free
 // blocks, holds a 32-block x all-rows score tile in accumulators (lane = block, 16 rows per
