@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_v(Dims dm, const uint16_t* 
   const uint16_t* src = V + (((size_t)b * dm.N + (size_t)s * kStep) * dm.Hkv + g) * D;
   for (int c = threadIdx.x; c < kStep * D / 8; c += kPackThreads) {
     const int r = c / (D / 8), col = c - r * (D / 8);
-    const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)r * dm.Hkv * D + col * 8);
+    const uint4 v = load_nt16(src + (size_t)r * dm.Hkv * D + col * 8);  // V is read once
     uint32_t* dst = reinterpret_cast<uint32_t*>(sv + r * RS + col * 8);
     dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
   }

@@ -24,6 +24,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// 16-byte global load marked non-temporal: for data a kernel streams once (its lines are not
+// worth keeping in the caches).
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
 // x + 0.0f: maps -0 to +0, leaves every other value unchanged.
 __device__ __forceinline__ float canon(float x) { return x + 0.0f; }
 

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
   auto chunk_src = [&](const uint16_t* base, int j, int i) {
     const int q = (int)threadIdx.x + i * kArtThreads;
     const int r = q / CH, cc = q - r * CH;
-    return *reinterpret_cast<const uint4*>(base + ((size_t)j * kArtBlk + r) * rstride + cc * 8);
+    return load_nt16(base + ((size_t)j * kArtBlk + r) * rstride + cc * 8);  // read once
   };
   uint4 kr[kArtPrefetch][CPT], vr[kArtPrefetch][CPT];
 #pragma unroll

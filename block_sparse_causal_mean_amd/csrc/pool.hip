@@ -83,11 +83,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_keys(const T* __restrict__ 
 #pragma unroll
     for (int k = 0; k < NCH / kPoolThreads; ++k) {
       const int c = threadIdx.x + k * kPoolThreads;
-      // read once here: a non-temporal load (no point keeping K's lines in the caches)
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 x = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(src + (size_t)(c / CPR) * span + (c % CPR) * E));
-      v[k] = make_uint4(x.x, x.y, x.z, x.w);
+      v[k] = load_nt16(src + (size_t)(c / CPR) * span + (c % CPR) * E);  // K is read once
     }
 #pragma unroll
     for (int k = 0; k < NCH / kPoolThreads; ++k) tile[threadIdx.x + k * kPoolThreads] = v[k];
