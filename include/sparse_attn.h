@@ -46,7 +46,7 @@ extern "C" {
 enum {
   SA_OK = 0,
   SA_ERR_INVALID = -1,     /* bad argument: null pointer, out-of-range value, small buffer */
-  SA_ERR_UNSUPPORTED = -2, /* valid but not supported by this build (shape, dtype) */
+  SA_ERR_UNSUPPORTED = -2, /* valid but not supported by this library version (shape, dtype) */
   SA_ERR_HIP = -3          /* a HIP call failed (launch, device query) */
 };
 
