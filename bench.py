@@ -9,10 +9,15 @@ another.  Prints ONE JSON line on stdout; progress goes to stderr.
 
   value         tokens/s = B * N * steps / timed seconds
   roofline      the attention kernel (the dominant one) against bf16 matrix-core peak, on
-                effective FLOPs (4 * tile * block * d per listed block), timed with HIP
-                events on the stream it runs on
-  score_roofline  the block-summary kernel against HBM peak (algorithmic bytes: keys read
-                once, summaries written once), timed after evicting the caches
+                effective FLOPs (4 * tile * block * d per listed block), timed on its own
+                with HIP events on the stream it runs on: the forward pass runs as its two
+                halves, sparse_attn_prepare_values (V to fp16 images) and
+                sparse_attn_forward_prepared (the attention kernel alone); the causal-exact
+                FLOP count (masked pairs of the diagonal blocks left out) is reported beside
+  score_roofline  the block-summary kernel against HBM peak on its algorithmic bytes (keys,
+                and values when output-aware, read once; the public summary planes written
+                once), timed after evicting the caches; the selection's private copies of
+                the summaries, written by the same kernel, are reported separately
   cpu_baseline  the CPU oracle on a bounded sample of the same workload (see "sample")
 """
 
@@ -66,6 +71,30 @@ def effective_flops(w: wl.Workload, kv_cnt: torch.Tensor) -> float:
     counts once per head)."""
     heads_per_list = w.n_q_heads // w.n_units
     return 4.0 * w.tile * w.block * w.head_dim * heads_per_list * float(kv_cnt.sum().item())
+
+
+def causal_exact_flops(w: wl.Workload, kv_idx: torch.Tensor, kv_cnt: torch.Tensor) -> float:
+    """4 d per (query row, key) pair the attention actually computes: every pair of a listed
+    block with the key at or before the row (the masked half of the diagonal blocks left
+    out), per query head."""
+    idx = kv_idx.cpu().numpy().astype(np.int64)
+    cnt = kv_cnt.cpu().numpy()
+    T, Bk = w.tile, w.block
+    valid = np.arange(idx.shape[-1])[None, None, None, :] < cnt[..., None]
+    t = np.broadcast_to(np.arange(idx.shape[2])[None, None, :, None], idx.shape)
+    j = idx[valid]
+    t = t[valid]
+    # rows i = tT .. tT+T-1, keys p = jB .. jB+B-1: pairs with p <= i
+    i0, p0 = t * T, j * Bk
+    full = p0 + Bk - 1 <= i0
+    pairs = np.where(full, T * Bk, 0).astype(np.float64)
+    part = ~full
+    if part.any():
+        r = np.arange(T)[None, :]
+        c = np.clip(i0[part][:, None] + r - p0[part][:, None] + 1, 0, Bk)
+        pairs[part] = c.sum(axis=1)
+    heads_per_list = w.n_q_heads // w.n_units
+    return 4.0 * w.head_dim * heads_per_list * float(pairs.sum())
 
 
 def vs_block_counts(w: wl.Workload, vert: np.ndarray, slash: np.ndarray) -> np.ndarray:
@@ -360,7 +389,10 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warmup steps done")
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # One step: score, select, then the forward pass as its two halves (V prepared, then the
+    # attention kernel), with an event between each so the attention kernel is timed alone.
+    bf16 = w.dtype == wl.BF16
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -369,26 +401,40 @@ def main():
         ev[i][1].record(s)
         pf.select(Q)
         ev[i][2].record(s)
-        pf.forward(Q, K, V)
-        ev[i][3].record(s)
+        if bf16:
+            pf.prepare_values(V)
+            ev[i][3].record(s)
+            pf.forward_prepared(Q, K)
+        else:
+            ev[i][3].record(s)
+            pf.forward(Q, K, V)
+        ev[i][4].record(s)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    stage = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(3)]
+    stage = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(4)]
                       for i in range(args.steps)])
-    ms_score, ms_select, ms_fwd = stage.mean(axis=0)
+    ms_score, ms_select, ms_prep, ms_attn = stage.mean(axis=0)
+    ms_fwd = ms_prep + ms_attn
     log(f"[bench] {args.steps} steps in {elapsed:.3f}s: score {ms_score:.3f} ms, select "
-        f"{ms_select:.3f} ms, forward {ms_fwd:.3f} ms")
+        f"{ms_select:.3f} ms, forward {ms_fwd:.3f} ms (values {ms_prep:.3f} + attention "
+        f"{ms_attn:.3f})")
 
     tokens = w.batch * w.seqlen
     value = tokens * args.steps / elapsed
     flops = effective_flops(w, pf.kv_cnt)
-    achieved = flops / (ms_fwd * 1e-3) / 1e12
+    exact_flops = causal_exact_flops(w, pf.kv_idx, pf.kv_cnt)
+    achieved = flops / (ms_attn * 1e-3) / 1e12
     dense = 4.0 * w.head_dim * w.seqlen * (w.seqlen + 1) / 2 * w.batch * w.n_q_heads
     traffic = traffic_from_profiles("attn_fwd_" + w.name)
 
     ms_cold = time_score_cold(pf, K, V)
-    kv_bytes = w.batch * w.seqlen * w.n_kv_heads * w.head_dim * 2
-    score_bytes = kv_bytes * (2 if w.output_aware else 1) + pf.summ.numel() * 4
+    elt = 2 if bf16 else 4
+    kv_bytes = w.batch * w.seqlen * w.n_kv_heads * w.head_dim * elt
+    planes = 2 if w.score_mode == wl.KMINMAX else 1
+    blocks = w.batch * w.n_blocks * w.n_kv_heads
+    public = 4 * (blocks * w.head_dim * planes + (blocks if w.output_aware else 0))
+    score_bytes = kv_bytes * (2 if w.output_aware else 1) + public
+    private_bytes = pf.summ.numel() * 4 - public
     score_gbs = score_bytes / (ms_cold * 1e-3) / 1e9
 
     gate = pf.gate.float().mean().item()
@@ -414,16 +460,25 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "kernel": "attn_bf16 (sparse_attn_forward)",
-                     "flops_per_launch": flops, "ms_per_launch": ms_fwd},
+                     "traffic": traffic,
+                     "kernel": ("attn_bf16 (sparse_attn_forward_prepared)" if bf16
+                                else "attn_f32 (sparse_attn_forward)"),
+                     "flops_per_launch": flops, "ms_per_launch": ms_attn,
+                     "causal_exact_flops_per_launch": exact_flops,
+                     "causal_exact_frac": exact_flops / (ms_attn * 1e-3) / 1e12
+                     / PEAK_BF16_TFLOPS},
         "score_roofline": {"bound": "hbm", "achieved": score_gbs, "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": score_gbs / PEAK_HBM_GBS,
                            "traffic": traffic_from_profiles("pool_keys_" + w.name),
-                           "bytes_per_launch": score_bytes, "ms_per_launch_cold": ms_cold,
+                           "bytes_per_launch": score_bytes,
+                           "private_copy_bytes_per_launch": private_bytes,
+                           "ms_per_launch_cold": ms_cold,
                            "kernel": "pool_keys (sparse_attn_score)"},
-        "stages_ms": {"score": ms_score, "select": ms_select, "forward": ms_fwd},
+        "stages_ms": {"score": ms_score, "select": ms_select, "forward": ms_fwd,
+                      "forward_values": ms_prep, "forward_attention": ms_attn},
         "selection": {"density_of_causal": density, "trip_fraction": gate,
-                      "dense_causal_flops": dense, "effective_flops": flops},
+                      "dense_causal_flops": dense, "effective_flops": flops,
+                      "causal_exact_flops": exact_flops},
     }
     if not args.no_cpu_baseline and rank == 0:
         log("[bench] timing the CPU oracle on a bounded sample")

@@ -32,7 +32,9 @@ SA_SELECT_PER_Q_HEAD, SA_SELECT_PER_KV_HEAD = 0, 1
 EXPORTS = ("sparse_attn_summary_bytes", "sparse_attn_select_workspace_bytes",
            "sparse_attn_index_width", "sparse_attn_score", "sparse_attn_select",
            "sparse_attn_forward_workspace_bytes", "sparse_attn_forward",
-           "sparse_attn_forward_vs", "sparse_attn_decode_art", "sparse_attn_last_error")
+           "sparse_attn_prepare_values", "sparse_attn_forward_prepared",
+           "sparse_attn_calibrate_tau", "sparse_attn_forward_vs", "sparse_attn_decode_art",
+           "sparse_attn_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -78,6 +80,11 @@ def load() -> ctypes.CDLL:
     lib.sparse_attn_forward_workspace_bytes.restype = ctypes.c_size_t
     lib.sparse_attn_forward.argtypes = [PP, P, P, P, P, P, ctypes.c_int32, ctypes.c_float, P,
                                         ctypes.c_size_t, P, ctypes.c_int32, P, P]
+    lib.sparse_attn_prepare_values.argtypes = [PP, P, P, ctypes.c_size_t, P]
+    lib.sparse_attn_forward_prepared.argtypes = [PP, P, P, P, ctypes.c_size_t, P, P,
+                                                 ctypes.c_int32, ctypes.c_float, P,
+                                                 ctypes.c_int32, P, P]
+    lib.sparse_attn_calibrate_tau.argtypes = [P, ctypes.c_int32, P, P]
     lib.sparse_attn_forward_vs.argtypes = [PP, P, P, P, P, ctypes.c_int32, P, ctypes.c_int32,
                                            ctypes.c_float, P, ctypes.c_size_t, P,
                                            ctypes.c_int32, P, P]
@@ -87,7 +94,8 @@ def load() -> ctypes.CDLL:
     lib.sparse_attn_last_error.argtypes = []
     lib.sparse_attn_last_error.restype = ctypes.c_char_p
     for f in ("sparse_attn_score", "sparse_attn_select", "sparse_attn_forward",
-              "sparse_attn_forward_vs", "sparse_attn_decode_art"):
+              "sparse_attn_prepare_values", "sparse_attn_forward_prepared",
+              "sparse_attn_calibrate_tau", "sparse_attn_forward_vs", "sparse_attn_decode_art"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -209,6 +217,41 @@ def forward(p: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
         _ptr(lse, "lse", p.batch * p.n_q_heads * p.seqlen * 4), _stream(stream)))
 
 
+def prepare_values(p: Problem, V: torch.Tensor, ws: torch.Tensor, stream=None):
+    """sparse_attn_prepare_values: V (bf16) into the forward workspace."""
+    kv = p.batch * p.seqlen * p.n_kv_heads * p.head_dim * _elt(p)
+    need = forward_workspace_bytes(p)
+    _check(load().sparse_attn_prepare_values(
+        ctypes.byref(p), _ptr(V, "V", kv), _ptr(ws, "ws", need),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def forward_prepared(p: Problem, Q: torch.Tensor, K: torch.Tensor, ws: torch.Tensor,
+                     kv_idx: torch.Tensor, kv_cnt: torch.Tensor, W: int, softmax_scale: float,
+                     O: torch.Tensor, out_dtype: int, lse: Optional[torch.Tensor] = None,
+                     stream=None):
+    """sparse_attn_forward_prepared: attention with V from prepare_values' workspace."""
+    n = p.seqlen // p.tile
+    q_bytes = p.batch * p.seqlen * p.n_q_heads * p.head_dim
+    kv = p.batch * p.seqlen * p.n_kv_heads * p.head_dim * _elt(p)
+    need = forward_workspace_bytes(p)
+    _check(load().sparse_attn_forward_prepared(
+        ctypes.byref(p), _ptr(Q, "Q", q_bytes * _elt(p)), _ptr(K, "K", kv),
+        _ptr(ws, "ws", need), 0 if ws is None else ws.numel() * ws.element_size(),
+        _ptr(kv_idx, "kv_idx", p.batch * units(p) * n * W * 4),
+        _ptr(kv_cnt, "kv_cnt", p.batch * units(p) * n * 4), W, softmax_scale,
+        _ptr(O, "O", q_bytes * (4 if out_dtype == SA_F32 else 2)), out_dtype,
+        _ptr(lse, "lse", p.batch * p.n_q_heads * p.seqlen * 4), _stream(stream)))
+
+
+def calibrate_tau(tau: torch.Tensor, tau_out: torch.Tensor, stream=None):
+    """sparse_attn_calibrate_tau: tau_out[0] = mean of the finite entries of tau (fp32 [B])."""
+    if tau.dtype != torch.float32 or tau_out.dtype != torch.float32:
+        raise ValueError("tau and tau_out must be float32")
+    _check(load().sparse_attn_calibrate_tau(_ptr(tau, "tau"), tau.numel(),
+                                            _ptr(tau_out, "tau_out", 4), _stream(stream)))
+
+
 def forward_vs(p: Problem, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
                vertical: torch.Tensor, slash: torch.Tensor, softmax_scale: float,
                ws: torch.Tensor, O: torch.Tensor, out_dtype: int,
@@ -299,6 +342,15 @@ class Prefill:
         forward(self.p, Q, K, V, self.kv_idx, self.kv_cnt, self.W, self.scale, self.fws,
                 self.O, self.out_dtype, self.lse, stream)
 
+    def prepare_values(self, V, stream=None):
+        """First half of forward (bf16): V into this object's forward workspace."""
+        prepare_values(self.p, V, self.fws, stream)
+
+    def forward_prepared(self, Q, K, stream=None):
+        """Second half of forward (bf16): the attention kernel over the prepared V."""
+        forward_prepared(self.p, Q, K, self.fws, self.kv_idx, self.kv_cnt, self.W, self.scale,
+                         self.O, self.out_dtype, self.lse, stream)
+
     def run(self, Q, K, V, stream=None):
         self.score(K, V, stream)
         self.select(Q, stream)
@@ -306,19 +358,19 @@ class Prefill:
         return self.O
 
     def calibrate_tau(self, Q, K, V=None) -> float:
-        """A threshold for SA_GATE_FIXED from calibration inputs (the Stem page pairs its
-        output-aware metric with a fixed, per-layer threshold; the gated-selection page's
-        per-call quantile is what calibrates it here): runs the summaries and the selection
-        with the quantile gate, whatever this object's gate mode, and returns the mean of
-        the per-batch-element thresholds, leaving out batch elements where nothing can trip
-        (-inf if none remain).  Overwrites this object's lists and statistics; synchronizes.
+        """A per-layer threshold for SA_GATE_FIXED from calibration inputs (gated-selection
+        page, Metodologia step 4: a per-layer empirical quantile of sigma_bar): runs the
+        summaries and the selection with the quantile gate, whatever this object's gate mode,
+        then sparse_attn_calibrate_tau on the per-sequence thresholds.  Overwrites this
+        object's lists and statistics; synchronizes to return the value.
         """
         b = budget(self.w)
         b.gate_mode = SA_GATE_QUANTILE
-        tau = torch.empty((self.w.batch,), dtype=torch.float32, device=self.summ.device)
+        dev = self.summ.device
+        tau = torch.empty((self.w.batch,), dtype=torch.float32, device=dev)
+        out = torch.empty((1,), dtype=torch.float32, device=dev)
         self.score(K, V)
         select(self.p, b, Q, self.summ, self.ws, self.kv_idx, self.kv_cnt, self.sigma,
                self.sigma_bar, self.gate, tau, None)
-        torch.cuda.synchronize()
-        t = tau[torch.isfinite(tau)]
-        return float(t.double().mean()) if t.numel() else float("-inf")
+        calibrate_tau(tau, out)
+        return float(out.cpu()[0])

@@ -122,6 +122,32 @@ int check_budget(const sa_budget* b, const sa::Dims& D, sa::BudgetDev* bd) {
   return SA_OK;
 }
 
+// LDS the selection kernels need grows with the number of blocks (one sort key each) and the
+// tile's staged query rows; refused here rather than failing at launch.
+int check_select_lds(const sa::Dims& D) {
+  const size_t need = sa::score_rank_lds(D);
+  if (need > sa::kMaxDynLds)
+    return fail(SA_ERR_UNSUPPORTED,
+                "selection needs %zu bytes of LDS per workgroup (at most %zu): %d blocks of %d "
+                "keys, %d-row tiles, head_dim %d%s",
+                need, sa::kMaxDynLds, D.n, D.blk, D.T, D.d,
+                D.score_mode == SA_KMINMAX ? ", K-min/K-max bound" : "");
+  if (sa::gate_lds(D) > sa::kMaxDynLds)
+    return fail(SA_ERR_UNSUPPORTED, "the gate needs %zu bytes of LDS (at most %zu)",
+                sa::gate_lds(D), sa::kMaxDynLds);
+  return SA_OK;
+}
+
+// The output-aware summaries hold one norm per (row, kv head) of a block in LDS.
+int check_score_lds(const sa::Dims& D) {
+  if (D.oam && sa::value_norms_lds(D) > sa::kMaxDynLds)
+    return fail(SA_ERR_UNSUPPORTED,
+                "output-aware scoring needs %zu bytes of LDS (block %d x %d kv heads x 4; at "
+                "most %zu)",
+                sa::value_norms_lds(D), D.blk, D.Hkv, sa::kMaxDynLds);
+  return SA_OK;
+}
+
 size_t summary_bytes(const sa::Dims& D) { return sa::summary_layout(D).bytes; }
 
 int hip_status(hipError_t e, const char* what) {
@@ -142,7 +168,9 @@ size_t sparse_attn_summary_bytes(const sa_problem* p) {
 size_t sparse_attn_select_workspace_bytes(const sa_problem* p, const sa_budget* b) {
   sa::Dims D;
   sa::BudgetDev bd;
-  if (check_problem(p, &D) != SA_OK || check_budget(b, D, &bd) != SA_OK) return 0;
+  if (check_problem(p, &D) != SA_OK || check_budget(b, D, &bd) != SA_OK ||
+      check_select_lds(D) != SA_OK)
+    return 0;
   return sa::select_ws_layout(D, bd).total;
 }
 
@@ -162,6 +190,7 @@ int sparse_attn_score(const sa_problem* p, const void* K, const void* V, void* s
   if (rc != SA_OK) return rc;
   if (!K || !summaries) return fail(SA_ERR_INVALID, "K and summaries must be non-NULL");
   if (D.oam && !V) return fail(SA_ERR_INVALID, "V is required when output_aware is set");
+  if ((rc = check_score_lds(D)) != SA_OK) return rc;
   g_err.clear();
   return hip_status(sa::launch_pool(D, K, V, static_cast<float*>(summaries),
                                     static_cast<hipStream_t>(stream)),
@@ -177,6 +206,7 @@ int sparse_attn_select(const sa_problem* p, const sa_budget* b, const void* Q,
   int rc = check_problem(p, &D);
   if (rc != SA_OK) return rc;
   if ((rc = check_budget(b, D, &bd)) != SA_OK) return rc;
+  if ((rc = check_select_lds(D)) != SA_OK) return rc;
   if (!Q || !summaries || !ws || !kv_idx || !kv_cnt)
     return fail(SA_ERR_INVALID, "Q, summaries, ws, kv_idx and kv_cnt must be non-NULL");
   const size_t need = sa::select_ws_layout(D, bd).total;
@@ -220,6 +250,61 @@ int sparse_attn_forward(const sa_problem* p, const void* Q, const void* K, const
   return hip_status(sa::launch_forward(D, Q, K, V, kv_idx, kv_cnt, W, softmax_scale, ws, O,
                                        out_dtype, lse, static_cast<hipStream_t>(stream)),
                     "sparse_attn_forward launch");
+}
+
+int sparse_attn_prepare_values(const sa_problem* p, const void* V, void* ws, size_t ws_bytes,
+                               void* stream) {
+  sa::Dims D;
+  int rc = check_problem(p, &D);
+  if (rc != SA_OK) return rc;
+  if (D.dtype != SA_BF16)
+    return fail(SA_ERR_UNSUPPORTED,
+                "fp32 problems read V directly: call sparse_attn_forward (no prepared values)");
+  if (!V || !ws) return fail(SA_ERR_INVALID, "V and ws must be non-NULL");
+  const size_t need = sa::forward_ws_bytes(D);
+  if (ws_bytes < need)
+    return fail(SA_ERR_INVALID, "forward workspace too small: %zu < %zu bytes", ws_bytes, need);
+  g_err.clear();
+  return hip_status(sa::launch_prepare_values(D, V, ws, static_cast<hipStream_t>(stream)),
+                    "sparse_attn_prepare_values launch");
+}
+
+int sparse_attn_forward_prepared(const sa_problem* p, const void* Q, const void* K,
+                                 const void* ws, size_t ws_bytes, const int32_t* kv_idx,
+                                 const int32_t* kv_cnt, int32_t W, float softmax_scale, void* O,
+                                 int32_t out_dtype, float* lse, void* stream) {
+  sa::Dims D;
+  int rc = check_problem(p, &D);
+  if (rc != SA_OK) return rc;
+  if (D.dtype != SA_BF16)
+    return fail(SA_ERR_UNSUPPORTED,
+                "fp32 problems read V directly: call sparse_attn_forward (no prepared values)");
+  if (!Q || !K || !ws || !kv_idx || !kv_cnt || !O)
+    return fail(SA_ERR_INVALID, "Q, K, ws, kv_idx, kv_cnt and O must be non-NULL");
+  const size_t need = sa::forward_ws_bytes(D);
+  if (ws_bytes < need)
+    return fail(SA_ERR_INVALID, "forward workspace too small: %zu < %zu bytes", ws_bytes, need);
+  if (W < 1) return fail(SA_ERR_INVALID, "W must be >= 1");
+  if (out_dtype != SA_F32 && out_dtype != SA_BF16)
+    return fail(SA_ERR_INVALID, "out_dtype must be SA_F32 or SA_BF16");
+  if (!isfinite(softmax_scale)) return fail(SA_ERR_INVALID, "softmax_scale is not finite");
+  if ((unsigned long long)D.N * D.Hkv * D.d * 2 >= (1ull << 32))
+    return fail(SA_ERR_UNSUPPORTED,
+                "seqlen * n_kv_heads * head_dim * 2 = %llu bytes of K per batch element: the "
+                "bf16 kernel addresses a batch element's keys with 32-bit offsets (< 2^32)",
+                (unsigned long long)D.N * D.Hkv * D.d * 2);
+  g_err.clear();
+  return hip_status(sa::launch_forward_prepared(D, Q, K, ws, kv_idx, kv_cnt, W, softmax_scale, O,
+                                                out_dtype, lse, static_cast<hipStream_t>(stream)),
+                    "sparse_attn_forward_prepared launch");
+}
+
+int sparse_attn_calibrate_tau(const float* tau, int32_t batch, float* tau_out, void* stream) {
+  if (!tau || !tau_out) return fail(SA_ERR_INVALID, "tau and tau_out must be non-NULL");
+  if (batch < 1) return fail(SA_ERR_INVALID, "batch must be >= 1");
+  g_err.clear();
+  return hip_status(sa::launch_tau_mean(tau, batch, tau_out, static_cast<hipStream_t>(stream)),
+                    "sparse_attn_calibrate_tau launch");
 }
 
 int sparse_attn_forward_vs(const sa_problem* p, const void* Q, const void* K, const void* V,

@@ -6,12 +6,19 @@
 // softmax is invariant to the order of the KV blocks, and the causal mask is applied before
 // accumulation.
 //
-// bf16 inputs (pack_v + attn_bf16):
-//   pack_v      once per call, V [B, N, Hkv, d] bf16 -> fp16 V^T step images (32 keys each,
-//               dense, swizzled): exactly the LDS image attn_bf16 wants.  Each V block is
-//               read by hundreds of tiles, so converting and transposing it once here takes
-//               that work out of the attention loop.  bf16 -> fp16 is exact for |v| in
-//               [2^-14, 65504]; smaller magnitudes keep an absolute error below 2^-25.
+// bf16 inputs (value_absmax + pack_v, then attn_bf16):
+//   value_absmax  partial maxima of |v| per (batch, kv head): bf16 magnitudes compared as
+//               integers (their bit patterns order like the values), kVmaxParts per head.
+//   pack_v      V [B, N, Hkv, d] bf16 -> fp16 V^T step images (32 keys each, dense,
+//               swizzled): exactly the LDS image attn_bf16 wants.  Each V block is read by
+//               hundreds of tiles, so converting and transposing it once here takes that work
+//               out of the attention loop.  fp16 holds less range than bf16, so every value
+//               of a (batch, kv head) is first multiplied by the power of two 2^e that brings
+//               its largest magnitude into [2^14, 2^15) (exact; e comes from value_absmax's
+//               partial maxima), and attn_bf16 multiplies that head's outputs by 2^-e.  Any
+//               finite bf16 V is then represented: values within a factor 2^29 of the head's
+//               largest magnitude exactly (bf16 -> fp16 is exact in fp16's normal range), the
+//               smaller ones with an absolute error below 2^-25 in scaled units.
 //   attn_bf16   one workgroup per (batch, q head, query tile), one wave per 32 query rows
 //               (4 waves for 128-row tiles, 2 for 64-row tiles), three workgroups per CU.  The
 //               tile's blocks are consumed in steps of 32 keys:
@@ -112,18 +119,91 @@ __device__ __forceinline__ int vswz(int d) { return (((d >> 1) ^ (d >> 3)) & 1) 
 
 constexpr int kPackThreads = 256;
 
-// V [B, N, Hkv, D] bf16 -> fp16 V^T step images [B, Hkv, N / 32] x (D x 32), one workgroup
-// per step.
+// Largest bf16 magnitude among the eight values of v, as its 15-bit pattern.
+__device__ __forceinline__ uint32_t absmax8(const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+  return m;
+}
+
+// Partial maxima of |v|: workgroup (b, g, c) covers rows [c R, (c + 1) R) of (batch b, kv
+// head g), R = ceil(N / kVmaxParts), and writes one 15-bit magnitude pattern to
+// part[(b Hkv + g) kVmaxParts + c].
+template <int D>
+__global__ __launch_bounds__(kPackThreads) void value_absmax(Dims dm,
+                                                             const uint16_t* __restrict__ V,
+                                                             uint32_t* __restrict__ part) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  constexpr int U = 8;        // loads in flight per thread
+  __shared__ uint32_t red[kPackThreads / 64];
+  const int id = (int)blockIdx.x;
+  const int c = id % kVmaxParts, bg = id / kVmaxParts;
+  const int g = bg % dm.Hkv, b = bg / dm.Hkv;
+  const int R = (dm.N + kVmaxParts - 1) / kVmaxParts;
+  const int q0 = min(dm.N, c * R) * CPR, q1 = min(dm.N, (c + 1) * R) * CPR;
+  const uint16_t* base = V + ((size_t)b * dm.N * dm.Hkv + g) * D;
+  const size_t rstride = (size_t)dm.Hkv * D;
+  uint32_t mx = 0;
+  for (int q = q0 + (int)threadIdx.x; q < q1; q += U * kPackThreads) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int qq = min(q + u * kPackThreads, q1 - 1);  // a repeated chunk changes no maximum
+      v[u] = load_nt16(base + (size_t)(qq / CPR) * rstride + (qq % CPR) * 8);  // read once
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = max(mx, absmax8(v[u]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = red[0];
+#pragma unroll
+    for (int w = 1; w < kPackThreads / 64; ++w) m = max(m, red[w]);
+    part[id] = m;
+  }
+}
+
+// The power-of-two exponent e of a (batch, kv head) from its largest magnitude (15-bit bf16
+// pattern): |v|max * 2^e lies in [2^14, 2^15); 0 when every value is zero.
+__device__ __forceinline__ int value_exponent(uint32_t mbits) {
+  if (mbits == 0) return 0;
+  int ex;
+  (void)frexpf(bf16_bits_to_f32(mbits), &ex);  // |v|max = f 2^ex, f in [0.5, 1)
+  return 15 - ex;
+}
+
+// V [B, N, Hkv, D] bf16 -> fp16 V^T step images [B, Hkv, N / 32] x (D x 32), each value
+// multiplied by its head's 2^e, one workgroup per step; the head's first step also writes e to
+// vexp[b Hkv + g].
 template <int D>
 __global__ __launch_bounds__(kPackThreads) void pack_v(Dims dm, const uint16_t* __restrict__ V,
-                                                       uint16_t* __restrict__ Vp) {
+                                                       const uint32_t* __restrict__ part,
+                                                       uint16_t* __restrict__ Vp,
+                                                       int32_t* __restrict__ vexp) {
   constexpr int RS = D + 2;  // LDS row stride (elements)
   __shared__ uint16_t sv[kStep * RS];
+  __shared__ int s_e;
   const int steps = dm.N / kStep;
   const int id = (int)blockIdx.x;  // (b * Hkv + g) * steps + s
   const int s = id % steps;
   const int bg = id / steps;
   const int g = bg % dm.Hkv, b = bg / dm.Hkv;
+  if (threadIdx.x < 64) {
+    static_assert(kVmaxParts == 64, "one partial maximum per lane");
+    uint32_t m = part[(size_t)bg * kVmaxParts + threadIdx.x];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if (threadIdx.x == 0) {
+      const int e = value_exponent(m);
+      s_e = e;
+      if (s == 0) vexp[bg] = e;
+    }
+  }
   const uint16_t* src = V + (((size_t)b * dm.N + (size_t)s * kStep) * dm.Hkv + g) * D;
   for (int c = threadIdx.x; c < kStep * D / 8; c += kPackThreads) {
     const int r = c / (D / 8), col = c - r * (D / 8);
@@ -132,6 +212,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_v(Dims dm, const uint16_t* 
     dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
   }
   __syncthreads();
+  const int e = s_e;
   uint4* out = reinterpret_cast<uint4*>(Vp + (size_t)id * D * kStep);
   for (int i = threadIdx.x; i < D * 4; i += kPackThreads) {
     const int d = i >> 2, pos = i & 3;
@@ -139,9 +220,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_v(Dims dm, const uint16_t* 
     const int key0 = 16 * (c >> 1) + 4 * (c & 1);  // keys key0 + (0..3), key0 + 8 + (0..3)
     float x[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[k] = bf16_bits_to_f32(sv[(key0 + k) * RS + d]);
-      x[4 + k] = bf16_bits_to_f32(sv[(key0 + 8 + k) * RS + d]);
+    for (int k = 0; k < 4; ++k) {  // exact: a power-of-two scaling that stays below 2^15
+      x[k] = ldexpf(bf16_bits_to_f32(sv[(key0 + k) * RS + d]), e);
+      x[4 + k] = ldexpf(bf16_bits_to_f32(sv[(key0 + 8 + k) * RS + d]), e);
     }
     uint32_t wv[4];
 #pragma unroll
@@ -578,9 +659,9 @@ template <int D, int QH, int NW, bool VS, int HPW, int KB>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf16(
     Dims dm, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ Vp, const int32_t* __restrict__ kv_idx,
-    const int32_t* __restrict__ kv_cnt, int W, VsIndex vs, float scale_log2,
-    void* __restrict__ O, int out_f32, float* __restrict__ lse) {
+    const uint16_t* __restrict__ Vp, const int32_t* __restrict__ vexp,
+    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int W, VsIndex vs,
+    float scale_log2, void* __restrict__ O, int out_f32, float* __restrict__ lse) {
   using C = Cfg<D, QH, NW, HPW, KB>;
   static_assert(HPW == 1 || !VS, "vertical-slash lists are per query head");
   static_assert(KB == 0 || !VS, "vertical-slash lists need tile = block");
@@ -756,6 +837,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
     seg_start = next_start;
   }
 
+  const int ve = -vexp[(size_t)b * dm.Hkv + g];  // undoes pack_v's 2^e of this kv head
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh) {
     const float l_tot = pair_sum(st.l_run[qh]);
@@ -769,7 +851,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
         const int d0 = dt * 32 + 8 * i + 4 * hi;
         float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = st.acc_o[qh][dt][4 * i + r] * inv;
+        for (int r = 0; r < 4; ++r) o[r] = ldexpf(st.acc_o[qh][dt][4 * i + r] * inv, ve);
         if (out_f32) {
           *reinterpret_cast<float4*>(static_cast<float*>(O) + orow + d0) =
               make_float4(o[0], o[1], o[2], o[3]);
@@ -855,22 +937,35 @@ __global__ __launch_bounds__(TR) void attn_f32(Dims dm, const float* __restrict_
     lse[((size_t)b * dm.Hq + h) * dm.N + qrow] = l > 0.0f ? m + __logf(l) : -INFINITY;
 }
 
-template <int D, int QH, int NW, bool VS, int HPW = 1, int KB = 0>
-hipError_t launch_bf16(const Dims& dm, const void* Q, const void* K, const void* V,
-                       const int32_t* kv_idx, const int32_t* kv_cnt, int W, const VsIndex& vs,
-                       float scale, void* ws, void* O, int out_dtype, float* lse,
-                       hipStream_t s) {
-  uint16_t* Vp = static_cast<uint16_t*>(ws);
-  const unsigned nsteps = (unsigned)((size_t)dm.B * dm.Hkv * (dm.N / kStep));
-  hipLaunchKernelGGL((pack_v<D>), dim3(nsteps), dim3(kPackThreads), 0, s, dm,
-                     static_cast<const uint16_t*>(V), Vp);
+template <int D>
+hipError_t launch_prepare(const Dims& dm, const void* V, void* ws, hipStream_t s) {
+  const ForwardWs L = forward_ws_layout(dm);
+  char* base = static_cast<char*>(ws);
+  uint32_t* part = reinterpret_cast<uint32_t*>(base + L.part);
+  hipLaunchKernelGGL((value_absmax<D>), dim3((unsigned)((size_t)dm.B * dm.Hkv * kVmaxParts)),
+                     dim3(kPackThreads), 0, s, dm, static_cast<const uint16_t*>(V), part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const unsigned nsteps = (unsigned)((size_t)dm.B * dm.Hkv * (dm.N / kStep));
+  hipLaunchKernelGGL((pack_v<D>), dim3(nsteps), dim3(kPackThreads), 0, s, dm,
+                     static_cast<const uint16_t*>(V), part,
+                     reinterpret_cast<uint16_t*>(base + L.vp),
+                     reinterpret_cast<int32_t*>(base + L.vexp));
+  return hipGetLastError();
+}
+
+template <int D, int QH, int NW, bool VS, int HPW = 1, int KB = 0>
+hipError_t launch_bf16(const Dims& dm, const void* Q, const void* K, const int32_t* kv_idx,
+                       const int32_t* kv_cnt, int W, const VsIndex& vs, float scale,
+                       const void* ws, void* O, int out_dtype, float* lse, hipStream_t s) {
+  const ForwardWs L = forward_ws_layout(dm);
+  const char* base = static_cast<const char*>(ws);
   const unsigned grid = (unsigned)((size_t)dm.B * dm.Hq / HPW * dm.nt);
   hipLaunchKernelGGL((attn_bf16<D, QH, NW, VS, HPW, KB>), dim3(grid), dim3(64 * NW), 0, s, dm,
-                     static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K), Vp,
-                     kv_idx, kv_cnt, W, vs, scale * kLog2e, O, out_dtype == SA_F32 ? 1 : 0,
-                     lse);
+                     static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                     reinterpret_cast<const uint16_t*>(base + L.vp),
+                     reinterpret_cast<const int32_t*>(base + L.vexp), kv_idx, kv_cnt, W, vs,
+                     scale * kLog2e, O, out_dtype == SA_F32 ? 1 : 0, lse);
   return hipGetLastError();
 }
 
@@ -890,52 +985,59 @@ hipError_t launch_f32(const Dims& dm, const void* Q, const void* K, const void* 
 }
 
 template <bool VS>
-hipError_t launch_bf16_shape(const Dims& dm, const void* Q, const void* K, const void* V,
-                             const int32_t* kv_idx, const int32_t* kv_cnt, int W,
-                             const VsIndex& vs, float scale, void* ws, void* O, int out_dtype,
-                             float* lse, hipStream_t s) {
+hipError_t launch_bf16_shape(const Dims& dm, const void* Q, const void* K, const int32_t* kv_idx,
+                             const int32_t* kv_cnt, int W, const VsIndex& vs, float scale,
+                             const void* ws, void* O, int out_dtype, float* lse, hipStream_t s) {
   if constexpr (!VS) {
     // 128-row tiles over 64-key blocks: four waves per tile, two steps per block.
     if (dm.m == 2)
-      return dm.d == 64 ? launch_bf16<64, 1, 4, false, 1, 64>(dm, Q, K, V, kv_idx, kv_cnt, W,
-                                                              vs, scale, ws, O, out_dtype, lse, s)
-                        : launch_bf16<128, 1, 4, false, 1, 64>(dm, Q, K, V, kv_idx, kv_cnt, W,
-                                                               vs, scale, ws, O, out_dtype, lse,
-                                                               s);
+      return dm.d == 64 ? launch_bf16<64, 1, 4, false, 1, 64>(dm, Q, K, kv_idx, kv_cnt, W, vs,
+                                                              scale, ws, O, out_dtype, lse, s)
+                        : launch_bf16<128, 1, 4, false, 1, 64>(dm, Q, K, kv_idx, kv_cnt, W, vs,
+                                                               scale, ws, O, out_dtype, lse, s);
     // 64-row tiles whose lists a kv head's query heads share (an even number of them): two
     // heads per workgroup, so each K/V step in LDS feeds four waves instead of two.
     if (dm.blk == 64 && dm.gs > 1 && dm.gs % 2 == 0)
-      return dm.d == 64 ? launch_bf16<64, 1, 4, false, 2>(dm, Q, K, V, kv_idx, kv_cnt, W, vs,
-                                                          scale, ws, O, out_dtype, lse, s)
-                        : launch_bf16<128, 1, 4, false, 2>(dm, Q, K, V, kv_idx, kv_cnt, W, vs,
-                                                           scale, ws, O, out_dtype, lse, s);
+      return dm.d == 64 ? launch_bf16<64, 1, 4, false, 2>(dm, Q, K, kv_idx, kv_cnt, W, vs, scale,
+                                                          ws, O, out_dtype, lse, s)
+                        : launch_bf16<128, 1, 4, false, 2>(dm, Q, K, kv_idx, kv_cnt, W, vs, scale,
+                                                           ws, O, out_dtype, lse, s);
   }
   if (dm.d == 64)
-    return dm.blk == 64 ? launch_bf16<64, 1, 2, VS>(dm, Q, K, V, kv_idx, kv_cnt, W, vs, scale,
-                                                      ws, O, out_dtype, lse, s)
-                        : launch_bf16<64, ATTN_QH, 4 / ATTN_QH, VS>(
-                              dm, Q, K, V, kv_idx, kv_cnt, W, vs, scale, ws, O, out_dtype, lse, s);
+    return dm.blk == 64 ? launch_bf16<64, 1, 2, VS>(dm, Q, K, kv_idx, kv_cnt, W, vs, scale, ws, O,
+                                                    out_dtype, lse, s)
+                        : launch_bf16<64, ATTN_QH, 4 / ATTN_QH, VS>(dm, Q, K, kv_idx, kv_cnt, W,
+                                                                    vs, scale, ws, O, out_dtype,
+                                                                    lse, s);
   if (dm.blk == 64)
-    return launch_bf16<128, 1, 2, VS>(dm, Q, K, V, kv_idx, kv_cnt, W, vs, scale, ws, O,
-                                      out_dtype, lse, s);
-  return launch_bf16<128, ATTN_QH, 4 / ATTN_QH, VS>(dm, Q, K, V, kv_idx, kv_cnt, W, vs, scale, ws,
-                                                    O, out_dtype, lse, s);
+    return launch_bf16<128, 1, 2, VS>(dm, Q, K, kv_idx, kv_cnt, W, vs, scale, ws, O, out_dtype,
+                                      lse, s);
+  return launch_bf16<128, ATTN_QH, 4 / ATTN_QH, VS>(dm, Q, K, kv_idx, kv_cnt, W, vs, scale, ws, O,
+                                                    out_dtype, lse, s);
 }
 
 }  // namespace
 
-size_t forward_ws_bytes(const Dims& dm) {
-  if (dm.dtype != SA_BF16) return 0;
-  // packed V^T step images: the size of V
-  return (size_t)dm.B * dm.N * dm.Hkv * dm.d * sizeof(uint16_t);
+hipError_t launch_prepare_values(const Dims& dm, const void* V, void* ws, hipStream_t s) {
+  return dm.d == 64 ? launch_prepare<64>(dm, V, ws, s) : launch_prepare<128>(dm, V, ws, s);
+}
+
+hipError_t launch_forward_prepared(const Dims& dm, const void* Q, const void* K,
+                                   const void* ws, const int32_t* kv_idx,
+                                   const int32_t* kv_cnt, int W, float scale, void* O,
+                                   int out_dtype, float* lse, hipStream_t s) {
+  return launch_bf16_shape<false>(dm, Q, K, kv_idx, kv_cnt, W, VsIndex{}, scale, ws, O,
+                                  out_dtype, lse, s);
 }
 
 hipError_t launch_forward(const Dims& dm, const void* Q, const void* K, const void* V,
                           const int32_t* kv_idx, const int32_t* kv_cnt, int W, float scale,
                           void* ws, void* O, int out_dtype, float* lse, hipStream_t s) {
-  if (dm.dtype == SA_BF16)
-    return launch_bf16_shape<false>(dm, Q, K, V, kv_idx, kv_cnt, W, VsIndex{}, scale, ws, O,
-                                    out_dtype, lse, s);
+  if (dm.dtype == SA_BF16) {
+    const hipError_t e = launch_prepare_values(dm, V, ws, s);
+    if (e != hipSuccess) return e;
+    return launch_forward_prepared(dm, Q, K, ws, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s);
+  }
   if (dm.m == 2)  // 128-row tiles over 64-key blocks
     return dm.d == 64
                ? launch_f32<64, 128, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
@@ -955,8 +1057,10 @@ hipError_t launch_forward(const Dims& dm, const void* Q, const void* K, const vo
 hipError_t launch_forward_vs(const Dims& dm, const void* Q, const void* K, const void* V,
                              const VsIndex& vs, float scale, void* ws, void* O, int out_dtype,
                              float* lse, hipStream_t s) {
-  return launch_bf16_shape<true>(dm, Q, K, V, nullptr, nullptr, 1, vs, scale, ws, O, out_dtype,
-                                 lse, s);
+  const hipError_t e = launch_prepare_values(dm, V, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_bf16_shape<true>(dm, Q, K, nullptr, nullptr, 1, vs, scale, ws, O, out_dtype, lse,
+                                 s);
 }
 
 }  // namespace sa

@@ -161,6 +161,31 @@ __device__ __forceinline__ void decode_tile_grouped(const Dims& dm, int& b, int&
   h = (pair - b * dm.Hkv) * dm.G + r;
 }
 
+// Dynamic LDS of the kernels whose need grows with the problem.  The host checks these
+// against kMaxDynLds before any launch (a CU has 160 KiB of LDS; the margin covers each
+// kernel's static LDS), so an oversized problem is refused, never launched.
+constexpr size_t kMaxDynLds = 160 * 1024 - 4096;
+inline size_t pow2_ceil(size_t x) {
+  size_t p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+// Selection's score-and-rank kernel: one 64-bit order key per block (rounded up to a power
+// of two for the sort), plus, for bf16, the tile's Q rows staged as bf16 (two planes for the
+// K-min/K-max bound) with rows padded by 8 elements.
+inline size_t score_rank_lds(const Dims& D) {
+  const size_t keys = sizeof(unsigned long long) * pow2_ceil((size_t)D.n);
+  if (D.dtype != SA_BF16) return keys;
+  const size_t npl = D.score_mode == SA_KMINMAX ? 2 : 1;
+  return keys + sizeof(uint16_t) * npl * D.T * (D.d + 8);
+}
+// Gate kernel: sigma_bar of every tile, then a power-of-two sort buffer.
+inline size_t gate_lds(const Dims& D) {
+  return sizeof(float) * ((size_t)D.nt + pow2_ceil((size_t)D.nt));
+}
+// value_norms: the L2 norm of every (row, kv head) of one block.
+inline size_t value_norms_lds(const Dims& D) { return sizeof(float) * (size_t)D.blk * D.Hkv; }
+
 // Workspace layout of sparse_attn_select (byte offsets, 256-byte aligned).
 struct SelectWs {
   size_t ranked, sigma, sigma_bar, gate, tau, total;
@@ -182,6 +207,9 @@ hipError_t launch_pool(const Dims& D, const void* K, const void* V, float* summ,
 hipError_t launch_select(const Dims& D, const BudgetDev& bd, const void* Q, const float* summ,
                          char* ws, int32_t* kv_idx, int32_t* kv_cnt, float* sigma,
                          float* sigma_bar, uint8_t* gate, float* tau, hipStream_t s);
+// Mean of the finite entries of tau[0 .. B) (fp32 sum in index order, one IEEE division by
+// their count), or -inf if none is finite; one thread.
+hipError_t launch_tau_mean(const float* tau, int B, float* out, hipStream_t s);
 // Vertical-slash index of the forward pass (per query head: vertical key blocks, ascending;
 // slash block offsets, ascending; each list ends at its first negative entry).
 struct VsIndex {
@@ -191,7 +219,30 @@ struct VsIndex {
 };
 constexpr int kVsMaxEntries = 511;  // nv + ns: the merged list plus the diagonal fit in LDS
 
-size_t forward_ws_bytes(const Dims& D);
+// Workspace of the bf16 forward pass (byte offsets, 256-byte aligned): the fp16 V^T step
+// images (the size of V), the partial maxima of |V| (kVmaxParts per batch and kv head,
+// uint32), and each (batch, kv head)'s power-of-two exponent (int32).
+constexpr int kVmaxParts = 64;  // partial maxima of |V| per (batch, kv head)
+struct ForwardWs {
+  size_t vp, part, vexp, total;
+};
+inline ForwardWs forward_ws_layout(const Dims& D) {
+  auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  ForwardWs w;
+  w.vp = 0;
+  w.part = a256((size_t)D.B * D.N * D.Hkv * D.d * sizeof(uint16_t));
+  w.vexp = a256(w.part + (size_t)D.B * D.Hkv * kVmaxParts * sizeof(uint32_t));
+  w.total = a256(w.vexp + (size_t)D.B * D.Hkv * sizeof(int32_t));
+  return w;
+}
+inline size_t forward_ws_bytes(const Dims& D) {
+  return D.dtype == SA_BF16 ? forward_ws_layout(D).total : 0;
+}
+hipError_t launch_prepare_values(const Dims& D, const void* V, void* ws, hipStream_t s);
+hipError_t launch_forward_prepared(const Dims& D, const void* Q, const void* K, const void* ws,
+                                   const int32_t* kv_idx, const int32_t* kv_cnt, int W,
+                                   float scale, void* O, int out_dtype, float* lse,
+                                   hipStream_t s);
 hipError_t launch_forward(const Dims& D, const void* Q, const void* K, const void* V,
                           const int32_t* kv_idx, const int32_t* kv_cnt, int W, float scale,
                           void* ws, void* O, int out_dtype, float* lse, hipStream_t s);

@@ -86,7 +86,11 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
   __shared__ __attribute__((aligned(16))) uint16_t vtiles[2][kArtBlk * D];
   __shared__ __attribute__((aligned(16))) uint32_t qs[kArtMaxG][D / 2];  // bf16 pairs
   __shared__ __attribute__((aligned(16))) float ps[kArtMaxG][kArtBlk];
-  __shared__ int live[kArtMaxG];
+  // Stop flags, double-buffered by step parity: step k reads live[k & 1] (every decision
+  // up to step k - 1) and each wave posts its own state for step k + 1 to live[(k + 1) & 1].
+  // A wave can only write live[k & 1] again in step k + 1, after the barrier that every wave
+  // passes once its reads of step k are done, so all waves read the same flags.
+  __shared__ int live[2][kArtMaxG];
 
   const int g = (int)blockIdx.x % dm.Hkv, b = (int)blockIdx.x / dm.Hkv;
   const int G = dm.G;
@@ -102,7 +106,8 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
     const int hh = i / (D / 2), c2 = i - hh * (D / 2);
     qs[hh][c2] = reinterpret_cast<const uint32_t*>(Q + ((size_t)b * dm.Hq + g * G + hh) * D)[c2];
   }
-  if (threadIdx.x < kArtMaxG) live[threadIdx.x] = (int)threadIdx.x < G ? 1 : 0;
+  if (threadIdx.x < 2 * kArtMaxG)
+    live[threadIdx.x / kArtMaxG][threadIdx.x % kArtMaxG] = (int)threadIdx.x % kArtMaxG < G ? 1 : 0;
 
   // Block k of the traversal: block 0, then n-1, n-2, ..., 1.
   auto block_of = [n](int k) { return k == 0 ? 0 : n - k; };
@@ -131,11 +136,11 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
   // One step of the traversal on the block whose chunks are in (kr, vr), in tile set k & 1;
   // refills the registers with block k + kArtPrefetch.  The barrier after the stores also
   // means every wave is done with step k - 1 (whose tile set step k + 1 overwrites) and has
-  // posted its stop decision.  Stores, barrier and refill happen on every step, also past the
-  // end and after every head stopped (valid blocks, never used), so that each step's memory
-  // operations are the same and the compiler's waits stay partial: a step waits for its own
-  // block only, with the later blocks still in flight.  Returns whether any head ran before
-  // this step (decisions up to step k - 1).
+  // posted its stop state to live[k & 1].  Stores, barrier and refill happen on every step,
+  // also past the end and after every head stopped (valid blocks, never used), so that each
+  // step's memory operations are the same and the compiler's waits stay partial: a step waits
+  // for its own block only, with the later blocks still in flight.  Returns whether any head
+  // was still running after step k - 1 (the same value in every wave).
   auto step = [&](int k, uint4 (&kr)[CPT], uint4 (&vr)[CPT]) -> bool {
     char* ktile = ktiles[k & 1];
     uint16_t* vtile = vtiles[k & 1];
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
     }
     __syncthreads();
     bool any = false;
-    for (int i = 0; i < G; ++i) any |= live[i] != 0;
+    for (int i = 0; i < G; ++i) any |= live[k & 1][i] != 0;
     {
       const int jn = block_of(min(k + kArtPrefetch, n - 1));
 #pragma unroll
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
         vr[i] = chunk_src(Vb, jn, i);
       }
     }
-    if (k < n && active && live[w]) {
+    if (k < n && active && stopped == 0) {
       // scores of key `lane`
       float s = 0.0f;
       auto d2 = [](uint32_t a, uint32_t b2, float c) {
@@ -220,12 +225,10 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
         const float dsc = fabsf(nx - np);
         const float ddr = (nx > 0.0f && np > 0.0f) ? 1.0f - dp / (nx * np) : 1.0f;
         run = (dsc < tau && ddr < phi) ? run + 1 : 0;
-        if (run >= patience) {
-          stopped = k + 1;
-          if (lane == 0) live[w] = 0;
-        }
+        if (run >= patience) stopped = k + 1;
       }
     }
+    if (active && lane == 0) live[(k + 1) & 1][w] = stopped == 0 ? 1 : 0;
     return any;
   };
 

@@ -17,7 +17,8 @@
 //   upper-bound ingredient only: it never decides a selection by itself).
 // value_norms: one workgroup per (batch, block).  Each (row, kv head) pair's squared norm is
 //   a fused multiply-add chain over the d coordinates in order, by one thread; the square
-//   roots go to LDS and one thread per kv head sums them in row order.
+//   roots go to LDS (block x Hkv floats, checked against the LDS size on the host) and one
+//   thread per kv head sums them in row order.
 
 #include "common.h"
 
@@ -172,8 +173,7 @@ __global__ __launch_bounds__(kPoolThreads) void value_norms(const T* __restrict_
     nrm[p] = __builtin_sqrtf(ss);  // correctly rounded (IEEE) with the build flags
   }
   __syncthreads();
-  if (threadIdx.x < Hkv) {
-    const int g = threadIdx.x;
+  for (int g = threadIdx.x; g < Hkv; g += kPoolThreads) {
     float acc = 0.0f;
     for (int r = 0; r < BLK; ++r) acc = acc + nrm[r * Hkv + g];
     vn[(size_t)bj * Hkv + g] = acc * (1.0f / (float)BLK);
@@ -200,7 +200,9 @@ hipError_t launch_keys_d(const Dims& D, const void* K, float* summ, hipStream_t 
 
 template <typename T, int BLK, int HD>
 hipError_t launch_vn(const Dims& D, const void* V, float* vn, hipStream_t s) {
-  const size_t lds = sizeof(float) * BLK * D.Hkv;
+  const size_t lds = value_norms_lds(D);
+  const hipError_t e = allow_lds(value_norms<T, BLK, HD>, lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((value_norms<T, BLK, HD>), dim3((unsigned)(D.B * D.n)),
                      dim3(kPoolThreads), lds, s, static_cast<const T*>(V), vn, D.N, D.n,
                      D.Hkv);

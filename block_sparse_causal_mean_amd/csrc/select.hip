@@ -730,9 +730,7 @@ __global__ __launch_bounds__(64 * kEmitWaves) void emit_kernel(Dims dm, BudgetDe
 template <typename T, int MODE, int OAM, int D, int TILE>
 hipError_t launch_score(const Dims& dm, const BudgetDev& bd, const void* Q, const float* summ,
                         int* ranked, float* sigma, hipStream_t s) {
-  int P = 1;
-  while (P < dm.n) P <<= 1;
-  const size_t lds = sizeof(unsigned long long) * P;
+  const size_t lds = score_rank_lds(dm);
   const unsigned grid = (unsigned)((size_t)dm.B * dm.Hu * dm.nt);
   hipError_t e = allow_lds(score_rank<T, MODE, OAM, D, TILE>, lds);
   if (e != hipSuccess) return e;
@@ -773,10 +771,7 @@ template <int MODE, int OAM, int D, int TILE, bool GRP>
 hipError_t launch_score_mfma_g(const Dims& dm, const BudgetDev& bd, const void* Q,
                              const float* summ, int* ranked, float* sigma, hipStream_t s) {
   const SummaryLayout L = summary_layout(dm);
-  int P = 1;
-  while (P < dm.n) P <<= 1;
-  constexpr int NPL = MODE == SA_KMINMAX ? 2 : 1;
-  const size_t lds = sizeof(unsigned long long) * P + sizeof(uint16_t) * NPL * TILE * (D + 8);
+  const size_t lds = score_rank_lds(dm);
   hipError_t e = allow_lds(score_rank_mfma<MODE, OAM, D, TILE, GRP>, lds);
   if (e != hipSuccess) return e;
   const char* base = reinterpret_cast<const char*>(summ);
@@ -826,7 +821,28 @@ hipError_t score_mfma_dispatch(const Dims& dm, const BudgetDev& bd, const void* 
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// A fixed gate threshold from the per-sequence quantile thresholds of calibration inputs:
+// their mean over the sequences where a tile can trip (a finite tau).
+__global__ void tau_mean_kernel(const float* __restrict__ tau, int B, float* __restrict__ out) {
+  if (threadIdx.x != 0) return;
+  float acc = 0.0f;
+  int c = 0;
+  for (int b = 0; b < B; ++b) {
+    const float x = tau[b];
+    if (isfinite(x)) {
+      acc = acc + x;
+      ++c;
+    }
+  }
+  *out = c > 0 ? acc / (float)c : -INFINITY;
+}
+
 }  // namespace
+
+hipError_t launch_tau_mean(const float* tau, int B, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(tau_mean_kernel, dim3(1), dim3(64), 0, s, tau, B, out);
+  return hipGetLastError();
+}
 
 SelectWs select_ws_layout(const Dims& dm, const BudgetDev& bd) {
   SelectWs w;
@@ -854,9 +870,7 @@ hipError_t launch_select(const Dims& dm, const BudgetDev& bd, const void* Q, con
                                      : score_dispatch<float>(dm, bd, Q, summ, ranked, sigma, s);
   if (e != hipSuccess) return e;
 
-  int P = 1;
-  while (P < dm.nt) P <<= 1;
-  const size_t glds = sizeof(float) * ((size_t)dm.nt + P);
+  const size_t glds = gate_lds(dm);
   if ((e = allow_lds(gate_kernel, glds)) != hipSuccess) return e;
   hipLaunchKernelGGL(gate_kernel, dim3((unsigned)dm.B), dim3(kGateThreads), glds, s, dm, bd,
                      sigma, sigma_bar, gate, tau);

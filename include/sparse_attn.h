@@ -31,7 +31,8 @@
  *     gives the calling thread's last message.
  *   - Supported in this version: head_dim in {64, 128}; block == tile in {64, 128}, or
  *     tile 128 over block 64;
- *     seqlen % block == 0; Hq % Hkv == 0; bf16 or fp32 inputs.
+ *     seqlen % block == 0; Hq % Hkv == 0; bf16 or fp32 inputs; at most 16384 blocks per
+ *     sequence, within the selection's LDS limit (sparse_attn_select).
  */
 #ifndef SPARSE_ATTN_H_
 #define SPARSE_ATTN_H_
@@ -128,6 +129,8 @@ int32_t sparse_attn_index_width(const sa_problem* p, const sa_budget* b);
  *   K          [B, N, Hkv, d] in p->dtype.
  *   V          [B, N, Hkv, d]; read only when p->output_aware, may be NULL otherwise.
  *   summaries  sparse_attn_summary_bytes(p) bytes, written.
+ * Output-aware scoring holds block * n_kv_heads fp32 norms in LDS: at most 159744 bytes,
+ * else SA_ERR_UNSUPPORTED before any HIP call.
  * Per block j and kv head g: kmean = (sum of the block's key rows in row order, fp32) / block;
  * kmin/kmax = per-coordinate min/max (exact); vnorm = (sum over rows in order of the fp32
  * L2 norm of the value row) / block.
@@ -153,14 +156,20 @@ int sparse_attn_score(const sa_problem* p, const void* K, const void* V, void* s
  * 2t+1 for 128-row tiles over 64-key blocks) minus the n_sink first blocks; they rank by
  * tile score, ties to the lower index; the diagonal and sink blocks are always kept.  Scores are
  * fp32 with a fixed reduction order, so the lists are reproducible bit for bit.
+ * LDS limit: one workgroup holds a 64-bit sort key per block, 8 * P bytes (P = n rounded up to
+ * a power of two), plus for bf16 inputs the tile's query rows, 2 * planes * tile * (d + 8)
+ * bytes (planes = 2 for SA_KMINMAX, else 1); the sum must not exceed 159744 bytes, else
+ * SA_ERR_UNSUPPORTED before any HIP call (so up to 8192 blocks always fit, and 16384 with
+ * SA_KMEAN, 64-row tiles).  sparse_attn_select_workspace_bytes returns 0 for such problems.
  */
 int sparse_attn_select(const sa_problem* p, const sa_budget* b, const void* Q,
                        const void* summaries, void* ws, size_t ws_bytes, int32_t* kv_idx,
                        int32_t* kv_cnt, float* sigma, float* sigma_bar, uint8_t* gate,
                        float* tau, void* stream);
 
-/* Bytes of device workspace `sparse_attn_forward` needs (0 for fp32 problems, the size of V
- * for bf16 ones).  0 also for an invalid problem (see sparse_attn_last_error). */
+/* Bytes of device workspace `sparse_attn_forward` needs: 0 for fp32 problems; for bf16 ones
+ * the size of V plus 256-byte-aligned room for 260 bytes per (batch, kv head) (the prepared
+ * values below).  0 also for an invalid problem (see sparse_attn_last_error). */
 size_t sparse_attn_forward_workspace_bytes(const sa_problem* p);
 
 /*
@@ -180,15 +189,51 @@ size_t sparse_attn_forward_workspace_bytes(const sa_problem* p);
  *   lse            optional fp32 [B, Hq, N]: natural-log log-sum-exp of the scaled logits.
  * Row i of tile t attends to every key of its listed blocks at a position <= i.
  * Precision: fp32 accumulation.  With bf16 inputs, Q K^T runs on bf16 matrix cores and P V on
- * fp16 ones (P rounded to fp16, V converted exactly from bf16), so bf16 V values must lie
- * below 65504 in magnitude.  fp32 inputs are computed in fp32 throughout.
+ * fp16 ones: P is rounded to fp16 (11 significant bits), and V, per (batch, kv head), is
+ * multiplied by the power of two 2^e that brings its largest magnitude into [2^14, 2^15),
+ * converted to fp16, and the outputs multiplied by 2^-e.  Every finite bf16 V is accepted:
+ * values within a factor 2^29 of their head's largest magnitude convert exactly, smaller ones
+ * with an absolute error below 2^-25 * 2^-e.  The error of O therefore scales with the
+ * magnitude of V.  fp32 inputs are computed in fp32 throughout.
  * Limit: with bf16 inputs, seqlen * n_kv_heads * head_dim * 2 (the bytes of K per batch
  * element) must be below 2^32, else SA_ERR_UNSUPPORTED.
+ * With bf16 inputs this call is sparse_attn_prepare_values followed by
+ * sparse_attn_forward_prepared on the same workspace.
  */
 int sparse_attn_forward(const sa_problem* p, const void* Q, const void* K, const void* V,
                         const int32_t* kv_idx, const int32_t* kv_cnt, int32_t W,
                         float softmax_scale, void* ws, size_t ws_bytes, void* O,
                         int32_t out_dtype, float* lse, void* stream);
+
+/*
+ * The two halves of sparse_attn_forward for bf16 problems, for callers that reuse one V across
+ * several attention calls or time the attention kernel on its own (SA_ERR_UNSUPPORTED for
+ * fp32 problems, whose forward pass reads V directly).
+ *
+ * sparse_attn_prepare_values: V [B, N, Hkv, d] bf16 -> ws (sparse_attn_forward_workspace_bytes
+ *   bytes): the largest magnitude of each (batch, kv head), its power-of-two exponent e, and V
+ *   times 2^e as fp16 in the attention kernel's transposed 32-key step layout (private).
+ * sparse_attn_forward_prepared: the attention of sparse_attn_forward, reading V from a
+ *   workspace that sparse_attn_prepare_values filled for the same problem and the same V
+ *   (stream order makes that call's results visible; another V gives another V's attention).
+ *   Other arguments and results as for sparse_attn_forward.
+ */
+int sparse_attn_prepare_values(const sa_problem* p, const void* V, void* ws, size_t ws_bytes,
+                               void* stream);
+int sparse_attn_forward_prepared(const sa_problem* p, const void* Q, const void* K,
+                                 const void* ws, size_t ws_bytes, const int32_t* kv_idx,
+                                 const int32_t* kv_cnt, int32_t W, float softmax_scale, void* O,
+                                 int32_t out_dtype, float* lse, void* stream);
+
+/*
+ * A threshold for SA_GATE_FIXED calibrated on sample inputs.  The gated-selection page
+ * (Metodologia step 4) gates each layer at an empirical quantile of sigma_bar; this call turns
+ * the per-sequence thresholds sparse_attn_select wrote (tau, [batch] fp32, from calibration
+ * inputs run with SA_GATE_QUANTILE) into one per-layer threshold: the mean of the finite
+ * entries (an fp32 sum in index order divided by their count), or -inf when none is finite
+ * (nothing could trip).  tau_out: one fp32, written.  Device pointers; one tiny kernel.
+ */
+int sparse_attn_calibrate_tau(const float* tau, int32_t batch, float* tau_out, void* stream);
 
 /*
  * Sparse attention over a vertical-slash index (VSPrefill page, Metodologia B.3: the fused

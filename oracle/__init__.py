@@ -61,6 +61,8 @@ def _load():
     lib.oracle_vs_lists.argtypes = [cfgp, P, ctypes.c_int, P, ctypes.c_int, P, P, ctypes.c_int]
     lib.oracle_decode_art.argtypes = [cfgp, P, P, P, ctypes.c_double, ctypes.c_int,
                                       ctypes.c_double, ctypes.c_double, ctypes.c_int, P, P, P, P]
+    lib.oracle_calibrated_tau.argtypes = [P, ctypes.c_int]
+    lib.oracle_calibrated_tau.restype = ctypes.c_float
     _lib = lib
     return lib
 
@@ -308,3 +310,9 @@ def threads() -> int:
 
 def budget(cfg: OracleCfg, t: int) -> int:
     return int(_load().oracle_budget(ctypes.byref(cfg), t))
+
+
+def calibrated_tau(tau) -> np.float32:
+    """Fixed-gate threshold from per-sequence thresholds: the mean of the finite ones."""
+    t = np.ascontiguousarray(tau, dtype=np.float32)
+    return np.float32(_load().oracle_calibrated_tau(_p(t), int(t.size)))

@@ -717,6 +717,22 @@ int oracle_decode_art(const oc_cfg* c, const void* Q, const void* K, const void*
   return fail ? -1 : 0;
 }
 
+/* Per-layer threshold for a fixed gate from calibration runs (gated-selection page,
+ * Metodologia step 4: the gate threshold is an empirical quantile per layer).  This build's
+ * reading: the mean of the per-sequence quantile thresholds tau[0 .. B) over the sequences
+ * where a tile can trip (finite tau), as an fp32 sum in index order divided by their count;
+ * -inf when there is none. */
+float oracle_calibrated_tau(const float* tau, int B) {
+  float acc = 0.0f;
+  int c = 0;
+  for (int b = 0; b < B; ++b)
+    if (isfinite(tau[b])) {
+      acc = acc + tau[b];
+      ++c;
+    }
+  return c > 0 ? acc / (float)c : -INFINITY;
+}
+
 /* Budget for tile t, exported so the tests can pin the schedule on its own. */
 int oracle_budget(const oc_cfg* c, int t) { return budget(c, t); }
 

@@ -168,7 +168,8 @@ def test_null_pointers_and_small_buffers_rejected(lib):
                                    float("inf"), FAKE, big, FAKE, api.SA_BF16, None,
                                    None) == api.SA_ERR_INVALID
     need = api.forward_workspace_bytes(p)
-    assert need == 1 * 32768 * 8 * 128 * 2
+    vbytes = 1 * 32768 * 8 * 128 * 2  # fp16 V images, then 64 partial maxima and one exponent
+    assert need == vbytes + ((8 * 64 * 4 + 255) // 256) * 256 + 256  # per (batch, kv head)
     r = lib.sparse_attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 65, 0.1, FAKE,
                                 need - 1, FAKE, api.SA_BF16, None, None)
     assert r == api.SA_ERR_INVALID and "workspace" in api.last_error()
@@ -250,3 +251,63 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0 and "one GPU" in (r.stdout + r.stderr)
+
+
+def test_selection_lds_limit_rejected_before_hip(lib):
+    """The selection keeps a sort key per block and the tile's query rows in LDS: problems
+    whose need exceeds a CU's LDS are refused with SA_ERR_UNSUPPORTED before any HIP call,
+    and the workspace query returns 0 for them."""
+    p, b = _ok_problem(), _ok_budget()
+    p.seqlen = 64 * 16384  # 16384 blocks: 128 KiB of keys
+    for over in (dict(score_mode=api.SA_KMINMAX), dict(tile=128)):
+        q = api.Problem.from_buffer_copy(p)
+        for k, v in over.items():
+            setattr(q, k, v)
+        assert lib.sparse_attn_select_workspace_bytes(ctypes.byref(q), ctypes.byref(b)) == 0
+        rc = lib.sparse_attn_select(ctypes.byref(q), ctypes.byref(b), FAKE, FAKE, FAKE, 1 << 50,
+                                    FAKE, FAKE, None, None, None, None, None)
+        assert rc == api.SA_ERR_UNSUPPORTED and "LDS" in api.last_error(), over
+    # the mean-pool backbone with 64-row tiles fits at the same length, and K-min/K-max fits
+    # at half of it
+    assert lib.sparse_attn_select_workspace_bytes(ctypes.byref(p), ctypes.byref(b)) > 0
+    p.seqlen, p.score_mode = 64 * 8192, api.SA_KMINMAX
+    assert lib.sparse_attn_select_workspace_bytes(ctypes.byref(p), ctypes.byref(b)) > 0
+
+
+def test_value_norm_lds_limit_rejected_before_hip(lib):
+    """Output-aware scoring holds block x n_kv_heads norms in LDS."""
+    p = api.problem(wl.WORKLOADS["stem_32k"])
+    p.block = p.tile = 128
+    p.n_q_heads = p.n_kv_heads = 320  # 128 x 320 x 4 bytes = 160 KiB
+    rc = lib.sparse_attn_score(ctypes.byref(p), FAKE, FAKE, FAKE, None)
+    assert rc == api.SA_ERR_UNSUPPORTED and "LDS" in api.last_error()
+
+
+def test_prepared_forward_validation(lib):
+    p = _ok_problem()
+    ws = api.forward_workspace_bytes(p)
+    assert lib.sparse_attn_prepare_values(ctypes.byref(p), FAKE, FAKE, ws - 1,
+                                          None) == api.SA_ERR_INVALID
+    assert lib.sparse_attn_prepare_values(ctypes.byref(p), None, FAKE, ws,
+                                          None) == api.SA_ERR_INVALID
+
+    def fwd(prob=p, ws_ptr=FAKE, ws_bytes=ws, W=65, out=api.SA_BF16, scale=0.1):
+        return lib.sparse_attn_forward_prepared(ctypes.byref(prob), FAKE, FAKE, ws_ptr, ws_bytes,
+                                                FAKE, FAKE, W, scale, FAKE, out, None, None)
+
+    assert fwd(ws_bytes=ws - 1) == api.SA_ERR_INVALID
+    assert fwd(ws_ptr=None) == api.SA_ERR_INVALID
+    assert fwd(W=0) == api.SA_ERR_INVALID
+    assert fwd(out=3) == api.SA_ERR_INVALID
+    assert fwd(scale=float("nan")) == api.SA_ERR_INVALID
+    f32 = api.problem(wl.WORKLOADS["tiny_ref"])
+    assert fwd(prob=f32, ws_bytes=1 << 40) == api.SA_ERR_UNSUPPORTED
+    assert "fp32" in api.last_error()
+    assert lib.sparse_attn_prepare_values(ctypes.byref(f32), FAKE, FAKE, 1 << 40,
+                                          None) == api.SA_ERR_UNSUPPORTED
+
+
+def test_calibrate_tau_validation(lib):
+    assert lib.sparse_attn_calibrate_tau(None, 2, FAKE, None) == api.SA_ERR_INVALID
+    assert lib.sparse_attn_calibrate_tau(FAKE, 0, FAKE, None) == api.SA_ERR_INVALID
+    assert lib.sparse_attn_calibrate_tau(FAKE, 2, None, None) == api.SA_ERR_INVALID

@@ -30,3 +30,23 @@ def test_effective_flops_count_shared_lists_once_per_head():
     c_shared = torch.full((1, shared.n_kv_heads, n), 3, dtype=torch.int32)
     assert bench.effective_flops(per_head, c_head) == bench.effective_flops(shared, c_shared)
     assert bench.effective_flops(shared, c_shared) == 4.0 * 64 * 64 * 128 * 32 * n * 3
+
+
+def test_causal_exact_flops_leave_out_the_masked_pairs():
+    """Dense causal lists: the exact count is 4 d per (row, key <= row) pair, N (N + 1) / 2
+    pairs per head, for tiles equal to blocks and for 128-row tiles over 64-key blocks;
+    without the diagonal blocks' masked pairs the count is the effective one."""
+    for w in (wl.WORKLOADS["prefill_128k"].resized(seqlen=1024, n_q_heads=2, n_kv_heads=1),
+              wl.WORKLOADS["llama8b_32k_t128"].resized(seqlen=1024, n_q_heads=2, n_kv_heads=1)):
+        m, nt = w.tile // w.block, w.n_tiles
+        W = m * nt
+        idx = torch.full((1, 2, nt, W), -1, dtype=torch.int32)
+        cnt = torch.zeros((1, 2, nt), dtype=torch.int32)
+        for t in range(nt):
+            idx[0, :, t, :m * (t + 1)] = torch.arange(m * (t + 1), dtype=torch.int32)
+            cnt[0, :, t] = m * (t + 1)
+        N = w.seqlen
+        assert bench.causal_exact_flops(w, idx, cnt) == 4.0 * w.head_dim * 2 * N * (N + 1) / 2
+        diag_masked = 2 * nt * 4.0 * w.head_dim * w.tile * (w.tile - 1) / 2
+        assert (bench.effective_flops(w, cnt) - bench.causal_exact_flops(w, idx, cnt)
+                == diag_masked)

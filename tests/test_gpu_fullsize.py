@@ -1,16 +1,16 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the benchmark times.
 
-The whole pipeline runs on the full input (bf16 output, no lse: exactly what bench.py runs).
-The oracle cannot redo every tile at these sizes in test time, so the check is layered:
+The whole pipeline runs on the full input (bf16 output, no lse: exactly what bench.py runs),
+and is compared with the oracle in full where the oracle can do it in test time:
 
-  * block summaries: every block, bit for bit (the oracle pools the full input cheaply);
-  * selection: sampled tiles (first, second, middle, last, tripped ones and random ones), every
-    head: sigma, sigma_bar, eligibility, kv_idx and kv_cnt bit for bit against oracle.select_tile;
-  * gate and lists everywhere: the properties that hold at any size (check_structure: tau is
-    the ceil(q M)-th smallest eligible sigma_bar, gate = eligible and sigma_bar <= tau, counts =
-    forced + kept, lists ascending with the diagonal last, sinks present, sigma in [0, 1]);
-  * attention: rows of the sampled tiles (all heads' first rows, random heads' rows) against the
-    fp64 oracle on the GPU's own lists, to 2e-2 plus the bf16 output cast.
+  * block summaries: every block, bit for bit;
+  * selection: the whole oracle selection (oracle.select) on the same input: sigma, sigma_bar,
+    tau, the gate bits, kv_idx and kv_cnt of every tile and selection unit, bit for bit; and the
+    properties that hold at any size (check_structure), as a second, independent reading;
+  * attention: one row of every tile (a random head and row) plus the first and last rows of
+    a few tiles for every head, against the fp64 oracle on the same lists: the bf16 output to
+    2e-2 plus half a bf16 ulp of |O| (the output cast), and an fp32 output of the same call to
+    the plain 2e-2.
 """
 
 import numpy as np
@@ -21,7 +21,7 @@ import oracle
 from block_sparse_causal_mean_amd import api
 from block_sparse_causal_mean_amd import workloads as wl
 
-from parity import bits, check_structure, out_tol, say
+from parity import TOL_BF16, assert_selection_equal, bits, check_structure, out_tol, say
 
 pytestmark = pytest.mark.gpu
 
@@ -29,18 +29,24 @@ FULL = ["llama8b_32k", "prefill_128k", "quest_64k", "stem_32k", "stem_additive_3
         "llama8b_32k_kvshared", "stem_32k_kvshared", "llama8b_32k_t128", "stem_32k_t128"]
 
 
-def _sample_tiles(n, gate_row, rng, extra=4):
-    tiles = {0, 1, n // 3, n // 2, n - 1}
-    tripped = np.nonzero(gate_row)[0]
-    if len(tripped):
-        tiles.update(int(x) for x in rng.choice(tripped, size=min(3, len(tripped)), replace=False))
-    tiles.update(int(x) for x in rng.integers(2, n - 1, size=extra))
-    return sorted(tiles)
+def _rows(w, rng):
+    """One random (head, row) in every tile of every batch element, plus the first and last
+    rows of tiles 0, 1, n/2 and n-1 for every head."""
+    n, T, Hq = w.n_tiles, w.tile, w.n_q_heads
+    rows = []
+    for b in range(w.batch):
+        heads = rng.integers(Hq, size=n)
+        offs = rng.integers(T, size=n)
+        rows += [(b, int(heads[t]), t * T + int(offs[t])) for t in range(n)]
+        for t in sorted({0, 1, n // 2, n - 1}):
+            for h in range(Hq):
+                rows += [(b, h, t * T), (b, h, t * T + T - 1)]
+    return np.array(rows, np.int64)
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_parity(name):
+def test_full_size_parity(name):
     w = wl.WORKLOADS[name]
     say(f"[full] {name}: generating inputs")
     inp = wl.make_inputs(w)
@@ -49,15 +55,12 @@ def test_full_size_sampled_parity(name):
     pf.run(d["Q"], d["K"], d["V"])
     torch.cuda.synchronize()
     say(f"[full] {name}: GPU pipeline done")
-    n, B, Hq, G = w.n_tiles, w.batch, w.n_q_heads, w.n_q_heads // w.n_kv_heads
-    kv_idx, kv_cnt = pf.kv_idx.cpu().numpy(), pf.kv_cnt.cpu().numpy()
-    sigma, sigma_bar = pf.sigma.cpu().numpy(), pf.sigma_bar.cpu().numpy()
-    gate, tau = pf.gate.cpu().numpy(), pf.tau.cpu().numpy()
-
-    # Properties of every tile.
-    check_structure(w, kv_idx, kv_cnt, gate, sigma, sigma_bar, tau)
-    trips = int(gate.sum())
-    say(f"[full] {name}: structure ok, {trips} tripped tiles of {B * n}")
+    B = w.batch
+    g = {"kv_idx": pf.kv_idx.cpu().numpy(), "kv_cnt": pf.kv_cnt.cpu().numpy(),
+         "sigma": pf.sigma.cpu().numpy(), "sigma_bar": pf.sigma_bar.cpu().numpy(),
+         "gate": pf.gate.cpu().numpy(), "tau": pf.tau.cpu().numpy()}
+    check_structure(w, g["kv_idx"], g["kv_cnt"], g["gate"], g["sigma"], g["sigma_bar"], g["tau"])
+    say(f"[full] {name}: structure ok, {int(g['gate'].sum())} tripped tiles of {B * w.n_tiles}")
 
     # Summaries, in full.
     cfg = oracle.make_cfg(w)
@@ -72,35 +75,27 @@ def test_full_size_sampled_parity(name):
     if w.output_aware:
         np.testing.assert_array_equal(bits(g_summ[off:off + B * w.n_blocks * w.n_kv_heads]),
                                       bits(summ["vn"].reshape(-1)))
+    say(f"[full] {name}: summaries equal; oracle selection of every tile ({oracle.threads()} "
+        f"threads)")
 
-    # Selection of sampled tiles, every head.
-    rng = np.random.default_rng(7)
-    rows = []
-    for b in range(B):
-        tiles = _sample_tiles(n, gate[b], rng)
-        for t in tiles:
-            one = oracle.select_tile(cfg, inp["Q"], summ, b, t)
-            np.testing.assert_array_equal(bits(sigma[b, :, t]), bits(one["sigma"]))
-            assert bits(sigma_bar[b, t]) == bits(one["sigma_bar"])
-            lists = one["lists"][int(gate[b, t])]
-            cnts = one["cnts"][int(gate[b, t])]
-            np.testing.assert_array_equal(kv_cnt[b, :, t], cnts)
-            np.testing.assert_array_equal(kv_idx[b, :, t, :], lists[:, :kv_idx.shape[-1]])
-            # rows to check: first and last row of the tile for every head, plus 16 random
-            # (head, row) pairs
-            for h in range(Hq):
-                rows.append((b, h, t * w.tile))
-                rows.append((b, h, t * w.tile + w.tile - 1))
-            for _ in range(16):
-                rows.append((b, int(rng.integers(Hq)), t * w.tile + int(rng.integers(w.tile))))
-        say(f"[full] {name}: batch {b}: tiles {tiles} match the oracle")
+    # The whole selection.
+    o_sel = oracle.select(cfg, inp["Q"], summ)
+    assert_selection_equal(g, o_sel)
+    say(f"[full] {name}: selection equal on every tile (tau {g['tau'].tolist()})")
 
-    rows = np.array(rows, np.int64)
-    O_ref, _ = oracle.forward(cfg, inp["Q"], inp["K"], inp["V"], kv_idx, kv_cnt, pf.scale,
-                              rows=rows)
+    # Attention: a row of every tile, bf16 output (the benchmark's) and fp32 output.
+    rows = _rows(w, np.random.default_rng(7))
+    O_ref, _ = oracle.forward(cfg, inp["Q"], inp["K"], inp["V"], g["kv_idx"], g["kv_cnt"],
+                              pf.scale, rows=rows)
     r = torch.as_tensor(rows, device="cuda")
-    O = pf.O[r[:, 0], r[:, 2], r[:, 1]].float().cpu().numpy()
-    err = np.abs(O.astype(np.float64) - O_ref)
-    tol = out_tol(w, api.SA_BF16, O_ref)
-    say(f"[full] {name}: {len(rows)} rows, max|O - O_ref| = {err.max():.3e}")
-    assert np.all(err <= tol), f"max err {err.max()} at row {rows[err.max(axis=1).argmax()]}"
+    O16 = pf.O[r[:, 0], r[:, 2], r[:, 1]].float().cpu().numpy().astype(np.float64)
+    err16 = np.abs(O16 - O_ref)
+    O32 = torch.empty(pf.O.shape, dtype=torch.float32, device="cuda")
+    api.forward(pf.p, d["Q"], d["K"], d["V"], pf.kv_idx, pf.kv_cnt, pf.W, pf.scale, pf.fws, O32,
+                api.SA_F32)
+    torch.cuda.synchronize()
+    err32 = np.abs(O32[r[:, 0], r[:, 2], r[:, 1]].cpu().numpy().astype(np.float64) - O_ref)
+    say(f"[full] {name}: {len(rows)} rows (every tile), max|O - O_ref| = {err32.max():.3e} "
+        f"(fp32 out), {err16.max():.3e} (bf16 out)")
+    assert np.all(err32 <= TOL_BF16), f"fp32 out: max err {err32.max()}"
+    assert np.all(err16 <= out_tol(w, api.SA_BF16, O_ref)), f"bf16 out: max err {err16.max()}"

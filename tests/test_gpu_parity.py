@@ -188,6 +188,18 @@ EDGE = {
     "tied_rows_kvshared": WL["prefill_128k_kvshared"].resized(seqlen=2048, n_q_heads=4,
                                                               n_kv_heads=2, k_max=4, k_min=4,
                                                               planted=False),
+    # all keys zero: every score is +0, sigma = 0 everywhere, ranking falls to the index
+    "zero_keys_kmean_oam": WL["stem_32k"].resized(batch=1, seqlen=1536, n_q_heads=4,
+                                                  n_kv_heads=2, k_max=4, k_min=2),
+    "zero_keys_quest": WL["quest_64k"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=2, k_max=4,
+                                               k_min=4),
+    # product output-aware score with all-zero value blocks: tile scores times 0 are -0 for
+    # negative maxima and +0 otherwise; both sides compare and subtract the canonical +0
+    "zero_value_blocks_oam": WL["stem_32k"].resized(batch=2, seqlen=2048, n_q_heads=4,
+                                                    n_kv_heads=2, k_max=6, k_min=3, q=0.3),
+    "zero_value_blocks_oam_t128": WL["stem_32k_t128"].resized(batch=1, seqlen=2048,
+                                                              n_q_heads=4, n_kv_heads=2,
+                                                              k_max=6, k_min=3, q=0.3),
 }
 
 
@@ -202,6 +214,18 @@ def _edge_inputs(name, w):
         for t in range(w.n_tiles):
             q[:, t * T:(t + 1) * T] = q[:, t * T:t * T + 1]
         inp["Q"] = q
+    if name.startswith("zero_keys"):
+        inp["K"] = torch.zeros_like(inp["K"])
+    if name.startswith("zero_value_blocks"):
+        # every third key block's values are zero; the keys of the first two of each six
+        # blocks are shifted down so that some tiles' maxima over them are negative
+        v, k = inp["V"].clone(), inp["K"].clone()
+        B = w.block
+        for j in range(0, w.n_blocks, 3):
+            v[:, j * B:(j + 1) * B] = 0
+        for j in range(0, w.n_blocks, 6):
+            k[:, j * B:(j + 2) * B] -= 6.0
+        inp["V"], inp["K"] = v, k
     if name.startswith("tied_blocks"):
         # every key block identical: all tile scores of a tile tie, ranking falls to the index
         k = inp["K"].clone()
@@ -378,3 +402,94 @@ def test_fixed_gate_with_calibrated_tau_reproduces_the_quantile_gate():
     cfg = oracle.make_cfg(wf)
     o_sel = oracle.select(cfg, inp["Q"], oracle.pool(cfg, inp["K"], inp["V"]))
     assert_selection_equal(f_run, o_sel)
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("case", ["non_uniform_norms", "zero_value_blocks"])
+def test_oam_product_golden_on_gpu(case, dtype):
+    """The hand-worked product output-aware examples (tests/golden/oam_product.json) through
+    the C ABI: summaries, sigma, tau, gate and lists equal the golden values bit for bit."""
+    import golden_inputs as gi
+    g = gi.load("oam_product.json")
+    c = next(x for x in g["cases"] if x["name"] == case)
+    w = gi.oam_product_workload(g, dtype)
+    inp = gi.oam_product_inputs(c, dtype)
+    out = run_gpu(w, inp, out_dtype=api.SA_F32)
+    np.testing.assert_array_equal(out["vn"][0, :, 0], np.float32(c["vnorm"]))
+    want_sigma = np.array([gi.f32(x) for x in c["sigma"]], np.float32)
+    np.testing.assert_array_equal(out["sigma"][0, 0].view(np.uint32), want_sigma.view(np.uint32))
+    assert out["tau"][0].view(np.uint32) == gi.f32(c["tau"]).view(np.uint32)
+    np.testing.assert_array_equal(out["gate"][0], c["gate"])
+    np.testing.assert_array_equal(out["kv_idx"][0, 0], c["kv_idx"])
+    np.testing.assert_array_equal(out["kv_cnt"][0, 0], c["kv_cnt"])
+    compare_outputs(w, out, inp, api.SA_F32, None)
+
+
+def _prepared_forward(w, d, pf, V, out_dtype=api.SA_F32):
+    """Attention over pf's lists with another V: prepare_values, then forward_prepared."""
+    O = torch.empty((w.batch, w.seqlen, w.n_q_heads, w.head_dim),
+                    dtype=torch.float32 if out_dtype == api.SA_F32 else torch.bfloat16,
+                    device="cuda")
+    api.prepare_values(pf.p, V, pf.fws)
+    api.forward_prepared(pf.p, d["Q"], d["K"], pf.fws, pf.kv_idx, pf.kv_cnt, pf.W, pf.scale, O,
+                         out_dtype)
+    torch.cuda.synchronize()
+    return O
+
+
+@pytest.mark.parametrize("name", ["llama8b_n32", "prefill_n32_planted", "stem_b2_t128"])
+def test_value_magnitudes_beyond_fp16(name):
+    """bf16 V far outside fp16's range (about 1e5 and 1e-6 in magnitude): P V runs on fp16
+    matrix cores after a per-(batch, kv head) power-of-two scaling, so scaling V by 2^k scales
+    every output by exactly 2^k (bit for bit), and V = c Z meets the bf16 bar on O / c against
+    the fp64 oracle (attention is linear in V)."""
+    w = SMALL[name]
+    inp = wl.make_inputs(w)
+    d = {k: v.cuda() for k, v in inp.items()}
+    pf = api.Prefill(w, out_dtype=api.SA_F32)
+    pf.run(d["Q"], d["K"], d["V"])
+    torch.cuda.synchronize()
+    base = pf.O.clone()
+    for k in (17, -20):
+        Vk = (d["V"].float() * 2.0 ** k).to(torch.bfloat16)  # exact: a power-of-two scaling
+        Ok = _prepared_forward(w, d, pf, Vk)
+        assert torch.equal(Ok, base * 2.0 ** k), f"2^{k}: not an exact scaling"
+        # the combined call gives the same bits as the two halves
+        O2 = torch.empty_like(Ok)
+        api.forward(pf.p, d["Q"], d["K"], Vk, pf.kv_idx, pf.kv_cnt, pf.W, pf.scale, pf.fws, O2,
+                    api.SA_F32)
+        torch.cuda.synchronize()
+        assert torch.equal(O2, Ok)
+    rng = np.random.default_rng(3)
+    rows = sample_rows(w, rng, max_rows=3000)
+    cfg = oracle.make_cfg(w)
+    kv_idx, kv_cnt = pf.kv_idx.cpu().numpy(), pf.kv_cnt.cpu().numpy()
+    for c in (1.0e5, -1.0e-6):
+        Z = torch.from_numpy(rng.standard_normal(tuple(inp["V"].shape)).astype(np.float32))
+        Vc = (Z * c).to(torch.bfloat16)
+        Oc = _prepared_forward(w, d, pf, Vc.cuda()).cpu().numpy()
+        O_ref, _ = oracle.forward(cfg, inp["Q"], inp["K"], Vc, kv_idx, kv_cnt, pf.scale,
+                                  rows=rows)
+        got = Oc if rows is None else Oc[rows[:, 0], rows[:, 2], rows[:, 1]]
+        err = np.abs(got.astype(np.float64) - O_ref).max() / abs(c)
+        say(f"[{name}] V = {c:g} Z: max|O - O_ref| / |c| = {err:.3e}")
+        assert np.isfinite(got).all() and err <= 2e-2
+
+
+def test_calibrated_tau_over_several_sequences():
+    """sparse_attn_calibrate_tau over per-sequence quantile thresholds equals the oracle's
+    mean of the finite thresholds; with one sequence it is that sequence's tau."""
+    w = WL["stem_additive_32k"].resized(batch=3, seqlen=2048, k_max=16, k_min=4)
+    inp = wl.make_inputs(w)
+    cfg = oracle.make_cfg(w)
+    o_sel = oracle.select(cfg, inp["Q"], oracle.pool(cfg, inp["K"], inp["V"]))
+    dev = {k: v.cuda() for k, v in inp.items()}
+    tau = api.Prefill(w).calibrate_tau(dev["Q"], dev["K"], dev["V"])
+    want = oracle.calibrated_tau(o_sel["tau"])
+    assert np.float32(tau).view(np.uint32) == want.view(np.uint32)
+    t = torch.tensor([0.25, -float("inf"), 0.5, 0.125], device="cuda")
+    out = torch.empty(1, device="cuda")
+    api.calibrate_tau(t, out)
+    assert out.item() == oracle.calibrated_tau(t.cpu().numpy())
+    api.calibrate_tau(torch.full((2,), -float("inf"), device="cuda"), out)
+    assert out.item() == -float("inf")

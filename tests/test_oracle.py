@@ -167,6 +167,146 @@ def test_vnorm_exact_powers_of_two_and_library_norm():
     np.testing.assert_allclose(s2["vn"][0, :, 0], ref, rtol=2e-6)
 
 
+# Exact emulations of the summaries' fp32 arithmetic, independent of the oracle: numpy's
+# scalar fp32 addition (IEEE, round to nearest even) in an explicit Python loop, the
+# Fraction-based fused multiply-add above, and a square root rounded by exact comparison
+# with the midpoints between neighbouring fp32 values.
+
+def _seq_sum_f32(xs) -> np.float32:
+    acc = np.float32(0.0)
+    for x in xs:
+        acc = np.float32(acc + np.float32(x))
+    return acc
+
+
+def _sqrt_f32_exact(x: np.float32) -> np.float32:
+    """Correctly rounded fp32 square root of a non-negative fp32 value."""
+    X = Fraction(float(x))
+    if X == 0:
+        return np.float32(0.0)
+    r = np.float32(math.sqrt(float(x)))
+    for _ in range(4):
+        lo = np.nextafter(r, np.float32(0.0))
+        hi = np.nextafter(r, np.float32(np.inf))
+        mid_lo = (Fraction(float(lo)) + Fraction(float(r))) / 2
+        mid_hi = (Fraction(float(r)) + Fraction(float(hi))) / 2
+        if X < mid_lo * mid_lo:
+            r = lo
+        elif X > mid_hi * mid_hi:
+            r = hi
+        else:
+            return r
+    raise AssertionError("square root emulation did not converge")
+
+
+def _pairwise_f32(xs) -> np.float32:
+    xs = [np.float32(x) for x in xs]
+    while len(xs) > 1:
+        xs = [np.float32(xs[i] + xs[i + 1]) if i + 1 < len(xs) else xs[i]
+              for i in range(0, len(xs), 2)]
+    return xs[0]
+
+
+def _wide_keys(shape, seed, dtype):
+    """Values spread over many binades, so that fp32 sums of a block round and the order of
+    the additions shows in the result bits."""
+    g = np.random.default_rng(seed)
+    x = g.standard_normal(shape) * 2.0 ** g.integers(-10, 11, shape)
+    return torch.from_numpy(x.astype(np.float32)).to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_pool_mean_is_row_order_fp32_sum(dtype):
+    """kmean of every (block, coordinate) is, bit for bit, the fp32 sum of the block's rows
+    in row order from +0, times 1/block; pairwise, reversed and fp64 sums give other bits on
+    these inputs, so the pin fixes the order."""
+    w = _small(head_dim=16, block=64, seqlen=256, dtype=dtype)
+    cfg = oracle.make_cfg(w)
+    tdt = torch.bfloat16 if dtype == wl.BF16 else torch.float32
+    K = _wide_keys((1, 256, 1, 16), 61, tdt)
+    s = oracle.pool(cfg, K)
+    k = K.float().numpy()[0, :, 0]
+    inv = np.float32(1.0 / 64)
+    differs = {"pairwise": 0, "reversed": 0, "fp64": 0}
+    for j in range(4):
+        for c in range(16):
+            col = k[j * 64:(j + 1) * 64, c]
+            want = np.float32(_seq_sum_f32(col) * inv)
+            assert s["kA"][0, j, 0, c].view(np.uint32) == want.view(np.uint32), (j, c)
+            differs["pairwise"] += np.float32(_pairwise_f32(col) * inv) != want
+            differs["reversed"] += np.float32(_seq_sum_f32(col[::-1]) * inv) != want
+            differs["fp64"] += np.float32(np.float32(col.astype(np.float64).sum()) * inv) != want
+    assert all(v > 0 for v in differs.values()), differs
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_vnorm_is_row_order_sum_of_rounded_row_norms(dtype):
+    """vnorm of every block is, bit for bit: per row the fused multiply-add chain of the
+    squares over coordinates in order, its correctly rounded square root, then the fp32 sum
+    of those norms in row order, times 1/block.  Unfused squares, pairwise or reversed row
+    sums, and the norm of the summed squares give other bits on these inputs."""
+    w = _small(head_dim=16, block=64, seqlen=256, dtype=dtype, output_aware=1)
+    cfg = oracle.make_cfg(w)
+    tdt = torch.bfloat16 if dtype == wl.BF16 else torch.float32
+    V = _wide_keys((1, 256, 1, 16), 62, tdt)
+    K = torch.zeros_like(V)
+    s = oracle.pool(cfg, K, V)
+    v = V.float().numpy()[0, :, 0]
+    inv = np.float32(1.0 / 64)
+    differs = {"unfused": 0, "pairwise": 0, "reversed": 0, "sqrt_of_sum": 0}
+    for j in range(4):
+        rows = v[j * 64:(j + 1) * 64]
+        norms, norms_unfused, sq = [], [], []
+        for r in rows:
+            ss, su = np.float32(0.0), np.float32(0.0)
+            for x in r:
+                ss = _fma_exact(x, x, ss)
+                su = np.float32(su + np.float32(x * x))
+            sq.append(ss)
+            norms.append(_sqrt_f32_exact(ss))
+            norms_unfused.append(_sqrt_f32_exact(su))
+        want = np.float32(_seq_sum_f32(norms) * inv)
+        assert s["vn"][0, j, 0].view(np.uint32) == want.view(np.uint32), j
+        differs["unfused"] += np.float32(_seq_sum_f32(norms_unfused) * inv) != want
+        differs["pairwise"] += np.float32(_pairwise_f32(norms) * inv) != want
+        differs["reversed"] += np.float32(_seq_sum_f32(norms[::-1]) * inv) != want
+        differs["sqrt_of_sum"] += _sqrt_f32_exact(np.float32(_seq_sum_f32(sq) * inv)) != want
+    if dtype == wl.BF16:  # squares of bf16 values are exact in fp32: fused = unfused
+        assert differs.pop("unfused") == 0
+    assert all(v > 0 for v in differs.values()), differs
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("case", ["non_uniform_norms", "zero_value_blocks"])
+def test_oam_product_golden(case, dtype):
+    """Product form of the output-aware score with value norms that differ per block
+    (tests/golden/oam_product.json): the products reorder the blocks against the plain
+    score, and all-zero value blocks with negative tile scores give -0 products that the
+    canonical form maps to +0 (sigma's bits show it)."""
+    import golden_inputs as gi
+    g = gi.load("oam_product.json")
+    c = next(x for x in g["cases"] if x["name"] == case)
+    w = gi.oam_product_workload(g, dtype)
+    inp = gi.oam_product_inputs(c, dtype)
+    cfg = oracle.make_cfg(w)
+    assert cfg.width == 5
+    s = oracle.pool(cfg, inp["K"], inp["V"])
+    np.testing.assert_array_equal(s["vn"][0, :, 0], np.float32(c["vnorm"]))
+    np.testing.assert_array_equal(s["kA"][0, :, 0, 0], np.float32(c["c"]))
+    out = oracle.select(cfg, inp["Q"], s)
+    want_sigma = np.array([gi.f32(x) for x in c["sigma"]], np.float32)
+    np.testing.assert_array_equal(out["sigma"][0, 0].view(np.uint32), want_sigma.view(np.uint32))
+    np.testing.assert_array_equal(out["sigma_bar"][0].view(np.uint32), want_sigma.view(np.uint32))
+    assert out["tau"][0].view(np.uint32) == gi.f32(c["tau"]).view(np.uint32)
+    np.testing.assert_array_equal(out["gate"][0], c["gate"])
+    np.testing.assert_array_equal(out["kv_idx"][0, 0], c["kv_idx"])
+    np.testing.assert_array_equal(out["kv_cnt"][0, 0], c["kv_cnt"])
+    # The plain score (no value norms) selects differently on these inputs.
+    plain = oracle.select(oracle.make_cfg(w, output_aware=0), inp["Q"], oracle.pool(
+        oracle.make_cfg(w, output_aware=0), inp["K"]))
+    assert not np.array_equal(plain["kv_idx"], out["kv_idx"])
+
+
 # ---------------------------------------------------------------------- block scores
 
 def test_quest_bound_is_upper_bound():
@@ -815,3 +955,15 @@ def test_art_constant_values_stop_after_patience():
     for p in (1, 3, 7):
         r = oracle.decode_art(cfg, Q, K, V, 0.25, 16, 1e-9, 1e-9, p)
         assert (r["stop"] == p + 1).all(), p
+
+
+def test_calibrated_tau_is_mean_of_finite_thresholds():
+    """Per-layer fixed-gate threshold from calibration runs: the mean of the per-sequence
+    thresholds where a tile can trip; hand values, exact rationals rounded once to fp32."""
+    ninf = -np.inf
+    assert oracle.calibrated_tau([0.25, ninf, 0.5, 0.125]) == _round_f32(Fraction(7, 24))
+    assert oracle.calibrated_tau([0.375]) == np.float32(0.375)
+    assert oracle.calibrated_tau([ninf, ninf]) == -np.inf
+    # fp32 sum in index order: 1 + 2^-24 rounds to 1 (tie to even) before 2^-24 is added again
+    x = float(2.0 ** -24)
+    assert oracle.calibrated_tau([1.0, x, x]) == np.float32(1.0) / np.float32(3.0)
