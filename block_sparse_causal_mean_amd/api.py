@@ -34,7 +34,7 @@ EXPORTS = ("sparse_attn_summary_bytes", "sparse_attn_select_workspace_bytes",
            "sparse_attn_forward_workspace_bytes", "sparse_attn_forward",
            "sparse_attn_prepare_values", "sparse_attn_forward_prepared",
            "sparse_attn_calibrate_tau", "sparse_attn_forward_vs", "sparse_attn_decode_art",
-           "sparse_attn_last_error")
+           "sparse_attn_select_noalloc", "sparse_attn_last_error")
 
 
 class Problem(ctypes.Structure):
@@ -91,11 +91,13 @@ def load() -> ctypes.CDLL:
     lib.sparse_attn_decode_art.argtypes = [PP, P, P, P, ctypes.c_float, ctypes.c_float,
                                            ctypes.c_float, ctypes.c_int32, P, ctypes.c_int32,
                                            P, P]
+    lib.sparse_attn_select_noalloc.argtypes = [PP, PB, P, P, P, P, P, P, P, P, P]
     lib.sparse_attn_last_error.argtypes = []
     lib.sparse_attn_last_error.restype = ctypes.c_char_p
     for f in ("sparse_attn_score", "sparse_attn_select", "sparse_attn_forward",
               "sparse_attn_prepare_values", "sparse_attn_forward_prepared",
-              "sparse_attn_calibrate_tau", "sparse_attn_forward_vs", "sparse_attn_decode_art"):
+              "sparse_attn_calibrate_tau", "sparse_attn_forward_vs", "sparse_attn_decode_art",
+              "sparse_attn_select_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -146,6 +148,25 @@ def index_width(p: Problem, b: Budget) -> int:
     w = load().sparse_attn_index_width(ctypes.byref(p), ctypes.byref(b))
     _check(min(w, 0))
     return w
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # the library's own selection workspace (per GPU)
+
+
+def select_noalloc(p: Problem, b: Budget, Q: torch.Tensor, summaries: torch.Tensor,
+                   kv_idx: torch.Tensor, kv_cnt: torch.Tensor, sigma=None, sigma_bar=None,
+                   gate=None, tau=None, stream=None):
+    """sparse_attn_select_noalloc: the selection with the library's own workspace."""
+    n = p.seqlen // p.tile
+    bhn = p.batch * units(p) * n
+    W = index_width(p, b)
+    _check(load().sparse_attn_select_noalloc(
+        ctypes.byref(p), ctypes.byref(b),
+        _ptr(Q, "Q", p.batch * p.seqlen * p.n_q_heads * p.head_dim * _elt(p)),
+        _ptr(summaries, "summaries", summary_bytes(p)), _ptr(kv_idx, "kv_idx", bhn * W * 4),
+        _ptr(kv_cnt, "kv_cnt", bhn * 4), _ptr(sigma, "sigma", bhn * 4),
+        _ptr(sigma_bar, "sigma_bar", p.batch * n * 4), _ptr(gate, "gate", p.batch * n),
+        _ptr(tau, "tau", p.batch * 4), _stream(stream)))
 
 
 def forward_workspace_bytes(p: Problem) -> int:

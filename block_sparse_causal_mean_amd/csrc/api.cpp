@@ -6,9 +6,17 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "common.h"
+
+// Selection workspace of sparse_attn_select_noalloc: a fixed device array instead of a caller
+// buffer (each GPU the library runs on holds its own copy until the process ends).  Host code
+// never uses this name as an address: it keeps the address hipGetSymbolAddress returns, per
+// device.
+constexpr size_t kScratchBytes = 64u << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
 
@@ -372,6 +380,52 @@ int sparse_attn_decode_art(const sa_problem* p, const void* Q, const void* K, co
                                           out_dtype, blocks_done,
                                           static_cast<hipStream_t>(stream)),
                     "sparse_attn_decode_art launch");
+}
+
+int sparse_attn_select_noalloc(const sa_problem* p, const sa_budget* b, const void* Q,
+                               const void* summaries, int32_t* kv_idx, int32_t* kv_cnt,
+                               float* sigma, float* sigma_bar, uint8_t* gate, float* tau,
+                               void* stream) {
+  sa::Dims D;
+  sa::BudgetDev bd;
+  int rc = check_problem(p, &D);
+  if (rc != SA_OK) return rc;
+  if ((rc = check_budget(b, D, &bd)) != SA_OK) return rc;
+  if ((rc = check_select_lds(D)) != SA_OK) return rc;
+  if (!Q || !summaries || !kv_idx || !kv_cnt)
+    return fail(SA_ERR_INVALID, "Q, summaries, kv_idx and kv_cnt must be non-NULL");
+  const size_t need = sa::select_ws_layout(D, bd).total;
+  if (need > kScratchBytes)
+    return fail(SA_ERR_UNSUPPORTED,
+                "the selection needs %zu bytes of workspace; sparse_attn_select_noalloc holds "
+                "%zu (use sparse_attn_select with a caller workspace)",
+                need, kScratchBytes);
+  // The device array's address on the current device, looked up once per device.
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if ((rc = hip_status(hipGetDevice(&dev), "hipGetDevice")) != SA_OK) return rc;
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SA_ERR_UNSUPPORTED, "device %d beyond the %d this entry point tracks", dev,
+                kMaxDevices);
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+      void* ptr = nullptr;
+      if ((rc = hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)),
+                           "hipGetSymbolAddress(scratch)")) != SA_OK)
+        return rc;
+      addr[dev] = ptr;
+    }
+    ws = addr[dev];
+  }
+  g_err.clear();
+  return hip_status(sa::launch_select(D, bd, Q, static_cast<const float*>(summaries),
+                                      static_cast<char*>(ws), kv_idx, kv_cnt, sigma, sigma_bar,
+                                      gate, tau, static_cast<hipStream_t>(stream)),
+                    "sparse_attn_select_noalloc launch");
 }
 
 const char* sparse_attn_last_error(void) { return g_err.c_str(); }

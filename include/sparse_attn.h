@@ -281,6 +281,22 @@ int sparse_attn_decode_art(const sa_problem* p, const void* Q, const void* K, co
                            float softmax_scale, float tau, float phi, int32_t patience, void* O,
                            int32_t out_dtype, int32_t* blocks_done, void* stream);
 
+/*
+ * sparse_attn_select without a caller workspace, for callers that cannot allocate device
+ * memory (code under stream capture into a graph, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and validation as sparse_attn_select minus ws and
+ * ws_bytes: the workspace is a 64 MiB array inside the library, one per GPU, held until the
+ * process ends.  Problems whose sparse_attn_select_workspace_bytes exceeds 64 MiB
+ * (67108864 bytes) are refused with SA_ERR_UNSUPPORTED before any HIP call.  Nothing is
+ * allocated or freed.  Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (concurrent streams, or threads) race and must be ordered by the caller.
+ * Nothing in the array needs to start at zero (each call writes what it reads).
+ */
+int sparse_attn_select_noalloc(const sa_problem* p, const sa_budget* b, const void* Q,
+                               const void* summaries, int32_t* kv_idx, int32_t* kv_cnt,
+                               float* sigma, float* sigma_bar, uint8_t* gate, float* tau,
+                               void* stream);
+
 /* The calling thread's last error message ("" if none).  Valid until its next call. */
 const char* sparse_attn_last_error(void);
 

@@ -311,3 +311,28 @@ def test_calibrate_tau_validation(lib):
     assert lib.sparse_attn_calibrate_tau(None, 2, FAKE, None) == api.SA_ERR_INVALID
     assert lib.sparse_attn_calibrate_tau(FAKE, 0, FAKE, None) == api.SA_ERR_INVALID
     assert lib.sparse_attn_calibrate_tau(FAKE, 2, None, None) == api.SA_ERR_INVALID
+
+
+def test_select_noalloc_validation(lib):
+    """The no-allocation selection validates as sparse_attn_select does and refuses problems
+    whose workspace exceeds its fixed 64 MiB, all before any HIP call."""
+    p, b = _ok_problem(), _ok_budget()
+
+    def call(prob=p, bud=b, Q=FAKE, kv_idx=FAKE):
+        return lib.sparse_attn_select_noalloc(ctypes.byref(prob), ctypes.byref(bud), Q, FAKE,
+                                              kv_idx, FAKE, None, None, None, None, None)
+
+    assert call(Q=None) == api.SA_ERR_INVALID
+    assert call(kv_idx=None) == api.SA_ERR_INVALID
+    bad = _ok_budget()
+    bad.k_min = 0
+    assert call(bud=bad) == api.SA_ERR_INVALID
+    big = api.problem(wl.WORKLOADS["quest_64k"].resized(batch=8))
+    bq = api.budget(wl.WORKLOADS["quest_64k"])
+    assert api.select_workspace_bytes(big, bq) > api.NOALLOC_SCRATCH_BYTES
+    assert call(prob=big, bud=bq) == api.SA_ERR_UNSUPPORTED
+    assert "67108864" in api.last_error()
+    # every benchmark workload fits
+    for name in wl.WORKLOAD_ORDER:
+        w = wl.WORKLOADS[name]
+        assert api.select_workspace_bytes(api.problem(w), api.budget(w)) <= api.NOALLOC_SCRATCH_BYTES
