@@ -248,7 +248,8 @@ int sparse_attn_forward(const sa_problem* p, const void* Q, const void* K, const
   if (W < 1) return fail(SA_ERR_INVALID, "W must be >= 1");
   if (out_dtype != SA_F32 && out_dtype != SA_BF16)
     return fail(SA_ERR_INVALID, "out_dtype must be SA_F32 or SA_BF16");
-  if (!isfinite(softmax_scale)) return fail(SA_ERR_INVALID, "softmax_scale is not finite");
+  if (!(isfinite(softmax_scale) && softmax_scale > 0.0f))
+    return fail(SA_ERR_INVALID, "softmax_scale must be finite and > 0");
   if (D.dtype == SA_BF16 && (unsigned long long)D.N * D.Hkv * D.d * 2 >= (1ull << 32))
     return fail(SA_ERR_UNSUPPORTED,
                 "seqlen * n_kv_heads * head_dim * 2 = %llu bytes of K per batch element: the "
@@ -295,7 +296,8 @@ int sparse_attn_forward_prepared(const sa_problem* p, const void* Q, const void*
   if (W < 1) return fail(SA_ERR_INVALID, "W must be >= 1");
   if (out_dtype != SA_F32 && out_dtype != SA_BF16)
     return fail(SA_ERR_INVALID, "out_dtype must be SA_F32 or SA_BF16");
-  if (!isfinite(softmax_scale)) return fail(SA_ERR_INVALID, "softmax_scale is not finite");
+  if (!(isfinite(softmax_scale) && softmax_scale > 0.0f))
+    return fail(SA_ERR_INVALID, "softmax_scale must be finite and > 0");
   if ((unsigned long long)D.N * D.Hkv * D.d * 2 >= (1ull << 32))
     return fail(SA_ERR_UNSUPPORTED,
                 "seqlen * n_kv_heads * head_dim * 2 = %llu bytes of K per batch element: the "
@@ -338,7 +340,8 @@ int sparse_attn_forward_vs(const sa_problem* p, const void* Q, const void* K, co
     return fail(SA_ERR_INVALID, "forward workspace too small: %zu < %zu bytes", ws_bytes, need);
   if (out_dtype != SA_F32 && out_dtype != SA_BF16)
     return fail(SA_ERR_INVALID, "out_dtype must be SA_F32 or SA_BF16");
-  if (!isfinite(softmax_scale)) return fail(SA_ERR_INVALID, "softmax_scale is not finite");
+  if (!(isfinite(softmax_scale) && softmax_scale > 0.0f))
+    return fail(SA_ERR_INVALID, "softmax_scale must be finite and > 0");
   if ((unsigned long long)D.N * D.Hkv * D.d * 2 >= (1ull << 32))
     return fail(SA_ERR_UNSUPPORTED,
                 "seqlen * n_kv_heads * head_dim * 2 = %llu bytes of K per batch element: the "

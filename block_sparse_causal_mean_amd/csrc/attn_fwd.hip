@@ -75,14 +75,9 @@ __device__ __forceinline__ int next_entry(const int32_t* __restrict__ list, int 
   return -1;
 }
 
-// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap, no LDS traffic).  The swap
-// hands each lane its own value and its partner's, one in each result; both lanes of a pair
-// combine the same two values, so they get bit-identical results.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
+// Sum of x over lanes l and l ^ 32 (v_permlane32_swap, no LDS traffic).  The swap hands each
+// lane its own value and its partner's, one in each result; both lanes of a pair combine the
+// same two values, so they get bit-identical results (pair_max_num below likewise).
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
@@ -305,11 +300,26 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 // accumulators hold exactly enough, and the rescale of O is skipped.
 constexpr float kLazy = 8.0f;
 
+// Per query row (lane-local, QH rows per lane): the running maximum m of the raw logits is
+// kept as two derived values, with c = scale log2 e:
+//   thr = m + kLazy / c  the raw logit above which m is raised (-inf while no key was seen),
+//   mc  = -m c           the exponent offset of P = 2^(s c + mc) (0 while no key was seen).
 template <int D, int QH>
 struct WaveState {
   f32x16 acc_o[QH][D / 32];
-  float m_run[QH], l_run[QH];
+  float l_run[QH];
+  float thr[QH];
+  float mc[QH];
 };
+
+// max of x over lanes l and l ^ 32 for values that are never NaN (logits, or -inf): a compare
+// and a select, without the quieting fmaxf adds for values it cannot see the origin of.
+__device__ __forceinline__ float pair_max_num(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return a > b ? a : b;
+}
 
 // Operand reads issued ahead of the products that use them: four when a read feeds one
 // product, two when it feeds two (fewer registers held for 64-row waves).
@@ -317,33 +327,36 @@ template <int QH>
 constexpr int kReadAhead = QH == 1 ? 4 : 2;
 
 // S^T for one step: QH accumulators of 32 keys x 32 query rows.  Each K chunk read from LDS
-// (ka_addr[c]: this lane's chunk 2c + hi) feeds QH products.
+// feeds QH products.  ka_addr[c] is this lane's address of chunk 2c + hi in ring slot 0 (kept
+// in registers for the whole kernel) and slotoff the step's slot offset, a compile-time
+// constant in the unrolled step loop that the read instruction takes as its immediate.
 template <int D, int QH>
-__device__ __forceinline__ void step_scores(const uint32_t (&ka_addr)[D / 16],
+__device__ __forceinline__ void step_scores(const uint32_t (&ka_addr)[D / 16], uint32_t slotoff,
                                             const bf16x8 (&qf)[QH][D / 16], f32x16 (&s)[QH]) {
   constexpr int DC = D / 16, PD = kReadAhead<QH>;
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh) s[qh] = (f32x16){};
   bf16x8 ka[PD];
 #pragma unroll
-  for (int i = 0; i < PD; ++i) ka[i] = lds_read<bf16x8>(ka_addr[i]);
+  for (int i = 0; i < PD; ++i) ka[i] = lds_read<bf16x8>(ka_addr[i] + slotoff);
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qh = 0; qh < QH; ++qh)
       s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c % PD], qf[qh][c], s[qh], 0, 0, 0);
-    if (c + PD < DC) ka[c % PD] = lds_read<bf16x8>(ka_addr[c + PD]);
+    if (c + PD < DC) ka[c % PD] = lds_read<bf16x8>(ka_addr[c + PD] + slotoff);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // Online softmax of one step's logits (masked on the diagonal block) and O^T += V^T P^T.
+// va_addr as ka_addr in step_scores (slot 0, loop-invariant), slotoff the step's slot.
 template <int D, int QH>
 __device__ __forceinline__ void step_softmax_pv(f32x16 (&s)[QH], const uint32_t (&va_addr)[2],
-                                                WaveState<D, QH>& st,
+                                                uint32_t slotoff, WaveState<D, QH>& st,
                                                 bool diag, int kbase, int qbase, int hi,
-                                                float scale_log2) {
+                                                float scale_log2, float lazy_raw) {
   constexpr int DT = D / 32;
   // Lane value v of s[qh] is key kbase + 8 (v >> 2) + 4 hi + (v & 3) of the tile, query row
   // qbase + 32 qh (+ lane % 32).
@@ -356,34 +369,42 @@ __device__ __forceinline__ void step_softmax_pv(f32x16 (&s)[QH], const uint32_t 
         if (kloc > qbase + 32 * qh) s[qh][v] = -INFINITY;
       }
   }
-  float alpha[QH];
+  // The row maximum is raised only when a logit passes thr (lazy rescaling, rare once the
+  // first blocks are in); the common path is the maximum, one compare and one vote.
+  float mloc[QH];
   bool any_raise = false;
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh) {
-    float mloc = -INFINITY;
+    float mx = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[qh][v]);
-    mloc = pair_max(mloc);
-    const float m = st.m_run[qh];
-    const bool raise = mloc > m && (m == -INFINITY || (mloc - m) * scale_log2 > kLazy);
-    const float m_new = raise ? mloc : m;
-    alpha[qh] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m - m_new) * scale_log2);
-    st.m_run[qh] = m_new;
-    any_raise |= raise;
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[qh][v]);
+    mloc[qh] = pair_max_num(mx);
+    any_raise |= mloc[qh] > st.thr[qh];
   }
   if (__any(any_raise)) {
 #pragma unroll
     for (int qh = 0; qh < QH; ++qh) {
-      st.l_run[qh] *= alpha[qh];
+      const bool raise = mloc[qh] > st.thr[qh];
+      const float mc_new = raise ? -mloc[qh] * scale_log2 : st.mc[qh];
+      // O and l scale by 2^((m - m_new) c) = 2^(mc_new - mc); nothing was accumulated yet
+      // while thr is -inf
+      const float alpha = !raise ? 1.0f
+                          : st.thr[qh] == -INFINITY
+                              ? 0.0f
+                              : __builtin_amdgcn_exp2f(mc_new - st.mc[qh]);
+      st.l_run[qh] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) st.acc_o[qh][dt] *= alpha[qh];
+      for (int dt = 0; dt < DT; ++dt) st.acc_o[qh][dt] *= alpha;
+      if (raise) {
+        st.thr[qh] = mloc[qh] + lazy_raw;
+        st.mc[qh] = mc_new;
+      }
     }
   }
   f16x8 pf[QH][2];
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh) {
-    const float m = st.m_run[qh];
-    const float mc = m == -INFINITY ? 0.0f : -m * scale_log2;
+    const float mc = st.mc[qh];
 #pragma unroll
     for (int v = 0; v < 16; ++v)
       pf[qh][v >> 3][v & 7] =
@@ -405,7 +426,7 @@ __device__ __forceinline__ void step_softmax_pv(f32x16 (&s)[QH], const uint32_t 
   constexpr int NP = DT * 2, PD = kReadAhead<QH>;
   auto vload = [&](int i) {
     const int dt = i >> 1, half = i & 1;
-    return lds_read<f16x8>(va_addr[half] + dt * 2048);
+    return lds_read<f16x8>(va_addr[half] + slotoff + dt * 2048);
   };
   f16x8 va[PD];
 #pragma unroll
@@ -720,16 +741,31 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
   for (int qh = 0; qh < QH; ++qh) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.acc_o[qh][dt] = (f32x16){};
-    st.m_run[qh] = -INFINITY;
     st.l_run[qh] = 0.0f;
+    st.thr[qh] = -INFINITY;
+    st.mc[qh] = 0.0f;
   }
+  const float lazy_raw = kLazy / scale_log2;  // kLazy in raw logit units (scale > 0)
 
   // Per-lane LDS read offsets within a slot: K chunk hi of row l32 and V^T chunk hi of row l32.
   // Chunk positions are chunk indices XOR a per-row value (kswz, vswz), so chunk 2c + hi sits
   // at koff ^ 32 c, and V^T chunk 2 + hi at voff ^ 32; slots are 1 KiB aligned, so the same
-  // holds for the LDS addresses.
+  // holds for the LDS addresses.  The addresses in ring slot 0 stay in registers for the whole
+  // kernel; a step adds its slot's offset as the read instruction's immediate.
   const int koff = l32 * 2 * D + 16 * (hi ^ kswz<D>(l32));
   const int voff = l32 * 64 + 16 * (hi ^ vswz(l32));
+  uint32_t ka_addr[DC], va_addr[2];
+  {
+    const uint32_t ring0 = lds_addr(ring);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      ka_addr[c] = ring0 + ((uint32_t)koff ^ (32u * c));
+      asm volatile("" : "+v"(ka_addr[c]));
+    }
+    va_addr[0] = ring0 + C::KSLOT + (uint32_t)voff;
+    va_addr[1] = ring0 + C::KSLOT + ((uint32_t)voff ^ 32u);
+    asm volatile("" : "+v"(va_addr[0]), "+v"(va_addr[1]));
+  }
   // Per-lane source offsets (elements, relative to a step's first key row) of this wave's K
   // regions: region w + NW k, lane i lands at image byte 1024 (w + NW k) + 16 i.
   int kgo[C::KREG / NW];
@@ -776,7 +812,11 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
         const uint32_t sub = a % NSUB;
         const char* kb = kbase + (j * kblk_bytes + sub * kstep_bytes);
         const char* vb = vbase + (j * NSUB + sub) * (uint32_t)C::VSLOT;
-        const uint32_t dst = ring_lds + slot_idx * SLOT + w * 1024;
+        // the slot base is re-derived here rather than kept per slot in scalar registers
+        // across the unrolled loop
+        uint32_t rb = ring_lds;
+        asm volatile("" : "+s"(rb));
+        const uint32_t dst = rb + slot_idx * SLOT + w * 1024;
 #pragma unroll
         for (int k = 0; k < C::KREG / NW; ++k) dma16(kb, kgo[k], dst + NW * k * 1024);
 #pragma unroll
@@ -786,49 +826,43 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
 #pragma unroll
       for (int m = 0; m < C::NR - 1; ++m) issue(m, entry_of(m), m);
       int jn = entry_of(C::NR - 1);  // block of the next group, read one step early
-      uint32_t rs = 0, is = C::NR - 1;  // ring slots read and refilled at step i
 
       // Step i (slot i % NR): wait until group i has landed (groups i+1 .. i+NR-2 may still be
       // in flight), barrier (every wave's part of group i is in, and every wave is done with
       // step i-1, whose slot the new group overwrites), issue group i+NR-1, then compute step i.
-      for (uint32_t i = 0; i <= last; ++i) {
-        wait_vm<(C::NR - 2) * LPW>();
-        barrier_only();
-        issue(i + C::NR - 1, jn, is);
-        jn = entry_of(i + C::NR);
-        const uint32_t slot = ring_lds + rs * SLOT;
-        is = rs;  // step i + 1 refills the slot step i reads
-        rs = rs == C::NR - 1 ? 0 : rs + 1;
-        // All of the step's read addresses up front, so that no read waits for its address; the
-        // empty asm keeps the compiler from re-deriving them next to the reads.
-        uint32_t ka_addr[DC], va_addr[2];
-        const uint32_t ka0 = slot + koff, va0 = slot + C::KSLOT + voff;
+      // The loop is unrolled by NR, so each step's slot (read and refilled) is a compile-time
+      // constant.
+      for (uint32_t i0 = 0; i0 <= last; i0 += C::NR) {
 #pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          ka_addr[c] = ka0 ^ (32u * c);
-          asm volatile("" : "+v"(ka_addr[c]));
+        for (int r = 0; r < C::NR; ++r) {
+          const uint32_t i = i0 + r;
+          if (i > last) break;
+          wait_vm<(C::NR - 2) * LPW>();
+          barrier_only();
+          issue(i + C::NR - 1, jn, (uint32_t)((r + C::NR - 1) % C::NR));
+          jn = entry_of(i + C::NR);
+          const uint32_t slotoff = (uint32_t)(r * SLOT);
+          const int e = (int)(i / NSUB), sub = (int)(i % NSUB);
+          // key offset of the step from the tile's first row, on the diagonal blocks (the
+          // second one starts BLK keys in); -1 elsewhere
+          int kofs;
+          bool diag;
+          if constexpr (KB == 0) {
+            diag = e == diag_e;
+            kofs = sub * kStep;
+          } else {
+            kofs = e == diag_e ? sub * kStep : (e == diag_e2 ? BLK + sub * kStep : -1);
+            diag = kofs >= 0;
+          }
+          // On a diagonal block, a step whose first key lies after this wave's last row is
+          // fully masked for the wave: skip it.
+          if (!diag || kofs < kStep * QH * (wr + 1)) {
+            f32x16 sc[QH];
+            step_scores<D, QH>(ka_addr, slotoff, qf, sc);
+            step_softmax_pv<D, QH>(sc, va_addr, slotoff, st, diag, kofs, qbase, hi, scale_log2,
+                                   lazy_raw);
+          }
         }
-        va_addr[0] = va0;
-        va_addr[1] = va0 ^ 32u;
-        asm volatile("" : "+v"(va_addr[0]), "+v"(va_addr[1]));
-        const int e = (int)(i / NSUB), sub = (int)(i % NSUB);
-        // key offset of the step from the tile's first row, on the diagonal blocks (the
-        // second one starts BLK keys in); -1 elsewhere
-        int kofs;
-        bool diag;
-        if constexpr (KB == 0) {
-          diag = e == diag_e;
-          kofs = sub * kStep;
-        } else {
-          kofs = e == diag_e ? sub * kStep : (e == diag_e2 ? BLK + sub * kStep : -1);
-          diag = kofs >= 0;
-        }
-        // On a diagonal block, a step whose first key lies after this wave's last row is
-        // fully masked for the wave: skip it.
-        if (diag && kofs >= kStep * QH * (wr + 1)) continue;
-        f32x16 sc[QH];
-        step_scores<D, QH>(ka_addr, qf, sc);
-        step_softmax_pv<D, QH>(sc, va_addr, st, diag, kofs, qbase, hi, scale_log2);
       }
       wait_vm<0>();  // dummy refills still in flight must land before the slots are reused
     }
@@ -864,7 +898,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
       }
     if (lse && hi == 0)
       lse[((size_t)b * dm.Hq + h) * dm.N + qrow] =
-          l_tot > 0.0f ? (st.m_run[qh] * scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+          l_tot > 0.0f ? (__log2f(l_tot) - st.mc[qh]) * kLn2 : -INFINITY;
   }
 }
 
