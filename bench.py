@@ -438,10 +438,9 @@ def main():
     score_gbs = score_bytes / (ms_cold * 1e-3) / 1e9
 
     gate = pf.gate.float().mean().item()
-    # causal (tile, block) pairs: tile t has m (t + 1) causal blocks, m = tile / block
-    m = w.tile // w.block
-    density = float(pf.kv_cnt.sum().item()) / (w.batch * w.n_units * m * w.n_tiles *
-                                               (w.n_tiles + 1) / 2)
+    # causal (tile, block) pairs: tile t has (t + 1) T / blk causal blocks, rounded up
+    causal = sum(((t + 1) * w.tile + w.block - 1) // w.block for t in range(w.n_tiles))
+    density = float(pf.kv_cnt.sum().item()) / (w.batch * w.n_units * causal)
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,

@@ -60,8 +60,10 @@ int check_problem(const sa_problem* p, sa::Dims* D) {
     return fail(SA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", p->head_dim);
   if (p->block != 64 && p->block != 128)
     return fail(SA_ERR_UNSUPPORTED, "block %d unsupported (64 or 128)", p->block);
-  if (p->tile != p->block && !(p->tile == 128 && p->block == 64))
-    return fail(SA_ERR_UNSUPPORTED, "tile (%d) must equal block (%d), or be 128 over block 64",
+  if (p->tile != p->block && !(p->tile == 128 && p->block == 64) &&
+      !(p->tile == 64 && p->block == 128))
+    return fail(SA_ERR_UNSUPPORTED,
+                "tile (%d) must equal block (%d), or be 128 over block 64, or 64 over block 128",
                 p->tile, p->block);
   const long long n = p->seqlen / p->block;
   if (n > kMaxTiles)
@@ -81,7 +83,8 @@ int check_problem(const sa_problem* p, sa::Dims* D) {
     D->n = (int)n;
     D->T = p->tile;
     D->nt = p->seqlen / p->tile;
-    D->m = p->tile / p->block;
+    D->m = p->tile >= p->block ? p->tile / p->block : 1;
+    D->tpb = p->tile >= p->block ? 1 : p->block / p->tile;
     D->dtype = p->dtype;
     D->score_mode = p->score_mode;
     D->oam = p->output_aware;
@@ -126,6 +129,7 @@ int check_budget(const sa_budget* b, const sa::Dims& D, sa::BudgetDev* bd) {
     if (w > D.n) w = D.n;
     bd->W = (int)w;
     bd->m = D.m;
+    bd->tpb = D.tpb;
   }
   return SA_OK;
 }

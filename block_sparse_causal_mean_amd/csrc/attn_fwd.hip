@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_v(Dims dm, const uint16_t* 
 template <int D, int QH, int NW, int HPW = 1, int KB = 0>
 struct Cfg {
   static constexpr int ROWS = 32 * QH * NW / HPW;  // query tile rows
-  static constexpr int BLK = KB ? KB : ROWS;       // keys per block (the tile's, or half)
+  static constexpr int BLK = KB ? KB : ROWS;       // keys per block: the tile rows, or half or twice
   static constexpr int WPH = NW / HPW;             // waves per query head
   static constexpr int NSUB = BLK / kStep;     // steps per block
   static constexpr int DC = D / 16;            // 16-coordinate chunks of the S^T products
@@ -505,7 +505,7 @@ __device__ void reorder_shared(const int32_t* __restrict__ list, const int32_t* 
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   int diag = -1, diag2 = -1;
-  const int d0 = dm.m * t;  // the tile's diagonal blocks d0 (and d0 + 1)
+  const int d0 = first_diag(dm.m, dm.tpb, t);  // the tile's diagonal blocks d0 (and d0 + 1)
   for (int i = lane; i < U; i += 64) {
     const int x = (int)(key[i] & 0xffffffu);
     lst[i] = x;
@@ -522,10 +522,10 @@ __device__ void reorder_shared(const int32_t* __restrict__ list, const int32_t* 
 }
 
 // Stages the next segment of a tile's list in LDS and orders it; run by the whole workgroup.
-// Usable entries are the tile's causal blocks (0 <= j < m (t + 1), m = 1 or 2 diagonal blocks
-// per tile) before the first negative entry; at most LCAP of them per segment (wave 0
-// compacts, the workgroup waits).  seg_info receives: usable entries, position of the first
-// diagonal block m t (-1 if absent), the list position the next segment starts at, whether
+// Usable entries are the tile's causal blocks (0 <= j < d0 + m, d0 = first_diag(t), m = 1 or 2
+// diagonal blocks per tile) before the first negative entry; at most LCAP of them per segment
+// (wave 0 compacts, the workgroup waits).  seg_info receives: usable entries, position of the
+// first diagonal block d0 (-1 if absent), the list position the next segment starts at, whether
 // this segment ends the list, and the position of the second diagonal block m t + 1.
 //
 // Single-segment lists are then ordered so that blocks listed by more of the kv head's query
@@ -539,7 +539,7 @@ __device__ __forceinline__ void stage_segment(const int32_t* __restrict__ list,
                                               int seg_start, int w, int lane, int* lst,
                                               int* seg_info, int* scratch, int scratch_ints) {
   // the tile's diagonal blocks: d0 (and d0 + 1 for tiles of two blocks); causal ones < dend
-  const int d0 = dm.m * t, dend = d0 + dm.m;
+  const int d0 = first_diag(dm.m, dm.tpb, t), dend = d0 + dm.m;
   if (w == 0) {
     int u = 0, base = seg_start, diag = -1, diag2 = -1, next = cnt, done = 1;
     while (base < cnt) {
@@ -686,6 +686,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
   using C = Cfg<D, QH, NW, HPW, KB>;
   static_assert(HPW == 1 || !VS, "vertical-slash lists are per query head");
   static_assert(KB == 0 || !VS, "vertical-slash lists need tile = block");
+  static_assert(KB == 0 || KB == C::ROWS / 2 || KB == 2 * C::ROWS,
+                "key blocks of half or twice the tile");
   constexpr int BLK = C::BLK, ROWS = C::ROWS, NSUB = C::NSUB, DC = C::DC, DT = C::DT;
   constexpr int LPW = C::LPW;
   // Ring of NR slots, each a K step image followed by a V^T step image.
@@ -716,6 +718,9 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
   const int32_t* list = VS ? nullptr : kv_idx + bht * W;
   const int cnt = VS ? 0 : max(0, min(kv_cnt[bht], W));
   const int qbase = wr * 32 * QH + l32;  // this lane's first query row within the tile
+  // tiles smaller than the key block: the tile's first row is rowoff keys into its diagonal
+  // block
+  const int rowoff = KB > ROWS ? (t % dm.tpb) * ROWS : 0;
   const int rstride = dm.Hkv * D;
   const uint16_t* Kg = K + ((size_t)b * dm.N * dm.Hkv + g) * D;
   const uint16_t* Vpg = Vp + ((size_t)b * dm.Hkv + g) * (size_t)dm.N * D;
@@ -850,9 +855,13 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
           if constexpr (KB == 0) {
             diag = e == diag_e;
             kofs = sub * kStep;
-          } else {
+          } else if constexpr (KB < ROWS) {
             kofs = e == diag_e ? sub * kStep : (e == diag_e2 ? BLK + sub * kStep : -1);
             diag = kofs >= 0;
+          } else {  // the tile's rows lie inside its diagonal block, rowoff keys in: steps
+                    // wholly before them need no mask
+            kofs = sub * kStep - rowoff;
+            diag = e == diag_e && kofs > -kStep;
           }
           // On a diagonal block, a step whose first key lies after this wave's last row is
           // fully masked for the wave: skip it.
@@ -923,7 +932,7 @@ __global__ __launch_bounds__(TR) void attn_f32(Dims dm, const float* __restrict_
   const int32_t* list = kv_idx + bht * W;
   const int cnt = min(kv_cnt[bht], W);
   const int qrow = t * TR + threadIdx.x;
-  const int jmax = dm.m * t + dm.m - 1;  // the tile's last causal block
+  const int jmax = first_diag(dm.m, dm.tpb, t) + dm.m - 1;  // the tile's last causal block
   const int rstride = dm.Hkv * D;
 
   float q[D], o[D];
@@ -1023,6 +1032,12 @@ hipError_t launch_bf16_shape(const Dims& dm, const void* Q, const void* K, const
                              const int32_t* kv_cnt, int W, const VsIndex& vs, float scale,
                              const void* ws, void* O, int out_dtype, float* lse, hipStream_t s) {
   if constexpr (!VS) {
+    // 64-row tiles inside 128-key blocks: two waves per tile, four steps per block.
+    if (dm.tpb == 2)
+      return dm.d == 64 ? launch_bf16<64, 1, 2, false, 1, 128>(dm, Q, K, kv_idx, kv_cnt, W, vs,
+                                                               scale, ws, O, out_dtype, lse, s)
+                        : launch_bf16<128, 1, 2, false, 1, 128>(dm, Q, K, kv_idx, kv_cnt, W, vs,
+                                                                scale, ws, O, out_dtype, lse, s);
     // 128-row tiles over 64-key blocks: four waves per tile, two steps per block.
     if (dm.m == 2)
       return dm.d == 64 ? launch_bf16<64, 1, 4, false, 1, 64>(dm, Q, K, kv_idx, kv_cnt, W, vs,
@@ -1072,6 +1087,11 @@ hipError_t launch_forward(const Dims& dm, const void* Q, const void* K, const vo
     if (e != hipSuccess) return e;
     return launch_forward_prepared(dm, Q, K, ws, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s);
   }
+  if (dm.tpb == 2)  // 64-row tiles inside 128-key blocks
+    return dm.d == 64
+               ? launch_f32<64, 64, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)
+               : launch_f32<128, 64, 128>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse,
+                                          s);
   if (dm.m == 2)  // 128-row tiles over 64-key blocks
     return dm.d == 64
                ? launch_f32<64, 128, 64>(dm, Q, K, V, kv_idx, kv_cnt, W, scale, O, out_dtype, lse, s)

@@ -49,7 +49,8 @@ __device__ __forceinline__ float order_key_inv(uint32_t k) {
 
 struct Dims {
   int B, N, Hq, Hkv, G, d, blk, n;  // n = N / blk key blocks
-  int T, nt, m;  // query tile rows, tiles N / T, diagonal blocks per tile T / blk (1 or 2)
+  int T, nt, m;  // query tile rows, tiles N / T, diagonal blocks per tile (T / blk, or 1)
+  int tpb;       // query tiles per key block (blk / T when a block holds several tiles, or 1)
   int gs, Hu;  // query heads per selection unit (1, or G when lists are per kv head); units
   int dtype, score_mode, oam;     // oam: SA_OAM_OFF, SA_OAM_PRODUCT or SA_OAM_ADDITIVE
   float oam_beta, oam_scale;      // additive form: beta and (float)(1 / sqrt(d))
@@ -59,10 +60,15 @@ struct BudgetDev {
   int k_max, k_min, kind, n_sink, gate_mode;
   float tau_fixed;
   double rho, q;
-  int R;  // ranked entries stored per (b, unit, t)
-  int W;  // entries per padded list
-  int m;  // diagonal blocks per tile: tile t's are m t .. m t + m - 1, its free ones < m t
+  int R;    // ranked entries stored per (b, unit, t)
+  int W;    // entries per padded list
+  int m;    // diagonal blocks per tile: tile t's are first_diag(t) .. + m - 1, its free ones
+  int tpb;  // before first_diag(t); tiles per block (see Dims)
 };
+
+// First diagonal block of query tile t, the block holding the tile's first row: t T / blk,
+// i.e. m t for tiles of m blocks, t / tpb for tpb tiles per block.
+__host__ __device__ __forceinline__ int first_diag(int m, int tpb, int t) { return m * t / tpb; }
 
 // Layout of the block-summary buffer.  The public part (documented in the header) comes
 // first: the fp32 planes [B, n, Hkv, d] (kmean, or kmin then kmax) and, when output-aware,

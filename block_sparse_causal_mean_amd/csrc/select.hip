@@ -50,9 +50,9 @@ __device__ __forceinline__ int budget_at(const BudgetDev& bd, int t, int n) {
   const long long k = (long long)bd.k_max * (n - t) / n;
   return k > bd.k_min ? (int)k : bd.k_min;
 }
-// Free blocks of tile t: the blocks before its diagonal ones (m t), minus the sinks.
+// Free blocks of tile t: the blocks before its diagonal ones, minus the sinks.
 __device__ __forceinline__ int n_free(const BudgetDev& bd, int t) {
-  const int d0 = bd.m * t;
+  const int d0 = first_diag(bd.m, bd.tpb, t);
   return d0 - (d0 < bd.n_sink ? d0 : bd.n_sink);
 }
 __device__ __forceinline__ int expanded(const BudgetDev& bd, int k) {
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
     if (threadIdx.x == 0) sigma[bht] = 1.0f;
     return;
   }
-  const int d0 = bd.m * t;                          // first diagonal block
+  const int d0 = first_diag(bd.m, bd.tpb, t);      // first diagonal block
   const int j0 = d0 < bd.n_sink ? d0 : bd.n_sink;  // first free block
   const int P = next_pow2(nf);
   for (int f = threadIdx.x; f < P; f += NT)
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     if (threadIdx.x == 0) sigma[bht] = 1.0f;
     return;
   }
-  const int d0 = bd.m * t;  // first diagonal block: the free blocks are [j0, d0)
+  const int d0 = first_diag(bd.m, bd.tpb, t);  // first diagonal block: free ones [j0, d0)
   const int j0 = d0 < bd.n_sink ? d0 : bd.n_sink;
   int P = 1;
   while (P < nf) P <<= 1;
@@ -676,7 +676,7 @@ __global__ __launch_bounds__(64 * kEmitWaves) void emit_kernel(Dims dm, BudgetDe
   const int kt = budget_at(bd, t, n);
   const int nf = n_free(bd, t);
   const bool elig = live && nf > kt;
-  const int d0 = bd.m * t, dend = d0 + bd.m;  // the tile's diagonal blocks [d0, dend)
+  const int d0 = first_diag(bd.m, bd.tpb, t), dend = d0 + bd.m;  // diagonal blocks [d0, dend)
   int keep = 0;
   if (elig) {
     const bool tripped = gate[(size_t)b * n + t] != 0;

@@ -167,6 +167,11 @@ for _base in ("llama8b_32k", "stem_32k"):
     WORKLOADS[_base + "_t128"] = dataclasses.replace(
         WORKLOADS[_base], name=_base + "_t128", q_tile=128)
 
+# Query tiles of 64 rows inside key blocks of 128 (the other direction of tile != block: two
+# tiles share a diagonal block, forced in both).  The 128K inputs, selected per 64-row tile.
+WORKLOADS["prefill_128k_t64"] = dataclasses.replace(
+    WORKLOADS["prefill_128k"], name="prefill_128k_t64", q_tile=64)
+
 # Decode with run-time termination (ART page): one new token per sequence and head over a
 # 16K-token cache, 64 sequences (one workgroup per sequence and kv head: 512, two per CU; the
 # sequential traversal needs the second workgroup to keep HBM busy).  The selection fields are

@@ -191,6 +191,11 @@ def select_tile(cfg: OracleCfg, Q, summ: dict, b: int, t: int) -> dict:
             "cnts": cnts}
 
 
+def diag_end(cfg: OracleCfg, t: int) -> int:
+    """One past tile t's last causal block (its diagonal blocks end there)."""
+    return int(_load().oracle_diag_end(ctypes.byref(cfg), t))
+
+
 def tile_scores(cfg: OracleCfg, Q, summ: dict, b: int, h: int, t: int) -> np.ndarray:
     """Scores of tile t's causal blocks (NaN for its forced ones), for selection unit h."""
     lib = _load()

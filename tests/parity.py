@@ -87,30 +87,31 @@ def check_structure(w, kv_idx, kv_cnt, gate, sigma, sigma_bar, tau):
     """Properties every selection output has at any size (vectorised over all tiles)."""
     B, Hq, n, W = kv_idx.shape
     assert n == w.n_tiles
-    m = w.tile // w.block  # diagonal blocks per tile: m t .. m t + m - 1
+    m = max(1, w.tile // w.block)  # diagonal blocks per tile: d0 .. d0 + m - 1
     t = np.arange(n)
+    d0 = t * w.tile // w.block     # the tile's first diagonal block
     cnt = kv_cnt
     assert np.all(cnt >= 1) and np.all(cnt <= W)
     col = np.arange(W)
     valid = col[None, None, None, :] < cnt[..., None]
     assert np.all(kv_idx[~valid] == -1)
     last = np.take_along_axis(kv_idx, (cnt - 1)[..., None], axis=-1)[..., 0]
-    assert np.all(last == (m * t + m - 1)[None, None, :]), "diagonal block missing or not last"
+    assert np.all(last == (d0 + m - 1)[None, None, :]), "diagonal block missing or not last"
     if m > 1:
         prev = np.take_along_axis(kv_idx, (cnt - 2)[..., None], axis=-1)[..., 0]
-        assert np.all(prev == (m * t + m - 2)[None, None, :]), "first diagonal block missing"
+        assert np.all(prev == (d0 + m - 2)[None, None, :]), "first diagonal block missing"
     d = np.diff(kv_idx, axis=-1)
     vd = valid[..., 1:]
     assert np.all(d[vd] > 0), "lists not strictly ascending"
     assert np.all(kv_idx[valid] >= 0)
     for s in range(min(w.n_sink, w.n_blocks)):
         has = (kv_idx == s).any(-1)
-        assert np.all(has[:, :, s // m:]), "sink missing"
+        assert np.all(has[:, :, d0 + m - 1 >= s]), "sink missing"
     assert np.all((sigma >= 0) & (sigma <= 1))
     # gate = eligible and sigma_bar <= tau, tau the ceil(q M)-th smallest eligible sigma_bar
     cfg = oracle.make_cfg(w)
     kt = np.array([oracle.budget(cfg, int(x)) for x in t])
-    nfree = m * t - np.minimum(m * t, w.n_sink)
+    nfree = d0 - np.minimum(d0, w.n_sink)
     elig = nfree > kt
     for b in range(B):
         sb = sigma_bar[b][elig]
@@ -123,5 +124,5 @@ def check_structure(w, kv_idx, kv_cnt, gate, sigma, sigma_bar, tau):
         np.testing.assert_array_equal(gate[b], (elig & (sigma_bar[b] <= tau[b])).astype(np.uint8))
         keep = np.where(gate[b] == 1, np.floor(w.rho * kt).astype(int), kt)
         keep = np.minimum(keep, nfree)
-        forced = m + np.minimum(m * t, w.n_sink)
+        forced = m + np.minimum(d0, w.n_sink)
         np.testing.assert_array_equal(cnt[b], np.broadcast_to(forced + keep, cnt[b].shape))

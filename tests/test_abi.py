@@ -98,7 +98,8 @@ BAD_PROBLEMS = [
     (dict(head_dim=96), api.SA_ERR_UNSUPPORTED),
     (dict(block=32, tile=32), api.SA_ERR_UNSUPPORTED),
     (dict(tile=256), api.SA_ERR_UNSUPPORTED),
-    (dict(block=128, tile=64), api.SA_ERR_UNSUPPORTED),
+    (dict(block=128, tile=32), api.SA_ERR_UNSUPPORTED),
+    (dict(block=64, tile=32), api.SA_ERR_UNSUPPORTED),
     (dict(seqlen=64 * 511, tile=128), api.SA_ERR_INVALID),
     (dict(seqlen=1000), api.SA_ERR_INVALID),
     (dict(n_q_heads=30), api.SA_ERR_INVALID),
@@ -336,3 +337,24 @@ def test_select_noalloc_validation(lib):
     for name in wl.WORKLOAD_ORDER:
         w = wl.WORKLOADS[name]
         assert api.select_workspace_bytes(api.problem(w), api.budget(w)) <= api.NOALLOC_SCRATCH_BYTES
+
+
+def test_tiles_inside_blocks_sizes(lib):
+    """64-row tiles inside 128-key blocks: one diagonal block per tile (W = 1 + n_sink +
+    floor(rho k_max)), twice the tiles of the 128-row case, the same summaries."""
+    w = wl.WORKLOADS["prefill_128k_t64"]
+    p, b = api.problem(w), api.budget(w)
+    p128 = api.problem(wl.WORKLOADS["prefill_128k"])
+    assert api.index_width(p, b) == 1 + 0 + 128 == w.index_width()
+    assert api.summary_bytes(p) == api.summary_bytes(p128)
+    assert api.select_workspace_bytes(p, b) > api.select_workspace_bytes(p128, b)
+
+
+def test_forward_rejects_non_positive_scale(lib):
+    p = _ok_problem()
+    big = 1 << 40
+    for scale in (0.0, -0.1):
+        assert lib.sparse_attn_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 65, scale,
+                                       FAKE, big, FAKE, api.SA_BF16, None,
+                                       None) == api.SA_ERR_INVALID
+        assert "> 0" in api.last_error()

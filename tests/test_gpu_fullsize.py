@@ -26,7 +26,8 @@ from parity import TOL_BF16, assert_selection_equal, bits, check_structure, out_
 pytestmark = pytest.mark.gpu
 
 FULL = ["llama8b_32k", "prefill_128k", "quest_64k", "stem_32k", "stem_additive_32k",
-        "llama8b_32k_kvshared", "stem_32k_kvshared", "llama8b_32k_t128", "stem_32k_t128"]
+        "llama8b_32k_kvshared", "stem_32k_kvshared", "llama8b_32k_t128", "stem_32k_t128",
+        "prefill_128k_t64"]
 
 
 def _rows(w, rng):

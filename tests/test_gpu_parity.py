@@ -74,6 +74,20 @@ SMALL = {
     "f32_t128_d128": WL["tiny_ref"].resized(seqlen=768, n_q_heads=2, n_kv_heads=2,
                                             head_dim=128, k_max=2, k_min=2, q_tile=128,
                                             score_mode=wl.KMINMAX),
+    # query tiles of 64 rows inside key blocks of 128 (two tiles per diagonal block)
+    "t64_blk128_planted": WL["prefill_128k_t64"].resized(seqlen=4096, k_max=6, k_min=6),
+    "t64_blk128_d64_sinks_oam": WL["stem_32k"].resized(
+        batch=2, seqlen=2560, n_q_heads=4, n_kv_heads=2, head_dim=64, block=128, q_tile=64,
+        k_max=8, k_min=2, n_sink=3),
+    "t64_blk128_quest_kvshared": WL["quest_64k"].resized(
+        seqlen=2048, n_q_heads=8, n_kv_heads=2, block=128, q_tile=64, k_max=4, k_min=4,
+        select_unit=wl.SELECT_PER_KV_HEAD),
+    "f32_t64_blk128": WL["tiny_ref"].resized(seqlen=1024, n_q_heads=2, n_kv_heads=1,
+                                             block=128, q_tile=64, k_max=2, k_min=2),
+    "f32_t64_blk128_d128": WL["tiny_ref"].resized(seqlen=768, n_q_heads=2, n_kv_heads=2,
+                                                  head_dim=128, block=128, q_tile=64, k_max=2,
+                                                  k_min=2, score_mode=wl.KMINMAX,
+                                                  output_aware=1),
 }
 
 MAX_ORACLE_ROWS = 6000
@@ -188,6 +202,17 @@ EDGE = {
     "tied_rows_kvshared": WL["prefill_128k_kvshared"].resized(seqlen=2048, n_q_heads=4,
                                                               n_kv_heads=2, k_max=4, k_min=4,
                                                               planted=False),
+    # 64-row tiles inside 128-key blocks
+    "t64_single_block": WL["prefill_128k_t64"].resized(seqlen=128, k_max=2, k_min=2),
+    "t64_dense_limit": WL["prefill_128k_t64"].resized(seqlen=1024, n_q_heads=4, n_kv_heads=2,
+                                                      k_max=64, k_min=64),
+    "t64_q1_all_trip": WL["prefill_128k_t64"].resized(seqlen=2048, n_q_heads=4, n_kv_heads=1,
+                                                      k_max=4, k_min=4, q=1.0),
+    "t64_fixed_gate_odd_sinks": WL["prefill_128k_t64"].resized(
+        seqlen=1536, n_q_heads=4, n_kv_heads=2, n_sink=3, k_max=4, k_min=2,
+        gate_mode=wl.GATE_FIXED, tau_fixed=0.3),
+    "tied_blocks_t64": WL["prefill_128k_t64"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=2,
+                                                      k_max=4, k_min=4),
     # all keys zero: every score is +0, sigma = 0 everywhere, ranking falls to the index
     "zero_keys_kmean_oam": WL["stem_32k"].resized(batch=1, seqlen=1536, n_q_heads=4,
                                                   n_kv_heads=2, k_max=4, k_min=2),
@@ -250,14 +275,15 @@ def test_edge_cases(name):
     check_structure(w, g["kv_idx"], g["kv_cnt"], g["gate"], g["sigma"], g["sigma_bar"],
                     g["tau"])
     compare_outputs(w, g, inp, api.SA_F32, sample_rows(w, np.random.default_rng(1)))
-    m = w.tile // w.block  # diagonal blocks per tile
+    m = max(1, w.tile // w.block)  # diagonal blocks per tile
     t = np.arange(w.n_tiles)
+    d0 = t * w.tile // w.block       # first diagonal block
     if name.endswith("dense_limit"):  # every causal block of every tile
-        assert np.all(g["kv_cnt"] == m * (t + 1))
+        assert np.all(g["kv_cnt"] == d0 + m)
     if name == "q0_no_trips" or name == "gate_off":
         assert g["gate"].sum() == 0
     if name.endswith("q1_all_trip"):  # tau = the largest eligible sigma_bar: every one trips
-        nfree = m * t - np.minimum(m * t, w.n_sink)
+        nfree = d0 - np.minimum(d0, w.n_sink)
         assert g["gate"].sum() == int((nfree > w.k_max).sum()) > 0
 
 
@@ -493,3 +519,30 @@ def test_calibrated_tau_over_several_sequences():
     assert out.item() == oracle.calibrated_tau(t.cpu().numpy())
     api.calibrate_tau(torch.full((2,), -float("inf"), device="cuda"), out)
     assert out.item() == -float("inf")
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_tiles_in_blocks_golden_on_gpu(dtype):
+    """The hand-worked 64-row tiles inside 128-key blocks (tests/golden/tiles_in_blocks.json)
+    through the C ABI: sigma, tau, gate and lists equal the golden values bit for bit."""
+    import golden_inputs as gi
+    g = gi.load("tiles_in_blocks.json")
+    w = WL["tiny_ref"].resized(seqlen=1024, n_q_heads=1, n_kv_heads=1, head_dim=64,
+                               block=g["block"], q_tile=g["tile"], k_max=g["k"], k_min=g["k"],
+                               rho=g["rho"], q=g["q"], dtype=dtype)
+    Q = np.zeros((1, 1024, 1, 64), np.float32)
+    Q[0, :, 0, 0] = 1.0
+    K = np.zeros((1, 1024, 1, 64), np.float32)
+    for j in range(8):
+        K[0, j * 128:(j + 1) * 128, 0, 0] = g["c"][j]
+    V = np.random.default_rng(4).standard_normal((1, 1024, 1, 64)).astype(np.float32)
+    tdt = torch.float32 if dtype == wl.F32 else torch.bfloat16
+    inp = {k: torch.from_numpy(v).to(tdt) for k, v in (("Q", Q), ("K", K), ("V", V))}
+    out = run_gpu(w, inp, out_dtype=api.SA_F32)
+    want = np.array([gi.f32(x) for x in g["sigma"]], np.float32)
+    np.testing.assert_array_equal(out["sigma"][0, 0].view(np.uint32), want.view(np.uint32))
+    assert out["tau"][0] == np.float32(g["tau"])
+    np.testing.assert_array_equal(out["gate"][0], g["gate"])
+    np.testing.assert_array_equal(out["kv_idx"][0, 0], g["kv_idx"])
+    np.testing.assert_array_equal(out["kv_cnt"][0, 0], g["kv_cnt"])
+    compare_outputs(w, out, inp, api.SA_F32, None)

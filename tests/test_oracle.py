@@ -967,3 +967,111 @@ def test_calibrated_tau_is_mean_of_finite_thresholds():
     # fp32 sum in index order: 1 + 2^-24 rounds to 1 (tie to even) before 2^-24 is added again
     x = float(2.0 ** -24)
     assert oracle.calibrated_tau([1.0, x, x]) == np.float32(1.0) / np.float32(3.0)
+
+
+# ------------------------------------------------ query tiles inside larger key blocks
+
+def _tiles_in_blocks_inputs(g, dtype=wl.F32):
+    w = _small(seqlen=1024, n_q_heads=1, n_kv_heads=1, head_dim=64, block=g["block"],
+               q_tile=g["tile"], k_max=g["k"], k_min=g["k"], rho=g["rho"], q=g["q"], dtype=dtype)
+    Q = np.zeros((1, 1024, 1, 64), np.float32)
+    Q[0, :, 0, 0] = 1.0
+    K = np.zeros((1, 1024, 1, 64), np.float32)
+    for j in range(8):
+        K[0, j * 128:(j + 1) * 128, 0, 0] = g["c"][j]
+    tdt = torch.float32 if dtype == wl.F32 else torch.bfloat16
+    return w, torch.from_numpy(Q).to(tdt), torch.from_numpy(K).to(tdt)
+
+
+def test_tiles_in_blocks_golden():
+    g = json.load(open(os.path.join(GOLDEN, "tiles_in_blocks.json")))
+    w, Q, K = _tiles_in_blocks_inputs(g)
+    cfg = oracle.make_cfg(w)
+    assert cfg.width == 5 == w.index_width() and oracle.n_tiles(cfg) == 16 == w.n_tiles
+    s = oracle.pool(cfg, K, K)
+    out = oracle.select(cfg, Q, s)
+    want = np.array([_f32(x) for x in g["sigma"]], np.float32)
+    np.testing.assert_array_equal(out["sigma"][0, 0].view(np.uint32), want.view(np.uint32))
+    np.testing.assert_array_equal(out["sigma_bar"][0].view(np.uint32), want.view(np.uint32))
+    assert out["tau"][0] == np.float32(g["tau"])
+    np.testing.assert_array_equal(out["gate"][0], g["gate"])
+    np.testing.assert_array_equal(out["kv_idx"][0, 0], g["kv_idx"])
+    np.testing.assert_array_equal(out["kv_cnt"][0, 0], g["kv_cnt"])
+    # tile 13's scores: blocks 0..5 free, its diagonal block 6 forced (NaN), nothing after
+    S = oracle.tile_scores(cfg, Q, s, 0, 0, 13)
+    assert len(S) == 7 and np.isnan(S[6]) and S[:6].tolist() == g["c"][:6]
+    assert [oracle.diag_end(cfg, t) for t in (0, 1, 2, 15)] == [1, 1, 2, 8]
+
+
+@pytest.mark.parametrize("seed,kw", [
+    (930, dict(n_q_heads=2, n_kv_heads=1, q=0.3)),
+    (940, dict(n_q_heads=4, n_kv_heads=2, n_sink=3, output_aware=1, score_mode=wl.KMINMAX,
+               budget_kind=wl.BUDGET_LINEAR_DECAY, k_min=1, q=0.5, dtype=wl.BF16)),
+    (950, dict(n_q_heads=4, n_kv_heads=2, q=0.4, select_unit=wl.SELECT_PER_KV_HEAD)),
+])
+def test_tiles_in_blocks_is_brute_force(seed, kw):
+    """Tiles of 32 rows inside blocks of 64 keys: the block holding the tile's rows and the
+    sinks are forced, the free blocks are the earlier ones, each tile score is the maximum of
+    the pinned row-score chain over the tile's rows (of every head of the unit), the kept free
+    blocks are the top of a stable sort, and sigma follows from the sorted scores."""
+    base = dict(seqlen=640, head_dim=16, block=64, q_tile=32, k_max=3, batch=2)
+    base.update(kw)
+    base.setdefault("k_min", 3)
+    w, cfg, Q, K, V, s = _random_case(seed, **base)
+    out = oracle.select(cfg, Q, s)
+    U, nt = oracle.units(cfg), w.n_tiles
+    gs = w.n_q_heads // U
+    assert out["kv_idx"].shape == (2, U, nt, w.index_width())
+    for b in range(2):
+        for u in range(U):
+            for t in range(nt):
+                d0 = t * 32 // 64
+                forced = {d0} | set(range(min(w.n_sink, d0)))
+                free = [j for j in range(d0 + 1) if j not in forced]
+                S = {j: max(oracle.row_score(cfg, Q, s, b, r, h, j)
+                            for h in range(u * gs, (u + 1) * gs)
+                            for r in range(32 * t, 32 * t + 32)) + np.float32(0)
+                     for j in free}
+                if w.output_aware:
+                    g = u * gs * w.n_kv_heads // w.n_q_heads
+                    S = {j: np.float32(S[j] * s["vn"][b, j, g]) + np.float32(0) for j in S}
+                order = sorted(free, key=lambda j: (-S[j], j))
+                cnt = out["kv_cnt"][b, u, t]
+                keep = cnt - len(forced)
+                assert sorted(order[:keep] + sorted(forced)) == out["kv_idx"][b, u, t][:cnt].tolist()
+                kt = oracle.budget(cfg, t)
+                if len(free) > kt:
+                    a0, a1, a2 = S[order[0]], S[order[kt - 1]], S[order[kt]]
+                    want = np.float32(0) if a0 == a2 else np.float32(a1 - a2) / np.float32(a0 - a2)
+                    assert out["sigma"][b, u, t] == want
+                else:
+                    assert out["sigma"][b, u, t] == 1.0 and keep == len(free)
+
+
+def test_tiles_in_blocks_attention_is_masked_dense():
+    """Row i of tile i // T attends exactly to the keys p <= i of its tile's listed blocks
+    (the diagonal block only up to the row); every block listed gives dense causal attention."""
+    w, cfg, Q, K, V, s = _random_case(960, seqlen=512, head_dim=16, block=64, q_tile=32,
+                                      k_max=2, k_min=2, n_q_heads=2, n_kv_heads=1, q=0.5)
+    sel = oracle.select(cfg, Q, s)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    O, _ = oracle.forward(cfg, Q, K, V, sel["kv_idx"], sel["kv_cnt"], scale)
+    q64, k64, v64 = (x.double().numpy() for x in (Q, K, V))
+    for h in range(2):
+        logits = q64[0, :, h] @ k64[0, :, 0].T * scale
+        mask = np.zeros((512, 512), bool)
+        for i in range(512):
+            lst = sel["kv_idx"][0, h, i // 32][:sel["kv_cnt"][0, h, i // 32]]
+            for j in lst:
+                mask[i, j * 64:(j + 1) * 64] = True
+            mask[i, i + 1:] = False
+        logits[~mask] = -np.inf
+        p = np.exp(logits - logits.max(1, keepdims=True))
+        ref = (p / p.sum(1, keepdims=True)) @ v64[0, :, 0]
+        np.testing.assert_allclose(O[0, :, h], ref, rtol=0, atol=1e-12)
+    dense_cfg = oracle.make_cfg(w, k_max=8, k_min=8)
+    full = oracle.select(dense_cfg, Q, s)
+    assert (full["kv_cnt"][0, 0] == np.arange(16) // 2 + 1).all()
+    Od, _ = oracle.forward(dense_cfg, Q, K, V, full["kv_idx"], full["kv_cnt"], scale)
+    ref, _ = _dense_sdpa(Q, K, V, scale)
+    np.testing.assert_allclose(Od, ref, rtol=0, atol=1e-12)
