@@ -167,6 +167,11 @@ for _base in ("llama8b_32k", "stem_32k"):
     WORKLOADS[_base + "_t128"] = dataclasses.replace(
         WORKLOADS[_base], name=_base + "_t128", q_tile=128)
 
+# The 128K recipe at one million tokens (the VSPrefill page's range reaches 1M): 8192 blocks
+# of 128 keys, the same budget, so each tile keeps under 2% of its causal blocks.
+WORKLOADS["prefill_1m"] = dataclasses.replace(
+    WORKLOADS["prefill_128k"], name="prefill_1m", seqlen=1 << 20)
+
 # Query tiles of 64 rows inside key blocks of 128 (the other direction of tile != block: two
 # tiles share a diagonal block, forced in both).  The 128K inputs, selected per 64-row tile.
 WORKLOADS["prefill_128k_t64"] = dataclasses.replace(

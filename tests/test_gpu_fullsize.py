@@ -100,3 +100,60 @@ def test_full_size_parity(name):
         f"(fp32 out), {err16.max():.3e} (bf16 out)")
     assert np.all(err32 <= TOL_BF16), f"fp32 out: max err {err32.max()}"
     assert np.all(err16 <= out_tol(w, api.SA_BF16, O_ref)), f"bf16 out: max err {err16.max()}"
+
+
+def _sample_tiles(n, gate_row, rng, extra=4):
+    tiles = {0, 1, n // 3, n // 2, n - 1}
+    tripped = np.nonzero(gate_row)[0]
+    if len(tripped):
+        tiles.update(int(x) for x in rng.choice(tripped, size=min(2, len(tripped)), replace=False))
+    tiles.update(int(x) for x in rng.integers(2, n - 1, size=extra))
+    return sorted(tiles)
+
+
+@pytest.mark.timeout(900)
+def test_one_million_tokens_sampled_parity():
+    """The 128K recipe at 2^20 tokens (8192 blocks of 128 keys).  The oracle's whole selection
+    would take tens of minutes here, so: every block summary bit for bit; the structure of
+    every tile's selection (tau from sigma_bar, gate, counts, lists); sampled tiles (first,
+    last, middle, tripped, random) against oracle.select_tile bit for bit, all heads; and
+    sampled output rows against the fp64 oracle."""
+    w = wl.WORKLOADS["prefill_1m"]
+    say("[1m] generating inputs")
+    inp = wl.make_inputs(w)
+    d = {k: v.cuda() for k, v in inp.items()}
+    pf = api.Prefill(w)
+    say("[1m] GPU pipeline")
+    pf.run(d["Q"], d["K"], d["V"])
+    torch.cuda.synchronize()
+    g = {"kv_idx": pf.kv_idx.cpu().numpy(), "kv_cnt": pf.kv_cnt.cpu().numpy(),
+         "sigma": pf.sigma.cpu().numpy(), "sigma_bar": pf.sigma_bar.cpu().numpy(),
+         "gate": pf.gate.cpu().numpy(), "tau": pf.tau.cpu().numpy()}
+    check_structure(w, g["kv_idx"], g["kv_cnt"], g["gate"], g["sigma"], g["sigma_bar"], g["tau"])
+    say(f"[1m] structure ok, {int(g['gate'].sum())} tripped tiles of {w.n_tiles}")
+    cfg = oracle.make_cfg(w)
+    summ = oracle.pool(cfg, inp["K"], inp["V"])
+    plane = w.n_blocks * w.n_kv_heads * w.head_dim
+    np.testing.assert_array_equal(bits(pf.summ[:plane].cpu().numpy()), bits(summ["kA"].reshape(-1)))
+    say("[1m] summaries equal")
+    rng = np.random.default_rng(11)
+    tiles = _sample_tiles(w.n_tiles, g["gate"][0], rng)
+    rows = []
+    for t in tiles:
+        one = oracle.select_tile(cfg, inp["Q"], summ, 0, t)
+        np.testing.assert_array_equal(bits(g["sigma"][0, :, t]), bits(one["sigma"]))
+        assert bits(g["sigma_bar"][0, t]) == bits(one["sigma_bar"])
+        tr = int(g["gate"][0, t])
+        np.testing.assert_array_equal(g["kv_cnt"][0, :, t], one["cnts"][tr])
+        np.testing.assert_array_equal(g["kv_idx"][0, :, t, :], one["lists"][tr][:, :g["kv_idx"].shape[-1]])
+        for h in range(w.n_q_heads):
+            rows.append((0, h, t * w.tile + int(rng.integers(w.tile))))
+        say(f"[1m] tile {t} (tripped {tr}) matches the oracle")
+    rows = np.array(rows, np.int64)
+    O_ref, _ = oracle.forward(cfg, inp["Q"], inp["K"], inp["V"], g["kv_idx"], g["kv_cnt"],
+                              pf.scale, rows=rows)
+    r = torch.as_tensor(rows, device="cuda")
+    O = pf.O[r[:, 0], r[:, 2], r[:, 1]].float().cpu().numpy().astype(np.float64)
+    err = np.abs(O - O_ref)
+    say(f"[1m] {len(rows)} rows, max|O - O_ref| = {err.max():.3e}")
+    assert np.all(err <= out_tol(w, api.SA_BF16, O_ref))
