@@ -73,8 +73,10 @@ __host__ __device__ __forceinline__ int first_diag(int m, int tpb, int t) { retu
 // Layout of the block-summary buffer.  The public part (documented in the header) comes
 // first: the fp32 planes [B, n, Hkv, d] (kmean, or kmin then kmax) and, when output-aware,
 // vnorm [B, n, Hkv].  The library-private part follows: knorm [B, n, Hkv] (fp32 L2 norm of
-// each block's scoring vector), then two copies of the planes in "chunk-major" order, grouped
-// by 32-block chunks per (batch, kv head), for the selection kernel:
+// each block's scoring vector), dnorm [B, n, Hkv] (L2 norm of the scoring vector's bf16
+// rounding residual x - bf16(x): per coordinate the larger of the two planes' for the bound),
+// then two copies of the planes in "chunk-major" order, grouped by 32-block chunks per (batch,
+// kv head), for the selection kernel:
 //   bfc  each plane rounded to bf16 (round to nearest even), the matrix-core prefilter's B
 //        operands: per chunk [plane][d/16 steps][64 lanes][8], lane (i, u) holding
 //        coordinates 16 step + 8u .. +7 of block 32 chunk + i, so every operand load of a
@@ -87,6 +89,7 @@ struct SummaryLayout {
   int nplanes;       // 1 (kmean) or 2 (kmin, kmax)
   size_t vn;         // float offset of vnorm (valid when output-aware)
   size_t kn;         // float offset of knorm
+  size_t dn;         // float offset of dnorm
   int ncb;           // 32-block chunks per (batch, kv head)
   size_t bfc_byte;   // byte offset of the bf16 chunk-major copy
   size_t bfc_chunk;  // bf16 elements per (batch, kv head, chunk)
@@ -101,11 +104,12 @@ inline SummaryLayout summary_layout(const Dims& D) {
   const size_t blocks = (size_t)D.B * D.n * D.Hkv;
   L.vn = L.plane * L.nplanes;
   L.kn = L.vn + (D.oam ? blocks : 0);
+  L.dn = L.kn + blocks;
   L.ncb = (D.n + 31) / 32;
   const size_t chunks = (size_t)D.B * D.Hkv * L.ncb;
   L.bfc_chunk = (size_t)L.nplanes * D.d * 32;  // [plane][d/16][64][8]
   L.xc_chunk = (size_t)L.nplanes * D.d * 32;       // [plane][d/8][32][8]
-  L.bfc_byte = ((L.kn + blocks) * sizeof(float) + 255) & ~(size_t)255;
+  L.bfc_byte = ((L.dn + blocks) * sizeof(float) + 255) & ~(size_t)255;
   L.xc_byte = (L.bfc_byte + chunks * L.bfc_chunk * sizeof(uint16_t) + 255) & ~(size_t)255;
   L.bytes = L.xc_byte + chunks * L.xc_chunk * sizeof(float);
   return L;

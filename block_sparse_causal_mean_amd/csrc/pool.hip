@@ -56,15 +56,15 @@ struct Vec16<float> {
 // first copied into LDS with every 16-byte load issued at once (8 per thread for bf16 at
 // BLK = HD = 128), so the memory system sees the whole tile in flight; then thread c sums
 // coordinate c over the rows in order from LDS (the fixed reduction order), writes the
-// summary, its bf16 rounding, and the block's L2 norm (a workgroup reduction in any order: it
-// only scales the prefilter's error bound).
+// summary, its bf16 rounding, the block's L2 norm and the L2 norm of the bf16 rounding
+// residual (workgroup reductions in any order: they only scale the prefilter's error bound).
 template <typename T, int MODE, int BLK, int HD>
 __global__ __launch_bounds__(kPoolThreads) void pool_keys(const T* __restrict__ K,
                                                           float* __restrict__ summ,
                                                           uint16_t* __restrict__ bfc,
                                                           float* __restrict__ xc, int N, int n,
                                                           int Hkv, size_t plane, size_t kn_off,
-                                                          int ncb) {
+                                                          size_t dn_off, int ncb) {
   constexpr int E = Vec16<T>::N;   // elements per 16-byte chunk
   constexpr int CPR = HD / E;      // chunks per row
   constexpr int NCH = BLK * CPR;   // chunks in the tile
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_keys(const T* __restrict__ 
   static_assert(NCH % kPoolThreads == 0, "tile chunks must split evenly over the threads");
   static_assert(HD <= kPoolThreads, "one thread per coordinate");
   __shared__ uint4 tile[NCH];
-  __shared__ float red[kPoolThreads / 64];
+  __shared__ float red[2][kPoolThreads / 64];
   const int id = (int)blockIdx.x;  // (b * n + j) * Hkv + g
   const int g = id % Hkv;
   const int bj = id / Hkv;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_keys(const T* __restrict__ 
     for (int k = 0; k < NCH / kPoolThreads; ++k) tile[threadIdx.x + k * kPoolThreads] = v[k];
   }
   __syncthreads();
-  float ss = 0.0f;
+  float ss = 0.0f, dd = 0.0f;  // this coordinate's |x|^2 and bf16 rounding residual^2
   const int c = threadIdx.x;
   if (c < HD) {
     const T* tv = reinterpret_cast<const T*>(tile);
@@ -133,19 +133,32 @@ __global__ __launch_bounds__(kPoolThreads) void pool_keys(const T* __restrict__ 
     const int lane = jl + 32 * u;
 #pragma unroll
     for (int p = 0; p < NPL; ++p) {
-      bc[(p * (HD / 16) + ks) * 512 + lane * 8 + e] = (uint16_t)f32_to_bf16_bits(v[p]);
+      const uint32_t h16 = f32_to_bf16_bits(v[p]);
+      bc[(p * (HD / 16) + ks) * 512 + lane * 8 + e] = (uint16_t)h16;
       xcp[(p * (HD / 8) + (c >> 3)) * 256 + jl * 8 + e] = v[p];
+      const float r = v[p] - bf16_bits_to_f32(h16);  // exact (Sterbenz)
+      dd = fmaxf(dd, r * r);
     }
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  for (int off = 32; off >= 1; off >>= 1) {
+    ss += __shfl_xor(ss, off);
+    dd += __shfl_xor(dd, off);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = ss;
+    red[1][threadIdx.x >> 6] = dd;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    float t = 0.0f;
+    float t = 0.0f, td = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kPoolThreads / 64; ++w) t += red[w];
+    for (int w = 0; w < kPoolThreads / 64; ++w) {
+      t += red[0][w];
+      td += red[1][w];
+    }
     summ[kn_off + (size_t)bj * Hkv + g] = __builtin_sqrtf(t);
+    summ[dn_off + (size_t)bj * Hkv + g] = __builtin_sqrtf(td);
   }
 }
 
@@ -188,7 +201,7 @@ hipError_t launch_keys(const Dims& D, const void* K, float* summ, hipStream_t s)
                      dim3(kPoolThreads), 0, s, static_cast<const T*>(K), summ,
                      reinterpret_cast<uint16_t*>(base + L.bfc_byte),
                      reinterpret_cast<float*>(base + L.xc_byte), D.N, D.n, D.Hkv, L.plane, L.kn,
-                     L.ncb);
+                     L.dn, L.ncb);
   return hipGetLastError();
 }
 

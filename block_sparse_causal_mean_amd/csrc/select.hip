@@ -293,15 +293,17 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
 // score is max_i s_ij over the tile's rows; only the row that attains it needs the canonical
 // fp32 chain.  A matrix-core pass computes approximate scores for every (row, block):
 //   shat_ij = q_i . bf16(x_j)   (bf16 MFMA, fp32 accumulation; bf16(x) is the fp32 summary
-//                                 rounded to nearest, within 2^-8 |x| per coordinate, so
-//                                 the rounding moves the product by at most 2^-8 |q_i| |x_j|)
-// with |shat_ij - s_ij| <= E_j = c * max_i |q_i| * |x_j| (x_j the block's scoring vector).
-// c = 1.125 * 2^-8 covers that rounding plus the fp32 accumulation of at most 2d products and
-// the canonical chain's own rounding, each below 2^-16 |q_i| |x_j|.  The row attaining
+//                                 rounded to nearest, r_j = x_j - bf16(x_j) its residual)
+// with |shat_ij - s_ij| <= E_j.  The rounding moves the product by |q_i . r_j|, at most
+// |q_i| |r_j| (Cauchy-Schwarz; for the bound backbone the residual takes per coordinate the
+// larger of the two planes'); the products q_c bf16(x_c) are exact in fp32, and the MFMA's
+// accumulation and the canonical chain's own rounding each stay below d 2^-24 sum_c |q_c x_c|
+// <= 2^-17 |q_i| |x_j| for d <= 128.  So E_j = max_i |q_i| (1.001 |r_j| + 2^-12 |x_j|), where
+// the factor 1.001 and the 2^-12 (far above 2 x 2^-17) absorb the fp32 rounding of the
+// norms themselves.  The row attaining
 // max_i s_ij then satisfies shat_ij >= max_i shat_ij - 2 E_j, so recomputing the canonical
 // chain for exactly those rows and taking their maximum gives the canonical tile score.
-// Usually one row per block qualifies (1.3 on average at 128K), so the fp32 chain work falls
-// by about the tile height.
+// Usually one row per block qualifies, so the fp32 chain work falls by about the tile height.
 //
 // One workgroup (4 waves) per (b, unit, t); a unit of several query heads takes one pass per
 // head, each block keeping its largest score.  The tile's Q rows are staged in LDS as bf16 (for
@@ -315,7 +317,8 @@ __global__ __launch_bounds__(TILE) void score_rank(Dims dm, BudgetDev bd,
 // each of 32 blocks.
 
 constexpr int kScoreThreads = 256;
-constexpr float kPrefilterC = 0x1.2p-8f;
+constexpr float kResidualC = 1.001f;   // |q . r| <= |q| |r|, with the norms' own rounding
+constexpr float kAccumC = 0x1p-12f;    // MFMA accumulation plus canonical chain rounding
 
 // GRP: selection units of several query heads (one list per kv head).  A separate
 // instantiation, because the loop over the unit's heads costs the one-head case registers.
@@ -325,7 +328,7 @@ template <int MODE, int OAM, int D, int TILE, bool GRP>
 __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     Dims dm, BudgetDev bd, const uint16_t* __restrict__ Q, const float* __restrict__ summ,
     const uint16_t* __restrict__ bfc, const float* __restrict__ xc, int* __restrict__ ranked,
-    float* __restrict__ sigma, size_t vn_off, size_t kn_off, int ncb) {
+    float* __restrict__ sigma, size_t vn_off, size_t kn_off, size_t dn_off, int ncb) {
   constexpr int NPL = MODE == SA_KMINMAX ? 2 : 1;  // staged Q planes (q, or q+ and q-)
   constexpr int QS = D + 8;                        // LDS row stride (bf16 elements)
   constexpr int RT = TILE / 32;                    // 32-row tiles
@@ -466,8 +469,10 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
 #pragma unroll
       for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, acc[rt][v]);
     const float M = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float kn = valid ? summ[kn_off + ((size_t)b * n + j) * dm.Hkv + g] : 0.0f;
-    const float thr = M - 2.0f * kPrefilterC * qmax * kn;
+    const size_t bj = ((size_t)b * n + j) * dm.Hkv + g;
+    const float kn = valid ? summ[kn_off + bj] : 0.0f;
+    const float dn = valid ? summ[dn_off + bj] : 0.0f;
+    const float thr = M - 2.0f * qmax * (kResidualC * dn + kAccumC * kn);
     unsigned long long cand = 0ull;
     if (valid) {
 #pragma unroll
@@ -780,7 +785,7 @@ hipError_t launch_score_mfma_g(const Dims& dm, const BudgetDev& bd, const void* 
                      lds, s, dm, bd, static_cast<const uint16_t*>(Q), summ,
                      reinterpret_cast<const uint16_t*>(base + L.bfc_byte),
                      reinterpret_cast<const float*>(base + L.xc_byte), ranked, sigma, L.vn, L.kn,
-                     L.ncb);
+                     L.dn, L.ncb);
   return hipGetLastError();
 }
 

@@ -76,10 +76,10 @@ def test_sizes(lib):
     assert api.select_workspace_bytes(p, b) >= 32 * 512 * 64 * 4
 
     def expect(B, n, Hkv, d, nplanes, oam):
-        # public fp32 planes (+ vnorm), then knorm, then 256-aligned private copies in 32-block
-        # chunks: bf16 of every plane, then fp32 of every plane
+        # public fp32 planes (+ vnorm), then knorm and dnorm, then 256-aligned private copies
+        # in 32-block chunks: bf16 of every plane, then fp32 of every plane
         plane = B * n * Hkv * d
-        head = plane * nplanes * 4 + (B * n * Hkv * 4 if oam else 0) + B * n * Hkv * 4
+        head = plane * nplanes * 4 + (B * n * Hkv * 4 if oam else 0) + 2 * B * n * Hkv * 4
         head = (head + 255) // 256 * 256
         chunks = B * Hkv * ((n + 31) // 32)
         bfc = chunks * nplanes * d * 32 * 2
