@@ -136,8 +136,8 @@ int check_budget(const sa_budget* b, const sa::Dims& D, sa::BudgetDev* bd) {
 
 // LDS the selection kernels need grows with the number of blocks (one sort key each) and the
 // tile's staged query rows; refused here rather than failing at launch.
-int check_select_lds(const sa::Dims& D) {
-  const size_t need = sa::score_rank_lds(D);
+int check_select_lds(const sa::Dims& D, const sa::BudgetDev& bd) {
+  const size_t need = sa::score_rank_lds(D, bd);
   if (need > sa::kMaxDynLds)
     return fail(SA_ERR_UNSUPPORTED,
                 "selection needs %zu bytes of LDS per workgroup (at most %zu): %d blocks of %d "
@@ -181,7 +181,7 @@ size_t sparse_attn_select_workspace_bytes(const sa_problem* p, const sa_budget* 
   sa::Dims D;
   sa::BudgetDev bd;
   if (check_problem(p, &D) != SA_OK || check_budget(b, D, &bd) != SA_OK ||
-      check_select_lds(D) != SA_OK)
+      check_select_lds(D, bd) != SA_OK)
     return 0;
   return sa::select_ws_layout(D, bd).total;
 }
@@ -218,7 +218,7 @@ int sparse_attn_select(const sa_problem* p, const sa_budget* b, const void* Q,
   int rc = check_problem(p, &D);
   if (rc != SA_OK) return rc;
   if ((rc = check_budget(b, D, &bd)) != SA_OK) return rc;
-  if ((rc = check_select_lds(D)) != SA_OK) return rc;
+  if ((rc = check_select_lds(D, bd)) != SA_OK) return rc;
   if (!Q || !summaries || !ws || !kv_idx || !kv_cnt)
     return fail(SA_ERR_INVALID, "Q, summaries, ws, kv_idx and kv_cnt must be non-NULL");
   const size_t need = sa::select_ws_layout(D, bd).total;
@@ -398,7 +398,7 @@ int sparse_attn_select_noalloc(const sa_problem* p, const sa_budget* b, const vo
   int rc = check_problem(p, &D);
   if (rc != SA_OK) return rc;
   if ((rc = check_budget(b, D, &bd)) != SA_OK) return rc;
-  if ((rc = check_select_lds(D)) != SA_OK) return rc;
+  if ((rc = check_select_lds(D, bd)) != SA_OK) return rc;
   if (!Q || !summaries || !kv_idx || !kv_cnt)
     return fail(SA_ERR_INVALID, "Q, summaries, kv_idx and kv_cnt must be non-NULL");
   const size_t need = sa::select_ws_layout(D, bd).total;

@@ -180,14 +180,30 @@ inline size_t pow2_ceil(size_t x) {
   while (p < x) p <<= 1;
   return p;
 }
-// Selection's score-and-rank kernel: one 64-bit order key per block (rounded up to a power
-// of two for the sort), plus, for bf16, the tile's Q rows staged as bf16 (two planes for the
-// K-min/K-max bound) with rows padded by 8 elements.
-inline size_t score_rank_lds(const Dims& D) {
-  const size_t keys = sizeof(unsigned long long) * pow2_ceil((size_t)D.n);
-  if (D.dtype != SA_BF16) return keys;
+// Selection's score-and-rank kernels.  fp32: one 64-bit order key per block (score bits,
+// then the block index), rounded up to a power of two for the sort.  bf16: the tile's Q rows
+// staged as bf16 (two planes for the K-min/K-max bound, rows padded by 8 elements) after the
+// keys; the keys are 32-bit (score bits only: a key's block index is its position) whenever
+// the Q area can hold the 64-bit keys the final sort needs (2 pow2_ceil(ranked entries) of
+// them), else 64-bit as for fp32.  Halving the keys keeps long sequences at two or three
+// workgroups per CU (at 2^20 tokens, 8192 blocks: 32 instead of 64 KiB of keys).
+inline size_t score_q_lds(const Dims& D) {
   const size_t npl = D.score_mode == SA_KMINMAX ? 2 : 1;
-  return keys + sizeof(uint16_t) * npl * D.T * (D.d + 8);
+  return sizeof(uint16_t) * npl * D.T * (D.d + 8);
+}
+inline bool score_keys_compact(const Dims& D, const BudgetDev& bd) {
+  if (D.dtype != SA_BF16) return false;
+  size_t rn = (size_t)(bd.R > bd.k_max + 1 ? bd.R : bd.k_max + 1);
+  if (rn > (size_t)D.n) rn = (size_t)D.n;
+  return 2 * pow2_ceil(rn) * sizeof(unsigned long long) <= score_q_lds(D);
+}
+inline size_t score_keys_lds(const Dims& D, const BudgetDev& bd) {
+  const size_t p = pow2_ceil((size_t)D.n);
+  return score_keys_compact(D, bd) ? (sizeof(unsigned) * p + 15) / 16 * 16
+                                   : sizeof(unsigned long long) * p;
+}
+inline size_t score_rank_lds(const Dims& D, const BudgetDev& bd) {
+  return score_keys_lds(D, bd) + (D.dtype == SA_BF16 ? score_q_lds(D) : 0);
 }
 // Gate kernel: sigma_bar of every tile, then a power-of-two sort buffer.
 inline size_t gate_lds(const Dims& D) {

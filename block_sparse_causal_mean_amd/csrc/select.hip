@@ -84,15 +84,18 @@ __device__ void bitonic_desc(unsigned long long* keys, int P) {
   }
 }
 
-// The Rn largest of keys[0 .. nf) (distinct 64-bit keys; keys[nf .. P) hold 0), sorted
-// descending, by NT threads.  A radix select over 8-bit digits from the top finds the Rn-th
-// largest key (a 256-bin LDS histogram per digit); the keys at or above it, exactly Rn of
-// them, are gathered into `small` and only those are sorted.  When that would not shrink the
-// sort at least fourfold, all P keys are sorted in place instead.  Returns where the sorted
-// top keys are.  Every thread of the workgroup must call it.
-template <int NT>
-__device__ const unsigned long long* top_desc(unsigned long long* keys, int nf, int P, int Rn,
-                                              unsigned long long* small, int small_cap) {
+// The Rn largest of the nf distinct 64-bit keys key_at(0 .. nf), sorted descending, by NT
+// threads.  A radix select over 8-bit digits from the top finds the Rn-th largest key (a
+// 256-bin LDS histogram per digit); the keys at or above it, exactly Rn of them, are gathered
+// into `small` and only those are sorted.  When that would not shrink the sort at least
+// fourfold, all P keys are sorted instead: in place when `inplace` holds them as 64-bit keys
+// (inplace[nf .. P) = 0), else copied into `small`, which the caller sizes for that (P <=
+// small_cap whenever the radix path is not taken).  Returns where the sorted top keys are.
+// Every thread of the workgroup must call it.
+template <int NT, typename KeyAt>
+__device__ const unsigned long long* top_desc(KeyAt key_at, unsigned long long* inplace, int nf,
+                                              int P, int Rn, unsigned long long* small,
+                                              int small_cap) {
   __shared__ unsigned int hist[256];
   __shared__ unsigned long long s_prefix;
   __shared__ int s_need, s_done;
@@ -100,8 +103,14 @@ __device__ const unsigned long long* top_desc(unsigned long long* keys, int nf, 
   int P2 = 1;
   while (P2 < Rn) P2 <<= 1;
   if (nf <= Rn || 4 * P2 > P || P2 > small_cap) {
-    bitonic_desc<NT>(keys, P);
-    return keys;
+    if (inplace) {
+      bitonic_desc<NT>(inplace, P);
+      return inplace;
+    }
+    for (int f = threadIdx.x; f < P; f += NT) small[f] = f < nf ? key_at(f) : 0ull;
+    __syncthreads();
+    bitonic_desc<NT>(small, P);
+    return small;
   }
   unsigned long long prefix = 0ull;
   int need = Rn, shift = 56;
@@ -110,7 +119,7 @@ __device__ const unsigned long long* top_desc(unsigned long long* keys, int nf, 
     __syncthreads();
     const int hs = shift + 8;  // the digits above this one must match the prefix
     for (int f = threadIdx.x; f < nf; f += NT) {
-      const unsigned long long key = keys[f];
+      const unsigned long long key = key_at(f);
       if (hs == 64 || (key >> hs) == (prefix >> hs))
         atomicAdd(&hist[(unsigned)(key >> shift) & 255u], 1u);
     }
@@ -153,7 +162,7 @@ __device__ const unsigned long long* top_desc(unsigned long long* keys, int nf, 
   for (int i = threadIdx.x; i < P2; i += NT) small[i] = 0ull;
   __syncthreads();
   for (int f = threadIdx.x; f < nf; f += NT) {
-    const unsigned long long key = keys[f];
+    const unsigned long long key = key_at(f);
     if ((key >> shift) >= (prefix >> shift)) small[atomicAdd(&s_cnt, 1u)] = key;
   }
   __syncthreads();
@@ -328,7 +337,8 @@ template <int MODE, int OAM, int D, int TILE, bool GRP>
 __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     Dims dm, BudgetDev bd, const uint16_t* __restrict__ Q, const float* __restrict__ summ,
     const uint16_t* __restrict__ bfc, const float* __restrict__ xc, int* __restrict__ ranked,
-    float* __restrict__ sigma, size_t vn_off, size_t kn_off, size_t dn_off, int ncb) {
+    float* __restrict__ sigma, size_t vn_off, size_t kn_off, size_t dn_off, int ncb,
+    int compact) {
   constexpr int NPL = MODE == SA_KMINMAX ? 2 : 1;  // staged Q planes (q, or q+ and q-)
   constexpr int QS = D + 8;                        // LDS row stride (bf16 elements)
   constexpr int RT = TILE / 32;                    // 32-row tiles
@@ -353,10 +363,19 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
   while (P < nf) P <<= 1;
   int Palloc = 1;
   while (Palloc < n) Palloc <<= 1;
-  uint16_t* qs = reinterpret_cast<uint16_t*>(keys + Palloc);  // [NPL][TILE][QS]
+  // Keys: 64-bit (score bits, then 0xffffffff - block), or with `compact` only the 32-bit
+  // score part, the block being j0 + the key's position.  Then the Q rows.
+  unsigned* kq = reinterpret_cast<unsigned*>(keys);
+  uint16_t* qs = reinterpret_cast<uint16_t*>(
+      compact ? reinterpret_cast<char*>(keys) + (4 * Palloc + 15) / 16 * 16
+              : reinterpret_cast<char*>(keys + Palloc));  // [NPL][TILE][QS]
 
-  for (int f = threadIdx.x; f < P; f += kScoreThreads)
-    keys[f] = f < nf ? (unsigned long long)(0xffffffffu - (unsigned)(j0 + f)) : 0ull;
+  for (int f = threadIdx.x; f < P; f += kScoreThreads) {
+    if (compact)
+      kq[f] = 0u;
+    else
+      keys[f] = f < nf ? (unsigned long long)(0xffffffffu - (unsigned)(j0 + f)) : 0ull;
+  }
 
   // The unit's query heads in turn (one pass per head).  Each free block's key holds the
   // largest tile score over the passes so far: the output-aware combine and the order key are
@@ -571,10 +590,16 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     if (valid && hi == 0) {
       float m = canon(best);
       m = oam_combine<OAM>(m, OAM ? summ[vn_off + ((size_t)b * n + j) * dm.Hkv + g] : 0.0f, dm);
-      const unsigned long long key =
-          ((unsigned long long)order_key(m) << 32) | (0xffffffffu - (unsigned)j);
-      // one lane per block and pass, passes separated by barriers: a plain maximum
-      keys[j - j0] = key > keys[j - j0] ? key : keys[j - j0];
+      // one lane per block and pass, passes separated by barriers: a plain maximum (the
+      // block part of a 64-bit key is the same in every pass)
+      const unsigned ok = order_key(m);
+      if (compact) {
+        kq[j - j0] = ok > kq[j - j0] ? ok : kq[j - j0];
+      } else {
+        const unsigned long long key =
+            ((unsigned long long)ok << 32) | (0xffffffffu - (unsigned)j);
+        keys[j - j0] = key > keys[j - j0] ? key : keys[j - j0];
+      }
     }
   }
   }
@@ -582,8 +607,13 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
   // Only the top R keys (and key kt, for sigma) are used: select them, then sort those.  The
   // Q staging area is free by now and holds the selected keys.
   const int R = min(max(expanded(bd, kt), kt), nf);
+  const auto key_at = [&](int f) -> unsigned long long {
+    return compact ? ((unsigned long long)kq[f] << 32) | (0xffffffffu - (unsigned)(j0 + f))
+                   : keys[f];
+  };
   const unsigned long long* top = top_desc<kScoreThreads>(
-      keys, nf, P, min(max(R, kt + 1), nf), reinterpret_cast<unsigned long long*>(qs),
+      key_at, compact ? nullptr : keys, nf, P, min(max(R, kt + 1), nf),
+      reinterpret_cast<unsigned long long*>(qs),
       NPL * TILE * QS * (int)sizeof(uint16_t) / (int)sizeof(unsigned long long));
   int* out = ranked + bht * bd.R;
   for (int r = threadIdx.x; r < R; r += kScoreThreads)
@@ -735,7 +765,7 @@ __global__ __launch_bounds__(64 * kEmitWaves) void emit_kernel(Dims dm, BudgetDe
 template <typename T, int MODE, int OAM, int D, int TILE>
 hipError_t launch_score(const Dims& dm, const BudgetDev& bd, const void* Q, const float* summ,
                         int* ranked, float* sigma, hipStream_t s) {
-  const size_t lds = score_rank_lds(dm);
+  const size_t lds = score_rank_lds(dm, bd);
   const unsigned grid = (unsigned)((size_t)dm.B * dm.Hu * dm.nt);
   hipError_t e = allow_lds(score_rank<T, MODE, OAM, D, TILE>, lds);
   if (e != hipSuccess) return e;
@@ -776,7 +806,7 @@ template <int MODE, int OAM, int D, int TILE, bool GRP>
 hipError_t launch_score_mfma_g(const Dims& dm, const BudgetDev& bd, const void* Q,
                              const float* summ, int* ranked, float* sigma, hipStream_t s) {
   const SummaryLayout L = summary_layout(dm);
-  const size_t lds = score_rank_lds(dm);
+  const size_t lds = score_rank_lds(dm, bd);
   hipError_t e = allow_lds(score_rank_mfma<MODE, OAM, D, TILE, GRP>, lds);
   if (e != hipSuccess) return e;
   const char* base = reinterpret_cast<const char*>(summ);
@@ -785,7 +815,7 @@ hipError_t launch_score_mfma_g(const Dims& dm, const BudgetDev& bd, const void* 
                      lds, s, dm, bd, static_cast<const uint16_t*>(Q), summ,
                      reinterpret_cast<const uint16_t*>(base + L.bfc_byte),
                      reinterpret_cast<const float*>(base + L.xc_byte), ranked, sigma, L.vn, L.kn,
-                     L.dn, L.ncb);
+                     L.dn, L.ncb, score_keys_compact(dm, bd) ? 1 : 0);
   return hipGetLastError();
 }
 

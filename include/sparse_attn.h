@@ -156,11 +156,14 @@ int sparse_attn_score(const sa_problem* p, const void* K, const void* V, void* s
  * 2t+1 for 128-row tiles over 64-key blocks) minus the n_sink first blocks; they rank by
  * tile score, ties to the lower index; the diagonal and sink blocks are always kept.  Scores are
  * fp32 with a fixed reduction order, so the lists are reproducible bit for bit.
- * LDS limit: one workgroup holds a 64-bit sort key per block, 8 * P bytes (P = n rounded up to
- * a power of two), plus for bf16 inputs the tile's query rows, 2 * planes * tile * (d + 8)
- * bytes (planes = 2 for SA_KMINMAX, else 1); the sum must not exceed 159744 bytes, else
- * SA_ERR_UNSUPPORTED before any HIP call (so up to 8192 blocks always fit, and 16384 with
- * SA_KMEAN, 64-row tiles).  sparse_attn_select_workspace_bytes returns 0 for such problems.
+ * LDS limit: one workgroup holds a sort key per block, P of them (P = n rounded up to a power
+ * of two), and for bf16 inputs the tile's query rows, Qb = 2 * planes * tile * (d + 8) bytes
+ * (planes = 2 for SA_KMINMAX, else 1).  Keys take 8 bytes, except with bf16 inputs when
+ * 16 * pow2(Rn) <= Qb, Rn = min(max(floor(rho * k_max), k_max + 1), n) (pow2 rounds up to a
+ * power of two): then 4 bytes, 4 * P rounded up to a multiple of 16.  Keys plus Qb must not
+ * exceed 159744 bytes, else SA_ERR_UNSUPPORTED before any HIP call (with 4-byte keys up to
+ * 16384 blocks always fit, and 32768 with SA_KMEAN and 64-row tiles; with 8-byte keys 8192).
+ * sparse_attn_select_workspace_bytes returns 0 for such problems.
  */
 int sparse_attn_select(const sa_problem* p, const sa_budget* b, const void* Q,
                        const void* summaries, void* ws, size_t ws_bytes, int32_t* kv_idx,

@@ -257,22 +257,36 @@ def test_bench_refuses_more_than_one_gpu():
 def test_selection_lds_limit_rejected_before_hip(lib):
     """The selection keeps a sort key per block and the tile's query rows in LDS: problems
     whose need exceeds a CU's LDS are refused with SA_ERR_UNSUPPORTED before any HIP call,
-    and the workspace query returns 0 for them."""
-    p, b = _ok_problem(), _ok_budget()
-    p.seqlen = 64 * 16384  # 16384 blocks: 128 KiB of keys
+    and the workspace query returns 0 for them.  Keys take 4 bytes while the query rows'
+    area can hold the final sort's 64-bit keys, else 8."""
+    p, b = _ok_problem(), _ok_budget()  # d 128, 64-row tiles: query rows 17408 B (34816 B
+    #                                     with two planes or 128-row tiles); k 32, rho 2
+
+    def fits(q, bb):
+        return lib.sparse_attn_select_workspace_bytes(ctypes.byref(q), ctypes.byref(bb)) > 0
+
+    def refused(q, bb):
+        assert lib.sparse_attn_select_workspace_bytes(ctypes.byref(q), ctypes.byref(bb)) == 0
+        rc = lib.sparse_attn_select(ctypes.byref(q), ctypes.byref(bb), FAKE, FAKE, FAKE,
+                                    1 << 50, FAKE, FAKE, None, None, None, None, None)
+        return rc == api.SA_ERR_UNSUPPORTED and "LDS" in api.last_error()
+
+    p.seqlen = 64 * 16384  # 16384 blocks, the most a problem may have
+    for over in (dict(), dict(score_mode=api.SA_KMINMAX), dict(tile=128),
+                 dict(score_mode=api.SA_KMINMAX, tile=128)):
+        q = api.Problem.from_buffer_copy(p)
+        for k, v in over.items():
+            setattr(q, k, v)
+        assert fits(q, b), over  # 64 KiB of 4-byte keys + at most 69632 B of query rows
+    # a budget whose final sort needs more than the query rows' area: 8-byte keys
+    wide = api.Budget.from_buffer_copy(b)
+    wide.k_max = wide.k_min = 2048  # Rn = 4096: 16 * 4096 > 34816
+    assert fits(p, wide)  # 128 KiB of keys + 17408 B
     for over in (dict(score_mode=api.SA_KMINMAX), dict(tile=128)):
         q = api.Problem.from_buffer_copy(p)
         for k, v in over.items():
             setattr(q, k, v)
-        assert lib.sparse_attn_select_workspace_bytes(ctypes.byref(q), ctypes.byref(b)) == 0
-        rc = lib.sparse_attn_select(ctypes.byref(q), ctypes.byref(b), FAKE, FAKE, FAKE, 1 << 50,
-                                    FAKE, FAKE, None, None, None, None, None)
-        assert rc == api.SA_ERR_UNSUPPORTED and "LDS" in api.last_error(), over
-    # the mean-pool backbone with 64-row tiles fits at the same length, and K-min/K-max fits
-    # at half of it
-    assert lib.sparse_attn_select_workspace_bytes(ctypes.byref(p), ctypes.byref(b)) > 0
-    p.seqlen, p.score_mode = 64 * 8192, api.SA_KMINMAX
-    assert lib.sparse_attn_select_workspace_bytes(ctypes.byref(p), ctypes.byref(b)) > 0
+        assert refused(q, wide), over  # 128 KiB + 34816 B
 
 
 def test_value_norm_lds_limit_rejected_before_hip(lib):

@@ -186,6 +186,11 @@ EDGE = {
                                                k_min=4, near_tie_keys=False),
     "tied_blocks": WL["llama8b_32k"].resized(seqlen=1536, n_q_heads=4, n_kv_heads=2, k_max=4,
                                              k_min=4),
+    # a top list longer than the query rows' LDS area can sort as 64-bit keys (k 300, rho 2:
+    # 600 ranked blocks; d 64): the selection keeps 64-bit sort keys (tiles of up to 639
+    # free blocks) instead of the 32-bit ones
+    "wide_sort_keys": WL["llama8b_32k"].resized(seqlen=64 * 640, n_q_heads=2, n_kv_heads=1,
+                                                head_dim=64, k_max=300, k_min=300, q=0.3),
     # 128-row tiles over 64-key blocks, and lists shared by a kv head's query heads
     "t128_single_tile": WL["llama8b_32k_t128"].resized(seqlen=128, k_max=2, k_min=2),
     "t128_dense_limit": WL["llama8b_32k_t128"].resized(seqlen=1024, n_q_heads=4, n_kv_heads=2,
