@@ -202,8 +202,24 @@ inline size_t score_keys_lds(const Dims& D, const BudgetDev& bd) {
   return score_keys_compact(D, bd) ? (sizeof(unsigned) * p + 15) / 16 * 16
                                    : sizeof(unsigned long long) * p;
 }
+// Threshold pruning of the bf16 selection (select.hip): a tile prunes when it has at least
+// kPruneRatio times as many free blocks as keys it ranks; survivors are listed kPruneListCap
+// positions at a time (uint16 each, after the keys).  Offered for compact keys and one query
+// head per unit, when some tile can qualify (its ranked keys are at least
+// max(floor(rho k_min), k_min + 1)) and the list fits the LDS.
+constexpr int kPruneRatio = 16;
+constexpr int kPruneListCap = 4096;
+inline bool score_prune_ok(const Dims& D, const BudgetDev& bd) {
+  if (!score_keys_compact(D, bd) || D.gs != 1) return false;
+  const long long ex = (long long)floor(bd.rho * (double)bd.k_min);
+  const long long rn = ex > bd.k_min + 1 ? ex : bd.k_min + 1;
+  if ((long long)D.n < (long long)kPruneRatio * rn) return false;
+  return score_keys_lds(D, bd) + sizeof(uint16_t) * kPruneListCap + score_q_lds(D) <=
+         kMaxDynLds;
+}
 inline size_t score_rank_lds(const Dims& D, const BudgetDev& bd) {
-  return score_keys_lds(D, bd) + (D.dtype == SA_BF16 ? score_q_lds(D) : 0);
+  return score_keys_lds(D, bd) + (score_prune_ok(D, bd) ? sizeof(uint16_t) * kPruneListCap : 0) +
+         (D.dtype == SA_BF16 ? score_q_lds(D) : 0);
 }
 // Gate kernel: sigma_bar of every tile, then a power-of-two sort buffer.
 inline size_t gate_lds(const Dims& D) {

@@ -64,6 +64,14 @@ __device__ __forceinline__ int next_pow2(int x) {
   return p;
 }
 
+// LDS scratch of the radix selections below (one per workgroup, reused).
+struct RadixLds {
+  unsigned int hist[256];
+  unsigned long long prefix;
+  int need, done;
+  unsigned int cnt;
+};
+
 // Bitonic sort of P (a power of two) 64-bit keys in LDS, descending, by NT threads.
 template <int NT>
 __device__ void bitonic_desc(unsigned long long* keys, int P) {
@@ -95,11 +103,12 @@ __device__ void bitonic_desc(unsigned long long* keys, int P) {
 template <int NT, typename KeyAt>
 __device__ const unsigned long long* top_desc(KeyAt key_at, unsigned long long* inplace, int nf,
                                               int P, int Rn, unsigned long long* small,
-                                              int small_cap) {
-  __shared__ unsigned int hist[256];
-  __shared__ unsigned long long s_prefix;
-  __shared__ int s_need, s_done;
-  __shared__ unsigned int s_cnt;
+                                              int small_cap, RadixLds& rl) {
+  unsigned int* hist = rl.hist;
+  unsigned long long& s_prefix = rl.prefix;
+  int& s_need = rl.need;
+  int& s_done = rl.done;
+  unsigned int& s_cnt = rl.cnt;
   int P2 = 1;
   while (P2 < Rn) P2 <<= 1;
   if (nf <= Rn || 4 * P2 > P || P2 > small_cap) {
@@ -168,6 +177,84 @@ __device__ const unsigned long long* top_desc(KeyAt key_at, unsigned long long* 
   __syncthreads();
   bitonic_desc<NT>(small, P2);
   return small;
+}
+
+// A threshold u with at least Rn of the 32-bit keys k[0 .. nf) at or above it (Rn <= nf), as
+// large as two histogram passes find: the keys' range [lo, hi] is cut into 256 bins of 2^s
+// keys; the bin holding the Rn-th largest key is cut again into 256, and u is the lower edge
+// of the bin holding it there.  (Binning the range spreads the keys over the bins, where an
+// 8-bit digit of keys that share their top bits would send them all to one bin.)  Every
+// thread must call it.
+template <int NT>
+__device__ unsigned rank_threshold_u32(const unsigned* k, int nf, int Rn, RadixLds& rl) {
+  unsigned lo = 0xffffffffu, hi = 0u;
+  for (int f = threadIdx.x; f < nf; f += NT) {
+    lo = min(lo, k[f]);
+    hi = max(hi, k[f]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, (unsigned)__shfl_xor((int)lo, off));
+    hi = max(hi, (unsigned)__shfl_xor((int)hi, off));
+  }
+  if (threadIdx.x == 0) {
+    rl.prefix = 0xffffffffull;  // low word: running minimum, high word: running maximum
+    rl.need = Rn;
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    atomicMin(reinterpret_cast<unsigned*>(&rl.prefix), lo);
+    atomicMax(reinterpret_cast<unsigned*>(&rl.prefix) + 1, hi);
+  }
+  __syncthreads();
+  lo = (unsigned)rl.prefix;
+  hi = (unsigned)(rl.prefix >> 32);
+  int need = Rn;
+  for (int pass = 0; pass < 2; ++pass) {
+    const unsigned span = hi - lo;
+    const int s = span >> 8 ? 32 - __builtin_clz(span >> 8) : 0;  // (hi - lo) >> s < 256
+    for (int i = threadIdx.x; i < 256; i += NT) rl.hist[i] = 0u;
+    __syncthreads();
+    for (int f = threadIdx.x; f < nf; f += NT) {
+      const unsigned key = k[f];
+      if (key >= lo && key <= hi) atomicAdd(&rl.hist[(key - lo) >> s], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane l holds bins 255 - 4l .. 252 - 4l; `above` counts the keys in higher bins
+      const int lane = threadIdx.x;
+      unsigned c[4], tot = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[e] = rl.hist[255 - 4 * lane - e];
+        tot += c[e];
+      }
+      unsigned incl = tot;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      unsigned above = incl - tot;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (above < (unsigned)need && above + c[e] >= (unsigned)need) {
+          rl.cnt = (unsigned)(255 - 4 * lane - e);
+          rl.need = need - (int)above;
+        }
+        above += c[e];
+      }
+    }
+    __syncthreads();
+    const unsigned bin = rl.cnt;
+    need = rl.need;
+    const unsigned new_lo = lo + (bin << s);
+    hi = (unsigned)min((unsigned long long)hi, (unsigned long long)new_lo + (1ull << s) - 1ull);
+    lo = new_lo;
+    __syncthreads();  // every thread has read rl before the next pass rewrites it
+    if (s == 0) break;
+  }
+  return lo;
 }
 
 template <typename T, int D>
@@ -329,9 +416,27 @@ constexpr int kScoreThreads = 256;
 constexpr float kResidualC = 1.001f;   // |q . r| <= |q| |r|, with the norms' own rounding
 constexpr float kAccumC = 0x1p-12f;    // MFMA accumulation plus canonical chain rounding
 
+// Threshold pruning for long rows of free blocks.  Only the top Rn = max(R, k + 1) order keys
+// are ever read, so a block that provably ranks below Rn others needs no canonical score.  A
+// first pass runs the prefilter alone: it brackets every block's (combined) tile score between
+// LB_j = combine(M_j - E_j) and UB_j = combine(M_j + E_j) (M_j the largest approximate row
+// score; combine is the monotone output-aware step or the identity) and keeps UB_j as the
+// block's key.  With U the Rn-th largest UB and D the largest UB_j - LB_j, at least Rn blocks
+// have an exact score >= U - D >= T, so every block with UB_j < T ranks strictly below them and
+// is dropped (key 0, below every real key); the surviving blocks get their canonical scores as
+// usual (a second prefilter over lists of 32 survivors, then the candidate rows' chains), and
+// the ranking over those keys is the ranking of the full row.  The rounding of M +- E is covered
+// by E's margin (kAccumC is 16 times the accumulation bound); D and T are widened by 2^-22
+// relative.  Used when a tile has at least kPruneRatio * Rn free blocks (where the survivors
+// are few; near-tied rows simply keep more of them) and one query head per selection unit
+// (common.h, score_prune_ok).
+constexpr int kListCap = kPruneListCap;  // survivors gathered per round (positions, uint16)
+
 // GRP: selection units of several query heads (one list per kv head).  A separate
 // instantiation, because the loop over the unit's heads costs the one-head case registers.
-template <int MODE, int OAM, int D, int TILE, bool GRP>
+// PRUNE: the threshold pruning above may run (compact keys, GRP false; the survivor list sits
+// after the keys).  Also separate: its extra state costs the other instantiations registers.
+template <int MODE, int OAM, int D, int TILE, bool GRP, bool PRUNE>
 // Three waves per SIMD (at most 168 registers): as many workgroups as the LDS allows (three
 // per CU), measured 23% faster than the compiler's default of two waves per SIMD.
 __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
@@ -339,12 +444,15 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     const uint16_t* __restrict__ bfc, const float* __restrict__ xc, int* __restrict__ ranked,
     float* __restrict__ sigma, size_t vn_off, size_t kn_off, size_t dn_off, int ncb,
     int compact) {
+  static_assert(!(GRP && PRUNE), "pruning serves one query head per unit");
   constexpr int NPL = MODE == SA_KMINMAX ? 2 : 1;  // staged Q planes (q, or q+ and q-)
   constexpr int QS = D + 8;                        // LDS row stride (bf16 elements)
   constexpr int RT = TILE / 32;                    // 32-row tiles
   constexpr int KS = D / 16;                       // 16-coordinate MFMA steps
   extern __shared__ __attribute__((aligned(16))) unsigned long long keys[];
   __shared__ float qmax_w[kScoreThreads / 64];
+  __shared__ RadixLds rl;
+  __shared__ unsigned s_dmax;
 
   int b, u, t;
   decode_unit(dm, b, u, t);
@@ -363,12 +471,18 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
   while (P < nf) P <<= 1;
   int Palloc = 1;
   while (Palloc < n) Palloc <<= 1;
+  const int R = min(max(expanded(bd, kt), kt), nf);  // ranked entries written
+  const int Rn = min(max(R, kt + 1), nf);            // keys read (key kt gives sigma)
+  const bool prune = PRUNE && compact && nf >= kPruneRatio * Rn;
   // Keys: 64-bit (score bits, then 0xffffffff - block), or with `compact` only the 32-bit
-  // score part, the block being j0 + the key's position.  Then the Q rows.
+  // score part, the block being j0 + the key's position.  Then, with PRUNE, the survivor
+  // list; then the Q rows.
   unsigned* kq = reinterpret_cast<unsigned*>(keys);
+  char* after_keys = compact ? reinterpret_cast<char*>(keys) + (4 * Palloc + 15) / 16 * 16
+                             : reinterpret_cast<char*>(keys + Palloc);
+  uint16_t* list = reinterpret_cast<uint16_t*>(after_keys);  // [kListCap]
   uint16_t* qs = reinterpret_cast<uint16_t*>(
-      compact ? reinterpret_cast<char*>(keys) + (4 * Palloc + 15) / 16 * 16
-              : reinterpret_cast<char*>(keys + Palloc));  // [NPL][TILE][QS]
+      after_keys + (PRUNE ? kListCap * sizeof(uint16_t) : 0));  // [NPL][TILE][QS]
 
   for (int f = threadIdx.x; f < P; f += kScoreThreads) {
     if (compact)
@@ -376,93 +490,21 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     else
       keys[f] = f < nf ? (unsigned long long)(0xffffffffu - (unsigned)(j0 + f)) : 0ull;
   }
-
-  // The unit's query heads in turn (one pass per head).  Each free block's key holds the
-  // largest tile score over the passes so far: the output-aware combine and the order key are
-  // monotone, so the maximum over all of the unit's rows is exact.
-  const int h_end = GRP ? (u + 1) * dm.gs : u + 1;
-  for (int h = GRP ? u * dm.gs : u; h < h_end; ++h) {
-  __syncthreads();  // the previous pass has finished reading qs and qmax_w
-
-  // Stage the tile's Q rows; row norms (any order: they only scale the bound) -> max.  Each
-  // thread takes a contiguous piece of one row (PPR pieces per row, all loads issued at
-  // once), so a row's sum of squares needs only PPR - 1 neighbouring-lane exchanges.
-  {
-    constexpr int EPT = TILE * D / kScoreThreads;  // elements per thread
-    constexpr int NV = EPT / 8;                    // 16-byte loads per thread
-    constexpr int PPR = D / EPT;                   // threads per row
-    static_assert(PPR == 2 || PPR == 4, "row pieces must pair within a lane quad");
-    const int r = threadIdx.x / PPR, piece = threadIdx.x % PPR;
-    const uint16_t* qsrc =
-        Q + (((size_t)b * dm.N + (size_t)t * TILE + r) * dm.Hq + h) * D + piece * EPT;
-    uint4 v[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) v[i] = *reinterpret_cast<const uint4*>(qsrc + 8 * i);
-    float ss = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float lo = bf16_lo(w[k]), hi = bf16_hi(w[k]);
-        ss = __builtin_fmaf(lo, lo, ss);
-        ss = __builtin_fmaf(hi, hi, ss);
-      }
-      uint16_t* dst = qs + r * QS + piece * EPT + 8 * i;
-      if (MODE == SA_KMEAN) {
-        *reinterpret_cast<uint4*>(dst) = v[i];
-      } else {
-        uint32_t pw[4], nw[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t neg = ((w[k] >> 15) & 0x00010001u) * 0xffffu;  // negative halves
-          pw[k] = w[k] & ~neg;
-          nw[k] = w[k] & neg;
-        }
-        *reinterpret_cast<uint4*>(dst) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-        *reinterpret_cast<uint4*>(dst + TILE * QS) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
-      }
-    }
-#pragma unroll
-    for (int off = 1; off < PPR; off <<= 1) ss += __shfl_xor(ss, off);
-    float rmax = ss;
-#pragma unroll
-    for (int off = PPR; off < 64; off <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, off));
-    if ((threadIdx.x & 63) == 0) qmax_w[threadIdx.x >> 6] = rmax;
-  }
-  __syncthreads();
-  float qmax2 = qmax_w[0];
-#pragma unroll
-  for (int k = 1; k < kScoreThreads / 64; ++k) qmax2 = fmaxf(qmax2, qmax_w[k]);
-  const float qmax = __builtin_sqrtf(qmax2);
+  if (threadIdx.x == 0) s_dmax = 0u;
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  // 32-block chunks of this (batch, kv head) covering the free blocks [j0, d0).
+  // Blocks of this (batch, kv head) in 32-block chunks: block j sits in chunk j / 32 at slot
+  // j % 32 of the chunk-major copies.
   const size_t chunk0 = ((size_t)b * dm.Hkv + g) * ncb;
   constexpr size_t BFC = (size_t)NPL * D * 32, XC = (size_t)NPL * D * 32;
+  float qmax = 0.0f;
 
-  for (int ch = (j0 >> 5) + wv; ch * 32 < d0; ch += kScoreThreads / 64) {
-    const int j = ch * 32 + l32;  // this lane's block
-    const bool valid = j >= j0 && j < d0;
-    const uint16_t* bc = bfc + (chunk0 + ch) * BFC + lane * 8;
-    // kmean, or kmin (plane 0) / kmax (plane 1): coordinates 8c .. 8c+7 of this lane's block
-    // at xk + (plane * D/8 + c) * 256
-    const float* xk = xc + (chunk0 + ch) * XC + l32 * 8;
-    // Mean-pooled backbone: this lane's half of the block's fp32 summary (coordinates
-    // D/2 * hi .. +D/2), requested now so it arrives while the matrix products run.
-    float xh[MODE == SA_KMEAN ? D / 2 : 1];
-    if constexpr (MODE == SA_KMEAN) {
-#pragma unroll
-      for (int c8 = 0; c8 < D / 16; ++c8) {
-        const float4 x0 = *reinterpret_cast<const float4*>(xk + (hi * (D / 16) + c8) * 256);
-        const float4 x1 = *reinterpret_cast<const float4*>(xk + (hi * (D / 16) + c8) * 256 + 4);
-        xh[8 * c8 + 0] = x0.x; xh[8 * c8 + 1] = x0.y; xh[8 * c8 + 2] = x0.z; xh[8 * c8 + 3] = x0.w;
-        xh[8 * c8 + 4] = x1.x; xh[8 * c8 + 5] = x1.y; xh[8 * c8 + 6] = x1.z; xh[8 * c8 + 7] = x1.w;
-      }
-    }
-
-    f32x16 acc[RT];
+  // Approximate scores of the tile's rows against the lane pair's block j = 32 c + sl (bf16
+  // MFMA; c is uniform over the wave when it walks whole chunks, which keeps the chunk's base
+  // address scalar).  Lane (l32, hi) gets rows 32rt + 8i + 4hi + r of its block.
+  auto approx = [&](int c, int sl, f32x16 (&acc)[RT]) {
+    const uint16_t* bc = bfc + (chunk0 + c) * BFC + (sl + 32 * hi) * 8;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) acc[rt] = (f32x16){};
 #pragma unroll
@@ -481,17 +523,46 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
         }
       }
     }
-    // Lane (l32, hi) holds block j's approximate scores of rows 32rt + 8i + 4hi + r.
+  };
+  // Prefilter error bound of block j (valid lanes).
+  auto err_bound = [&](int j, bool valid) {
+    const size_t bj = ((size_t)b * n + j) * dm.Hkv + g;
+    const float kn = valid ? summ[kn_off + bj] : 0.0f;
+    const float dn = valid ? summ[dn_off + bj] : 0.0f;
+    return qmax * (kResidualC * dn + kAccumC * kn);
+  };
+  auto value_norm = [&](int j) {
+    return OAM ? summ[vn_off + ((size_t)b * n + j) * dm.Hkv + g] : 0.0f;
+  };
+
+  // The order key of block j = 32 c + sl's canonical (combined) tile score, on lanes hi == 0
+  // of valid blocks: the prefilter's candidate rows, then their canonical fp32 chains.
+  auto exact_key = [&](int c, int sl, bool valid) -> unsigned {
+    const int j = 32 * c + sl;
+    // kmean, or kmin (plane 0) / kmax (plane 1): coordinates 8c .. 8c+7 of this lane's block
+    // at xk + (plane * D/8 + c) * 256
+    const float* xk = xc + (chunk0 + c) * XC + sl * 8;
+    // Mean-pooled backbone: this lane's half of the block's fp32 summary (coordinates
+    // D/2 * hi .. +D/2), requested now so it arrives while the matrix products run.
+    float xh[MODE == SA_KMEAN ? D / 2 : 1];
+    if constexpr (MODE == SA_KMEAN) {
+#pragma unroll
+      for (int c8 = 0; c8 < D / 16; ++c8) {
+        const float4 x0 = *reinterpret_cast<const float4*>(xk + (hi * (D / 16) + c8) * 256);
+        const float4 x1 = *reinterpret_cast<const float4*>(xk + (hi * (D / 16) + c8) * 256 + 4);
+        xh[8 * c8 + 0] = x0.x; xh[8 * c8 + 1] = x0.y; xh[8 * c8 + 2] = x0.z; xh[8 * c8 + 3] = x0.w;
+        xh[8 * c8 + 4] = x1.x; xh[8 * c8 + 5] = x1.y; xh[8 * c8 + 6] = x1.z; xh[8 * c8 + 7] = x1.w;
+      }
+    }
+    f32x16 acc[RT];
+    approx(c, sl, acc);
     float mloc = -INFINITY;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, acc[rt][v]);
     const float M = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const size_t bj = ((size_t)b * n + j) * dm.Hkv + g;
-    const float kn = valid ? summ[kn_off + bj] : 0.0f;
-    const float dn = valid ? summ[dn_off + bj] : 0.0f;
-    const float thr = M - 2.0f * qmax * (kResidualC * dn + kAccumC * kn);
+    const float thr = M - 2.0f * err_bound(j, valid);
     unsigned long long cand = 0ull;
     if (valid) {
 #pragma unroll
@@ -587,34 +658,216 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     }
     }
     best = fmaxf(best, __shfl_xor(best, 32));
-    if (valid && hi == 0) {
-      float m = canon(best);
-      m = oam_combine<OAM>(m, OAM ? summ[vn_off + ((size_t)b * n + j) * dm.Hkv + g] : 0.0f, dm);
-      // one lane per block and pass, passes separated by barriers: a plain maximum (the
-      // block part of a 64-bit key is the same in every pass)
-      const unsigned ok = order_key(m);
-      if (compact) {
-        kq[j - j0] = ok > kq[j - j0] ? ok : kq[j - j0];
-      } else {
-        const unsigned long long key =
-            ((unsigned long long)ok << 32) | (0xffffffffu - (unsigned)j);
-        keys[j - j0] = key > keys[j - j0] ? key : keys[j - j0];
+    unsigned key = 0u;
+    if (valid && hi == 0) key = order_key(oam_combine<OAM>(canon(best), value_norm(j), dm));
+    return key;
+  };
+
+  // The unit's query heads in turn (one pass per head).  Each free block's key holds the
+  // largest tile score over the passes so far: the output-aware combine and the order key are
+  // monotone, so the maximum over all of the unit's rows is exact.
+  const int h_end = GRP ? (u + 1) * dm.gs : u + 1;
+  for (int h = GRP ? u * dm.gs : u; h < h_end; ++h) {
+  __syncthreads();  // the previous pass has finished reading qs and qmax_w
+
+  // Stage the tile's Q rows; row norms (any order: they only scale the bound) -> max.  Each
+  // thread takes a contiguous piece of one row (PPR pieces per row, all loads issued at
+  // once), so a row's sum of squares needs only PPR - 1 neighbouring-lane exchanges.
+  {
+    constexpr int EPT = TILE * D / kScoreThreads;  // elements per thread
+    constexpr int NV = EPT / 8;                    // 16-byte loads per thread
+    constexpr int PPR = D / EPT;                   // threads per row
+    static_assert(PPR == 2 || PPR == 4, "row pieces must pair within a lane quad");
+    const int r = threadIdx.x / PPR, piece = threadIdx.x % PPR;
+    const uint16_t* qsrc =
+        Q + (((size_t)b * dm.N + (size_t)t * TILE + r) * dm.Hq + h) * D + piece * EPT;
+    uint4 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = *reinterpret_cast<const uint4*>(qsrc + 8 * i);
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lo = bf16_lo(w[k]), hi = bf16_hi(w[k]);
+        ss = __builtin_fmaf(lo, lo, ss);
+        ss = __builtin_fmaf(hi, hi, ss);
       }
+      uint16_t* dst = qs + r * QS + piece * EPT + 8 * i;
+      if (MODE == SA_KMEAN) {
+        *reinterpret_cast<uint4*>(dst) = v[i];
+      } else {
+        uint32_t pw[4], nw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t neg = ((w[k] >> 15) & 0x00010001u) * 0xffffu;  // negative halves
+          pw[k] = w[k] & ~neg;
+          nw[k] = w[k] & neg;
+        }
+        *reinterpret_cast<uint4*>(dst) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+        *reinterpret_cast<uint4*>(dst + TILE * QS) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < PPR; off <<= 1) ss += __shfl_xor(ss, off);
+    float rmax = ss;
+#pragma unroll
+    for (int off = PPR; off < 64; off <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, off));
+    if ((threadIdx.x & 63) == 0) qmax_w[threadIdx.x >> 6] = rmax;
+  }
+  __syncthreads();
+  float qmax2 = qmax_w[0];
+#pragma unroll
+  for (int k = 1; k < kScoreThreads / 64; ++k) qmax2 = fmaxf(qmax2, qmax_w[k]);
+  // uniform over the workgroup: kept in a scalar register
+  qmax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_sqrtf(qmax2))));
+
+  if constexpr (!PRUNE) {
+    // Every free block: aligned 32-block chunks covering [j0, d0), dealt to the waves.
+    for (int ch = (j0 >> 5) + wv; ch * 32 < d0; ch += kScoreThreads / 64) {
+      const int j = ch * 32 + l32;  // this lane's block
+      const bool valid = j >= j0 && j < d0;
+      const unsigned ok = exact_key(ch, l32, valid);
+      if (valid && hi == 0) {
+        // one lane per block and pass, passes separated by barriers: a plain maximum (the
+        // block part of a 64-bit key is the same in every pass)
+        if (compact) {
+          kq[j - j0] = ok > kq[j - j0] ? ok : kq[j - j0];
+        } else {
+          const unsigned long long key =
+              ((unsigned long long)ok << 32) | (0xffffffffu - (unsigned)j);
+          keys[j - j0] = key > keys[j - j0] ? key : keys[j - j0];
+        }
+      }
+    }
+  } else {
+    if constexpr (PRUNE) {
+      if (prune) {
+        // First pass of the pruning: the prefilter alone, UB_j as the key, max of UB_j - LB_j.
+        float dmax = 0.0f;
+        for (int ch = (j0 >> 5) + wv; ch * 32 < d0; ch += kScoreThreads / 64) {
+          const int j = ch * 32 + l32;
+          const bool valid = j >= j0 && j < d0;
+          f32x16 acc[RT];
+          approx(ch, l32, acc);
+          float mloc = -INFINITY;
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, acc[rt][v]);
+          const float M = fmaxf(mloc, __shfl_xor(mloc, 32));
+          if (valid && hi == 0) {
+            const float E = err_bound(j, valid);
+            const float vn = value_norm(j);
+            const float ub = oam_combine<OAM>(canon(M + E), vn, dm);
+            const float lb = oam_combine<OAM>(canon(M - E), vn, dm);
+            kq[j - j0] = order_key(ub);
+            dmax = fmaxf(dmax, ub - lb);
+          }
+        }
+        dmax = wave_max(dmax);
+        if (lane == 0) atomicMax(&s_dmax, __float_as_uint(dmax));  // >= 0: bits order as values
+        __syncthreads();
+      }
+    }
+    // Blocks to score exactly: without pruning every free block, in aligned 32-block chunks
+    // covering [j0, d0) dealt to the waves (one round); with it the survivors of each round of
+    // kListCap positions, listed, 32 per wave pass (the others' keys become 0).  A listed
+    // position is read and written by one thread of the scan, then by the lane that scores it,
+    // after a barrier.
+    unsigned Tk = 0u;
+    if constexpr (PRUNE) {
+      if (prune) {
+        const float U = order_key_inv(rank_threshold_u32<kScoreThreads>(kq, nf, Rn, rl));
+        const float dm_ = __uint_as_float(s_dmax) * (1.0f + 0x1p-22f);
+        float T = U - dm_;
+        T = T - fabsf(T) * 0x1p-22f;
+        Tk = order_key(T);
+      }
+    }
+    for (int base = 0; base < (prune ? nf : 1); base += kListCap) {
+      int items = ((d0 + 31) >> 5) - (j0 >> 5);  // chunks
+      if (prune) {
+        const int end = min(nf, base + kListCap);
+        if (threadIdx.x == 0) rl.cnt = 0u;
+        __syncthreads();
+        for (int f = base + (int)threadIdx.x; f < end; f += kScoreThreads) {
+          if (kq[f] >= Tk)
+            list[atomicAdd(&rl.cnt, 1u)] = (uint16_t)(f - base);
+          else
+            kq[f] = 0u;
+        }
+        __syncthreads();
+        items = ((int)rl.cnt + 31) >> 5;
+      }
+      const int cnt = prune ? (int)rl.cnt : 0;
+      for (int it = wv; it < items; it += kScoreThreads / 64) {
+        int j;
+        bool valid;
+        if (prune) {
+          valid = 32 * it + l32 < cnt;
+          j = j0 + base + (valid ? (int)list[32 * it + l32] : 0);
+        } else {
+          j = ((j0 >> 5) + it) * 32 + l32;  // this lane's block
+          valid = j >= j0 && j < d0;
+        }
+        const unsigned ok = exact_key(j >> 5, j & 31, valid);
+        if (valid && hi == 0) {
+          // one lane per block and pass, passes separated by barriers: a plain maximum (the
+          // block part of a 64-bit key is the same in every pass)
+          if (compact) {
+            kq[j - j0] = prune || ok > kq[j - j0] ? ok : kq[j - j0];
+          } else {
+            const unsigned long long key =
+                ((unsigned long long)ok << 32) | (0xffffffffu - (unsigned)j);
+            keys[j - j0] = key > keys[j - j0] ? key : keys[j - j0];
+          }
+        }
+      }
+      if (prune) __syncthreads();  // the list is rebuilt by the next round
     }
   }
   }
   __syncthreads();
   // Only the top R keys (and key kt, for sigma) are used: select them, then sort those.  The
   // Q staging area is free by now and holds the selected keys.
-  const int R = min(max(expanded(bd, kt), kt), nf);
   const auto key_at = [&](int f) -> unsigned long long {
     return compact ? ((unsigned long long)kq[f] << 32) | (0xffffffffu - (unsigned)(j0 + f))
                    : keys[f];
   };
-  const unsigned long long* top = top_desc<kScoreThreads>(
-      key_at, compact ? nullptr : keys, nf, P, min(max(R, kt + 1), nf),
-      reinterpret_cast<unsigned long long*>(qs),
-      NPL * TILE * QS * (int)sizeof(uint16_t) / (int)sizeof(unsigned long long));
+  unsigned long long* small = reinterpret_cast<unsigned long long*>(qs);
+  const int small_cap = NPL * TILE * QS * (int)sizeof(uint16_t) / (int)sizeof(unsigned long long);
+  const unsigned long long* top = nullptr;
+  if constexpr (PRUNE) {
+    if (prune) {
+      // The survivors' keys (the only nonzero ones) gathered into the list area as 64-bit
+      // keys, when they fit, so that the ranking reads those alone.
+      constexpr int kSurvCap = kListCap * (int)sizeof(uint16_t) / (int)sizeof(unsigned long long);
+      unsigned long long* surv = reinterpret_cast<unsigned long long*>(list);
+      if (threadIdx.x == 0) rl.cnt = 0u;
+      __syncthreads();
+      for (int f = threadIdx.x; f < nf; f += kScoreThreads) {
+        if (kq[f]) {
+          const unsigned slot = atomicAdd(&rl.cnt, 1u);
+          if (slot < (unsigned)kSurvCap) surv[slot] = key_at(f);
+        }
+      }
+      __syncthreads();
+      const int S = (int)rl.cnt;
+      if (S <= kSurvCap) {
+        int PS = 1;
+        while (PS < S) PS <<= 1;
+        for (int f = S + (int)threadIdx.x; f < PS; f += kScoreThreads) surv[f] = 0ull;
+        __syncthreads();
+        top = top_desc<kScoreThreads>([&](int f) { return surv[f]; }, surv, S, PS, Rn, small,
+                                      small_cap, rl);
+      }
+    }
+  }
+  if (!top)
+    top = top_desc<kScoreThreads>(key_at, compact ? nullptr : keys, nf, P, Rn, small,
+                                  small_cap, rl);
   int* out = ranked + bht * bd.R;
   for (int r = threadIdx.x; r < R; r += kScoreThreads)
     out[r] = (int)(0xffffffffu - (unsigned)top[r]);
@@ -802,16 +1055,16 @@ hipError_t score_dispatch(const Dims& dm, const BudgetDev& bd, const void* Q, co
   return score_by_oam<T, SA_KMINMAX>(dm, bd, Q, summ, ranked, sigma, s);
 }
 
-template <int MODE, int OAM, int D, int TILE, bool GRP>
+template <int MODE, int OAM, int D, int TILE, bool GRP, bool PRUNE>
 hipError_t launch_score_mfma_g(const Dims& dm, const BudgetDev& bd, const void* Q,
                              const float* summ, int* ranked, float* sigma, hipStream_t s) {
   const SummaryLayout L = summary_layout(dm);
   const size_t lds = score_rank_lds(dm, bd);
-  hipError_t e = allow_lds(score_rank_mfma<MODE, OAM, D, TILE, GRP>, lds);
+  hipError_t e = allow_lds(score_rank_mfma<MODE, OAM, D, TILE, GRP, PRUNE>, lds);
   if (e != hipSuccess) return e;
   const char* base = reinterpret_cast<const char*>(summ);
   const unsigned grid = (unsigned)((size_t)dm.B * dm.Hu * dm.nt);
-  hipLaunchKernelGGL((score_rank_mfma<MODE, OAM, D, TILE, GRP>), dim3(grid), dim3(kScoreThreads),
+  hipLaunchKernelGGL((score_rank_mfma<MODE, OAM, D, TILE, GRP, PRUNE>), dim3(grid), dim3(kScoreThreads),
                      lds, s, dm, bd, static_cast<const uint16_t*>(Q), summ,
                      reinterpret_cast<const uint16_t*>(base + L.bfc_byte),
                      reinterpret_cast<const float*>(base + L.xc_byte), ranked, sigma, L.vn, L.kn,
@@ -822,9 +1075,11 @@ hipError_t launch_score_mfma_g(const Dims& dm, const BudgetDev& bd, const void* 
 template <int MODE, int OAM, int D, int TILE>
 hipError_t launch_score_mfma(const Dims& dm, const BudgetDev& bd, const void* Q,
                              const float* summ, int* ranked, float* sigma, hipStream_t s) {
-  return dm.gs > 1 ? launch_score_mfma_g<MODE, OAM, D, TILE, true>(dm, bd, Q, summ, ranked, sigma, s)
-                   : launch_score_mfma_g<MODE, OAM, D, TILE, false>(dm, bd, Q, summ, ranked, sigma,
-                                                                    s);
+  if (dm.gs > 1)
+    return launch_score_mfma_g<MODE, OAM, D, TILE, true, false>(dm, bd, Q, summ, ranked, sigma, s);
+  if (score_prune_ok(dm, bd))
+    return launch_score_mfma_g<MODE, OAM, D, TILE, false, true>(dm, bd, Q, summ, ranked, sigma, s);
+  return launch_score_mfma_g<MODE, OAM, D, TILE, false, false>(dm, bd, Q, summ, ranked, sigma, s);
 }
 
 template <int MODE, int OAM>

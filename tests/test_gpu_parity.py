@@ -230,6 +230,32 @@ EDGE = {
     "zero_value_blocks_oam_t128": WL["stem_32k_t128"].resized(batch=1, seqlen=2048,
                                                               n_q_heads=4, n_kv_heads=2,
                                                               k_max=6, k_min=3, q=0.3),
+    # threshold pruning of long rows (tiles with at least 16 times as many free blocks as
+    # ranked keys): a prefilter pass, survivors above a safe threshold, exact scores for those
+    # only.  Small k makes short sequences qualify.
+    "prune_kmean": WL["llama8b_32k"].resized(seqlen=64 * 192, n_q_heads=2, n_kv_heads=1,
+                                             k_max=2, k_min=2, q=0.3),
+    "prune_kmean_d64_batch2": WL["llama8b_32k"].resized(batch=2, seqlen=64 * 160, n_q_heads=2,
+                                                        n_kv_heads=1, head_dim=64, k_max=2,
+                                                        k_min=2),
+    "prune_oam_sinks_decay": WL["stem_32k"].resized(batch=1, seqlen=64 * 256, n_q_heads=2,
+                                                    n_kv_heads=1, k_max=8, k_min=2),
+    "prune_additive": WL["stem_additive_32k"].resized(batch=1, seqlen=64 * 256, n_q_heads=2,
+                                                      n_kv_heads=1, k_max=4, k_min=2),
+    "prune_t128": WL["llama8b_32k_t128"].resized(seqlen=64 * 256, n_q_heads=2, n_kv_heads=1,
+                                                 k_max=2, k_min=2),
+    "prune_t64_in_block128": WL["prefill_128k_t64"].resized(seqlen=128 * 128, n_q_heads=2,
+                                                            n_kv_heads=1, k_max=2, k_min=2),
+    "prune_block128_planted": WL["prefill_128k"].resized(seqlen=128 * 160, n_q_heads=2,
+                                                         n_kv_heads=1, k_max=2, k_min=2),
+    "prune_quest_near_ties": WL["quest_64k"].resized(seqlen=64 * 192, n_q_heads=2, n_kv_heads=1,
+                                                     k_max=2, k_min=2),
+    "tied_blocks_prune": WL["llama8b_32k"].resized(seqlen=64 * 192, n_q_heads=2, n_kv_heads=1,
+                                                   k_max=2, k_min=2),
+    "tied_rows_prune": WL["prefill_128k"].resized(seqlen=128 * 160, n_q_heads=2, n_kv_heads=1,
+                                                  k_max=2, k_min=2, planted=False),
+    "zero_value_blocks_prune": WL["stem_32k"].resized(batch=1, seqlen=64 * 256, n_q_heads=2,
+                                                      n_kv_heads=1, k_max=6, k_min=2, q=0.3),
 }
 
 
