@@ -745,12 +745,60 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     if constexpr (PRUNE) {
       if (prune) {
         // First pass of the pruning: the prefilter alone, UB_j as the key, max of UB_j - LB_j.
+        // The next chunk's operands are requested while this chunk's products run.
+        constexpr int NB = NPL * KS;
+        auto load_ops = [&](int c, bf16x8 (&bo)[NB]) {
+          const uint16_t* bc = bfc + (chunk0 + c) * BFC + (l32 + 32 * hi) * 8;
+#pragma unroll
+          for (int pl = 0; pl < NPL; ++pl) {
+            const int xp = MODE == SA_KMINMAX ? 1 - pl : 0;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+              bo[pl * KS + ks] =
+                  *reinterpret_cast<const bf16x8*>(bc + (size_t)xp * (KS * 512) + 512 * ks);
+          }
+        };
         float dmax = 0.0f;
-        for (int ch = (j0 >> 5) + wv; ch * 32 < d0; ch += kScoreThreads / 64) {
+        bf16x8 bnext[NB];
+        int ch = (j0 >> 5) + wv;
+        if (ch * 32 < d0) load_ops(ch, bnext);
+        for (; ch * 32 < d0; ch += kScoreThreads / 64) {
           const int j = ch * 32 + l32;
           const bool valid = j >= j0 && j < d0;
+          bf16x8 bcur[NB];
+#pragma unroll
+          for (int i = 0; i < NB; ++i) bcur[i] = bnext[i];
+          if ((ch + kScoreThreads / 64) * 32 < d0) load_ops(ch + kScoreThreads / 64, bnext);
+          const size_t bj = ((size_t)b * n + (valid ? j : j0)) * dm.Hkv + g;
+          const float kn = summ[kn_off + bj], dn = summ[dn_off + bj];
+          const float vn = OAM ? summ[vn_off + bj] : 0.0f;
+          // Products in (plane, 16-coordinate step) order, each step's four row tiles
+          // together; the next step's Q fragments are read from LDS before this step's
+          // products, and the order is pinned so that the reads stay ahead.
           f32x16 acc[RT];
-          approx(ch, l32, acc);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[rt] = (f32x16){};
+          const uint16_t* ap = qs + (size_t)l32 * QS + 8 * hi;
+          auto a_frag = [&](int i, int rt) {
+            return *reinterpret_cast<const bf16x8*>(ap + (size_t)((i / KS) * TILE + rt * 32) * QS +
+                                                    16 * (i % KS));
+          };
+          bf16x8 acur[RT], anxt[RT];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acur[rt] = a_frag(0, rt);
+#pragma unroll
+          for (int i = 0; i < NB; ++i) {
+            if (i + 1 < NB) {
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt) anxt[rt] = a_frag(i + 1, rt);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[rt], bcur[i], acc[rt], 0, 0, 0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) acur[rt] = anxt[rt];
+            __builtin_amdgcn_sched_barrier(0);
+          }
           float mloc = -INFINITY;
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
@@ -758,8 +806,7 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
             for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, acc[rt][v]);
           const float M = fmaxf(mloc, __shfl_xor(mloc, 32));
           if (valid && hi == 0) {
-            const float E = err_bound(j, valid);
-            const float vn = value_norm(j);
+            const float E = qmax * (kResidualC * dn + kAccumC * kn);
             const float ub = oam_combine<OAM>(canon(M + E), vn, dm);
             const float lb = oam_combine<OAM>(canon(M - E), vn, dm);
             kq[j - j0] = order_key(ub);
