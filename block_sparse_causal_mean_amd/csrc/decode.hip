@@ -111,10 +111,19 @@ __global__ __launch_bounds__(kArtThreads) void art_decode(
 
   // Block k of the traversal: block 0, then n-1, n-2, ..., 1.
   auto block_of = [n](int k) { return k == 0 ? 0 : n - k; };
-  auto chunk_src = [&](const uint16_t* base, int j, int i) {
+  // This thread's chunks of a block: chunk i is row r, 16-byte column cc, at a fixed element
+  // offset from the block's first row; the block's base is uniform, so a load's address is a
+  // scalar base plus that offset.
+  uint32_t coff[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
     const int q = (int)threadIdx.x + i * kArtThreads;
     const int r = q / CH, cc = q - r * CH;
-    return load_nt16(base + ((size_t)j * kArtBlk + r) * rstride + cc * 8);  // read once
+    coff[i] = (uint32_t)(r * rstride + cc * 8);
+  }
+  auto chunk_src = [&](const uint16_t* base, int j, int i) {
+    const uint16_t* blk = base + (size_t)__builtin_amdgcn_readfirstlane(j) * kArtBlk * rstride;
+    return load_nt16(blk + coff[i]);  // read once
   };
   uint4 kr[kArtPrefetch][CPT], vr[kArtPrefetch][CPT];
 #pragma unroll
