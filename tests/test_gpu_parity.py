@@ -15,8 +15,8 @@ import oracle
 from block_sparse_causal_mean_amd import api
 from block_sparse_causal_mean_amd import workloads as wl
 
-from parity import (assert_selection_equal, assert_summaries_equal, check_structure, out_tol,
-                    run_gpu, say)
+from parity import (assert_selection_equal, assert_summaries_equal, bits, check_structure,
+                    out_tol, run_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -577,3 +577,28 @@ def test_tiles_in_blocks_golden_on_gpu(dtype):
     np.testing.assert_array_equal(out["kv_idx"][0, 0], g["kv_idx"])
     np.testing.assert_array_equal(out["kv_cnt"][0, 0], g["kv_cnt"])
     compare_outputs(w, out, inp, api.SA_F32, None)
+
+
+def test_pruning_over_several_survivor_rounds():
+    """Tiles with more than 4096 free blocks, pruned, list their survivors in two rounds of
+    4096 positions: 4160 blocks of 64 keys, one head pair, k = 2.  The whole structure of
+    every tile, and the last tiles (two rounds), the middle ones (one round) and some early,
+    unpruned ones, against oracle.select_tile bit for bit."""
+    w = WL["llama8b_32k"].resized(seqlen=64 * 4160, n_q_heads=1, n_kv_heads=1, head_dim=64,
+                                  k_max=2, k_min=2, q=0.3)
+    inp = wl.make_inputs(w)
+    say(f"[prune rounds] {w.n_blocks} blocks: GPU pipeline")
+    g = run_gpu(w, inp, out_dtype=api.SA_F32)
+    check_structure(w, g["kv_idx"], g["kv_cnt"], g["gate"], g["sigma"], g["sigma_bar"],
+                    g["tau"])
+    cfg = oracle.make_cfg(w)
+    summ = oracle.pool(cfg, inp["K"], inp["V"])
+    assert_summaries_equal(w, g, summ)
+    n = w.n_tiles
+    for t in (3, 40, 64, 2000, 4095, 4097, 4120, n - 2, n - 1):
+        one = oracle.select_tile(cfg, inp["Q"], summ, 0, t)
+        np.testing.assert_array_equal(bits(g["sigma"][0, :, t]), bits(one["sigma"]))
+        tr = int(g["gate"][0, t])
+        np.testing.assert_array_equal(g["kv_cnt"][0, :, t], one["cnts"][tr])
+        np.testing.assert_array_equal(g["kv_idx"][0, :, t, :], one["lists"][tr])
+    say("[prune rounds] sampled tiles equal")
