@@ -421,8 +421,9 @@ constexpr float kAccumC = 0x1p-12f;    // MFMA accumulation plus canonical chain
 // first pass runs the prefilter alone: it brackets every block's (combined) tile score between
 // LB_j = combine(M_j - E_j) and UB_j = combine(M_j + E_j) (M_j the largest approximate row
 // score; combine is the monotone output-aware step or the identity) and keeps UB_j as the
-// block's key.  With U the Rn-th largest UB and D the largest UB_j - LB_j, at least Rn blocks
-// have an exact score >= U - D >= T, so every block with UB_j < T ranks strictly below them and
+// block's key.  With U a value that at least Rn of the UB_j reach (rank_threshold_u32 finds it
+// at or just below the Rn-th largest) and D the largest UB_j - LB_j, at least Rn blocks have
+// an exact score >= U - D >= T, so every block with UB_j < T ranks strictly below them and
 // is dropped (key 0, below every real key); the surviving blocks get their canonical scores as
 // usual (a second prefilter over lists of 32 survivors, then the candidate rows' chains), and
 // the ranking over those keys is the ranking of the full row.  The rounding of M +- E is covered
