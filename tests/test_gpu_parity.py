@@ -373,6 +373,71 @@ def test_forward_any_block_order_and_skipped_entries():
     check(O2, "skipped entries")
 
 
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_per_head_lists_that_differ_between_heads(head_dim):
+    """64-row tiles over 64-key blocks with a list per query head, where the lists of the two
+    query heads of each kv head differ in every way tile by tile: identical, disjoint, nested,
+    one of them empty, or random with a block after the tile and a sentinel before kv_cnt, in
+    shuffled order.  Every row against the fp64 oracle on the same lists (rows of empty lists
+    must be zero)."""
+    w = WL["llama8b_32k"].resized(seqlen=64 * 40, n_q_heads=4, n_kv_heads=2, head_dim=head_dim)
+    inp = wl.make_inputs(w)
+    d = {k: v.cuda() for k, v in inp.items()}
+    n, W = w.n_blocks, 24
+    rng = np.random.default_rng(5)
+    idx = np.full((1, 4, n, W), -1, np.int32)
+    cnt = np.zeros((1, 4, n), np.int32)
+
+    def put(h, t, row, count=None):
+        row = list(row)
+        idx[0, h, t, :len(row)] = row
+        cnt[0, h, t] = len(row) if count is None else count
+
+    for t in range(n):
+        causal = np.arange(t + 1)
+        for pair in (0, 2):
+            mode = (t + pair) % 6
+            pick = rng.permutation(causal)[:min(t + 1, 12)]
+            if mode == 0:  # identical
+                a = b = pick
+            elif mode == 1:  # disjoint
+                a, b = causal[0::2], causal[1::2]
+                a, b = rng.permutation(a)[:W], rng.permutation(b)[:W]
+            elif mode == 2:  # nested
+                a, b = pick, pick[:len(pick) // 2]
+            elif mode == 3:  # the second head's list is empty
+                a, b = pick, []
+            elif mode == 4:  # the first head's list is empty
+                a, b = [], rng.permutation(causal)[:W]
+            else:  # a block after the tile first, then the list, then a sentinel
+                extra = [t + 1] if t + 1 < n else []
+                a = extra + list(pick)
+                b = extra + list(rng.permutation(causal)[:5])
+            put(pair, t, a)
+            if mode == 5:
+                put(pair + 1, t, b, count=min(W, len(b) + 2))
+            else:
+                put(pair + 1, t, b)
+    p = api.problem(w)
+    fws = torch.empty(max(api.forward_workspace_bytes(p), 1), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(w.head_dim)
+    O = torch.empty(1, w.seqlen, 4, w.head_dim, dtype=torch.float32, device="cuda")
+    api.forward(p, d["Q"], d["K"], d["V"], torch.as_tensor(idx).cuda(),
+                torch.as_tensor(cnt).cuda(), W, scale, fws, O, api.SA_F32)
+    torch.cuda.synchronize()
+    cfg = oracle.make_cfg(w)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        O_ref, _ = oracle.forward(cfg, inp["Q"], inp["K"], inp["V"], idx, cnt, scale)
+    got = O.cpu().numpy().astype(np.float64)
+    tile_of_row = np.arange(w.seqlen) // w.tile
+    empty = (cnt[0] == 0)[:, tile_of_row].T  # [N, Hq]: rows whose list is empty
+    err = np.abs(got[0] - O_ref[0])[~empty].max()
+    say(f"[per-head lists d={head_dim}] {int((~empty).sum())} rows, max|O - O_ref| = {err:.3e}; "
+        f"{int(empty.sum())} rows of empty lists")
+    assert err <= out_tol(w, api.SA_F32, O_ref[0][~empty])
+    assert float(np.abs(got[0][empty]).max()) == 0.0
+
+
 def test_runs_are_deterministic():
     w = SMALL["stem_b2_n32"]
     inp = wl.make_inputs(w)
