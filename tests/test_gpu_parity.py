@@ -438,6 +438,72 @@ def test_per_head_lists_that_differ_between_heads(head_dim):
     assert float(np.abs(got[0][empty]).max()) == 0.0
 
 
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_lists_that_differ_between_the_two_tiles_of_a_block(head_dim):
+    """64-row tiles inside 128-key blocks: the two tiles of a block have lists of their own,
+    which tile pair by tile pair are identical, disjoint, nested, one of them empty, or random
+    with a block after the tile and a sentinel before kv_cnt, in shuffled order.  Every row
+    against the fp64 oracle on the same lists (rows of empty lists must be zero)."""
+    w = WL["prefill_128k_t64"].resized(seqlen=128 * 24, n_q_heads=2, n_kv_heads=1,
+                                       head_dim=head_dim)
+    assert w.tile == 64 and w.block == 128
+    inp = wl.make_inputs(w)
+    d = {k: v.cuda() for k, v in inp.items()}
+    nt, W = w.n_tiles, 20
+    rng = np.random.default_rng(6)
+    idx = np.full((1, 2, nt, W), -1, np.int32)
+    cnt = np.zeros((1, 2, nt), np.int32)
+
+    def put(h, t, row, count=None):
+        row = list(row)
+        idx[0, h, t, :len(row)] = row
+        cnt[0, h, t] = len(row) if count is None else count
+
+    for h in range(2):
+        for blk in range(nt // 2):
+            t0, t1 = 2 * blk, 2 * blk + 1
+            causal = np.arange(blk + 1)  # the free blocks before the diagonal one, and it
+            mode = (blk + h) % 6
+            pick = rng.permutation(causal)[:min(blk + 1, 10)]
+            extra = [blk + 1] if blk + 1 < nt // 2 else []
+            if mode == 0:  # identical
+                a = b = pick
+            elif mode == 1:  # disjoint
+                a, b = causal[0::2], causal[1::2]
+            elif mode == 2:  # nested
+                a, b = pick, pick[:len(pick) // 2]
+            elif mode == 3:  # the second tile's list is empty
+                a, b = pick, []
+            elif mode == 4:  # the first tile's list is empty
+                a, b = [], rng.permutation(causal)[:W]
+            else:  # a block after the tiles first, then the list, then a sentinel
+                a = extra + list(pick)
+                b = extra + list(rng.permutation(causal)[:4])
+            put(h, t0, rng.permutation(np.array(a, np.int64)) if len(a) else [])
+            if mode == 5:
+                put(h, t1, b, count=min(W, len(b) + 2))
+            else:
+                put(h, t1, rng.permutation(np.array(b, np.int64)) if len(b) else [])
+    p = api.problem(w)
+    fws = torch.empty(max(api.forward_workspace_bytes(p), 1), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(w.head_dim)
+    O = torch.empty(1, w.seqlen, 2, w.head_dim, dtype=torch.float32, device="cuda")
+    api.forward(p, d["Q"], d["K"], d["V"], torch.as_tensor(idx).cuda(),
+                torch.as_tensor(cnt).cuda(), W, scale, fws, O, api.SA_F32)
+    torch.cuda.synchronize()
+    cfg = oracle.make_cfg(w)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        O_ref, _ = oracle.forward(cfg, inp["Q"], inp["K"], inp["V"], idx, cnt, scale)
+    got = O.cpu().numpy().astype(np.float64)
+    tile_of_row = np.arange(w.seqlen) // w.tile
+    empty = (cnt[0] == 0)[:, tile_of_row].T  # [N, Hq]: rows whose list is empty
+    err = np.abs(got[0] - O_ref[0])[~empty].max()
+    say(f"[tile-pair lists d={head_dim}] {int((~empty).sum())} rows, max|O - O_ref| = "
+        f"{err:.3e}; {int(empty.sum())} rows of empty lists")
+    assert err <= out_tol(w, api.SA_F32, O_ref[0][~empty])
+    assert float(np.abs(got[0][empty]).max()) == 0.0
+
+
 def test_runs_are_deterministic():
     w = SMALL["stem_b2_n32"]
     inp = wl.make_inputs(w)
