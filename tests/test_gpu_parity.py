@@ -572,6 +572,57 @@ def test_forward_long_lists_in_segments(name):
         assert float(O[0, 5 * w.block:6 * w.block].abs().max()) == 0.0
 
 
+@pytest.mark.parametrize("W", [200, 600])
+def test_long_lists_of_64_row_tiles_in_128_key_blocks(W):
+    """64-row tiles inside 128-key blocks with long lists: dense causal lists cut to W entries,
+    ascending for one head and descending for the other, on both tiles of several blocks.
+    W = 200 keeps both tiles' lists within the kernel's staging area, so a block's two tiles
+    share one workgroup over the union of their lists; W = 600 does not, so each tile runs
+    alone with its list consumed in segments.  Sampled rows against the fp64 oracle."""
+    n = 600  # key blocks
+    w = WL["prefill_128k_t64"].resized(seqlen=n * 128, n_q_heads=2, n_kv_heads=1)
+    assert w.tile == 64 and w.block == 128
+    nt = w.n_tiles
+    inp = wl.make_inputs(w)
+    d = {k: v.cuda() for k, v in inp.items()}
+    p = api.problem(w)
+    fws = torch.empty(max(api.forward_workspace_bytes(p), 1), dtype=torch.uint8, device="cuda")
+    cfg = oracle.make_cfg(w)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    blocks = [n - 1, 420, 257, 100, 3]
+    idx = np.full((1, 2, nt, W), -1, np.int32)
+    cnt = np.zeros((1, 2, nt), np.int32)
+    for h in range(2):
+        for b in blocks:
+            row = list(range(b + 1))
+            if h == 1:
+                row = row[::-1]
+            row = row[:W]
+            for t in (2 * b, 2 * b + 1):
+                idx[0, h, t, :len(row)] = row
+                cnt[0, h, t] = len(row)
+    O = torch.empty(1, w.seqlen, 2, w.head_dim, dtype=torch.float32, device="cuda")
+    api.forward(p, d["Q"], d["K"], d["V"], torch.as_tensor(idx).cuda(),
+                torch.as_tensor(cnt).cuda(), W, scale, fws, O, api.SA_F32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    rows = []
+    for b in blocks:
+        for t in (2 * b, 2 * b + 1):
+            for h in range(2):
+                for r in (0, w.tile - 1, int(rng.integers(w.tile))):
+                    rows.append((0, h, t * w.tile + r))
+    rows = np.array(rows, np.int64)
+    O_ref, _ = oracle.forward(cfg, inp["Q"], inp["K"], inp["V"], idx, cnt, scale, rows=rows)
+    r = torch.as_tensor(rows, device="cuda")
+    got = O[r[:, 0], r[:, 2], r[:, 1]].cpu().numpy().astype(np.float64)
+    err = np.abs(got - O_ref).max()
+    say(f"[t64 long lists W={W}] {len(rows)} rows, max|O - O_ref| = {err:.3e}")
+    assert err <= out_tol(w, api.SA_F32, O_ref)
+    # rows of tiles with empty lists are zero
+    assert float(O[0, 5 * w.tile:6 * w.tile].abs().max()) == 0.0
+
+
 def test_fixed_gate_with_calibrated_tau_reproduces_the_quantile_gate():
     """A fixed threshold calibrated on an input (the per-call quantile's tau) gives that
     input the same gate, lists and counts as the quantile gate; the fixed-gate run also
