@@ -536,6 +536,31 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     return OAM ? summ[vn_off + ((size_t)b * n + j) * dm.Hkv + g] : 0.0f;
   };
 
+  // Canonical chain of query row `row` against the bound backbone's block whose fp32 planes
+  // start at xk (kmin plane 0, kmax plane 1, chunk-major): x_c = (q_c >= 0 ? kmax_c : kmin_c),
+  // one fused multiply-add per coordinate in order.
+  auto chain_bound = [&](const float* xk, int row) -> float {
+    const uint16_t* qr = qs + (size_t)row * QS;
+    const uint16_t* qn = qs + (size_t)(TILE + row) * QS;
+    float sv = 0.0f;
+#pragma unroll 2
+    for (int c0 = 0; c0 < D; c0 += 8) {
+      uint4 qv = *reinterpret_cast<const uint4*>(qr + c0);
+      const uint4 q2 = *reinterpret_cast<const uint4*>(qn + c0);
+      qv.x |= q2.x; qv.y |= q2.y; qv.z |= q2.z; qv.w |= q2.w;
+      const float4 x0 = *reinterpret_cast<const float4*>(xk + (c0 / 8) * 256);
+      const float4 x1 = *reinterpret_cast<const float4*>(xk + (c0 / 8) * 256 + 4);
+      const float4 y0 = *reinterpret_cast<const float4*>(xk + (D / 8 + c0 / 8) * 256);
+      const float4 y1 = *reinterpret_cast<const float4*>(xk + (D / 8 + c0 / 8) * 256 + 4);
+      const float q8[8] = {bf16_lo(qv.x), bf16_hi(qv.x), bf16_lo(qv.y), bf16_hi(qv.y),
+                           bf16_lo(qv.z), bf16_hi(qv.z), bf16_lo(qv.w), bf16_hi(qv.w)};
+      const float xa[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      const float xb[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sv = __builtin_fmaf(q8[k], q8[k] >= 0.0f ? xb[k] : xa[k], sv);
+    }
+    return sv;
+  };
   // The order key of block j = 32 c + sl's canonical (combined) tile score, on lanes hi == 0
   // of valid blocks: the prefilter's candidate rows, then their canonical fp32 chains.
   auto exact_key = [&](int c, int sl, bool valid) -> unsigned {
@@ -630,32 +655,7 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
       const int bit = __builtin_ctzll(cand);
       cand &= cand - 1;
       const int row = 32 * (bit >> 4) + 8 * ((bit & 15) >> 2) + 4 * hi + (bit & 3);
-      const uint16_t* qr = qs + (size_t)row * QS;
-      const uint16_t* qn = qs + (size_t)(TILE + row) * QS;
-      float sv = 0.0f;
-#pragma unroll 2
-      for (int c0 = 0; c0 < D; c0 += 8) {
-        uint4 qv = *reinterpret_cast<const uint4*>(qr + c0);
-        if (MODE == SA_KMINMAX) {
-          const uint4 q2 = *reinterpret_cast<const uint4*>(qn + c0);
-          qv.x |= q2.x; qv.y |= q2.y; qv.z |= q2.z; qv.w |= q2.w;
-        }
-        const float4 x0 = *reinterpret_cast<const float4*>(xk + (c0 / 8) * 256);
-        const float4 x1 = *reinterpret_cast<const float4*>(xk + (c0 / 8) * 256 + 4);
-        const float q8[8] = {bf16_lo(qv.x), bf16_hi(qv.x), bf16_lo(qv.y), bf16_hi(qv.y),
-                             bf16_lo(qv.z), bf16_hi(qv.z), bf16_lo(qv.w), bf16_hi(qv.w)};
-        float xa[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        if (MODE == SA_KMINMAX) {
-          const float4 y0 = *reinterpret_cast<const float4*>(xk + (D / 8 + c0 / 8) * 256);
-          const float4 y1 = *reinterpret_cast<const float4*>(xk + (D / 8 + c0 / 8) * 256 + 4);
-          const float xb[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-#pragma unroll
-          for (int k = 0; k < 8; ++k) xa[k] = q8[k] >= 0.0f ? xb[k] : xa[k];
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) sv = __builtin_fmaf(q8[k], xa[k], sv);
-      }
-      best = fmaxf(best, sv);
+      best = fmaxf(best, chain_bound(xk, row));
     }
     }
     best = fmaxf(best, __shfl_xor(best, 32));
@@ -724,7 +724,80 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
   // uniform over the workgroup: kept in a scalar register
   qmax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_sqrtf(qmax2))));
 
-  if constexpr (!PRUNE) {
+  if constexpr (!PRUNE && MODE == SA_KMINMAX && !GRP && RT <= 2) {
+    // The bound backbone on tiles of up to 64 rows: pairs of aligned 32-block chunks covering
+    // [j0, d0), dealt to the waves.  Both lanes of a block hold half of its rows' approximate
+    // scores, and nearly every block has a single candidate row, so one chunk at a time would
+    // leave one lane of each pair idle through the canonical chains.  With two chunks per pass,
+    // lane hi = 0 runs the chains of its block in the first chunk and lane hi = 1 those of its
+    // block in the second, each over the candidate rows of both halves (the same rows and the
+    // same chains as one chunk at a time).
+    for (int ch = (j0 >> 5) + 2 * wv; ch * 32 < d0; ch += 2 * (kScoreThreads / 64)) {
+      const bool has_b = (ch + 1) * 32 < d0;  // wave-uniform: the second chunk has free blocks
+      // Candidate rows of chunk c's block l32 among this lane's half (bit 16 rt + v: row
+      // 32 rt + 8 (v >> 2) + 4 hi + (v & 3)).
+      auto cand_mask = [&](int c) -> unsigned {
+        const int jj = 32 * c + l32;
+        const bool vv = jj >= j0 && jj < d0;
+        f32x16 acc[RT];
+        approx(c, l32, acc);
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, acc[rt][v]);
+        const float M = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const float thr = M - 2.0f * err_bound(jj, vv);
+        unsigned m = 0u;
+        if (vv) {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (acc[rt][v] >= thr) m |= 1u << (rt * 16 + v);
+        }
+        return m;
+      };
+      const unsigned ma = cand_mask(ch);
+      __builtin_amdgcn_sched_barrier(0);
+      const unsigned mb = has_b ? cand_mask(ch + 1) : 0u;
+      __builtin_amdgcn_sched_barrier(0);
+      // v_permlane32_swap(x, x): the partner's value is the first result in lanes 32-63 and
+      // the second in lanes 0-31.
+      const auto sa = __builtin_amdgcn_permlane32_swap(ma, ma, false, false);
+      const auto sb = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
+      const unsigned pa = hi ? sa[0] : sa[1], pb = hi ? sb[0] : sb[1];
+      unsigned r0 = hi ? pb : ma;  // this lane's block: candidates among the rows of half 0
+      unsigned r1 = hi ? mb : pa;  // and of half 1
+      const int cm = ch + hi;
+      const int j = 32 * cm + l32;
+      const bool valid = j >= j0 && j < d0;
+      const float* xk = xc + (chunk0 + cm) * XC + l32 * 8;
+      float best = -INFINITY;
+      while (r0 | r1) {
+        int bit, half;
+        if (r0) {
+          bit = __builtin_ctz(r0);
+          r0 &= r0 - 1u;
+          half = 0;
+        } else {
+          bit = __builtin_ctz(r1);
+          r1 &= r1 - 1u;
+          half = 1;
+        }
+        const int row = 32 * (bit >> 4) + 8 * ((bit & 15) >> 2) + 4 * half + (bit & 3);
+        best = fmaxf(best, chain_bound(xk, row));
+      }
+      if (valid) {
+        const unsigned ok = order_key(oam_combine<OAM>(canon(best), value_norm(j), dm));
+        if (compact) {
+          kq[j - j0] = ok;
+        } else {
+          keys[j - j0] = ((unsigned long long)ok << 32) | (0xffffffffu - (unsigned)j);
+        }
+      }
+    }
+  } else if constexpr (!PRUNE) {
     // Every free block: aligned 32-block chunks covering [j0, d0), dealt to the waves.
     for (int ch = (j0 >> 5) + wv; ch * 32 < d0; ch += kScoreThreads / 64) {
       const int j = ch * 32 + l32;  // this lane's block
