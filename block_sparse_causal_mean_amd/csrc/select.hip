@@ -37,6 +37,8 @@
 // sigma_bar = sum over units in order divided by their count; the quantile rank
 // ceil(q * M) in fp64.
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace sa {
@@ -561,6 +563,24 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
     }
     return sv;
   };
+  // Canonical chain of query row `row` against the mean-pooled block whose fp32 summary starts
+  // at xk (chunk-major): one fused multiply-add per coordinate in order.
+  auto chain_mean = [&](const float* xk, int row) -> float {
+    const uint16_t* qr = qs + (size_t)row * QS;
+    float sv = 0.0f;
+#pragma unroll 2
+    for (int c0 = 0; c0 < D; c0 += 8) {
+      const uint4 qv = *reinterpret_cast<const uint4*>(qr + c0);
+      const float4 x0 = *reinterpret_cast<const float4*>(xk + (c0 / 8) * 256);
+      const float4 x1 = *reinterpret_cast<const float4*>(xk + (c0 / 8) * 256 + 4);
+      const float q8[8] = {bf16_lo(qv.x), bf16_hi(qv.x), bf16_lo(qv.y), bf16_hi(qv.y),
+                           bf16_lo(qv.z), bf16_hi(qv.z), bf16_lo(qv.w), bf16_hi(qv.w)};
+      const float xa[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sv = __builtin_fmaf(q8[k], xa[k], sv);
+    }
+    return sv;
+  };
   // The order key of block j = 32 c + sl's canonical (combined) tile score, on lanes hi == 0
   // of valid blocks: the prefilter's candidate rows, then their canonical fp32 chains.
   auto exact_key = [&](int c, int sl, bool valid) -> unsigned {
@@ -724,19 +744,30 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
   // uniform over the workgroup: kept in a scalar register
   qmax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_sqrtf(qmax2))));
 
-  if constexpr (!PRUNE && MODE == SA_KMINMAX && !GRP && RT <= 2) {
-    // The bound backbone on tiles of up to 64 rows: pairs of aligned 32-block chunks covering
-    // [j0, d0), dealt to the waves.  Both lanes of a block hold half of its rows' approximate
-    // scores, and nearly every block has a single candidate row, so one chunk at a time would
-    // leave one lane of each pair idle through the canonical chains.  With two chunks per pass,
-    // lane hi = 0 runs the chains of its block in the first chunk and lane hi = 1 those of its
-    // block in the second, each over the candidate rows of both halves (the same rows and the
-    // same chains as one chunk at a time).
+  if constexpr (!PRUNE && !GRP) {
+    // Pairs of aligned 32-block chunks covering [j0, d0), dealt to the waves.  Both lanes of a
+    // block hold half of its rows' approximate scores, and nearly every block has a single
+    // candidate row, so one chunk at a time would leave one lane of each pair idle through the
+    // canonical chains.  With two chunks per pass, lane hi = 0 runs the chains of its block in
+    // the first chunk and lane hi = 1 those of its block in the second, each over the
+    // candidate rows of both halves (the same rows and the same chains as one chunk at a time).
+    using Mask = std::conditional_t<RT <= 2, unsigned, unsigned long long>;
+    auto partner = [&](Mask m) -> Mask {  // the value of lane l ^ 32 (v_permlane32_swap)
+      const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)m, (unsigned)m, false, false);
+      const unsigned plo = hi ? lo[0] : lo[1];
+      if constexpr (RT <= 2) {
+        return plo;
+      } else {
+        const unsigned mh = (unsigned)(m >> 32);
+        const auto up = __builtin_amdgcn_permlane32_swap(mh, mh, false, false);
+        return ((unsigned long long)(hi ? up[0] : up[1]) << 32) | plo;
+      }
+    };
     for (int ch = (j0 >> 5) + 2 * wv; ch * 32 < d0; ch += 2 * (kScoreThreads / 64)) {
       const bool has_b = (ch + 1) * 32 < d0;  // wave-uniform: the second chunk has free blocks
       // Candidate rows of chunk c's block l32 among this lane's half (bit 16 rt + v: row
       // 32 rt + 8 (v >> 2) + 4 hi + (v & 3)).
-      auto cand_mask = [&](int c) -> unsigned {
+      auto cand_mask = [&](int c) -> Mask {
         const int jj = 32 * c + l32;
         const bool vv = jj >= j0 && jj < d0;
         f32x16 acc[RT];
@@ -748,27 +779,23 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
           for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, acc[rt][v]);
         const float M = fmaxf(mloc, __shfl_xor(mloc, 32));
         const float thr = M - 2.0f * err_bound(jj, vv);
-        unsigned m = 0u;
+        Mask m = 0;
         if (vv) {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-              if (acc[rt][v] >= thr) m |= 1u << (rt * 16 + v);
+              if (acc[rt][v] >= thr) m |= (Mask)1 << (rt * 16 + v);
         }
         return m;
       };
-      const unsigned ma = cand_mask(ch);
+      const Mask ma = cand_mask(ch);
       __builtin_amdgcn_sched_barrier(0);
-      const unsigned mb = has_b ? cand_mask(ch + 1) : 0u;
+      const Mask mb = has_b ? cand_mask(ch + 1) : (Mask)0;
       __builtin_amdgcn_sched_barrier(0);
-      // v_permlane32_swap(x, x): the partner's value is the first result in lanes 32-63 and
-      // the second in lanes 0-31.
-      const auto sa = __builtin_amdgcn_permlane32_swap(ma, ma, false, false);
-      const auto sb = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
-      const unsigned pa = hi ? sa[0] : sa[1], pb = hi ? sb[0] : sb[1];
-      unsigned r0 = hi ? pb : ma;  // this lane's block: candidates among the rows of half 0
-      unsigned r1 = hi ? mb : pa;  // and of half 1
+      const Mask pa = partner(ma), pb = partner(mb);
+      Mask r0 = hi ? pb : ma;  // this lane's block: candidates among the rows of half 0
+      Mask r1 = hi ? mb : pa;  // and of half 1
       const int cm = ch + hi;
       const int j = 32 * cm + l32;
       const bool valid = j >= j0 && j < d0;
@@ -777,16 +804,19 @@ __global__ __launch_bounds__(kScoreThreads, 3) void score_rank_mfma(
       while (r0 | r1) {
         int bit, half;
         if (r0) {
-          bit = __builtin_ctz(r0);
-          r0 &= r0 - 1u;
+          bit = (int)__builtin_ctzll((unsigned long long)r0);
+          r0 &= r0 - 1;
           half = 0;
         } else {
-          bit = __builtin_ctz(r1);
-          r1 &= r1 - 1u;
+          bit = (int)__builtin_ctzll((unsigned long long)r1);
+          r1 &= r1 - 1;
           half = 1;
         }
         const int row = 32 * (bit >> 4) + 8 * ((bit & 15) >> 2) + 4 * half + (bit & 3);
-        best = fmaxf(best, chain_bound(xk, row));
+        if constexpr (MODE == SA_KMINMAX)
+          best = fmaxf(best, chain_bound(xk, row));
+        else
+          best = fmaxf(best, chain_mean(xk, row));
       }
       if (valid) {
         const unsigned ok = order_key(oam_combine<OAM>(canon(best), value_norm(j), dm));
