@@ -607,7 +607,7 @@ __device__ __forceinline__ void stage_segment(const int32_t* __restrict__ list,
 // mask in bits 16-17 (bit 16 + k: list k has it), in ascending block order; the waves of a
 // tile skip the products of the blocks their tile's list does not have, so each tile attends
 // to exactly its own blocks.  Built as a bitmap of the causal blocks per list in `scratch`
-// (2 * ceil(dend / 32) + 2 ints, at most 4 KiB), then compacted by wave 0.  seg_info as
+// (2 * ceil(dend / 32) + 2 ints, just over 4 KiB at 16384 blocks), then compacted by wave 0.  seg_info as
 // stage_segment's, one segment.  The host uses this only when both lists together fit in
 // LCAP entries (2 W <= LCAP).
 template <int LCAP>
@@ -769,7 +769,9 @@ __device__ void stage_vs(const int32_t* __restrict__ vrow, int nv,
 
 // D head dim, QH 32-row query groups per wave, NW waves per workgroup; VS: the tile's list
 // comes from a vertical-slash index (stage_vs) instead of kv_idx / kv_cnt; HPW query heads
-// per workgroup (2: consecutive query heads of one kv head, which share their lists).
+// per workgroup (2: consecutive query heads of one kv head, which share their lists); TPW
+// 64-row tiles per workgroup (2: the two tiles of a 128-key block, streamed as the union of
+// their lists, stage_union).
 template <int D, int QH, int NW, bool VS, int HPW, int KB, int TPW>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf16(
