@@ -251,18 +251,27 @@ struct Cfg {
   static constexpr int DT = D / 32;            // 32-coordinate tiles of O^T
   static constexpr int KSLOT = kStep * D * 2;  // bytes of a K step image
   static constexpr int VSLOT = D * kStep * 2;  // bytes of a V^T step image
-  // Ring slots (a K and a V^T image each).  Three for 4-wave workgroups (three workgroups
-  // per CU); two for 2-wave workgroups, whose 32 KiB ring lets four of them share a CU
-  // instead of three (measured 8-12% faster on 64-row tiles despite the shallower ring).
-  static constexpr int NR = NW == 2 ? 2 : 3;
+  // 4-wave workgroups: a ring of NR = 3 slots, each a K and a V^T image, refilled a whole
+  // slot at a time (three workgroups per CU).
+  // 2-wave workgroups (SPLIT): a ring of three single images, K and V^T of consecutive steps
+  // in turn (image 2i is step i's K, image 2i + 1 its V^T, image m in buffer m % 3).  Step i's
+  // K buffer is refilled with step i + 1's V^T once every wave's S products are done, and
+  // step i's V^T buffer with step i + 2's K once its P V^T products are, so each image still
+  // has a whole step to land, in 24 KiB instead of the 32 KiB of two full slots: six such
+  // workgroups share a CU (three waves per SIMD) instead of four.
+  static constexpr bool SPLIT = NW == 2;
+  static constexpr int NR = SPLIT ? 2 : 3;
+  static constexpr int RING = SPLIT ? 3 * KSLOT : NR * (KSLOT + VSLOT);  // bytes
   static constexpr int KREG = KSLOT / 1024;    // 1 KiB load regions per image
   static constexpr int VREG = VSLOT / 1024;
   static constexpr int LPW = (KREG + VREG) / NW;  // loads per wave per refill group
+  static constexpr int LPI = KREG / NW;           // loads per wave per image (SPLIT)
   static_assert(KREG % NW == 0 && VREG % NW == 0, "load regions must split evenly");
+  static_assert(!SPLIT || KSLOT == VSLOT, "split-ring buffers hold either image");
   static constexpr int LCAP = 512;             // list entries staged in LDS per segment
-  // Waves per SIMD the register allocation must allow: three for 32-row waves in 4-wave
-  // workgroups (168 registers), two otherwise (256).
-  static constexpr int WPE = QH == 1 && NW == 4 ? 3 : 2;
+  // Waves per SIMD the register allocation must allow: three for 32-row waves (168
+  // registers), two for 64-row waves (256).
+  static constexpr int WPE = QH == 1 ? 3 : 2;
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -358,12 +367,15 @@ __device__ __forceinline__ void step_scores(const uint32_t (&ka_addr)[D / 16], u
 }
 
 // Online softmax of one step's logits (masked on the diagonal block) and O^T += V^T P^T.
-// va_addr as ka_addr in step_scores (slot 0, loop-invariant), slotoff the step's slot.
-template <int D, int QH>
+// va_addr as ka_addr in step_scores (slot 0, loop-invariant), slotoff the offset of the step's
+// V^T image from there.  pre_pv() runs between the softmax and the first V^T operand read
+// (a split ring's wait for that image).
+template <int D, int QH, typename PrePv>
 __device__ __forceinline__ void step_softmax_pv(f32x16 (&s)[QH], const uint32_t (&va_addr)[2],
                                                 uint32_t slotoff, WaveState<D, QH>& st,
                                                 bool diag, int kbase, int qbase, int hi,
-                                                float scale_log2, float lazy_raw) {
+                                                float scale_log2, float lazy_raw,
+                                                PrePv&& pre_pv) {
   constexpr int DT = D / 32;
   // Lane value v of s[qh] is key kbase + 8 (v >> 2) + 4 hi + (v & 3) of the tile, query row
   // qbase + 32 qh (+ lane % 32).
@@ -435,6 +447,7 @@ __device__ __forceinline__ void step_softmax_pv(f32x16 (&s)[QH], const uint32_t 
     const int dt = i >> 1, half = i & 1;
     return lds_read<f16x8>(va_addr[half] + slotoff + dt * 2048);
   };
+  pre_pv();
   f16x8 va[PD];
 #pragma unroll
   for (int i = 0; i < PD; ++i) va[i] = vload(i);
@@ -790,7 +803,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
   constexpr int LPW = C::LPW;
   // Ring of NR slots, each a K step image followed by a V^T step image.
   constexpr int SLOT = C::KSLOT + C::VSLOT;
-  __shared__ __attribute__((aligned(1024))) char ring[C::NR * SLOT];
+  __shared__ __attribute__((aligned(1024))) char ring[C::RING];
   __shared__ int lst[C::LCAP];
   // usable entries, position of diagonal block d0, next entry, done, position of d0 + 1
   __shared__ int seg_info[5];
@@ -873,8 +886,10 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
       ka_addr[c] = ring0 + ((uint32_t)koff ^ (32u * c));
       asm volatile("" : "+v"(ka_addr[c]));
     }
-    va_addr[0] = ring0 + C::KSLOT + (uint32_t)voff;
-    va_addr[1] = ring0 + C::KSLOT + ((uint32_t)voff ^ 32u);
+    // (a split ring's buffers hold either image: V^T offsets then start at the ring's base)
+    const uint32_t vbase0 = ring0 + (C::SPLIT ? 0u : (uint32_t)C::KSLOT);
+    va_addr[0] = vbase0 + (uint32_t)voff;
+    va_addr[1] = vbase0 + ((uint32_t)voff ^ 32u);
     asm volatile("" : "+v"(va_addr[0]), "+v"(va_addr[1]));
   }
   // Per-lane source offsets (elements, relative to a step's first key row) of this wave's K
@@ -901,7 +916,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
                            2 * t, w, lane, lst, seg_info, reinterpret_cast<int*>(ring));
     } else {
       stage_segment<C::LCAP>(list, kv_cnt, cnt, bht, dm, h, t, W, seg_start, w, lane, lst,
-                             seg_info, reinterpret_cast<int*>(ring), C::NR * SLOT / 4);
+                             seg_info, reinterpret_cast<int*>(ring), C::RING / 4);
     }
     const int U = seg_info[0], diag_e = seg_info[1], next_start = seg_info[2];
     const int diag_e2 = KB ? seg_info[4] : -1;  // second diagonal block (128-row tiles)
@@ -909,9 +924,9 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
     const int nsteps = U * NSUB;
 
     if (nsteps > 0) {
-      // Refill group m: K step m and V step m into ring slot m % NR.  Steps past the end reload
-      // the last step (valid memory, into a slot nobody reads again) so that every group
-      // issues the same LPW loads per wave, which the partial waits below count on.
+      // Refills: steps past the end reload the last step (valid memory, into a slot or buffer
+      // nobody reads again) so that every refill issues the same loads per wave, which the
+      // partial waits below count on.
       // Scalar address arithmetic is kept to 32-bit unsigned sums and shifts: byte offsets
       // within this (batch, kv head)'s K rows and V^T images are below 2^32 (the host checks
       // N * Hkv * d * 2 < 2^32), and the ring slots of a step are carried, not divided out.
@@ -926,68 +941,137 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
         const int x = lst[min(m, last) / NSUB];
         return TPW == 2 ? x & 0xffff : x;
       };
-      auto issue = [&](uint32_t m, int jv, uint32_t slot_idx) {
+      // K step m's and V^T step m's global sources (scalar bases) for block jv
+      auto k_src = [&](uint32_t m, int jv) {
         const uint32_t a = min(m, last);
         const uint32_t j = (uint32_t)__builtin_amdgcn_readfirstlane(jv);  // uniform: SGPR
-        const uint32_t sub = a % NSUB;
-        const char* kb = kbase + (j * kblk_bytes + sub * kstep_bytes);
-        const char* vb = vbase + (j * NSUB + sub) * (uint32_t)C::VSLOT;
-        // the slot base is re-derived here rather than kept per slot in scalar registers
-        // across the unrolled loop
+        return kbase + (j * kblk_bytes + (a % NSUB) * kstep_bytes);
+      };
+      auto v_src = [&](uint32_t m, int jv) {
+        const uint32_t a = min(m, last);
+        const uint32_t j = (uint32_t)__builtin_amdgcn_readfirstlane(jv);
+        return vbase + (j * NSUB + a % NSUB) * (uint32_t)C::VSLOT;
+      };
+      // LDS byte offset of this wave's first region in the ring at `off`; the ring base is
+      // re-derived here rather than kept per slot in scalar registers across the unrolled loop
+      auto ring_dst = [&](uint32_t off) {
         uint32_t rb = ring_lds;
         asm volatile("" : "+s"(rb));
-        const uint32_t dst = rb + slot_idx * SLOT + w * 1024;
+        return rb + off + w * 1024;
+      };
+      auto issue_k = [&](uint32_t m, int jv, uint32_t off) {
+        const char* kb = k_src(m, jv);
+        const uint32_t dst = ring_dst(off);
 #pragma unroll
         for (int k = 0; k < C::KREG / NW; ++k) dma16(kb, kgo[k], dst + NW * k * 1024);
-#pragma unroll
-        for (int k = 0; k < C::VREG / NW; ++k)
-          dma16(vb + NW * k * 1024, vlo, dst + C::KSLOT + NW * k * 1024);
       };
+      auto issue_v = [&](uint32_t m, int jv, uint32_t off) {
+        const char* vb = v_src(m, jv);
+        const uint32_t dst = ring_dst(off);
 #pragma unroll
-      for (int m = 0; m < C::NR - 1; ++m) issue(m, entry_of(m), m);
-      int jn = entry_of(C::NR - 1);  // block of the next group, read one step early
+        for (int k = 0; k < C::VREG / NW; ++k) dma16(vb + NW * k * 1024, vlo, dst + NW * k * 1024);
+      };
+      // Step i's geometry for this wave: whether it computes the step at all, whether the step
+      // lies on a diagonal block (masked), and its key offset from the tile's first row there.
+      struct StepGeo {
+        bool run, diag;
+        int kofs;
+      };
+      auto geometry = [&](uint32_t i) {
+        const int e = (int)(i / NSUB), sub = (int)(i % NSUB);
+        // key offset of the step from the tile's first row, on the diagonal blocks (the
+        // second one starts BLK keys in); -1 elsewhere
+        int kofs;
+        bool diag;
+        if constexpr (KB == 0) {
+          diag = e == diag_e;
+          kofs = sub * kStep;
+        } else if constexpr (KB < ROWS) {
+          kofs = e == diag_e ? sub * kStep : (e == diag_e2 ? BLK + sub * kStep : -1);
+          diag = kofs >= 0;
+        } else {  // the tile's rows lie inside its diagonal block, rowoff keys in: steps
+                  // wholly before them need no mask
+          kofs = sub * kStep - rowoff;
+          diag = e == diag_e && kofs > -kStep;
+        }
+        // On a diagonal block, a step whose first key lies after this wave's last row is
+        // fully masked for the wave: skip it.
+        // With the union of two tiles' lists, a block the wave's tile did not select.
+        const bool other =
+            TPW == 2 && !((__builtin_amdgcn_readfirstlane(lst[e]) >> (16 + pb)) & 1);
+        return StepGeo{!other && (!diag || kofs < kStep * QH * (wr + 1)), diag, kofs};
+      };
 
-      // Step i (slot i % NR): wait until group i has landed (groups i+1 .. i+NR-2 may still be
-      // in flight), barrier (every wave's part of group i is in, and every wave is done with
-      // step i-1, whose slot the new group overwrites), issue group i+NR-1, then compute step i.
-      // The loop is unrolled by NR, so each step's slot (read and refilled) is a compile-time
-      // constant.
-      for (uint32_t i0 = 0; i0 <= last; i0 += C::NR) {
+      if constexpr (C::SPLIT) {
+        // Image m in buffer m % 3 (2i: step i's K, 2i + 1: its V^T).  Step i: wait for its K
+        // (its V^T may still be in flight), barrier (every wave's part of the K image is in,
+        // and every wave is done with step i-1's P V^T products, whose buffer the next K
+        // overwrites), issue step i+1's K, S products and softmax; then wait for its V^T
+        // (step i+1's K may still be in flight), barrier (every wave is done with step i's S
+        // products), issue step i+1's V^T into step i's K buffer, P V^T products.  A wave that
+        // skips the step still takes part in both barriers and issues.  Unrolled by 3, so
+        // every buffer is a compile-time constant.
+        constexpr uint32_t IB = (uint32_t)C::KSLOT;
+        issue_k(0, entry_of(0), 0);
+        issue_v(0, entry_of(0), IB);
+        int jn = entry_of(1);  // block of step i + 1
+        for (uint32_t i0 = 0; i0 <= last; i0 += 3) {
 #pragma unroll
-        for (int r = 0; r < C::NR; ++r) {
-          const uint32_t i = i0 + r;
-          if (i > last) break;
-          wait_vm<(C::NR - 2) * LPW>();
-          barrier_only();
-          issue(i + C::NR - 1, jn, (uint32_t)((r + C::NR - 1) % C::NR));
-          jn = entry_of(i + C::NR);
-          const uint32_t slotoff = (uint32_t)(r * SLOT);
-          const int e = (int)(i / NSUB), sub = (int)(i % NSUB);
-          // key offset of the step from the tile's first row, on the diagonal blocks (the
-          // second one starts BLK keys in); -1 elsewhere
-          int kofs;
-          bool diag;
-          if constexpr (KB == 0) {
-            diag = e == diag_e;
-            kofs = sub * kStep;
-          } else if constexpr (KB < ROWS) {
-            kofs = e == diag_e ? sub * kStep : (e == diag_e2 ? BLK + sub * kStep : -1);
-            diag = kofs >= 0;
-          } else {  // the tile's rows lie inside its diagonal block, rowoff keys in: steps
-                    // wholly before them need no mask
-            kofs = sub * kStep - rowoff;
-            diag = e == diag_e && kofs > -kStep;
+          for (int r = 0; r < 3; ++r) {
+            const uint32_t i = i0 + r;
+            if (i > last) break;
+            wait_vm<C::LPI>();
+            barrier_only();
+            issue_k(i + 1, jn, (uint32_t)((2 * r + 2) % 3) * IB);
+            auto pre_pv = [&] {
+              wait_vm<C::LPI>();
+              barrier_only();
+              issue_v(i + 1, jn, (uint32_t)((2 * r) % 3) * IB);
+              jn = entry_of(i + 2);
+            };
+            const StepGeo gs = geometry(i);
+            if (gs.run) {
+              f32x16 sc[QH];
+              step_scores<D, QH>(ka_addr, (uint32_t)((2 * r) % 3) * IB, qf, sc);
+              step_softmax_pv<D, QH>(sc, va_addr, (uint32_t)((2 * r + 1) % 3) * IB, st, gs.diag,
+                                     gs.kofs, qbase, hi, scale_log2, lazy_raw, pre_pv);
+            } else {
+              pre_pv();
+            }
           }
-          // On a diagonal block, a step whose first key lies after this wave's last row is
-          // fully masked for the wave: skip it.
-          // With the union of two tiles' lists, a block the wave's tile did not select.
-          const bool other =
-              TPW == 2 && !((__builtin_amdgcn_readfirstlane(lst[e]) >> (16 + pb)) & 1);
-          if (!other && (!diag || kofs < kStep * QH * (wr + 1))) {
-            f32x16 sc[QH];
-            step_scores<D, QH>(ka_addr, slotoff, qf, sc);
-            step_softmax_pv<D, QH>(sc, va_addr, slotoff, st, diag, kofs, qbase, hi, scale_log2,
-                                   lazy_raw);
+        }
+      } else {
+        // Refill group m: K step m and V step m into ring slot m % NR.
+        auto issue = [&](uint32_t m, int jv, uint32_t slot_idx) {
+          issue_k(m, jv, slot_idx * SLOT);
+          issue_v(m, jv, slot_idx * SLOT + C::KSLOT);
+        };
+#pragma unroll
+        for (int m = 0; m < C::NR - 1; ++m) issue(m, entry_of(m), m);
+        int jn = entry_of(C::NR - 1);  // block of the next group, read one step early
+
+        // Step i (slot i % NR): wait until group i has landed (groups i+1 .. i+NR-2 may still
+        // be in flight), barrier (every wave's part of group i is in, and every wave is done
+        // with step i-1, whose slot the new group overwrites), issue group i+NR-1, then
+        // compute step i.  The loop is unrolled by NR, so each step's slot (read and refilled)
+        // is a compile-time constant.
+        for (uint32_t i0 = 0; i0 <= last; i0 += C::NR) {
+#pragma unroll
+          for (int r = 0; r < C::NR; ++r) {
+            const uint32_t i = i0 + r;
+            if (i > last) break;
+            wait_vm<(C::NR - 2) * LPW>();
+            barrier_only();
+            issue(i + C::NR - 1, jn, (uint32_t)((r + C::NR - 1) % C::NR));
+            jn = entry_of(i + C::NR);
+            const uint32_t slotoff = (uint32_t)(r * SLOT);
+            const StepGeo gs = geometry(i);
+            if (gs.run) {
+              f32x16 sc[QH];
+              step_scores<D, QH>(ka_addr, slotoff, qf, sc);
+              step_softmax_pv<D, QH>(sc, va_addr, slotoff, st, gs.diag, gs.kofs, qbase, hi,
+                                     scale_log2, lazy_raw, [] {});
+            }
           }
         }
       }
