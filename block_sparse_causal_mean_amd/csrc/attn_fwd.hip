@@ -35,7 +35,8 @@
 //               with partial vector-memory waits so a step never waits for later steps'
 //               loads.  (For 128-row tiles a 3-slot ring fits three workgroups per CU,
 //               three waves per SIMD: measured 5% faster than a 4-slot ring at two
-//               workgroups per CU; 64-row tiles use two slots, see Cfg.)
+//               workgroups per CU; 2-wave workgroups for 64-row tiles use a split ring of
+//               three single K or V^T images instead, which fits six of them per CU, see Cfg.)
 //               The template also builds 64-row waves (QH = 2: one K read feeds two products),
 //               which halves LDS operand traffic but needs over 256 registers, i.e. one wave
 //               per SIMD; on gfx950 it measured slower, so the launcher uses QH = 1.
