@@ -261,7 +261,7 @@ struct Cfg {
   // has a whole step to land, in 24 KiB instead of the 32 KiB of two full slots: six such
   // workgroups share a CU (three waves per SIMD) instead of four.
   static constexpr bool SPLIT = NW == 2;
-  static constexpr int NR = SPLIT ? 2 : 3;
+  static constexpr int NR = 3;  // slots of the 4-wave ring (a split ring is three images)
   static constexpr int RING = SPLIT ? 3 * KSLOT : NR * (KSLOT + VSLOT);  // bytes
   static constexpr int KREG = KSLOT / 1024;    // 1 KiB load regions per image
   static constexpr int VREG = VSLOT / 1024;
@@ -802,7 +802,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, QH, NW, HPW, KB>::WPE))) void attn_bf1
                 "key blocks of half or twice the tile");
   constexpr int BLK = C::BLK, ROWS = C::ROWS, NSUB = C::NSUB, DC = C::DC, DT = C::DT;
   constexpr int LPW = C::LPW;
-  // Ring of NR slots, each a K step image followed by a V^T step image.
+  // Ring of NR slots, each a K step image followed by a V^T step image; for 2-wave
+  // workgroups three single images (Cfg::SPLIT).
   constexpr int SLOT = C::KSLOT + C::VSLOT;
   __shared__ __attribute__((aligned(1024))) char ring[C::RING];
   __shared__ int lst[C::LCAP];
