@@ -157,3 +157,72 @@ def test_one_million_tokens_sampled_parity():
     err = np.abs(O - O_ref)
     say(f"[1m] {len(rows)} rows, max|O - O_ref| = {err.max():.3e}")
     assert np.all(err <= out_tol(w, api.SA_BF16, O_ref))
+
+
+MAX_BLOCKS = {
+    # 16384 key blocks of 64 keys (2^20 tokens), the most a problem may have: the mean-pooled
+    # and the bound backbone, two query heads on one kv head, d = 64, k = 4
+    "kmean": wl.WORKLOADS["llama8b_32k"].resized(seqlen=64 * 16384, n_q_heads=2, n_kv_heads=1,
+                                                 head_dim=64, k_max=4, k_min=4),
+    "bound": wl.WORKLOADS["quest_64k"].resized(seqlen=64 * 16384, n_q_heads=2, n_kv_heads=1,
+                                               head_dim=64, k_max=4, k_min=4),
+}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(MAX_BLOCKS))
+def test_most_blocks_a_problem_may_have_sampled_parity(name):
+    """16384 blocks of 64 keys, the largest block count the library admits (the selection's
+    sort keys and the gate's LDS are sized for it): every block summary bit for bit; the
+    structure of every tile's selection; sampled tiles (first, last, middle, tripped, random)
+    against oracle.select_tile bit for bit in both heads; output rows (one in every tile, and
+    one per head in each sampled tile) against the fp64 oracle."""
+    w = MAX_BLOCKS[name]
+    assert w.n_blocks == 16384 and w.n_tiles == 16384
+    say(f"[max {name}] generating inputs")
+    inp = wl.make_inputs(w)
+    d = {k: v.cuda() for k, v in inp.items()}
+    pf = api.Prefill(w)
+    say(f"[max {name}] GPU pipeline")
+    pf.run(d["Q"], d["K"], d["V"])
+    torch.cuda.synchronize()
+    g = {"kv_idx": pf.kv_idx.cpu().numpy(), "kv_cnt": pf.kv_cnt.cpu().numpy(),
+         "sigma": pf.sigma.cpu().numpy(), "sigma_bar": pf.sigma_bar.cpu().numpy(),
+         "gate": pf.gate.cpu().numpy(), "tau": pf.tau.cpu().numpy()}
+    check_structure(w, g["kv_idx"], g["kv_cnt"], g["gate"], g["sigma"], g["sigma_bar"], g["tau"])
+    say(f"[max {name}] structure ok, {int(g['gate'].sum())} tripped tiles of {w.n_tiles}")
+    cfg = oracle.make_cfg(w)
+    summ = oracle.pool(cfg, inp["K"], inp["V"])
+    planes = 2 if w.score_mode == wl.KMINMAX else 1
+    plane = w.n_blocks * w.n_kv_heads * w.head_dim
+    got = bits(pf.summ[:planes * plane].cpu().numpy())
+    np.testing.assert_array_equal(got[:plane], bits(summ["kA"].reshape(-1)))
+    if planes == 2:
+        np.testing.assert_array_equal(got[plane:], bits(summ["kB"].reshape(-1)))
+    say(f"[max {name}] summaries equal")
+    rng = np.random.default_rng(13)
+    tiles = _sample_tiles(w.n_tiles, g["gate"][0], rng)
+    rows = []
+    for t in tiles:
+        one = oracle.select_tile(cfg, inp["Q"], summ, 0, t)
+        np.testing.assert_array_equal(bits(g["sigma"][0, :, t]), bits(one["sigma"]))
+        assert bits(g["sigma_bar"][0, t]) == bits(one["sigma_bar"])
+        tr = int(g["gate"][0, t])
+        np.testing.assert_array_equal(g["kv_cnt"][0, :, t], one["cnts"][tr])
+        np.testing.assert_array_equal(g["kv_idx"][0, :, t, :],
+                                      one["lists"][tr][:, :g["kv_idx"].shape[-1]])
+        for h in range(w.n_q_heads):
+            rows.append((0, h, t * w.tile + int(rng.integers(w.tile))))
+        say(f"[max {name}] tile {t} (tripped {tr}) matches the oracle")
+    # and one random (head, row) of every tile
+    heads = rng.integers(w.n_q_heads, size=w.n_tiles)
+    offs = rng.integers(w.tile, size=w.n_tiles)
+    rows += [(0, int(heads[t]), t * w.tile + int(offs[t])) for t in range(w.n_tiles)]
+    rows = np.array(rows, np.int64)
+    O_ref, _ = oracle.forward(cfg, inp["Q"], inp["K"], inp["V"], g["kv_idx"], g["kv_cnt"],
+                              pf.scale, rows=rows)
+    r = torch.as_tensor(rows, device="cuda")
+    O = pf.O[r[:, 0], r[:, 2], r[:, 1]].float().cpu().numpy().astype(np.float64)
+    err = np.abs(O - O_ref)
+    say(f"[max {name}] {len(rows)} rows, max|O - O_ref| = {err.max():.3e}")
+    assert np.all(err <= out_tol(w, api.SA_BF16, O_ref))
